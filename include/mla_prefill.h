@@ -1,0 +1,223 @@
+/*
+ * mla_prefill.h -- C ABI of the MI355X (gfx950) MLA varlen-prefill library.
+ *
+ * Two operations, each defined by one Ascend Transformer Boost C API page:
+ *
+ *   mla_prefill_get_workspace_size / mla_prefill
+ *     "MLA Prefill" page, Definition and the AtbMLAPreFillGetWorkspaceSize
+ *     Members table. For every sequence b of a variable-length batch and every
+ *     query head h it computes
+ *         S  = qkScale * (Q . K^T + QRope . KRope^T) + mask
+ *         O  = softmax_rows(S) . V
+ *     with a split head: an embeddimV-element "nope" part (Q, K, V) and a
+ *     64-element rope part (QRope, KRope). The page's two-phase protocol
+ *     (plan the workspace, then run) is kept; the page's atb::Operation and
+ *     atb::Context handles are replaced by a stateless call that takes the
+ *     same arguments twice plus a HIP stream.
+ *
+ *   paged_cache_load
+ *     "PagedCacheLoadOperation" page, Definition and Members table. Copies the
+ *     tokens of each sequence out of a block-paged K/V cache into packed
+ *     key/value tensors. The page's plan phase is folded in: the gather needs
+ *     no workspace.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are passed as mla_tensor descriptors: a data pointer, a dtype
+ *     code and a row-major shape. Every tensor is dense and row-major ("ND"
+ *     on the pages). Device tensors must be 16-byte aligned.
+ *   - Ownership: the caller owns every tensor, the workspace and the stream.
+ *     The library allocates and frees no device memory and keeps no pointer
+ *     after a call returns. Host arrays are read before the call returns.
+ *   - Calls that take a stream only enqueue work on it (hipStream_t passed as
+ *     void*; NULL is the default stream) and return without synchronising.
+ *   - Return value: MLA_OK (0) or a negative MLA_ERR_* code. Arguments are
+ *     validated completely before any HIP call: on an error nothing is
+ *     enqueued and no output is touched. mla_last_error() returns a
+ *     thread-local message describing the last failure of the calling thread.
+ *   - The library holds no state and is safe to call from several threads.
+ */
+#ifndef MLA_PREFILL_H
+#define MLA_PREFILL_H
+
+#include <stdbool.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. The pages allow float16/bf16 for attention data and
+ * float16/bf16/int8 for paged caches; int32 is used for lengths and tables. */
+enum mla_dtype {
+    MLA_FP16 = 1,
+    MLA_BF16 = 2,
+    MLA_INT8 = 3,
+    MLA_INT32 = 4
+};
+
+/* maskType. The "MLA Prefill" page names the modes (Members table, rows
+ * Mask and maskType) but prints no integer values; these are ours.
+ *   MLA_MASK_UNDEFINED  all-zero mask: every key of the sequence is visible.
+ *   MLA_MASK_SPEC       causal, bottom-right aligned (query i of a sequence
+ *                       sits at key position kvSeqLen - qSeqLen + i and sees
+ *                       keys 0..that position). With qSeqLen == 1 the single
+ *                       query sees every key, i.e. the mask only acts when
+ *                       qSeqLen > 1.
+ *   MLA_MASK_CAUSAL     same visibility rule as MLA_MASK_SPEC.
+ *   MLA_MASK_FREE       a 512 x 512 tile (argument mask) placed on the
+ *                       diagonal 512-blocks of key-position space: for a
+ *                       query at position p and key j, blocks with
+ *                       j/512 < p/512 are fully visible, j/512 > p/512 fully
+ *                       masked, and j/512 == p/512 adds
+ *                       mask[p % 512][j % 512]. A causal tile (0 on and below
+ *                       the diagonal, -inf above) reproduces MLA_MASK_CAUSAL. */
+enum mla_mask_type {
+    MLA_MASK_UNDEFINED = 0,
+    MLA_MASK_SPEC = 1,
+    MLA_MASK_CAUSAL = 2,
+    MLA_MASK_FREE = 3
+};
+
+/* kvCacheCfg ("PagedCacheLoadOperation" page, Members table): NZ = 0 is the
+ * page's default, ND = 1. Only ND is implemented; NZ returns
+ * MLA_ERR_UNSUPPORTED. */
+enum mla_kv_cache_cfg {
+    MLA_KV_CACHE_NZ = 0,
+    MLA_KV_CACHE_ND = 1
+};
+
+/* Status codes (0 = success, like atb::Status on the pages). */
+enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_NULL = -1,        /* a required pointer or descriptor is NULL */
+    MLA_ERR_SHAPE = -2,       /* a shape disagrees with the others or with the lengths */
+    MLA_ERR_DTYPE = -3,       /* a dtype is not allowed or dtypes disagree */
+    MLA_ERR_VALUE = -4,       /* a scalar argument or length is out of range */
+    MLA_ERR_UNSUPPORTED = -5, /* a valid request this build does not implement */
+    MLA_ERR_WORKSPACE = -6,   /* workspace NULL, too small or misaligned */
+    MLA_ERR_RUNTIME = -7      /* a HIP call failed (no device, launch error, ...) */
+};
+
+/* Dense row-major tensor. shape[0..ndim-1] are used; ndim is 1..4. */
+typedef struct mla_tensor {
+    void *data;
+    int32_t dtype;     /* enum mla_dtype */
+    int32_t ndim;
+    int64_t shape[4];
+} mla_tensor;
+
+/*
+ * mla_prefill_get_workspace_size -- plan phase of "MLA Prefill"
+ * (AtbMLAPreFillGetWorkspaceSize on the page). Host only: no HIP call.
+ *
+ * Arguments (the page's Members table, same order):
+ *   q          device, [nTokens, headNum*D] or [nTokens, headNum, D], fp16/bf16.
+ *              nTokens = sum of q_seqlen. D = embeddimV; this build runs D = 128.
+ *   q_rope     device, [nTokens, headNum*64] or [nTokens, headNum, 64], same dtype.
+ *   k          device, packed [sum kv_seqlen, kvHeadNum, D], or padded
+ *              [batch, max_seq, kvHeadNum*D] (sequence b's keys start at row
+ *              b*max_seq). A shape valid both ways is read as packed.
+ *   k_rope     device, like k with 64 in place of D.
+ *   v          device, like k.
+ *   q_seqlen   HOST int32 [batch], each >= 0.
+ *   kv_seqlen  HOST int32 [batch], each >= 0. qSeqLen may exceed kvSeqLen;
+ *              under a causal mode the rows with no visible key return 0.
+ *   mask       device [512, 512] fp16/bf16, additive; required for
+ *              MLA_MASK_FREE, ignored (may be NULL) otherwise. Its dtype may
+ *              differ from the data dtype.
+ *   head_num   query heads (> 0).
+ *   qk_scale   finite float multiplying the whole 192-deep product, rope
+ *              term included, before the mask is added.
+ *   kv_head_num  KV heads (> 0, divides head_num). Query head h reads KV
+ *              head h / (head_num / kv_head_num).
+ *   mask_type  enum mla_mask_type.
+ *   cache_mode only 0 (K/V given as contiguous tensors) is accepted; the page
+ *              documents no other value. Other values: MLA_ERR_UNSUPPORTED.
+ *   atten_out  device, [nTokens, headNum*D] or [nTokens, headNum, D], same dtype as q.
+ *   workspace_size  out: bytes of device workspace mla_prefill needs.
+ * A row of a sequence that sees no key (kv_seqlen 0, or fully masked) is
+ * written as zeros.
+ */
+int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,
+                                   const mla_tensor *k, const mla_tensor *k_rope,
+                                   const mla_tensor *v, const mla_tensor *q_seqlen,
+                                   const mla_tensor *kv_seqlen, const mla_tensor *mask,
+                                   int32_t head_num, float qk_scale, int32_t kv_head_num,
+                                   int32_t mask_type, uint8_t cache_mode,
+                                   const mla_tensor *atten_out, uint64_t *workspace_size);
+
+/*
+ * mla_prefill -- run phase of "MLA Prefill" (AtbMLAPreFill on the page).
+ * The first 14 arguments are those of mla_prefill_get_workspace_size, with
+ * the same values. workspace: device memory of at least the planned size,
+ * 16-byte aligned (NULL allowed when the planned size is 0). The call copies
+ * a work list built from the host lengths into the workspace and enqueues the
+ * attention kernel on stream; the workspace must stay untouched until that
+ * work has run. Errors: validation codes as above, MLA_ERR_WORKSPACE,
+ * MLA_ERR_RUNTIME when a HIP call fails.
+ */
+int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
+                const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
+                const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
+                const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
+                void *stream);
+
+/*
+ * paged_cache_load -- "PagedCacheLoadOperation" page (AtbPagedCacheLoad).
+ *
+ *   key_cache     device ND [num_blocks, block_size, num_heads, head_size_k],
+ *                 fp16/bf16/int8.
+ *   value_cache   device ND [num_blocks, block_size, num_heads, head_size_v], same
+ *                 dtype, num_blocks and block_size; or NULL to gather keys only
+ *                 (then value must be NULL too).
+ *   block_tables  device int32 [batch, max_blocks]: block ids of each sequence.
+ *   context_lens  device int32. Plain mode: [batch] token counts. Cumulative
+ *                 mode (is_seq_lens_cumsum_type): running totals, either
+ *                 [batch + 1] starting with 0 or [batch] inclusive totals.
+ *   key, value    device outputs [num_tokens, num_heads, head_size_k / _v] of the
+ *                 cache dtype, num_tokens = total tokens gathered; sequence b's
+ *                 tokens are packed in batch order.
+ *   seq_starts    device int32 [batch]: token offset of each sequence inside its
+ *                 block table's logical space. Read only when has_seq_starts;
+ *                 otherwise every sequence starts at 0 and it may be NULL.
+ *   kv_cache_cfg  MLA_KV_CACHE_ND (1). MLA_KV_CACHE_NZ: MLA_ERR_UNSUPPORTED.
+ *
+ * Token t of sequence b is logical position s_b + t, found in block
+ * block_tables[b][(s_b + t) / block_size] at slot (s_b + t) % block_size. The
+ * copy is bit-exact. Lengths and tables live on the device, so the host cannot
+ * check them: a token whose output row lies beyond num_tokens, whose table
+ * column lies beyond max_blocks, or whose block id lies outside
+ * [0, num_blocks) is not written.
+ */
+int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
+                     const mla_tensor *block_tables, const mla_tensor *context_lens,
+                     const mla_tensor *key, const mla_tensor *value,
+                     const mla_tensor *seq_starts, int8_t kv_cache_cfg,
+                     bool is_seq_lens_cumsum_type, bool has_seq_starts, void *stream);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char *mla_last_error(void);
+
+/*
+ * mla_prefill_plan_host -- host-only view of the work list mla_prefill copies
+ * into its workspace, for inspection and tests. Writes, into buf (host
+ * memory of buf_size bytes), the same bytes mla_prefill would place at the
+ * start of the workspace: batch records {q_offset, kv_offset, q_len, kv_len}
+ * (int32 each), then work items {batch, first_q_row, kv_tiles, 0} (int32
+ * each), heaviest first. kv_padded_max_seq: 0 for packed K/V, else max_seq of
+ * the padded layout. *n_items receives the number of work items; one item
+ * covers MLA_PLAN_Q_ROWS query rows and its kv_tiles tiles of
+ * MLA_PLAN_KV_COLS keys each. Returns MLA_ERR_WORKSPACE if buf is too small.
+ */
+#define MLA_PLAN_Q_ROWS 128
+#define MLA_PLAN_KV_COLS 64
+int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch,
+                          int32_t mask_type, int64_t kv_padded_max_seq, void *buf,
+                          uint64_t buf_size, int32_t *n_items);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PREFILL_H */

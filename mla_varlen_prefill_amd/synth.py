@@ -1,0 +1,160 @@
+"""Seeded synthetic workloads for MLA varlen prefill and the paged gather.
+
+This module only draws inputs: lengths, random tensors, block tables and mask
+tiles. It holds none of the attention or gather arithmetic, so the CPU oracle
+and the HIP path can both be fed from it without sharing any computation.
+
+Workloads (shapes follow the Ascend Transformer Boost "MLA Prefill" and
+"PagedCacheLoadOperation" pages' Members tables; the pages name no dataset,
+so these synthetic inputs are the workload):
+
+  tiny      batch 2, q = kv = {17, 40}, 4 heads, bf16 N(0, 1), causal
+  single    batch 1, q = kv = 4096, 128 heads, bf16 N(0, 1), causal
+  varlen    16 sequences, q = kv ~ U{128..8192}, 128 heads, fp16 N(0, 0.5), causal
+  chunked   batch 8, kv = 16384, q = 2048 (last 2048 positions), 128 heads, bf16
+  paged     32 sequences, ctx ~ U{1024..32768}, block size 128, 128 heads, bf16,
+            block tables = a seeded permutation of all block ids
+
+All use embeddimV = 128, rope 64 and qkScale = 1/sqrt(192).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+D_NOPE = 128
+D_ROPE = 64
+MASK_TILE = 512
+BLOCK_SIZE = 128
+
+MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
+
+WORKLOADS = {
+    "tiny": dict(batch=2, heads=4, kv_heads=4, dtype=torch.bfloat16, sigma=1.0, seed=0),
+    "single": dict(batch=1, heads=128, kv_heads=128, dtype=torch.bfloat16, sigma=1.0, seed=1),
+    "varlen": dict(batch=16, heads=128, kv_heads=128, dtype=torch.float16, sigma=0.5, seed=2),
+    "chunked": dict(batch=8, heads=128, kv_heads=128, dtype=torch.bfloat16, sigma=1.0, seed=3),
+    "paged": dict(batch=32, heads=128, kv_heads=128, dtype=torch.bfloat16, sigma=1.0, seed=4),
+}
+
+QK_SCALE = 1.0 / math.sqrt(D_NOPE + D_ROPE)
+
+
+def workload_seqlens(name: str, seed: int | None = None):
+    """(q_seqlen, kv_seqlen) int32 numpy arrays of a named workload."""
+    w = WORKLOADS[name]
+    seed = w["seed"] if seed is None else seed
+    if name == "tiny":
+        q = np.array([17, 40], dtype=np.int32)
+        return q, q.copy()
+    if name == "single":
+        q = np.array([4096], dtype=np.int32)
+        return q, q.copy()
+    if name == "varlen":
+        rng = np.random.default_rng(seed)
+        q = rng.integers(128, 8192, size=16, endpoint=True).astype(np.int32)
+        return q, q.copy()
+    if name == "chunked":
+        return np.full(8, 2048, dtype=np.int32), np.full(8, 16384, dtype=np.int32)
+    if name == "paged":
+        rng = np.random.default_rng(seed)
+        ctx = rng.integers(1024, 32768, size=32, endpoint=True).astype(np.int32)
+        return ctx, ctx.copy()
+    raise KeyError(name)
+
+
+def _randn(shape, dtype, sigma, seed, device):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(dtype)
+
+
+def attention_inputs(q_seqlen, kv_seqlen, heads, kv_heads, dtype=torch.bfloat16, sigma=1.0,
+                     seed=0, device="cpu", d_nope=D_NOPE, d_rope=D_ROPE, kv_padded_max_seq=0):
+    """Seeded Q, QRope, K, KRope, V in packed varlen layout.
+
+    Q [sum q, H, D], QRope [sum q, H, 64]; K, V [sum kv, Hkv, D], KRope
+    [sum kv, Hkv, 64]. With kv_padded_max_seq > 0, K/KRope/V are instead
+    [batch, max_seq, Hkv * dim] with rows past each sequence's length drawn too.
+    Values: N(0, sigma^2) drawn in fp32 from torch.Generator(seed * 100 + k),
+    k = 0..4, then rounded to dtype.
+    """
+    nq = int(np.sum(q_seqlen))
+    nk = int(np.sum(kv_seqlen))
+    base = int(seed) * 100
+    t = {}
+    t["q"] = _randn((nq, heads, d_nope), dtype, sigma, base + 0, device)
+    t["q_rope"] = _randn((nq, heads, d_rope), dtype, sigma, base + 1, device)
+    if kv_padded_max_seq:
+        b = len(q_seqlen)
+        m = int(kv_padded_max_seq)
+        t["k"] = _randn((b, m, kv_heads * d_nope), dtype, sigma, base + 2, device)
+        t["k_rope"] = _randn((b, m, kv_heads * d_rope), dtype, sigma, base + 3, device)
+        t["v"] = _randn((b, m, kv_heads * d_nope), dtype, sigma, base + 4, device)
+    else:
+        t["k"] = _randn((nk, kv_heads, d_nope), dtype, sigma, base + 2, device)
+        t["k_rope"] = _randn((nk, kv_heads, d_rope), dtype, sigma, base + 3, device)
+        t["v"] = _randn((nk, kv_heads, d_nope), dtype, sigma, base + 4, device)
+    return t
+
+
+def workload_inputs(name: str, device="cpu", seed: int | None = None):
+    """Inputs of a named workload: (tensors, q_seqlen, kv_seqlen, params)."""
+    w = WORKLOADS[name]
+    seed = w["seed"] if seed is None else seed
+    qs, ks = workload_seqlens(name, seed)
+    t = attention_inputs(qs, ks, w["heads"], w["kv_heads"], w["dtype"], w["sigma"], seed, device)
+    params = dict(head_num=w["heads"], kv_head_num=w["kv_heads"], qk_scale=QK_SCALE,
+                  mask_type=MASK_CAUSAL)
+    return t, qs, ks, params
+
+
+def causal_mask_tile(dtype=torch.float16, device="cpu"):
+    """512 x 512 tile: 0 where column <= row, -inf above the diagonal."""
+    tile = torch.zeros((MASK_TILE, MASK_TILE), dtype=torch.float32)
+    upper = torch.ones((MASK_TILE, MASK_TILE), dtype=torch.bool).triu(1)
+    tile[upper] = float("-inf")
+    return tile.to(dtype).to(device)
+
+
+def random_mask_tile(seed, dtype=torch.float16, device="cpu", p_masked=0.2, scale=2.0):
+    """Seeded 512 x 512 tile of finite N(0, scale^2) values with a fraction of -inf
+    entries, the diagonal kept finite so every query row keeps a visible key."""
+    rng = np.random.default_rng(seed)
+    tile = rng.standard_normal((MASK_TILE, MASK_TILE)) * scale
+    tile[rng.random((MASK_TILE, MASK_TILE)) < p_masked] = -np.inf
+    np.fill_diagonal(tile, rng.standard_normal(MASK_TILE))
+    return torch.from_numpy(tile.astype(np.float32)).to(dtype).to(device)
+
+
+def paged_inputs(context_lens, heads=128, head_size_k=D_NOPE, head_size_v=D_NOPE,
+                 head_size_rope=D_ROPE, block_size=BLOCK_SIZE, dtype=torch.bfloat16,
+                 seed=4, device="cpu", with_rope=True):
+    """Paged caches and a block table for the given context lengths.
+
+    num_blocks = batch * ceil(max_ctx / block_size); the table is a seeded
+    permutation of all block ids reshaped to [batch, ceil(max_ctx / block_size)],
+    so unused tail columns still hold valid ids. Caches are fully drawn.
+    """
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    batch = len(ctx)
+    cols = int(-(-int(ctx.max()) // block_size)) if batch else 1
+    num_blocks = batch * cols
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(num_blocks).astype(np.int32).reshape(batch, cols)
+    base = int(seed) * 100
+    out = {
+        "block_tables": torch.from_numpy(table).to(device),
+        "context_lens": torch.from_numpy(ctx.astype(np.int32)).to(device),
+        "key_cache": _randn((num_blocks, block_size, heads, head_size_k), dtype, 1.0, base + 5, device),
+        "value_cache": _randn((num_blocks, block_size, heads, head_size_v), dtype, 1.0, base + 6, device),
+    }
+    if with_rope:
+        out["rope_cache"] = _randn((num_blocks, block_size, heads, head_size_rope), dtype, 1.0,
+                                   base + 7, device)
+    return out

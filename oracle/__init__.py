@@ -1,0 +1,196 @@
+"""CPU oracle for MLA varlen prefill and the paged cache gather.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``. The product package never imports
+it, and it shares no code, tables or helpers with the HIP path.
+
+* ``attention_head`` / ``attention`` wrap ``oracle.c``: plain fp64 softmax
+  attention written from the Ascend Transformer Boost "MLA Prefill" C API page
+  (Definition; AtbMLAPreFillGetWorkspaceSize Members table).
+* ``paged_cache_load`` is a plain numpy gather written from the Ascend
+  Transformer Boost "PagedCacheLoadOperation" page (Members table: keyCache,
+  valueCache, blockTables, contextLens, seqStarts, isSeqLensCumsumType,
+  hasSeqStarts), ND cache layout.
+
+Mask-type codes (the page names the modes but prints no integer values):
+UNDEFINED 0, SPEC 1, CAUSAL 2, MASK_FREE 3.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
+MASK_TILE = 512
+
+_lib = None
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """Compile the C oracle with gcc (IEEE arithmetic: no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = LIB):
+    """Load a compiled oracle library (building it first if it is missing)."""
+    global _lib
+    if path == LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lp = ctypes.POINTER(ctypes.c_long)
+    lib.oracle_attention_head.argtypes = [dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_long,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                          ctypes.c_int, dp, lp, ctypes.c_long, dp, dp]
+    lib.oracle_attention_head.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
+    if path == LIB:
+        _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops run on (OMP_NUM_THREADS or all cores)."""
+    return int(load().oracle_num_threads())
+
+
+def _dptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attention_head(q, qr, k, kr, v, qk_scale, mask_type, mask=None, rows=None,
+                   return_weights=False, lib=None):
+    """Attention for one (sequence, query head).
+
+    q [qlen, D], qr [qlen, R], k [kvlen, D], kr [kvlen, R], v [kvlen, Dv]: values
+    already converted exactly to float64. ``rows`` selects query rows (default
+    all). Query row i sits at key position kvlen - qlen + i. Returns
+    out [n_rows, Dv] (and the softmax weights [n_rows, kvlen] if asked).
+    """
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    qr = np.ascontiguousarray(qr, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    kr = np.ascontiguousarray(kr, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    qlen, d_nope = q.shape
+    kvlen = k.shape[0]
+    d_rope = qr.shape[1]
+    d_v = v.shape[1]
+    assert qr.shape == (qlen, d_rope) and kr.shape == (kvlen, d_rope)
+    assert k.shape == (kvlen, d_nope) and v.shape[0] == kvlen
+    rows = np.arange(qlen, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), d_v), dtype=np.float64)
+    weights = np.zeros((len(rows), kvlen), dtype=np.float64) if return_weights else None
+    tile = None
+    if mask_type == MASK_FREE:
+        tile = np.ascontiguousarray(mask, dtype=np.float64)
+        assert tile.shape == (MASK_TILE, MASK_TILE)
+    rc = lib.oracle_attention_head(
+        _dptr(q), _dptr(qr), _dptr(k), _dptr(kr), _dptr(v), qlen, kvlen, d_nope, d_rope, d_v,
+        float(qk_scale), int(mask_type), _dptr(tile) if tile is not None else None,
+        rows.ctypes.data_as(ctypes.POINTER(ctypes.c_long)), len(rows), _dptr(out),
+        _dptr(weights) if weights is not None else None)
+    if rc != 0:
+        raise ValueError("oracle_attention_head rejected its arguments")
+    return (out, weights) if return_weights else out
+
+
+def kv_head_of(h: int, head_num: int, kv_head_num: int) -> int:
+    """Query head h reads kv head h // (headNum / kvHeadNum): contiguous groups."""
+    return h // (head_num // kv_head_num)
+
+
+def attention(q, qr, k, kr, v, q_seqlen, kv_seqlen, head_num, kv_head_num, qk_scale,
+              mask_type, mask=None, kv_padded=False, lib=None):
+    """Full varlen problem.
+
+    q [sum qlen, H, D], qr [sum qlen, H, R]; k/kr/v packed [sum kvlen, Hkv, *] or,
+    with ``kv_padded``, [batch, max_seq, Hkv, *]. Returns [sum qlen, H, Dv] float64.
+    """
+    q_seqlen = [int(x) for x in q_seqlen]
+    kv_seqlen = [int(x) for x in kv_seqlen]
+    assert len(q_seqlen) == len(kv_seqlen)
+    assert head_num > 0 and kv_head_num > 0 and head_num % kv_head_num == 0
+    d_v = v.shape[-1]
+    out = np.zeros((q.shape[0], head_num, d_v), dtype=np.float64)
+    qoff = 0
+    koff = 0
+    for b, (ql, kl) in enumerate(zip(q_seqlen, kv_seqlen)):
+        for h in range(head_num):
+            hk = kv_head_of(h, head_num, kv_head_num)
+            if kv_padded:
+                ks, krs, vs = k[b, :kl, hk], kr[b, :kl, hk], v[b, :kl, hk]
+            else:
+                ks, krs, vs = k[koff:koff + kl, hk], kr[koff:koff + kl, hk], v[koff:koff + kl, hk]
+            out[qoff:qoff + ql, h] = attention_head(q[qoff:qoff + ql, h], qr[qoff:qoff + ql, h],
+                                                    ks, krs, vs, qk_scale, mask_type, mask, lib=lib)
+        qoff += ql
+        koff += kl
+    return out
+
+
+def sequence_spans(context_lens, batch, is_cumsum):
+    """(offset, length) of each batch's rows in the packed gather output.
+
+    Plain mode: contextLens[b] is the length, offsets are running sums.
+    Cumsum mode: contextLens holds running totals, either [batch + 1] with a
+    leading 0 or [batch] inclusive totals.
+    """
+    ctx = [int(x) for x in context_lens]
+    spans = []
+    if not is_cumsum:
+        assert len(ctx) == batch
+        off = 0
+        for n in ctx:
+            spans.append((off, n))
+            off += n
+    elif len(ctx) == batch + 1:
+        spans = [(ctx[b], ctx[b + 1] - ctx[b]) for b in range(batch)]
+    else:
+        assert len(ctx) == batch
+        prev = 0
+        for b in range(batch):
+            spans.append((prev, ctx[b] - prev))
+            prev = ctx[b]
+    return spans
+
+
+def paged_cache_load(key_cache, value_cache, block_tables, context_lens, seq_starts=None,
+                     is_seq_lens_cumsum=False, has_seq_starts=False):
+    """Gather each sequence's tokens out of a block-paged ND cache.
+
+    key_cache [num_blocks, block_size, heads, head_size_k] (any dtype: a byte
+    copy), block_tables [batch, max_blocks] int, context_lens [batch] or
+    [batch+1]. Token t of sequence b is cache position s_b + t, which lives in
+    block block_tables[b][(s_b + t) // block_size] at slot (s_b + t) % block_size;
+    s_b = seq_starts[b] when has_seq_starts, else 0. Returns (key, value); value
+    is None when value_cache is None.
+    """
+    block_tables = np.asarray(block_tables)
+    batch = block_tables.shape[0]
+    block_size = key_cache.shape[1]
+    spans = sequence_spans(context_lens, batch, is_seq_lens_cumsum)
+    total = sum(n for _, n in spans)
+    key = np.zeros((total,) + key_cache.shape[2:], dtype=key_cache.dtype)
+    value = None if value_cache is None else np.zeros((total,) + value_cache.shape[2:], dtype=value_cache.dtype)
+    for b, (off, n) in enumerate(spans):
+        start = int(seq_starts[b]) if has_seq_starts else 0
+        pos = start + np.arange(n)
+        blocks = block_tables[b, pos // block_size]
+        slots = pos % block_size
+        key[off:off + n] = key_cache[blocks, slots]
+        if value is not None:
+            value[off:off + n] = value_cache[blocks, slots]
+    return key, value

@@ -1,0 +1,59 @@
+"""Float64 brute force for MLA prefill attention, used to pin the C oracle.
+
+Built by a different route from ``oracle/oracle.c`` on purpose:
+* queries and keys are concatenated ([Q | QRope], [K | KRope]) and multiplied
+  as whole matrices;
+* KV heads are expanded with ``np.repeat`` instead of an index formula;
+* the mask is materialised as a full [q_len, kv_len] matrix, causal via
+  ``np.tril`` with a diagonal offset and MASK_FREE by pasting the 512 x 512
+  tile into a block matrix of key-position space.
+Follows the "MLA Prefill" page's Members table (Q, QRope, K, kRope, V,
+qkScale, Mask, maskType) read as: scale the whole product, then add the mask.
+"""
+import numpy as np
+
+TILE = 512
+UNDEFINED, SPEC, CAUSAL, FREE = 0, 1, 2, 3
+
+
+def mask_matrix(q_len, kv_len, mask_type, tile=None):
+    if mask_type == UNDEFINED:
+        return np.zeros((q_len, kv_len))
+    if mask_type in (SPEC, CAUSAL):
+        keep = np.tril(np.ones((q_len, kv_len), dtype=bool), k=kv_len - q_len)
+        return np.where(keep, 0.0, -np.inf)
+    assert mask_type == FREE
+    nblk = max(1, -(-kv_len // TILE))
+    big = np.full((nblk * TILE, nblk * TILE), -np.inf)
+    for rb in range(nblk):
+        rows = slice(rb * TILE, (rb + 1) * TILE)
+        big[rows, : rb * TILE] = 0.0
+        big[rows, rb * TILE:(rb + 1) * TILE] = tile
+    m = np.full((q_len, kv_len), -np.inf)
+    for i in range(q_len):
+        p = kv_len - q_len + i
+        if p >= 0:
+            m[i] = big[p, :kv_len]
+    return m
+
+
+def attention(q, qr, k, kr, v, q_seqlen, kv_seqlen, heads, kv_heads, scale, mask_type, tile=None):
+    q_all = np.concatenate([q, qr], axis=-1)
+    k_all = np.repeat(np.concatenate([k, kr], axis=-1), heads // kv_heads, axis=1)
+    v_all = np.repeat(v, heads // kv_heads, axis=1)
+    out = np.zeros((q.shape[0], heads, v.shape[-1]))
+    qo = ko = 0
+    for ql, kl in zip(q_seqlen, kv_seqlen):
+        ql, kl = int(ql), int(kl)
+        m = mask_matrix(ql, kl, mask_type, tile)
+        for h in range(heads):
+            s = scale * (q_all[qo:qo + ql, h] @ k_all[ko:ko + kl, h].T) + m
+            for i in range(ql):
+                row = s[i]
+                if kl == 0 or not np.isfinite(row).any():
+                    continue
+                e = np.exp(row - row.max())
+                out[qo + i, h] = (e / e.sum()) @ v_all[ko:ko + kl, h]
+        qo += ql
+        ko += kl
+    return out

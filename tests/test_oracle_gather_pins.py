@@ -1,0 +1,98 @@
+"""Pins of the paged-gather oracle ("PagedCacheLoadOperation" page, Members
+table) against round trips and identities the page's definitions fix."""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def scatter_to_cache(rows, lens, table, block_size, num_blocks, starts=None):
+    """Place each sequence's contiguous rows into a paged cache (the inverse of
+    the gather, written as a plain per-token loop)."""
+    cache = np.full((num_blocks, block_size) + rows.shape[1:], -7, dtype=rows.dtype)
+    off = 0
+    for b, n in enumerate(lens):
+        s = 0 if starts is None else int(starts[b])
+        for t in range(n):
+            pos = s + t
+            cache[table[b][pos // block_size], pos % block_size] = rows[off + t]
+        off += n
+    return cache
+
+
+def test_round_trip_through_permuted_table():
+    rng = np.random.default_rng(0)
+    bs, lens = 4, [5, 12, 1, 8]
+    cols = max(-(-n // bs) for n in lens)
+    nb = len(lens) * cols
+    table = rng.permutation(nb).reshape(len(lens), cols).astype(np.int32)
+    rows = rng.integers(-1000, 1000, size=(sum(lens), 3, 5)).astype(np.int16)
+    cache = scatter_to_cache(rows, lens, table, bs, nb)
+    key, value = oracle.paged_cache_load(cache, cache[:, :, :, :2], table, lens)
+    assert np.array_equal(key, rows)
+    assert np.array_equal(value, rows[:, :, :2])
+
+
+def test_identity_table_is_a_reshape():
+    rng = np.random.default_rng(1)
+    bs, nbps = 8, 3
+    cache = rng.integers(0, 255, size=(2 * nbps, bs, 2, 4)).astype(np.uint8)
+    table = np.arange(2 * nbps, dtype=np.int32).reshape(2, nbps)
+    key, _ = oracle.paged_cache_load(cache, None, table, [bs * nbps, bs * nbps])
+    assert np.array_equal(key, cache.reshape(-1, 2, 4))
+
+
+def test_cumsum_forms_equal_plain_lengths():
+    rng = np.random.default_rng(2)
+    bs, lens = 4, [3, 9, 0, 6]
+    nb = 4 * 3
+    table = rng.permutation(nb).reshape(4, 3).astype(np.int32)
+    cache = rng.standard_normal((nb, bs, 2, 2)).astype(np.float32)
+    plain, _ = oracle.paged_cache_load(cache, None, table, lens)
+    inclusive = np.cumsum(lens)
+    exclusive = np.concatenate([[0], inclusive])
+    a, _ = oracle.paged_cache_load(cache, None, table, inclusive, is_seq_lens_cumsum=True)
+    b, _ = oracle.paged_cache_load(cache, None, table, exclusive, is_seq_lens_cumsum=True)
+    assert np.array_equal(a, plain) and np.array_equal(b, plain)
+
+
+def test_seq_start_shift_identity():
+    """gather(len, start s) equals gather(len + s, start 0) without its first s rows."""
+    rng = np.random.default_rng(3)
+    bs, nb = 4, 24
+    table = rng.permutation(nb).reshape(3, 8).astype(np.int32)
+    cache = rng.standard_normal((nb, bs, 1, 3)).astype(np.float32)
+    lens, starts = [5, 7, 2], [3, 10, 0]
+    shifted, _ = oracle.paged_cache_load(cache, None, table, lens, seq_starts=starts,
+                                         has_seq_starts=True)
+    longer, _ = oracle.paged_cache_load(cache, None, table, [n + s for n, s in zip(lens, starts)])
+    off_long = np.concatenate([[0], np.cumsum([n + s for n, s in zip(lens, starts)])])
+    expect = np.concatenate([longer[off_long[b] + starts[b]:off_long[b + 1]] for b in range(3)])
+    assert np.array_equal(shifted, expect)
+    # with has_seq_starts false the starts are ignored
+    ignored, _ = oracle.paged_cache_load(cache, None, table, lens, seq_starts=starts,
+                                         has_seq_starts=False)
+    zero, _ = oracle.paged_cache_load(cache, None, table, lens, seq_starts=[0, 0, 0],
+                                      has_seq_starts=True)
+    assert np.array_equal(ignored, zero)
+
+
+def test_round_trip_with_seq_starts():
+    rng = np.random.default_rng(4)
+    bs, lens, starts = 8, [9, 4], [6, 17]
+    cols = 4
+    table = rng.permutation(2 * cols).reshape(2, cols).astype(np.int32)
+    rows = rng.standard_normal((sum(lens), 2, 2)).astype(np.float32)
+    cache = scatter_to_cache(rows, lens, table, bs, 2 * cols, starts)
+    key, _ = oracle.paged_cache_load(cache, None, table, lens, seq_starts=starts,
+                                     has_seq_starts=True)
+    assert np.array_equal(key, rows)
+
+
+def test_page_block_table_width_formula():
+    """The page gives blockTables as [len(contextLens), (max(contextLens) - 1)
+    // block_size + 1]: the widest sequence uses exactly that many blocks."""
+    lens, bs = [1, 128, 129, 300], 128
+    width = (max(lens) - 1) // bs + 1
+    assert width == 3
+    assert all((n - 1) // bs + 1 <= width for n in lens)
