@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the MLA varlen-prefill hot path on one MI355X.
+
+One step = one pass of the path over one batch of synthetic input:
+mla_prefill_get_workspace_size-style validation and planning on the host, the
+work-list copy, and the attention kernel (the ``single`` workload: batch 1,
+4096 query and key tokens, 128 heads, embeddimV 128 + rope 64, bf16,
+causal). Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line with the throughput in algorithmic TFLOP/s (640 FLOP per
+visible (query, key, head) triple), the kernel's roofline position measured
+with HIP events on the launch stream, the CPU oracle timed on a bounded sample
+of the same workload, and the paged gather's bandwidth on the paged workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mla_varlen_prefill_amd as mla  # noqa: E402
+from mla_varlen_prefill_amd import synth  # noqa: E402
+
+METRIC = "MLA prefill attention TFLOP/s at 1 MI355X + % of bf16 MFMA peak"
+PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+FLOP_PER_PAIR = 2 * (128 + 64) + 2 * 128
+PMC_FILE = os.path.join(ROOT, "profiles", "mla_fwd_single_pmc.json")
+
+
+def visible_pairs(qs, ks, mask_type):
+    """Visible (query, key) pairs of one head."""
+    total = 0
+    for ql, kl in zip(qs, ks):
+        ql, kl = int(ql), int(kl)
+        if mask_type == synth.MASK_UNDEFINED:
+            total += ql * kl
+            continue
+        p = kl - ql + np.arange(ql, dtype=np.int64)  # key position of each row
+        total += int(np.clip(p + 1, 0, kl).sum())
+    return total
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("mla_fwd.hip", "kernels.h"):
+        with open(os.path.join(ROOT, "mla_varlen_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_attention(name, steps, warmup):
+    t, qs, ks, params = synth.workload_inputs(name, device="cuda")
+    H = params["head_num"]
+    out = torch.empty_like(t["q"])
+    args = dict(q=t["q"], q_rope=t["q_rope"], k=t["k"], k_rope=t["k_rope"], v=t["v"], q_seqlen=qs,
+                kv_seqlen=ks, mask=None, head_num=H, qk_scale=params["qk_scale"],
+                kv_head_num=params["kv_head_num"], mask_type=params["mask_type"], cache_mode=0, atten_out=out)
+    ws_bytes = mla.mla_prefill_get_workspace_size(**args)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        mla.mla_prefill(**args, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        mla.mla_prefill(**args, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    flops = FLOP_PER_PAIR * H * visible_pairs(qs, ks, params["mask_type"])
+    return dict(tensors=t, qs=qs, ks=ks, params=params, out=out, flops=flops,
+                ms_per_step=(t1 - t0) * 1e3 / steps, launch_ms=float(np.mean(launch_ms)),
+                launch_ms_min=float(np.min(launch_ms)))
+
+
+def cpu_baseline(res, seconds):
+    """The oracle as it stands, on whole heads of the same workload until about
+    ``seconds`` of CPU time have been spent (at least one head)."""
+    import oracle
+    t, qs, ks, params = res["tensors"], res["qs"], res["ks"], res["params"]
+    oracle.build()
+    ql, kl = int(qs[0]), int(ks[0])
+    flops = 0
+    spent = 0.0
+    heads = 0
+    for h in range(params["head_num"]):
+        hk = oracle.kv_head_of(h, params["head_num"], params["kv_head_num"])
+        a = [t["q"][:ql, h], t["q_rope"][:ql, h], t["k"][:kl, hk], t["k_rope"][:kl, hk], t["v"][:kl, hk]]
+        a = [x.double().cpu().numpy() for x in a]
+        s = time.perf_counter()
+        oracle.attention_head(*a, params["qk_scale"], params["mask_type"])
+        spent += time.perf_counter() - s
+        flops += FLOP_PER_PAIR * visible_pairs([ql], [kl], params["mask_type"])
+        heads += 1
+        if spent >= seconds:
+            break
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{heads} of {params['head_num']} heads, all {ql} query rows each, of the same workload "
+                      f"({spent:.1f} s, fp64)"}
+
+
+def bench_gather(steps):
+    lens, _ = synth.workload_seqlens("paged")
+    caches = synth.paged_inputs(lens, device="cuda", with_rope=True)
+    total = int(lens.sum())
+    heads = caches["key_cache"].shape[2]
+    key = torch.empty((total, heads, 128), dtype=torch.bfloat16, device="cuda")
+    value = torch.empty_like(key)
+    rope = torch.empty((total, heads, 64), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        mla.paged_cache_load(caches["key_cache"], caches["value_cache"], caches["block_tables"],
+                             caches["context_lens"], key, value, None, mla.KV_CACHE_ND, False, False, stream)
+        mla.paged_cache_load(caches["rope_cache"], None, caches["block_tables"], caches["context_lens"], rope,
+                             None, None, mla.KV_CACHE_ND, False, False, stream)
+
+    step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nbytes = 2 * total * (key[0].numel() + value[0].numel() + rope[0].numel()) * 2  # read + write
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del caches, key, value, rope
+    torch.cuda.empty_cache()
+    return {"workload": "paged", "tokens": total, "bytes_per_step": nbytes, "ms_per_step": ms,
+            "value": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="single", choices=["single", "varlen", "chunked", "tiny"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gather", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path runs on a single MI355X, without collectives).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    res = bench_attention(args.workload, args.steps, args.warmup)
+    flops = res["flops"]
+    value = flops / (res["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (res["launch_ms"] * 1e-3) / 1e12
+    w = synth.WORKLOADS[args.workload]
+    dtype = "bf16" if w["dtype"] == torch.bfloat16 else "fp16"
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "batch": len(res["qs"]),
+                   "q_seqlen": [int(x) for x in res["qs"]] if len(res["qs"]) <= 16 else "varlen",
+                   "kv_seqlen": [int(x) for x in res["ks"]] if len(res["ks"]) <= 16 else "varlen",
+                   "heads": w["heads"], "kv_heads": w["kv_heads"], "embeddim_v": 128, "rope_dim": 64,
+                   "mask": "causal", "flops_per_step": flops},
+        "pct_of_peak": round(100.0 * value / PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS, 4), "traffic": traffic_from_profile(),
+                     "kernel": "mla_fwd_kernel", "avg_launch_ms": round(res["launch_ms"], 4),
+                     "min_launch_ms": round(res["launch_ms_min"], 4)},
+    }
+    if not args.no_gather and args.workload == "single":
+        res_t = res.pop("tensors") if args.no_cpu_baseline else None
+        line["gather"] = bench_gather(max(2, min(args.steps, 5)))
+        del res_t
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

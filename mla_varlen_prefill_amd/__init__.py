@@ -1,0 +1,221 @@
+"""MLA varlen prefill on MI355X (gfx950): Python binding of the C ABI.
+
+The functions below carry the names of the C entry points declared in
+``include/mla_prefill.h`` and only marshal arguments: torch tensors become
+``mla_tensor`` descriptors (data pointer, dtype code, shape), host length
+arrays are passed as int32 pointers, and the current torch stream is passed as
+the HIP stream. Every step of the computation runs in the HIP library
+``libmla_prefill.so`` built from ``csrc/``; there is no other code path, and a
+missing library is an error.
+
+``prefill`` is a convenience wrapper that allocates the output and the
+workspace with torch and calls the two-phase pair.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "MASK_UNDEFINED", "MASK_SPEC", "MASK_CAUSAL", "MASK_FREE", "KV_CACHE_NZ", "KV_CACHE_ND",
+    "MlaError", "mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load",
+    "mla_last_error", "mla_prefill_plan_host", "prefill", "library_path",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_prefill.so")
+
+MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
+KV_CACHE_NZ, KV_CACHE_ND = 0, 1
+PLAN_Q_ROWS, PLAN_KV_COLS = 128, 64
+
+STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
+          -4: "MLA_ERR_VALUE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
+          -7: "MLA_ERR_RUNTIME"}
+
+_DTYPE = {torch.float16: 1, torch.bfloat16: 2, torch.int8: 3, torch.int32: 4,
+          np.dtype(np.int32): 4, np.dtype(np.int8): 3, np.dtype(np.float16): 1}
+
+
+class MlaError(RuntimeError):
+    """A C entry point returned a non-zero status."""
+
+    def __init__(self, fn, code, message):
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+        super().__init__(f"{fn}: {self.status}: {message}")
+
+
+class MlaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mla_varlen_prefill_amd.build`"
+                           " (there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    T = ctypes.POINTER(MlaTensor)
+    lib.mla_prefill_get_workspace_size.argtypes = [T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
+                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_uint8, T,
+                                                   ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prefill.argtypes = [T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                ctypes.c_int32, ctypes.c_uint8, T, ctypes.c_void_p, ctypes.c_uint64,
+                                ctypes.c_void_p]
+    lib.paged_cache_load.argtypes = [T, T, T, T, T, T, T, ctypes.c_int8, ctypes.c_bool, ctypes.c_bool,
+                                     ctypes.c_void_p]
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.POINTER(ctypes.c_int32)]
+    for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def mla_last_error() -> str:
+    return _load().mla_last_error().decode()
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise MlaError(fn, rc, mla_last_error())
+
+
+def _desc(t, keep):
+    """mla_tensor descriptor of a torch tensor or numpy array (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        if not t.flags["C_CONTIGUOUS"]:
+            raise ValueError("host arrays must be C-contiguous")
+        keep.append(t)
+        ptr, shape, dt = t.ctypes.data, t.shape, _DTYPE.get(t.dtype, 0)
+    else:
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous (row-major)")
+        ptr, shape, dt = t.data_ptr(), tuple(t.shape), _DTYPE.get(t.dtype, 0)
+    if len(shape) > 4:
+        raise ValueError("at most 4 dimensions")
+    d = MlaTensor()
+    d.data = ptr if ptr else None
+    d.dtype = dt
+    d.ndim = len(shape)
+    for i, s in enumerate(shape):
+        d.shape[i] = int(s)
+    keep.append(d)
+    return ctypes.pointer(d)
+
+
+def _host_int32(x):
+    """Host int32 array of lengths (list, numpy array or CPU tensor)."""
+    if isinstance(x, torch.Tensor):
+        if x.is_cuda:
+            raise ValueError("q_seqlen / kv_seqlen are host arrays")
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _prefill_args(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                  mask_type, cache_mode, atten_out, keep):
+    qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)
+    return [_desc(q, keep), _desc(q_rope, keep), _desc(k, keep), _desc(k_rope, keep), _desc(v, keep),
+            _desc(qs, keep), _desc(ks, keep), _desc(mask, keep), int(head_num), float(qk_scale),
+            int(kv_head_num), int(mask_type), int(cache_mode), _desc(atten_out, keep)]
+
+
+def mla_prefill_get_workspace_size(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
+                                   kv_head_num, mask_type, cache_mode, atten_out) -> int:
+    """Bytes of device workspace ``mla_prefill`` needs (host-only planning call)."""
+    lib = _load()
+    keep = []
+    args = _prefill_args(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                         mask_type, cache_mode, atten_out, keep)
+    size = ctypes.c_uint64(0)
+    _check("mla_prefill_get_workspace_size", lib.mla_prefill_get_workspace_size(*args, ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                mask_type, cache_mode, atten_out, workspace, stream=None) -> None:
+    """Enqueue MLA prefill attention on ``stream`` (default: torch's current stream)."""
+    lib = _load()
+    keep = []
+    args = _prefill_args(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                         mask_type, cache_mode, atten_out, keep)
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_prefill", lib.mla_prefill(*args, ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size),
+                                          _stream_ptr(stream)))
+
+
+def paged_cache_load(key_cache, value_cache, block_tables, context_lens, key, value, seq_starts=None,
+                     kv_cache_cfg=KV_CACHE_ND, is_seq_lens_cumsum_type=False, has_seq_starts=False,
+                     stream=None) -> None:
+    """Enqueue the paged K/V gather on ``stream`` (default: torch's current stream)."""
+    lib = _load()
+    keep = []
+    _check("paged_cache_load", lib.paged_cache_load(
+        _desc(key_cache, keep), _desc(value_cache, keep), _desc(block_tables, keep), _desc(context_lens, keep),
+        _desc(key, keep), _desc(value, keep), _desc(seq_starts, keep), int(kv_cache_cfg),
+        bool(is_seq_lens_cumsum_type), bool(has_seq_starts), _stream_ptr(stream)))
+
+
+def mla_prefill_plan_host(q_seqlen, kv_seqlen, mask_type, kv_padded_max_seq=0):
+    """The work list mla_prefill would copy to its workspace, decoded.
+
+    Returns (seqs [batch, 4] int32 = q_offset, kv_offset, q_len, kv_len;
+    items [n, 4] int32 = batch, first_q_row, kv_tiles, 0).
+    """
+    lib = _load()
+    qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)
+    batch = len(qs)
+    n = ctypes.c_int32(0)
+    max_items = int(np.sum((qs.astype(np.int64) + PLAN_Q_ROWS - 1) // PLAN_Q_ROWS)) if batch else 0
+    seq_bytes = (batch * 16 + 255) // 256 * 256
+    buf = np.zeros(seq_bytes + max_items * 16 + 16, dtype=np.uint8)
+    _check("mla_prefill_plan_host", lib.mla_prefill_plan_host(
+        qs.ctypes.data, ks.ctypes.data, batch, int(mask_type), int(kv_padded_max_seq), buf.ctypes.data,
+        buf.nbytes, ctypes.byref(n)))
+    seqs = buf[:batch * 16].view(np.int32).reshape(batch, 4).copy()
+    items = buf[seq_bytes:seq_bytes + n.value * 16].view(np.int32).reshape(n.value, 4).copy()
+    return seqs, items
+
+
+def prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num, qk_scale=1.0,
+            mask_type=MASK_UNDEFINED, mask=None, out=None, stream=None):
+    """Allocate the output and workspace with torch and run the two-phase pair."""
+    if out is None:
+        d = q.shape[-1] if q.dim() == 3 else q.shape[1] // head_num
+        out = torch.empty((q.shape[0], head_num, d), dtype=q.dtype, device=q.device)
+    ws = mla_prefill_get_workspace_size(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
+                                        kv_head_num, mask_type, 0, out)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+    mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num, mask_type,
+                0, out, workspace, stream)
+    if stream is not None and isinstance(stream, torch.cuda.Stream):
+        workspace.record_stream(stream)
+    return out

@@ -1,0 +1,463 @@
+// C ABI of the MLA varlen-prefill library: argument validation, the host work
+// planner, and the launches. Operations and argument meanings follow the
+// Ascend Transformer Boost C API pages "MLA Prefill" and
+// "PagedCacheLoadOperation" (Definition and Members tables).
+#include "mla_prefill.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using mla::FWD_BM;
+using mla::FWD_BN;
+using mla::HEAD_DIM;
+using mla::MASK_TILE;
+using mla::ROPE_DIM;
+using mla::SeqRec;
+using mla::WorkItem;
+
+static_assert(MLA_PLAN_Q_ROWS == FWD_BM, "plan row count must match the kernel tile");
+static_assert(MLA_PLAN_KV_COLS == FWD_BN, "plan key count must match the kernel tile");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MLA_OK;
+}
+
+int64_t numel(const mla_tensor *t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+    return n;
+}
+
+size_t elem_size(int dtype) {
+    switch (dtype) {
+        case MLA_FP16:
+        case MLA_BF16: return 2;
+        case MLA_INT8: return 1;
+        case MLA_INT32: return 4;
+        default: return 0;
+    }
+}
+
+// Structural checks shared by every tensor argument.
+int check_tensor(const mla_tensor *t, const char *name, bool device) {
+    if (t == nullptr) return fail(MLA_ERR_NULL, "%s: descriptor is NULL", name);
+    if (t->ndim < 1 || t->ndim > 4) return fail(MLA_ERR_SHAPE, "%s: ndim %d not in 1..4", name, t->ndim);
+    for (int i = 0; i < t->ndim; ++i)
+        if (t->shape[i] < 0) return fail(MLA_ERR_SHAPE, "%s: negative extent", name);
+    if (elem_size(t->dtype) == 0) return fail(MLA_ERR_DTYPE, "%s: unknown dtype code %d", name, t->dtype);
+    if (numel(t) > 0 && t->data == nullptr) return fail(MLA_ERR_NULL, "%s: data is NULL", name);
+    if (device && numel(t) > 0 && (reinterpret_cast<uintptr_t>(t->data) & 15) != 0)
+        return fail(MLA_ERR_VALUE, "%s: device data must be 16-byte aligned", name);
+    return MLA_OK;
+}
+
+bool is_half(int dtype) { return dtype == MLA_FP16 || dtype == MLA_BF16; }
+
+// [n, heads * dim] or [n, heads, dim]; returns dim through *dim_out (0 if the
+// shape does not fit).
+bool token_head_shape(const mla_tensor *t, int64_t heads, int64_t *n_out, int64_t *dim_out) {
+    if (t->ndim == 3 && t->shape[1] == heads) {
+        *n_out = t->shape[0];
+        *dim_out = t->shape[2];
+        return true;
+    }
+    if (t->ndim == 2 && heads > 0 && t->shape[1] % heads == 0) {
+        *n_out = t->shape[0];
+        *dim_out = t->shape[1] / heads;
+        return true;
+    }
+    return false;
+}
+
+struct Problem {
+    int dtype = 0;
+    int32_t batch = 0;
+    int32_t heads = 0;
+    int32_t kv_heads = 0;
+    int64_t n_q = 0;
+    int64_t n_kv = 0;
+    int64_t kv_padded_max_seq = 0;  // 0: packed
+    int mask_type = 0;
+    int mask_dtype = 0;
+    const int32_t *q_seqlen = nullptr;
+    const int32_t *kv_seqlen = nullptr;
+};
+
+// KV tensor layout: packed [sum kv, Hkv, dim] or padded [batch, max_seq, Hkv * dim].
+int kv_layout(const mla_tensor *t, const char *name, const Problem &pr, int64_t dim, int32_t max_kv,
+              int64_t *padded_max_seq) {
+    if (t->ndim != 3) return fail(MLA_ERR_SHAPE, "%s: expected 3 dimensions", name);
+    if (t->shape[0] == pr.n_kv && t->shape[1] == pr.kv_heads && t->shape[2] == dim) {
+        *padded_max_seq = 0;
+        return MLA_OK;
+    }
+    if (t->shape[0] == pr.batch && t->shape[2] == (int64_t)pr.kv_heads * dim && t->shape[1] >= max_kv) {
+        *padded_max_seq = t->shape[1];
+        return MLA_OK;
+    }
+    return fail(MLA_ERR_SHAPE,
+                "%s: shape must be packed [%lld, %d, %lld] or padded [%d, max_seq >= %d, %lld]", name,
+                (long long)pr.n_kv, pr.kv_heads, (long long)dim, pr.batch, max_kv,
+                (long long)pr.kv_heads * dim);
+}
+
+int validate_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
+                     const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
+                     const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                     float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
+                     const mla_tensor *out, Problem *pr) {
+    int rc;
+    if ((rc = check_tensor(q, "q", true)) || (rc = check_tensor(q_rope, "q_rope", true)) ||
+        (rc = check_tensor(k, "k", true)) || (rc = check_tensor(k_rope, "k_rope", true)) ||
+        (rc = check_tensor(v, "v", true)) || (rc = check_tensor(q_seqlen, "q_seqlen", false)) ||
+        (rc = check_tensor(kv_seqlen, "kv_seqlen", false)) ||
+        (rc = check_tensor(out, "atten_out", true)))
+        return rc;
+    if (head_num <= 0) return fail(MLA_ERR_VALUE, "headNum must be > 0 (got %d)", head_num);
+    if (kv_head_num <= 0) return fail(MLA_ERR_VALUE, "kvHeadNum must be > 0 (got %d)", kv_head_num);
+    if (head_num % kv_head_num != 0)
+        return fail(MLA_ERR_VALUE, "headNum %d is not a multiple of kvHeadNum %d", head_num, kv_head_num);
+    if (!std::isfinite(qk_scale)) return fail(MLA_ERR_VALUE, "qkScale must be finite");
+    if (mask_type < MLA_MASK_UNDEFINED || mask_type > MLA_MASK_FREE)
+        return fail(MLA_ERR_VALUE, "maskType %d is not a known mask type", mask_type);
+    if (cache_mode != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "cacheMode %d: only 0 (contiguous K/V) is implemented", cache_mode);
+
+    // dtypes
+    if (!is_half(q->dtype)) return fail(MLA_ERR_DTYPE, "q: dtype must be fp16 or bf16");
+    const mla_tensor *same[] = {q_rope, k, k_rope, v, out};
+    const char *same_names[] = {"q_rope", "k", "k_rope", "v", "atten_out"};
+    for (int i = 0; i < 5; ++i)
+        if (same[i]->dtype != q->dtype) return fail(MLA_ERR_DTYPE, "%s: dtype differs from q", same_names[i]);
+    if (q_seqlen->dtype != MLA_INT32 || kv_seqlen->dtype != MLA_INT32)
+        return fail(MLA_ERR_DTYPE, "q_seqlen / kv_seqlen must be int32");
+
+    // lengths
+    if (q_seqlen->ndim != 1 || kv_seqlen->ndim != 1 || q_seqlen->shape[0] != kv_seqlen->shape[0])
+        return fail(MLA_ERR_SHAPE, "q_seqlen and kv_seqlen must both be [batch]");
+    if (q_seqlen->shape[0] > INT32_MAX) return fail(MLA_ERR_VALUE, "batch too large");
+    pr->batch = (int32_t)q_seqlen->shape[0];
+    pr->heads = head_num;
+    pr->kv_heads = kv_head_num;
+    pr->dtype = q->dtype;
+    pr->mask_type = mask_type;
+    pr->q_seqlen = static_cast<const int32_t *>(q_seqlen->data);
+    pr->kv_seqlen = static_cast<const int32_t *>(kv_seqlen->data);
+    int64_t sum_q = 0, sum_kv = 0;
+    int32_t max_kv = 0;
+    for (int32_t b = 0; b < pr->batch; ++b) {
+        int32_t ql = pr->q_seqlen[b], kl = pr->kv_seqlen[b];
+        if (ql < 0 || kl < 0) return fail(MLA_ERR_VALUE, "sequence %d has a negative length", b);
+        sum_q += ql;
+        sum_kv += kl;
+        max_kv = std::max(max_kv, kl);
+    }
+    if (sum_q > INT32_MAX || sum_kv > INT32_MAX)
+        return fail(MLA_ERR_VALUE, "total tokens exceed 2^31 - 1");
+    pr->n_q = sum_q;
+    pr->n_kv = sum_kv;
+
+    // Q, QRope, attenOut
+    int64_t nq, dq, nqr, dqr, no, dout;
+    if (!token_head_shape(q, head_num, &nq, &dq))
+        return fail(MLA_ERR_SHAPE, "q: expected [nTokens, headNum*D] or [nTokens, headNum, D]");
+    if (!token_head_shape(q_rope, head_num, &nqr, &dqr))
+        return fail(MLA_ERR_SHAPE, "q_rope: expected [nTokens, headNum*64] or [nTokens, headNum, 64]");
+    if (!token_head_shape(out, head_num, &no, &dout))
+        return fail(MLA_ERR_SHAPE, "atten_out: expected [nTokens, headNum*D] or [nTokens, headNum, D]");
+    if (nq != sum_q || nqr != sum_q || no != sum_q)
+        return fail(MLA_ERR_SHAPE, "q / q_rope / atten_out rows must equal sum(qSeqLen) = %lld",
+                    (long long)sum_q);
+    if (dqr != ROPE_DIM) return fail(MLA_ERR_SHAPE, "q_rope: rope dimension must be 64 (got %lld)", (long long)dqr);
+    if (dout != dq) return fail(MLA_ERR_SHAPE, "atten_out: head dimension %lld differs from q's %lld",
+                                (long long)dout, (long long)dq);
+
+    // K, KRope, V share one layout
+    int64_t pad_k, pad_kr, pad_v;
+    if ((rc = kv_layout(k, "k", *pr, dq, max_kv, &pad_k)) ||
+        (rc = kv_layout(k_rope, "k_rope", *pr, ROPE_DIM, max_kv, &pad_kr)) ||
+        (rc = kv_layout(v, "v", *pr, dq, max_kv, &pad_v)))
+        return rc;
+    if (pad_k != pad_kr || pad_k != pad_v)
+        return fail(MLA_ERR_SHAPE, "k, k_rope and v must share one layout (packed or padded)");
+    pr->kv_padded_max_seq = pad_k;
+    if (pad_k && (int64_t)pr->batch * pad_k > INT32_MAX)
+        return fail(MLA_ERR_VALUE, "padded K/V rows exceed 2^31 - 1");
+
+    if (mask_type == MLA_MASK_FREE) {
+        if (mask == nullptr) return fail(MLA_ERR_NULL, "mask: required for MASK_FREE");
+        if ((rc = check_tensor(mask, "mask", true))) return rc;
+        if (!is_half(mask->dtype)) return fail(MLA_ERR_DTYPE, "mask: dtype must be fp16 or bf16");
+        if (mask->ndim != 2 || mask->shape[0] != MASK_TILE || mask->shape[1] != MASK_TILE)
+            return fail(MLA_ERR_SHAPE, "mask: expected [512, 512]");
+        pr->mask_dtype = mask->dtype;
+    }
+    if (dq != HEAD_DIM)
+        return fail(MLA_ERR_UNSUPPORTED, "embeddimV %lld: this build implements 128", (long long)dq);
+    if ((int64_t)head_num > 65535) return fail(MLA_ERR_UNSUPPORTED, "headNum above 65535");
+    return MLA_OK;
+}
+
+// Number of FWD_BN-key tiles (counted from key 0) that query rows
+// [q_row0, q_end) of a sequence can see under mask_type.
+int32_t visible_tiles(int mask_type, int32_t q_len, int32_t kv_len, int32_t q_end) {
+    int64_t visible;
+    int64_t p_last = (int64_t)kv_len - q_len + q_end - 1;  // key position of the last row
+    switch (mask_type) {
+        case MLA_MASK_UNDEFINED: visible = kv_len; break;
+        case MLA_MASK_SPEC:
+        case MLA_MASK_CAUSAL: visible = std::min<int64_t>(kv_len, std::max<int64_t>(p_last + 1, 0)); break;
+        default:  // MLA_MASK_FREE: every key up to the end of the last row's 512-block
+            visible = p_last < 0 ? 0 : std::min<int64_t>(kv_len, (p_last / MASK_TILE + 1) * MASK_TILE);
+    }
+    return (int32_t)((visible + FWD_BN - 1) / FWD_BN);
+}
+
+struct Plan {
+    std::vector<SeqRec> seqs;
+    std::vector<WorkItem> items;
+};
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+uint64_t plan_bytes(const Plan &p) {
+    if (p.items.empty()) return 0;
+    return align256(p.seqs.size() * sizeof(SeqRec)) + p.items.size() * sizeof(WorkItem);
+}
+
+// Work list: one item per FWD_BM query rows of each sequence, heaviest first
+// so the long causal rows start early and short ones fill the tail.
+void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int mask_type,
+                int64_t kv_padded_max_seq, Plan *plan) {
+    plan->seqs.resize(batch);
+    plan->items.clear();
+    int64_t q_off = 0, kv_off = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        SeqRec &s = plan->seqs[b];
+        s.q_off = (int32_t)q_off;
+        s.kv_off = (int32_t)(kv_padded_max_seq ? (int64_t)b * kv_padded_max_seq : kv_off);
+        s.q_len = q_seqlen[b];
+        s.kv_len = kv_seqlen[b];
+        for (int32_t r = 0; r < s.q_len; r += FWD_BM) {
+            int32_t q_end = std::min(s.q_len, r + FWD_BM);
+            plan->items.push_back({b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), 0});
+        }
+        q_off += s.q_len;
+        kv_off += s.kv_len;
+    }
+    std::stable_sort(plan->items.begin(), plan->items.end(),
+                     [](const WorkItem &a, const WorkItem &b) { return a.kv_tiles > b.kv_tiles; });
+}
+
+void write_plan(const Plan &p, uint8_t *dst) {
+    std::memcpy(dst, p.seqs.data(), p.seqs.size() * sizeof(SeqRec));
+    std::memcpy(dst + align256(p.seqs.size() * sizeof(SeqRec)), p.items.data(),
+                p.items.size() * sizeof(WorkItem));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mla_last_error(void) { return g_last_error.c_str(); }
+
+int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch,
+                          int32_t mask_type, int64_t kv_padded_max_seq, void *buf, uint64_t buf_size,
+                          int32_t *n_items) {
+    if (batch < 0) return fail(MLA_ERR_VALUE, "batch must be >= 0");
+    if (batch > 0 && (q_seqlen == nullptr || kv_seqlen == nullptr))
+        return fail(MLA_ERR_NULL, "length arrays are NULL");
+    if (n_items == nullptr) return fail(MLA_ERR_NULL, "n_items is NULL");
+    if (mask_type < MLA_MASK_UNDEFINED || mask_type > MLA_MASK_FREE)
+        return fail(MLA_ERR_VALUE, "maskType %d is not a known mask type", mask_type);
+    for (int32_t b = 0; b < batch; ++b)
+        if (q_seqlen[b] < 0 || kv_seqlen[b] < 0) return fail(MLA_ERR_VALUE, "negative length");
+    Plan plan;
+    build_plan(q_seqlen, kv_seqlen, batch, mask_type, kv_padded_max_seq, &plan);
+    *n_items = (int32_t)plan.items.size();
+    uint64_t need = plan_bytes(plan);
+    if (need > 0) {
+        if (buf == nullptr || buf_size < need)
+            return fail(MLA_ERR_WORKSPACE, "plan needs %llu bytes", (unsigned long long)need);
+        write_plan(plan, static_cast<uint8_t *>(buf));
+    }
+    return ok();
+}
+
+int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,
+                                   const mla_tensor *k, const mla_tensor *k_rope,
+                                   const mla_tensor *v, const mla_tensor *q_seqlen,
+                                   const mla_tensor *kv_seqlen, const mla_tensor *mask,
+                                   int32_t head_num, float qk_scale, int32_t kv_head_num,
+                                   int32_t mask_type, uint8_t cache_mode,
+                                   const mla_tensor *atten_out, uint64_t *workspace_size) {
+    if (workspace_size == nullptr) return fail(MLA_ERR_NULL, "workspace_size is NULL");
+    Problem pr;
+    int rc = validate_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
+                              kv_head_num, mask_type, cache_mode, atten_out, &pr);
+    if (rc) return rc;
+    Plan plan;
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.mask_type, pr.kv_padded_max_seq, &plan);
+    *workspace_size = plan_bytes(plan);
+    return ok();
+}
+
+int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
+                const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
+                const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
+                const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
+                void *stream) {
+    Problem pr;
+    int rc = validate_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
+                              kv_head_num, mask_type, cache_mode, atten_out, &pr);
+    if (rc) return rc;
+    Plan plan;
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.mask_type, pr.kv_padded_max_seq, &plan);
+    const uint64_t need = plan_bytes(plan);
+    if (need == 0) return ok();  // no query rows: nothing to write
+    if (workspace == nullptr || workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given",
+                    (unsigned long long)need, (unsigned long long)workspace_size);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (plan.items.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
+
+    std::vector<uint8_t> host(need);
+    write_plan(plan, host.data());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipMemcpyAsync: %s", hipGetErrorString(e));
+
+    mla::FwdParams p{};
+    p.q = q->data;
+    p.q_rope = q_rope->data;
+    p.k = k->data;
+    p.k_rope = k_rope->data;
+    p.v = v->data;
+    p.mask = (mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
+    p.out = atten_out->data;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    p.seqs = reinterpret_cast<const SeqRec *>(ws);
+    p.items = reinterpret_cast<const WorkItem *>(ws + align256(plan.seqs.size() * sizeof(SeqRec)));
+    p.heads = head_num;
+    p.kv_heads = kv_head_num;
+    p.group = head_num / kv_head_num;
+    p.mask_type = mask_type;
+    p.mask_is_bf16 = (mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;
+    p.scale_log2 = (float)((double)qk_scale * 1.4426950408889634);
+    e = mla::launch_mla_fwd(p, pr.dtype, (int)plan.items.size(), s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
+                     const mla_tensor *block_tables, const mla_tensor *context_lens,
+                     const mla_tensor *key, const mla_tensor *value, const mla_tensor *seq_starts,
+                     int8_t kv_cache_cfg, bool is_seq_lens_cumsum_type, bool has_seq_starts,
+                     void *stream) {
+    int rc;
+    if ((rc = check_tensor(key_cache, "key_cache", true)) || (rc = check_tensor(key, "key", true)) ||
+        (rc = check_tensor(block_tables, "block_tables", true)) ||
+        (rc = check_tensor(context_lens, "context_lens", true)))
+        return rc;
+    if ((value_cache == nullptr) != (value == nullptr))
+        return fail(MLA_ERR_NULL, "value_cache and value must both be given or both be NULL");
+    if (value_cache && ((rc = check_tensor(value_cache, "value_cache", true)) ||
+                        (rc = check_tensor(value, "value", true))))
+        return rc;
+    if (kv_cache_cfg == MLA_KV_CACHE_NZ)
+        return fail(MLA_ERR_UNSUPPORTED, "kvCacheCfg NZ: only the ND cache layout is implemented");
+    if (kv_cache_cfg != MLA_KV_CACHE_ND) return fail(MLA_ERR_VALUE, "kvCacheCfg %d is unknown", kv_cache_cfg);
+
+    const int dt = key_cache->dtype;
+    if (!(dt == MLA_FP16 || dt == MLA_BF16 || dt == MLA_INT8))
+        return fail(MLA_ERR_DTYPE, "key_cache: dtype must be fp16, bf16 or int8");
+    if (key->dtype != dt) return fail(MLA_ERR_DTYPE, "key: dtype differs from key_cache");
+    if (value_cache && (value_cache->dtype != dt || value->dtype != dt))
+        return fail(MLA_ERR_DTYPE, "value_cache / value: dtype differs from key_cache");
+    if (block_tables->dtype != MLA_INT32 || context_lens->dtype != MLA_INT32)
+        return fail(MLA_ERR_DTYPE, "block_tables / context_lens must be int32");
+
+    if (key_cache->ndim != 4) return fail(MLA_ERR_SHAPE, "key_cache: expected ND [num_blocks, block_size, heads, head_size]");
+    const int64_t nb = key_cache->shape[0], bs = key_cache->shape[1], heads = key_cache->shape[2];
+    if (bs <= 0) return fail(MLA_ERR_SHAPE, "key_cache: block_size must be > 0");
+    if (key->ndim != 3 || key->shape[1] != heads || key->shape[2] != key_cache->shape[3])
+        return fail(MLA_ERR_SHAPE, "key: expected [num_tokens, %lld, %lld]", (long long)heads,
+                    (long long)key_cache->shape[3]);
+    const int64_t num_tokens = key->shape[0];
+    if (value_cache) {
+        if (value_cache->ndim != 4 || value_cache->shape[0] != nb || value_cache->shape[1] != bs ||
+            value_cache->shape[2] != heads)
+            return fail(MLA_ERR_SHAPE, "value_cache: expected [%lld, %lld, %lld, head_size_v]", (long long)nb,
+                        (long long)bs, (long long)heads);
+        if (value->ndim != 3 || value->shape[0] != num_tokens || value->shape[1] != heads ||
+            value->shape[2] != value_cache->shape[3])
+            return fail(MLA_ERR_SHAPE, "value: expected [%lld, %lld, %lld]", (long long)num_tokens,
+                        (long long)heads, (long long)value_cache->shape[3]);
+    }
+    if (block_tables->ndim != 2) return fail(MLA_ERR_SHAPE, "block_tables: expected [batch, max_blocks]");
+    const int64_t batch = block_tables->shape[0];
+    if (batch > mla::GATHER_MAX_BATCH)
+        return fail(MLA_ERR_UNSUPPORTED, "batch above %d", mla::GATHER_MAX_BATCH);
+    if (context_lens->ndim != 1) return fail(MLA_ERR_SHAPE, "context_lens: expected one dimension");
+    const int64_t n_ctx = context_lens->shape[0];
+    if (!(n_ctx == batch || (is_seq_lens_cumsum_type && n_ctx == batch + 1)))
+        return fail(MLA_ERR_SHAPE, "context_lens: expected [batch]%s", is_seq_lens_cumsum_type ? " or [batch + 1]" : "");
+    if (has_seq_starts) {
+        if (seq_starts == nullptr) return fail(MLA_ERR_NULL, "seq_starts: required when has_seq_starts");
+        if ((rc = check_tensor(seq_starts, "seq_starts", true))) return rc;
+        if (seq_starts->dtype != MLA_INT32) return fail(MLA_ERR_DTYPE, "seq_starts must be int32");
+        if (seq_starts->ndim != 1 || seq_starts->shape[0] != batch)
+            return fail(MLA_ERR_SHAPE, "seq_starts: expected [batch]");
+    }
+    if (num_tokens == 0 || batch == 0) return ok();
+
+    mla::GatherParams p{};
+    p.key_cache = key_cache->data;
+    p.value_cache = value_cache ? value_cache->data : nullptr;
+    p.key = key->data;
+    p.value = value ? value->data : nullptr;
+    p.block_tables = static_cast<const int32_t *>(block_tables->data);
+    p.context_lens = static_cast<const int32_t *>(context_lens->data);
+    p.seq_starts = has_seq_starts ? static_cast<const int32_t *>(seq_starts->data) : nullptr;
+    p.num_blocks = nb;
+    p.block_size = bs;
+    p.max_blocks = block_tables->shape[1];
+    p.num_tokens = num_tokens;
+    p.row_bytes_k = heads * key_cache->shape[3] * (int64_t)elem_size(dt);
+    p.row_bytes_v = value_cache ? heads * value_cache->shape[3] * (int64_t)elem_size(dt) : 0;
+    p.batch = (int32_t)batch;
+    p.ctx_entries = (int32_t)n_ctx;
+    p.cumsum = is_seq_lens_cumsum_type ? 1 : 0;
+    p.has_seq_starts = has_seq_starts ? 1 : 0;
+    hipError_t e = mla::launch_paged_gather(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "gather launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

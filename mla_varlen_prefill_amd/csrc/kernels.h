@@ -1,0 +1,80 @@
+// Internal interface between the C-ABI host code (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Tile shape of the attention kernel: one workgroup owns FWD_BM query rows of
+// one (sequence, head) and walks the visible keys in tiles of FWD_BN.
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+constexpr int FWD_THREADS = 256;
+constexpr int HEAD_DIM = 128;   // embeddimV handled by the kernel
+constexpr int ROPE_DIM = 64;    // rope part, fixed by the operator definition
+constexpr int MASK_TILE = 512;  // side of the MASK_FREE tile
+
+// Per-sequence record of the work list (int32 x 4).
+struct SeqRec {
+    int32_t q_off;   // first query row of the sequence in Q / attenOut
+    int32_t kv_off;  // first key row in K / KRope / V (packed offset or b * max_seq)
+    int32_t q_len;
+    int32_t kv_len;
+};
+
+// One workgroup's work: FWD_BM query rows starting at q_row0 of sequence b,
+// and the number of FWD_BN-key tiles (from key 0) that any of them can see.
+struct WorkItem {
+    int32_t b;
+    int32_t q_row0;
+    int32_t kv_tiles;
+    int32_t pad;
+};
+
+struct FwdParams {
+    const void *q;        // [nq, H, 128]
+    const void *q_rope;   // [nq, H, 64]
+    const void *k;        // rows of Hkv * 128
+    const void *k_rope;   // rows of Hkv * 64
+    const void *v;        // rows of Hkv * 128
+    const void *mask;     // [512, 512] or nullptr
+    void *out;            // [nq, H, 128]
+    const SeqRec *seqs;
+    const WorkItem *items;
+    int32_t heads;
+    int32_t kv_heads;
+    int32_t group;        // heads / kv_heads
+    int32_t mask_type;    // enum mla_mask_type
+    int32_t mask_is_bf16; // dtype of the MASK_FREE tile
+    float scale_log2;     // qkScale * log2(e)
+};
+
+// dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). n_items workgroups per head.
+hipError_t launch_mla_fwd(const FwdParams &p, int dtype, int n_items, hipStream_t stream);
+
+struct GatherParams {
+    const void *key_cache;
+    const void *value_cache;  // may be null
+    void *key;
+    void *value;              // null iff value_cache is null
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    const int32_t *seq_starts; // null unless has_seq_starts
+    int64_t num_blocks;
+    int64_t block_size;
+    int64_t max_blocks;       // columns of block_tables
+    int64_t num_tokens;       // rows of key / value
+    int64_t row_bytes_k;      // bytes of one token row (heads * head_size_k * elem)
+    int64_t row_bytes_v;
+    int32_t batch;
+    int32_t ctx_entries;      // batch or batch + 1
+    int32_t cumsum;
+    int32_t has_seq_starts;
+};
+
+constexpr int GATHER_MAX_BATCH = 8192;  // offsets table in LDS: (batch + 1) * 4 bytes
+
+hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream);
+
+}  // namespace mla

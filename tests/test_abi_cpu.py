@@ -1,0 +1,234 @@
+"""Host-side tests of the C ABI: exports, validation, the work planner.
+
+These run without a GPU: every call here either fails validation before any
+HIP call, or only plans on the host.
+"""
+import ctypes
+import glob
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import mla_varlen_prefill_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_contract.json")
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M):
+            names.append(m.group(1))
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert {"mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load"} <= set(names)
+    lib = ctypes.CDLL(mla.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+
+
+def test_binding_uses_the_c_names():
+    for n in declared_functions():
+        assert callable(getattr(mla, n, None)), f"binding lacks {n}"
+
+
+# ------------------------------------------------------------------ validation
+
+def tensors(qs=(17, 40), ks=None, h=4, hk=4, d=128, dtype=torch.bfloat16):
+    ks = qs if ks is None else ks
+    nq, nk = sum(qs), sum(ks)
+    z = lambda *s, dt=dtype: torch.zeros(s, dtype=dt)
+    return dict(q=z(nq, h, d), q_rope=z(nq, h, 64), k=z(nk, hk, d), k_rope=z(nk, hk, 64), v=z(nk, hk, d),
+                q_seqlen=np.array(qs, np.int32), kv_seqlen=np.array(ks, np.int32), mask=None, head_num=h,
+                qk_scale=0.1, kv_head_num=hk, mask_type=mla.MASK_CAUSAL, cache_mode=0, atten_out=z(nq, h, d))
+
+
+def ws_size(t):
+    return mla.mla_prefill_get_workspace_size(**t)
+
+
+def status_of(t):
+    try:
+        ws_size(t)
+        return "MLA_OK"
+    except mla.MlaError as e:
+        return e.status
+
+
+def test_valid_problem_plans():
+    assert ws_size(tensors()) > 0
+    assert ws_size(tensors(qs=(0, 0), ks=(5, 0))) == 0  # no query rows: nothing to do
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda t: t.update(head_num=0), "MLA_ERR_VALUE"),                      # page default 0 is invalid
+    (lambda t: t.update(kv_head_num=0), "MLA_ERR_VALUE"),
+    (lambda t: t.update(kv_head_num=3), "MLA_ERR_VALUE"),                   # 4 % 3 != 0
+    (lambda t: t.update(qk_scale=float("nan")), "MLA_ERR_VALUE"),
+    (lambda t: t.update(mask_type=7), "MLA_ERR_VALUE"),
+    (lambda t: t.update(cache_mode=1), "MLA_ERR_UNSUPPORTED"),
+    (lambda t: t.update(q_seqlen=np.array([17, 41], np.int32)), "MLA_ERR_SHAPE"),
+    (lambda t: t.update(kv_seqlen=np.array([17], np.int32)), "MLA_ERR_SHAPE"),
+    (lambda t: t.update(kv_seqlen=np.array([-1, 58], np.int32)), "MLA_ERR_VALUE"),
+    (lambda t: t.update(q_rope=torch.zeros(57, 4, 32, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (lambda t: t.update(v=torch.zeros(57, 4, 128, dtype=torch.float16)), "MLA_ERR_DTYPE"),
+    (lambda t: t.update(atten_out=torch.zeros(57, 4, 64, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (lambda t: t.update(k=torch.zeros(57, 2, 128, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (lambda t: t.update(mask_type=mla.MASK_FREE), "MLA_ERR_NULL"),         # MASK_FREE needs the tile
+    (lambda t: t.update(mask_type=mla.MASK_FREE, mask=torch.zeros(256, 512, dtype=torch.float16)),
+     "MLA_ERR_SHAPE"),
+    (lambda t: t.update(mask_type=mla.MASK_FREE, mask=torch.zeros(512, 512, dtype=torch.float32)),
+     "MLA_ERR_DTYPE"),
+    (lambda t: t.update(q=torch.zeros(57, 4, 128, dtype=torch.float32)), "MLA_ERR_DTYPE"),
+])
+def test_validation_errors(mutate, status):
+    t = tensors()
+    mutate(t)
+    assert status_of(t) == status
+    assert mla.mla_last_error() != ""
+
+
+def test_unsupported_head_dim_after_shape_checks():
+    assert status_of(tensors(d=64)) == "MLA_ERR_UNSUPPORTED"
+
+
+def test_mask_ignored_unless_mask_free():
+    t = tensors()
+    t["mask"] = torch.zeros(3, dtype=torch.float32)  # would be invalid for MASK_FREE
+    assert status_of(t) == "MLA_OK"
+
+
+def test_two_dimensional_forms_and_padded_kv_accepted():
+    t = tensors()
+    t["q"] = t["q"].reshape(57, -1)
+    t["atten_out"] = t["atten_out"].reshape(57, -1)
+    t["q_rope"] = t["q_rope"].reshape(57, -1)
+    assert status_of(t) == "MLA_OK"
+    t = tensors(qs=(17, 40), ks=(30, 50))
+    t["k"] = torch.zeros(2, 64, 4 * 128, dtype=torch.bfloat16)
+    t["k_rope"] = torch.zeros(2, 64, 4 * 64, dtype=torch.bfloat16)
+    t["v"] = torch.zeros(2, 64, 4 * 128, dtype=torch.bfloat16)
+    assert status_of(t) == "MLA_OK"
+    t["v"] = torch.zeros(80, 4, 128, dtype=torch.bfloat16)  # packed while k is padded
+    assert status_of(t) == "MLA_ERR_SHAPE"
+
+
+def test_workspace_checks_before_any_launch():
+    t = tensors()
+    need = ws_size(t)
+    small = torch.zeros(need - 1, dtype=torch.uint8)
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_prefill(**t, workspace=small, stream=0)
+    assert e.value.status == "MLA_ERR_WORKSPACE"
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
+def test_no_device_is_a_runtime_error():
+    t = tensors()
+    ws = torch.zeros(ws_size(t), dtype=torch.uint8)
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_prefill(**t, workspace=ws, stream=0)
+    assert e.value.status == "MLA_ERR_RUNTIME"
+
+
+def gather_args(**kw):
+    a = dict(key_cache=torch.zeros(4, 8, 2, 16, dtype=torch.bfloat16),
+             value_cache=torch.zeros(4, 8, 2, 16, dtype=torch.bfloat16),
+             block_tables=torch.zeros(2, 2, dtype=torch.int32), context_lens=torch.zeros(2, dtype=torch.int32),
+             key=torch.zeros(10, 2, 16, dtype=torch.bfloat16), value=torch.zeros(10, 2, 16, dtype=torch.bfloat16),
+             seq_starts=None, kv_cache_cfg=mla.KV_CACHE_ND, is_seq_lens_cumsum_type=False, has_seq_starts=False)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_cache_cfg=mla.KV_CACHE_NZ), "MLA_ERR_UNSUPPORTED"),
+    (dict(kv_cache_cfg=5), "MLA_ERR_VALUE"),
+    (dict(value=None), "MLA_ERR_NULL"),
+    (dict(key=torch.zeros(10, 2, 8, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (dict(key=torch.zeros(10, 2, 16, dtype=torch.float16)), "MLA_ERR_DTYPE"),
+    (dict(block_tables=torch.zeros(2, 2, dtype=torch.int64)), "MLA_ERR_DTYPE"),
+    (dict(context_lens=torch.zeros(3, dtype=torch.int32)), "MLA_ERR_SHAPE"),   # [batch+1] needs cumsum
+    (dict(has_seq_starts=True), "MLA_ERR_NULL"),
+    (dict(has_seq_starts=True, seq_starts=torch.zeros(3, dtype=torch.int32)), "MLA_ERR_SHAPE"),
+    (dict(key_cache=torch.zeros(4, 8, 32, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (dict(key_cache=torch.zeros(4, 8, 2, 16, dtype=torch.float32)), "MLA_ERR_DTYPE"),
+])
+def test_gather_validation_errors(kw, status):
+    with pytest.raises(mla.MlaError) as e:
+        mla.paged_cache_load(**gather_args(**kw), stream=0)
+    assert e.value.status == status
+
+
+# ------------------------------------------------------------------ planner
+
+def visible_count(mask_type, ql, kl, i):
+    """Keys row i can see, from a materialised mask row."""
+    p = kl - ql + i
+    j = np.arange(kl)
+    if mask_type == mla.MASK_UNDEFINED:
+        vis = np.ones(kl, bool)
+    elif mask_type in (mla.MASK_SPEC, mla.MASK_CAUSAL):
+        vis = j <= p
+    else:
+        vis = (j // 512 <= p // 512) & (p >= 0)
+    return int(vis.nonzero()[0].max()) + 1 if vis.any() else 0
+
+
+@pytest.mark.parametrize("mask_type", [0, 1, 2, 3])
+@pytest.mark.parametrize("case", [([17, 40], [17, 40]), ([300, 1, 0, 129], [1000, 1, 5, 100]),
+                                  ([2048] * 3, [16384] * 3), ([700], [100])])
+def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
+    qs, ks = case
+    seqs, items = mla.mla_prefill_plan_host(qs, ks, mask_type)
+    # batch records are prefix sums
+    assert (seqs[:, 0] == np.concatenate([[0], np.cumsum(qs)[:-1]])).all()
+    assert (seqs[:, 1] == np.concatenate([[0], np.cumsum(ks)[:-1]])).all()
+    assert (seqs[:, 2] == qs).all() and (seqs[:, 3] == ks).all()
+    # every (b, q-tile) exactly once
+    want = sorted((b, r) for b, n in enumerate(qs) for r in range(0, n, mla.PLAN_Q_ROWS))
+    assert sorted((int(b), int(r)) for b, r, _, _ in items) == want
+    # tile range = tiles holding the furthest visible key of any row in the item
+    for b, r, nt, _ in items:
+        ql, kl = qs[b], ks[b]
+        far = max(visible_count(mask_type, ql, kl, i) for i in range(r, min(ql, r + mla.PLAN_Q_ROWS)))
+        assert nt == -(-far // mla.PLAN_KV_COLS), (b, r)
+    # heaviest first
+    assert (np.diff(items[:, 2]) <= 0).all()
+
+
+def test_plan_padded_offsets():
+    seqs, _ = mla.mla_prefill_plan_host([3, 4, 5], [7, 8, 9], 2, kv_padded_max_seq=10)
+    assert list(seqs[:, 1]) == [0, 10, 20]
+
+
+# ------------------------------------------------------------------ page contract
+
+def test_page_contract_values():
+    g = json.load(open(GOLDEN))
+    assert g["paged_cache_load"]["kvCacheCfg"]["value"] == {"K_CACHE_V_CACHE_NZ": mla.KV_CACHE_NZ,
+                                                            "K_CACHE_V_CACHE_ND": mla.KV_CACHE_ND}
+    assert g["mla_prefill"]["rope_dim"]["value"] == 64
+    assert g["mla_prefill"]["mask_shape"]["value"] == [512, 512]
+    import inspect
+    sig = inspect.signature(mla.prefill)
+    assert sig.parameters["qk_scale"].default == g["mla_prefill"]["qkScale_default"]["value"]
+    assert sig.parameters["mask_type"].default == mla.MASK_UNDEFINED
+    sig = inspect.signature(mla.paged_cache_load)
+    assert sig.parameters["is_seq_lens_cumsum_type"].default is g["paged_cache_load"][
+        "isSeqLensCumsumType_default"]["value"]
+    assert sig.parameters["has_seq_starts"].default is g["paged_cache_load"]["hasSeqStarts_default"]["value"]
+    # the page's headNum / kvHeadNum default of 0 is rejected as a value
+    t = tensors()
+    t["head_num"] = g["mla_prefill"]["headNum_default"]["value"]
+    assert status_of(t) == "MLA_ERR_VALUE"

@@ -1,0 +1,144 @@
+"""GPU parity of the paged gather against the numpy oracle: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import mla_varlen_prefill_amd as mla
+from mla_varlen_prefill_amd import synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def gather_gpu(caches, lens_dev, total, seq_starts=None, cumsum=False, has_starts=False, with_value=True,
+               key_name="key_cache", value_name="value_cache"):
+    kc = caches[key_name]
+    vc = caches[value_name] if with_value else None
+    key = torch.full((total,) + tuple(kc.shape[2:]), 77, dtype=kc.dtype, device=DEV) if kc.dtype == torch.int8 \
+        else torch.full((total,) + tuple(kc.shape[2:]), float("nan"), dtype=kc.dtype, device=DEV)
+    value = None
+    if vc is not None:
+        value = torch.zeros((total,) + tuple(vc.shape[2:]), dtype=vc.dtype, device=DEV)
+    mla.paged_cache_load(kc, vc, caches["block_tables"], lens_dev, key, value, seq_starts,
+                         mla.KV_CACHE_ND, cumsum, has_starts)
+    torch.cuda.synchronize()
+    return key, value
+
+
+def as_bits(t):
+    if t.dtype in (torch.float16, torch.bfloat16):
+        return t.view(torch.int16).cpu().numpy()
+    return t.cpu().numpy()
+
+
+def oracle_gather(caches, lens, starts=None, cumsum=False, has_starts=False, with_value=True,
+                  key_name="key_cache", value_name="value_cache"):
+    kc = as_bits(caches[key_name])
+    vc = as_bits(caches[value_name]) if with_value else None
+    table = caches["block_tables"].cpu().numpy()
+    return oracle.paged_cache_load(kc, vc, table, lens, starts, cumsum, has_starts)
+
+
+def test_gather_small_bit_exact():
+    lens = [1, 127, 128, 129, 500, 3]
+    _say(f"[gpu] gather lens={lens}")
+    caches = synth.paged_inputs(lens, heads=4, head_size_k=128, head_size_v=128, block_size=128, seed=1,
+                                device=DEV)
+    key, value = gather_gpu(caches, caches["context_lens"], sum(lens))
+    rk, rv = oracle_gather(caches, lens)
+    assert np.array_equal(as_bits(key), rk) and np.array_equal(as_bits(value), rv)
+
+
+@pytest.mark.parametrize("form", ["inclusive", "exclusive"])
+def test_gather_cumsum_forms(form):
+    lens = [7, 0, 300, 64]
+    caches = synth.paged_inputs(lens, heads=2, block_size=64, seed=2, device=DEV)
+    inc = np.cumsum(lens).astype(np.int32)
+    ctx = inc if form == "inclusive" else np.concatenate([[0], inc]).astype(np.int32)
+    key, value = gather_gpu(caches, torch.from_numpy(ctx).to(DEV), sum(lens), cumsum=True)
+    rk, rv = oracle_gather(caches, lens)
+    assert np.array_equal(as_bits(key), rk) and np.array_equal(as_bits(value), rv)
+
+
+def test_gather_seq_starts():
+    lens, starts = [50, 9, 200], [10, 120, 0]
+    ctx = [n + s for n, s in zip(lens, starts)]
+    caches = synth.paged_inputs(ctx, heads=2, block_size=32, seed=3, device=DEV)
+    st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    key, value = gather_gpu(caches, torch.tensor(lens, dtype=torch.int32, device=DEV), sum(lens), st,
+                            has_starts=True)
+    rk, rv = oracle_gather(caches, lens, starts, has_starts=True)
+    assert np.array_equal(as_bits(key), rk) and np.array_equal(as_bits(value), rv)
+    # has_seq_starts false ignores the starts
+    key2, _ = gather_gpu(caches, torch.tensor(lens, dtype=torch.int32, device=DEV), sum(lens), st,
+                         has_starts=False)
+    rk2, _ = oracle_gather(caches, lens)
+    assert np.array_equal(as_bits(key2), rk2)
+
+
+def test_gather_keys_only_rope_cache():
+    lens = [300, 17]
+    caches = synth.paged_inputs(lens, heads=4, block_size=128, seed=4, device=DEV)
+    key, value = gather_gpu(caches, caches["context_lens"], sum(lens), with_value=False, key_name="rope_cache")
+    assert value is None
+    rk, _ = oracle_gather(caches, lens, with_value=False, key_name="rope_cache")
+    assert np.array_equal(as_bits(key), rk)
+
+
+def test_gather_int8_and_odd_row_bytes():
+    """int8 caches and rows that are not a multiple of 16 bytes (byte path)."""
+    lens = [40, 13]
+    nb, bs = 8, 16
+    g = torch.Generator(device=DEV).manual_seed(5)
+    kc = torch.randint(-128, 127, (nb, bs, 3, 5), dtype=torch.int8, device=DEV, generator=g)
+    vc = torch.randint(-128, 127, (nb, bs, 3, 7), dtype=torch.int8, device=DEV, generator=g)
+    table = torch.from_numpy(np.random.default_rng(5).permutation(nb).reshape(2, 4).astype(np.int32)).to(DEV)
+    caches = {"key_cache": kc, "value_cache": vc, "block_tables": table}
+    key, value = gather_gpu(caches, torch.tensor(lens, dtype=torch.int32, device=DEV), sum(lens))
+    rk, rv = oracle_gather(caches, lens)
+    assert np.array_equal(key.cpu().numpy(), rk) and np.array_equal(value.cpu().numpy(), rv)
+
+
+def test_gather_skips_out_of_range_rows():
+    """A block id outside the cache leaves its output rows untouched."""
+    lens = [20]
+    caches = synth.paged_inputs(lens, heads=2, block_size=8, seed=6, device=DEV)
+    caches["block_tables"][0, 1] = 10_000
+    key, _ = gather_gpu(caches, caches["context_lens"], 20)
+    assert torch.isnan(key[8:16].float()).all()
+    table = caches["block_tables"].cpu().numpy().copy()
+    kc = as_bits(caches["key_cache"])
+    for t in (0, 7, 16, 19):
+        assert np.array_equal(as_bits(key[t]), kc[table[0, t // 8], t % 8])
+
+
+def test_gather_full_paged_workload_sampled_rows():
+    """The paged workload at full size (32 sequences, ctx up to 32768, 128 heads):
+    every output token is checked against the cache slot it must come from on a
+    seeded sample, plus each sequence's first and last token."""
+    lens, _ = synth.workload_seqlens("paged")
+    _say(f"[gpu] full paged gather, total tokens {int(lens.sum())}")
+    caches = synth.paged_inputs(lens, device=DEV, with_rope=True)
+    total = int(lens.sum())
+    key, value = gather_gpu(caches, caches["context_lens"], total)
+    rope, _ = gather_gpu(caches, caches["context_lens"], total, with_value=False, key_name="rope_cache")
+    table = caches["block_tables"].cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(lens)])
+    rng = np.random.default_rng(7)
+    picks = set(int(x) for x in rng.integers(0, total, size=4096))
+    for b in range(len(lens)):
+        picks |= {int(off[b]), int(off[b + 1] - 1)}
+    picks = np.array(sorted(picks))
+    b_of = np.searchsorted(off, picks, side="right") - 1
+    t_of = picks - off[b_of]
+    blocks = torch.from_numpy(table[b_of, t_of // 128].astype(np.int64)).to(DEV)
+    slots = torch.from_numpy((t_of % 128).astype(np.int64)).to(DEV)
+    idx = torch.from_numpy(picks).to(DEV)
+    for out, cache in ((key, "key_cache"), (value, "value_cache"), (rope, "rope_cache")):
+        want = caches[cache][blocks, slots]
+        assert torch.equal(out[idx].view(torch.int16), want.view(torch.int16))
