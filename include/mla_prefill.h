@@ -201,20 +201,26 @@ const char *mla_last_error(void);
 
 /*
  * mla_prefill_plan_host -- host-only view of the work list mla_prefill copies
- * into its workspace, for inspection and tests. Writes, into buf (host
- * memory of buf_size bytes), the same bytes mla_prefill would place at the
- * start of the workspace: batch records {q_offset, kv_offset, q_len, kv_len}
- * (int32 each), then work items {batch, first_q_row, kv_tiles, 0} (int32
- * each), heaviest first. kv_padded_max_seq: 0 for packed K/V, else max_seq of
- * the padded layout. *n_items receives the number of work items; one item
- * covers MLA_PLAN_Q_ROWS query rows and its kv_tiles tiles of
- * MLA_PLAN_KV_COLS keys each. Returns MLA_ERR_WORKSPACE if buf is too small.
+ * into its workspace, for inspection and tests. No HIP call. Writes, into buf
+ * (host memory of buf_size bytes), the same bytes mla_prefill would place at
+ * the start of the workspace, three arrays each starting on a 256-byte
+ * boundary:
+ *   batch records  {q_offset, kv_offset, q_len, kv_len}  int32 x 4, batch of them
+ *   work items     {batch, first_q_row, kv_tiles, 0}    int32 x 4, *n_items of them
+ *   tasks          {item, head}                          int32 x 2, *n_tasks of them
+ * One work item covers MLA_PLAN_Q_ROWS query rows of a sequence; kv_tiles
+ * counts the tiles of MLA_PLAN_KV_COLS keys (from key 0) those rows can see.
+ * Task i is the work of workgroup i of the launch (item -1: an empty padding
+ * task). kv_padded_max_seq: 0 for packed K/V, else max_seq of the padded
+ * layout. Returns MLA_ERR_WORKSPACE if buf is too small, MLA_ERR_VALUE for bad
+ * lengths or head counts.
  */
-#define MLA_PLAN_Q_ROWS 128
+#define MLA_PLAN_Q_ROWS 256
 #define MLA_PLAN_KV_COLS 64
 int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch,
-                          int32_t mask_type, int64_t kv_padded_max_seq, void *buf,
-                          uint64_t buf_size, int32_t *n_items);
+                          int32_t head_num, int32_t kv_head_num, int32_t mask_type,
+                          int64_t kv_padded_max_seq, void *buf, uint64_t buf_size,
+                          int32_t *n_items, int32_t *n_tasks);
 
 #ifdef __cplusplus
 }

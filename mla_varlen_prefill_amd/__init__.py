@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_pref
 
 MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
 KV_CACHE_NZ, KV_CACHE_ND = 0, 1
-PLAN_Q_ROWS, PLAN_KV_COLS = 128, 64
+PLAN_Q_ROWS, PLAN_KV_COLS = 256, 64
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_VALUE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
@@ -80,7 +80,8 @@ def _load():
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                          ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint64,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
     for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -184,25 +185,35 @@ def paged_cache_load(key_cache, value_cache, block_tables, context_lens, key, va
         bool(is_seq_lens_cumsum_type), bool(has_seq_starts), _stream_ptr(stream)))
 
 
-def mla_prefill_plan_host(q_seqlen, kv_seqlen, mask_type, kv_padded_max_seq=0):
+def mla_prefill_plan_host(q_seqlen, kv_seqlen, head_num, kv_head_num, mask_type, kv_padded_max_seq=0):
     """The work list mla_prefill would copy to its workspace, decoded.
 
     Returns (seqs [batch, 4] int32 = q_offset, kv_offset, q_len, kv_len;
-    items [n, 4] int32 = batch, first_q_row, kv_tiles, 0).
+    items [n, 4] int32 = batch, first_q_row, kv_tiles, 0;
+    tasks [m, 2] int32 = item (-1: padding), head -- task i is workgroup i).
     """
     lib = _load()
     qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)
     batch = len(qs)
-    n = ctypes.c_int32(0)
-    max_items = int(np.sum((qs.astype(np.int64) + PLAN_Q_ROWS - 1) // PLAN_Q_ROWS)) if batch else 0
-    seq_bytes = (batch * 16 + 255) // 256 * 256
-    buf = np.zeros(seq_bytes + max_items * 16 + 16, dtype=np.uint8)
-    _check("mla_prefill_plan_host", lib.mla_prefill_plan_host(
-        qs.ctypes.data, ks.ctypes.data, batch, int(mask_type), int(kv_padded_max_seq), buf.ctypes.data,
-        buf.nbytes, ctypes.byref(n)))
+    n_items, n_tasks = ctypes.c_int32(0), ctypes.c_int32(0)
+    args = (qs.ctypes.data, ks.ctypes.data, batch, int(head_num), int(kv_head_num), int(mask_type),
+            int(kv_padded_max_seq))
+    rc = lib.mla_prefill_plan_host(*args, None, 0, ctypes.byref(n_items), ctypes.byref(n_tasks))
+    if rc not in (0, -6):  # -6: buffer too small, counts are filled in
+        _check("mla_prefill_plan_host", rc)
+
+    def up(x):
+        return (x + 255) // 256 * 256
+
+    off_items = up(batch * 16)
+    off_tasks = off_items + up(n_items.value * 16)
+    buf = np.zeros(max(1, off_tasks + n_tasks.value * 8), dtype=np.uint8)
+    _check("mla_prefill_plan_host", lib.mla_prefill_plan_host(*args, buf.ctypes.data, buf.nbytes,
+                                                              ctypes.byref(n_items), ctypes.byref(n_tasks)))
     seqs = buf[:batch * 16].view(np.int32).reshape(batch, 4).copy()
-    items = buf[seq_bytes:seq_bytes + n.value * 16].view(np.int32).reshape(n.value, 4).copy()
-    return seqs, items
+    items = buf[off_items:off_items + n_items.value * 16].view(np.int32).reshape(n_items.value, 4).copy()
+    tasks = buf[off_tasks:off_tasks + n_tasks.value * 8].view(np.int32).reshape(n_tasks.value, 2).copy()
+    return seqs, items, tasks
 
 
 def prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num, qk_scale=1.0,

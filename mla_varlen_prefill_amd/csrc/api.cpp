@@ -22,6 +22,9 @@ using mla::HEAD_DIM;
 using mla::MASK_TILE;
 using mla::ROPE_DIM;
 using mla::SeqRec;
+using mla::MLA_CUS_PER_XCD;
+using mla::MLA_XCDS;
+using mla::Task;
 using mla::WorkItem;
 
 static_assert(MLA_PLAN_Q_ROWS == FWD_BM, "plan row count must match the kernel tile");
@@ -237,24 +240,52 @@ int32_t visible_tiles(int mask_type, int32_t q_len, int32_t kv_len, int32_t q_en
     return (int32_t)((visible + FWD_BN - 1) / FWD_BN);
 }
 
+// Relative cost of a task: its key tiles plus one for the fixed per-workgroup
+// work (Q load, pipeline fill, epilogue).
+int64_t task_work(const WorkItem &it) { return (int64_t)it.kv_tiles + 1; }
+
 struct Plan {
     std::vector<SeqRec> seqs;
     std::vector<WorkItem> items;
+    std::vector<Task> tasks;  // one per workgroup, in launch order
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+uint64_t items_offset(const Plan &p) { return align256(p.seqs.size() * sizeof(SeqRec)); }
+uint64_t tasks_offset(const Plan &p) { return items_offset(p) + align256(p.items.size() * sizeof(WorkItem)); }
+
 uint64_t plan_bytes(const Plan &p) {
     if (p.items.empty()) return 0;
-    return align256(p.seqs.size() * sizeof(SeqRec)) + p.items.size() * sizeof(WorkItem);
+    return tasks_offset(p) + p.tasks.size() * sizeof(Task);
 }
 
-// Work list: one item per FWD_BM query rows of each sequence, heaviest first
-// so the long causal rows start early and short ones fill the tail.
-void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int mask_type,
-                int64_t kv_padded_max_seq, Plan *plan) {
+// Work list.
+//  * Items: one per FWD_BM query rows of each sequence, with the number of
+//    key tiles its rows can see.
+//  * Tasks: one workgroup each, an item for one query head.
+//  * Launch order. Tasks that read the same K/V stream (same sequence and KV
+//    head) form a group. Groups are dealt, heaviest first, to the XCD queue
+//    with the least work so far; block i of the launch is taken from queue
+//    i % MLA_XCDS (the hardware hands consecutive workgroups to consecutive
+//    XCDs). Each queue is cut into batches of whole groups holding at least
+//    twice as many tasks as the XCD has CUs, and each batch is ordered
+//    heaviest task first. The tasks of a group thus run together on one XCD
+//    and share its L2 while they stream the same keys, and the heaviest
+//    first order inside a batch keeps the XCD's CUs evenly loaded to the end.
+//    Short queues are padded with empty tasks.
+void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int32_t heads,
+                int32_t kv_heads, int mask_type, int64_t kv_padded_max_seq, Plan *plan) {
     plan->seqs.resize(batch);
     plan->items.clear();
+    plan->tasks.clear();
+    const int32_t group = kv_heads > 0 ? heads / kv_heads : 1;
+    struct Group {
+        int64_t work;
+        int32_t b, hk;
+    };
+    std::vector<Group> groups;
+    std::vector<int32_t> seq_first(batch + 1, 0);  // items of sequence b: [seq_first[b], seq_first[b+1])
     int64_t q_off = 0, kv_off = 0;
     for (int32_t b = 0; b < batch; ++b) {
         SeqRec &s = plan->seqs[b];
@@ -262,21 +293,56 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         s.kv_off = (int32_t)(kv_padded_max_seq ? (int64_t)b * kv_padded_max_seq : kv_off);
         s.q_len = q_seqlen[b];
         s.kv_len = kv_seqlen[b];
-        for (int32_t r = 0; r < s.q_len; r += FWD_BM) {
-            int32_t q_end = std::min(s.q_len, r + FWD_BM);
-            plan->items.push_back({b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), 0});
-        }
         q_off += s.q_len;
         kv_off += s.kv_len;
+        seq_first[b] = (int32_t)plan->items.size();
+        int64_t seq_work = 0;
+        for (int32_t r = 0; r < s.q_len; r += FWD_BM) {
+            int32_t q_end = std::min(s.q_len, r + FWD_BM);
+            WorkItem it{b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), 0};
+            seq_work += task_work(it);
+            plan->items.push_back(it);
+        }
+        if (seq_work > 0)
+            for (int32_t hk = 0; hk < kv_heads; ++hk) groups.push_back({seq_work * group, b, hk});
     }
-    std::stable_sort(plan->items.begin(), plan->items.end(),
-                     [](const WorkItem &a, const WorkItem &b) { return a.kv_tiles > b.kv_tiles; });
+    seq_first[batch] = (int32_t)plan->items.size();
+    std::stable_sort(groups.begin(), groups.end(), [](const Group &x, const Group &y) { return x.work > y.work; });
+    std::vector<std::vector<Group>> xcd_groups(MLA_XCDS);
+    std::vector<int64_t> load(MLA_XCDS, 0);
+    for (const Group &gr : groups) {
+        const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+        load[x] += gr.work;
+        xcd_groups[x].push_back(gr);
+    }
+    std::vector<std::vector<Task>> queue(MLA_XCDS);
+    std::vector<Task> pending;
+    for (int x = 0; x < MLA_XCDS; ++x) {
+        auto flush = [&]() {
+            std::stable_sort(pending.begin(), pending.end(), [&](const Task &u, const Task &v) {
+                return task_work(plan->items[u.item]) > task_work(plan->items[v.item]);
+            });
+            queue[x].insert(queue[x].end(), pending.begin(), pending.end());
+            pending.clear();
+        };
+        for (const Group &gr : xcd_groups[x]) {
+            for (int32_t i = seq_first[gr.b]; i < seq_first[gr.b + 1]; ++i)
+                for (int32_t h = gr.hk * group; h < (gr.hk + 1) * group; ++h) pending.push_back({i, h});
+            if (pending.size() >= 2 * (size_t)MLA_CUS_PER_XCD) flush();
+        }
+        flush();
+    }
+    size_t longest = 0;
+    for (const auto &q : queue) longest = std::max(longest, q.size());
+    plan->tasks.assign(longest * MLA_XCDS, Task{-1, 0});
+    for (int x = 0; x < MLA_XCDS; ++x)
+        for (size_t k = 0; k < queue[x].size(); ++k) plan->tasks[k * MLA_XCDS + x] = queue[x][k];
 }
 
 void write_plan(const Plan &p, uint8_t *dst) {
     std::memcpy(dst, p.seqs.data(), p.seqs.size() * sizeof(SeqRec));
-    std::memcpy(dst + align256(p.seqs.size() * sizeof(SeqRec)), p.items.data(),
-                p.items.size() * sizeof(WorkItem));
+    std::memcpy(dst + items_offset(p), p.items.data(), p.items.size() * sizeof(WorkItem));
+    std::memcpy(dst + tasks_offset(p), p.tasks.data(), p.tasks.size() * sizeof(Task));
 }
 
 }  // namespace
@@ -285,20 +351,23 @@ extern "C" {
 
 const char *mla_last_error(void) { return g_last_error.c_str(); }
 
-int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch,
-                          int32_t mask_type, int64_t kv_padded_max_seq, void *buf, uint64_t buf_size,
-                          int32_t *n_items) {
+int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int32_t head_num,
+                          int32_t kv_head_num, int32_t mask_type, int64_t kv_padded_max_seq, void *buf,
+                          uint64_t buf_size, int32_t *n_items, int32_t *n_tasks) {
     if (batch < 0) return fail(MLA_ERR_VALUE, "batch must be >= 0");
     if (batch > 0 && (q_seqlen == nullptr || kv_seqlen == nullptr))
         return fail(MLA_ERR_NULL, "length arrays are NULL");
-    if (n_items == nullptr) return fail(MLA_ERR_NULL, "n_items is NULL");
+    if (n_items == nullptr || n_tasks == nullptr) return fail(MLA_ERR_NULL, "n_items / n_tasks is NULL");
+    if (head_num <= 0 || kv_head_num <= 0 || head_num % kv_head_num != 0)
+        return fail(MLA_ERR_VALUE, "headNum / kvHeadNum invalid");
     if (mask_type < MLA_MASK_UNDEFINED || mask_type > MLA_MASK_FREE)
         return fail(MLA_ERR_VALUE, "maskType %d is not a known mask type", mask_type);
     for (int32_t b = 0; b < batch; ++b)
         if (q_seqlen[b] < 0 || kv_seqlen[b] < 0) return fail(MLA_ERR_VALUE, "negative length");
     Plan plan;
-    build_plan(q_seqlen, kv_seqlen, batch, mask_type, kv_padded_max_seq, &plan);
+    build_plan(q_seqlen, kv_seqlen, batch, head_num, kv_head_num, mask_type, kv_padded_max_seq, &plan);
     *n_items = (int32_t)plan.items.size();
+    *n_tasks = (int32_t)plan.tasks.size();
     uint64_t need = plan_bytes(plan);
     if (need > 0) {
         if (buf == nullptr || buf_size < need)
@@ -321,7 +390,8 @@ int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope
                               kv_head_num, mask_type, cache_mode, atten_out, &pr);
     if (rc) return rc;
     Plan plan;
-    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.mask_type, pr.kv_padded_max_seq, &plan);
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
+               &plan);
     *workspace_size = plan_bytes(plan);
     return ok();
 }
@@ -337,7 +407,8 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
                               kv_head_num, mask_type, cache_mode, atten_out, &pr);
     if (rc) return rc;
     Plan plan;
-    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.mask_type, pr.kv_padded_max_seq, &plan);
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
+               &plan);
     const uint64_t need = plan_bytes(plan);
     if (need == 0) return ok();  // no query rows: nothing to write
     if (workspace == nullptr || workspace_size < need)
@@ -345,7 +416,7 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
                     (unsigned long long)need, (unsigned long long)workspace_size);
     if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
         return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    if (plan.items.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
+    if (plan.tasks.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
 
     std::vector<uint8_t> host(need);
     write_plan(plan, host.data());
@@ -363,14 +434,20 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
     p.out = atten_out->data;
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     p.seqs = reinterpret_cast<const SeqRec *>(ws);
-    p.items = reinterpret_cast<const WorkItem *>(ws + align256(plan.seqs.size() * sizeof(SeqRec)));
+    p.items = reinterpret_cast<const WorkItem *>(ws + items_offset(plan));
+    p.tasks = reinterpret_cast<const Task *>(ws + tasks_offset(plan));
     p.heads = head_num;
     p.kv_heads = kv_head_num;
     p.group = head_num / kv_head_num;
+    p.n_tasks = (int32_t)plan.tasks.size();
     p.mask_type = mask_type;
     p.mask_is_bf16 = (mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;
-    p.scale_log2 = (float)((double)qk_scale * 1.4426950408889634);
-    e = mla::launch_mla_fwd(p, pr.dtype, (int)plan.items.size(), s);
+    // A zero (or denormal) scale is replaced by +-1e-30: the kernel divides mask
+    // values by the scale, and the change is below fp32 resolution of the scores.
+    double scale = (double)qk_scale;
+    if (std::fabs(scale) < 1e-30) scale = std::signbit(scale) ? -1e-30 : 1e-30;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    e = mla::launch_mla_fwd(p, pr.dtype, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "attention launch: %s", hipGetErrorString(e));
     return ok();
 }

@@ -8,9 +8,9 @@ namespace mla {
 
 // Tile shape of the attention kernel: one workgroup owns FWD_BM query rows of
 // one (sequence, head) and walks the visible keys in tiles of FWD_BN.
-constexpr int FWD_BM = 128;
+constexpr int FWD_BM = 256;
 constexpr int FWD_BN = 64;
-constexpr int FWD_THREADS = 256;
+constexpr int FWD_THREADS = 512;
 constexpr int HEAD_DIM = 128;   // embeddimV handled by the kernel
 constexpr int ROPE_DIM = 64;    // rope part, fixed by the operator definition
 constexpr int MASK_TILE = 512;  // side of the MASK_FREE tile
@@ -32,6 +32,18 @@ struct WorkItem {
     int32_t pad;
 };
 
+// One workgroup's task: a work item and a query head. item == -1 marks an
+// empty padding task.
+struct Task {
+    int32_t item;
+    int32_t head;
+};
+
+// MI355X: 8 XCDs of 32 CUs; consecutive workgroups of a launch go to
+// consecutive XCDs.
+constexpr int MLA_XCDS = 8;
+constexpr int MLA_CUS_PER_XCD = 32;
+
 struct FwdParams {
     const void *q;        // [nq, H, 128]
     const void *q_rope;   // [nq, H, 64]
@@ -42,16 +54,18 @@ struct FwdParams {
     void *out;            // [nq, H, 128]
     const SeqRec *seqs;
     const WorkItem *items;
+    const Task *tasks;
     int32_t heads;
     int32_t kv_heads;
     int32_t group;        // heads / kv_heads
     int32_t mask_type;    // enum mla_mask_type
     int32_t mask_is_bf16; // dtype of the MASK_FREE tile
+    int32_t n_tasks;      // workgroups to launch
     float scale_log2;     // qkScale * log2(e)
 };
 
-// dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). n_items workgroups per head.
-hipError_t launch_mla_fwd(const FwdParams &p, int dtype, int n_items, hipStream_t stream);
+// dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). One workgroup per task.
+hipError_t launch_mla_fwd(const FwdParams &p, int dtype, hipStream_t stream);
 
 struct GatherParams {
     const void *key_cache;

@@ -186,16 +186,16 @@ def visible_count(mask_type, ql, kl, i):
 
 
 @pytest.mark.parametrize("mask_type", [0, 1, 2, 3])
-@pytest.mark.parametrize("case", [([17, 40], [17, 40]), ([300, 1, 0, 129], [1000, 1, 5, 100]),
-                                  ([2048] * 3, [16384] * 3), ([700], [100])])
+@pytest.mark.parametrize("case", [([17, 40], [17, 40], 4, 4), ([300, 1, 0, 129], [1000, 1, 5, 100], 8, 2),
+                                  ([2048] * 3, [16384] * 3, 16, 16), ([700], [100], 2, 1)])
 def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
-    qs, ks = case
-    seqs, items = mla.mla_prefill_plan_host(qs, ks, mask_type)
+    qs, ks, heads, kv_heads = case
+    seqs, items, tasks = mla.mla_prefill_plan_host(qs, ks, heads, kv_heads, mask_type)
     # batch records are prefix sums
     assert (seqs[:, 0] == np.concatenate([[0], np.cumsum(qs)[:-1]])).all()
     assert (seqs[:, 1] == np.concatenate([[0], np.cumsum(ks)[:-1]])).all()
     assert (seqs[:, 2] == qs).all() and (seqs[:, 3] == ks).all()
-    # every (b, q-tile) exactly once
+    # every (b, q-tile) is one item
     want = sorted((b, r) for b, n in enumerate(qs) for r in range(0, n, mla.PLAN_Q_ROWS))
     assert sorted((int(b), int(r)) for b, r, _, _ in items) == want
     # tile range = tiles holding the furthest visible key of any row in the item
@@ -203,12 +203,31 @@ def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
         ql, kl = qs[b], ks[b]
         far = max(visible_count(mask_type, ql, kl, i) for i in range(r, min(ql, r + mla.PLAN_Q_ROWS)))
         assert nt == -(-far // mla.PLAN_KV_COLS), (b, r)
-    # heaviest first
-    assert (np.diff(items[:, 2]) <= 0).all()
+    # every (item, head) is exactly one task; the rest is padding
+    real = tasks[tasks[:, 0] >= 0]
+    assert sorted(map(tuple, real.tolist())) == sorted((i, h) for i in range(len(items)) for h in range(heads))
+    assert len(tasks) % 8 == 0
+    # the tasks reading one K/V stream (sequence, kv head) sit on one XCD (task index mod 8)
+    xcd_of = {}
+    for i, (it, h) in enumerate(tasks.tolist()):
+        if it < 0:
+            continue
+        key = (int(items[it][0]), h // (heads // kv_heads))
+        assert xcd_of.setdefault(key, i % 8) == i % 8
+
+
+def test_plan_balances_xcds_on_causal_workload():
+    """4096-token causal prefill with 128 heads: every XCD gets the same work."""
+    seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 128, 128, mla.MASK_CAUSAL)
+    work = np.zeros(8)
+    for i, (it, h) in enumerate(tasks.tolist()):
+        if it >= 0:
+            work[i % 8] += items[it][2] + 1
+    assert work.max() == work.min()
 
 
 def test_plan_padded_offsets():
-    seqs, _ = mla.mla_prefill_plan_host([3, 4, 5], [7, 8, 9], 2, kv_padded_max_seq=10)
+    seqs, _, _ = mla.mla_prefill_plan_host([3, 4, 5], [7, 8, 9], 2, 2, 2, kv_padded_max_seq=10)
     assert list(seqs[:, 1]) == [0, 10, 20]
 
 
