@@ -35,6 +35,7 @@ PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 FLOP_PER_PAIR = 2 * (128 + 64) + 2 * 128
 PMC_FILE = os.path.join(ROOT, "profiles", "mla_fwd_single_pmc.json")
+COPY_BYTES = 1 << 30  # plain copy of known size, for scaling the HBM counters
 
 
 def visible_pairs(qs, ks, mask_type):
@@ -69,6 +70,54 @@ def traffic_from_profile():
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def calibration_copy():
+    """A plain device copy of COPY_BYTES (reads and writes COPY_BYTES of HBM)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def summarize_pmc(fetch_dir, write_dir, out_json):
+    """Turn two rocprofv3 --pmc runs of `bench.py --calibrate-copy` (one with
+    FETCH_SIZE, one with WRITE_SIZE) into HBM bytes per attention launch.
+
+    Each counter is scaled by COPY_BYTES over what it read for the plain copy
+    kernel in the same run."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        copy = [v for (i, k), v in vals.items() if "copy" in k.lower() and "mla" not in k]
+        attn = [v for (i, k), v in vals.items() if "mla_fwd_kernel" in k]
+        return max(copy), attn
+
+    fetch_copy, fetch_attn = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write_copy, write_attn = per_dispatch(write_dir, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch_copy * 1024.0)
+    w_scale = COPY_BYTES / (write_copy * 1024.0)
+    fetch = float(np.median(fetch_attn)) * 1024.0 * f_scale
+    write = float(np.median(write_attn)) * 1024.0 * w_scale
+    rec = {"kernel": "mla_fwd_kernel", "workload": "single", "kernel_source_sha256_16": kernel_source_hash(),
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "attn_fetch_kib_median": float(np.median(fetch_attn)), "attn_write_kib_median": float(np.median(write_attn)),
+           "hbm_fetch_bytes_per_launch": fetch, "hbm_write_bytes_per_launch": write,
+           "hbm_bytes_per_launch": fetch + write, "dispatches": len(fetch_attn)}
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def bench_attention(name, steps, warmup):
@@ -167,7 +216,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain copy of known size first (for scaling rocprofv3 HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
+                    help="turn FETCH_SIZE / WRITE_SIZE rocprofv3 runs into HBM bytes per launch, then exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
               "(the path runs on a single MI355X, without collectives).", file=sys.stderr)
@@ -176,6 +232,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.calibrate_copy:
+        calibration_copy()
     res = bench_attention(args.workload, args.steps, args.warmup)
     flops = res["flops"]
     value = flops / (res["ms_per_step"] * 1e-3) / 1e12

@@ -86,10 +86,22 @@ extern "C" __device__ i32x4 mla_raw_buffer_load_b128(i32x4 rsrc, int voffset, in
 extern "C" __device__ void mla_raw_buffer_store_b64(i16x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i16");
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 struct Bf16 {
     typedef bf16x8 vec8;
     typedef bf16x4 vec4;
+    typedef bf16x2 pair;
     typedef __bf16 scalar;
+    static __device__ __forceinline__ pair pack(float a, float b) {
+        return pair{static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    }
+    // acc + x[0] + x[1], products and sum in fp32
+    static __device__ __forceinline__ float dot2_ones(pair x, float acc) {
+        const pair one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+        return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+    }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -97,7 +109,15 @@ struct Bf16 {
 struct Fp16 {
     typedef f16x8 vec8;
     typedef f16x4 vec4;
+    typedef f16x2 pair;
     typedef _Float16 scalar;
+    static __device__ __forceinline__ pair pack(float a, float b) {
+        return pair{static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    }
+    static __device__ __forceinline__ float dot2_ones(pair x, float acc) {
+        const pair one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+        return __builtin_amdgcn_fdot2(x, one, acc, false);
+    }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
     }
@@ -367,10 +387,10 @@ void mla_fwd_kernel(const FwdParams p) {
     auto valu_block = [&](int kt) __attribute__((always_inline)) {
         float mx = -INFINITY;
         if (wave_full(kt)) {
+            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+            for (int t = 0; t < 32; ++t) m4[t & 3] = fmaxf(m4[t & 3], s[t >> 4][t & 15]);
+            mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
         } else {
             const int key0 = kt * BN;
             const unsigned short *mrow = nullptr;
@@ -414,15 +434,21 @@ void mla_fwd_kernel(const FwdParams p) {
             m_run = m_new;
         }
         const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        float lsum = 0.f;
+        // probabilities, rounded to the input dtype; the row sum is taken over
+        // the rounded values (the ones the PV product uses) with dot2 against
+        // (1, 1), in four independent partial sums
+        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
+        for (int t = 0; t < 32; t += 2) {
             const int kb = t >> 4, e = t & 15;
-            const float pe = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
-            lsum += pe;
-            pb[kb * 2 + (e >> 3)][e & 7] = static_cast<typename T::scalar>(pe);
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -mc));
+            const typename T::pair pr = T::pack(p0, p1);
+            lsum[(t >> 1) & 3] = T::dot2_ones(pr, lsum[(t >> 1) & 3]);
+            pb[kb * 2 + (e >> 3)][e & 7] = pr[0];
+            pb[kb * 2 + (e >> 3)][(e & 7) + 1] = pr[1];
         }
-        l_run += lsum;
+        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
     };
 
     const std::integral_constant<bool, true> yes{};
