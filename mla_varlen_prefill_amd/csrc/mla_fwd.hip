@@ -7,28 +7,31 @@
 //
 // One workgroup = 8 waves = FWD_BM = 256 query rows of one (sequence, head).
 //
-//  * Each wave owns 32 query rows. Their Q | QRope (32 x 192) stay in VGPRs as
-//    the B operand of v_mfma_f32_32x32x16 (12 k-steps of 16: 8 nope, 4 rope).
-//  * Keys are walked in tiles of FWD_BN = 64. K-nope (64 x 128), K-rope
-//    (64 x 64) and V (64 x 128) of a tile are copied HBM -> LDS by the
-//    buffer-load-to-LDS DMA path (no VGPR staging), into a 3-stage ring.
-//    Key rows past the sequence end fall outside the buffer range and
-//    arrive as zeros.
-//  * LDS rows are XOR-swizzled in 16-byte chunks so that both the 16-byte
-//    reads of K (one key row per lane) and the transposing 8-byte reads of V
-//    are free of bank conflicts without padding.
+//  * Each wave owns 32 query rows. Their Q (32 x 128) stays in VGPRs as the
+//    B operand of v_mfma_f32_32x32x16 (8 k-steps of 16); QRope of the
+//    workgroup's 256 rows (4 more k-steps) sits in LDS.
+//  * Keys are walked in tiles of FWD_BN = 64 through a 3-stage LDS ring. K-nope
+//    (64 x 128) and K-rope (64 x 64) of a tile are copied HBM -> LDS by the
+//    buffer-load-to-LDS DMA path; V (64 x 128) is loaded to VGPRs and written
+//    transposed, V^T (128 x 64), as (key, key + 1) dword pairs. Key rows past
+//    the sequence end fall outside the buffer range and arrive as zeros.
+//  * LDS rows are XOR-swizzled in 16-byte chunks so that every MFMA operand is
+//    one conflict-free 16-byte read per lane, without padding.
 //  * Scores are computed transposed, S^T = K . Q^T: the accumulator holds one
 //    query row per lane (lanes l and l + 32 share it), so row max / row sum
 //    take one cross-lane swap, and the probabilities already sit in the
-//    B-operand layout of O^T = V^T . P^T. V^T operands come straight from the
-//    row-major V tile through ds_read_b64_tr_b16.
+//    B-operand layout of O^T = V^T . P^T. K rows are stored with bits 2 and 3
+//    of the key index swapped, which makes each lane's 8 probabilities of a
+//    16-key step consecutive keys, the k-order of a V^T operand read.
 //  * Ping-pong schedule. The waves form two groups, one wave of each per
 //    SIMD. Workgroup barriers cut time into intervals; in every interval one
 //    group runs a matrix block (O += P_j V_j, then S_{j+1} = K_{j+1} Q^T: 40
-//    MFMAs fed from LDS two operands ahead) while the other runs a vector
+//    MFMAs fed from LDS a few operands ahead) while the other runs a vector
 //    block (mask, row max, online-softmax update and probabilities of one
 //    tile), and the roles swap at each barrier. The matrix core of each SIMD
 //    is thus fed by one wave while the other wave's softmax runs on the VALU.
+//    The leading group issues all tile loads, spread over its matrix blocks,
+//    so the vector blocks carry no memory instructions.
 //  * Online softmax in fp32 with exp2 (log2(e) folded into the scale). The
 //    running max is only moved -- and O rescaled -- when a tile raises some
 //    row's max by more than 2^8 in probability units, so most tiles skip the
@@ -56,11 +59,18 @@ constexpr int STAGES = 3;
 #ifndef MLA_PREFETCH
 #define MLA_PREFETCH 2
 #endif
+#ifndef MLA_LOAD_SPACING
+#define MLA_LOAD_SPACING 4
+#endif
+constexpr int LOAD_SPACING = MLA_LOAD_SPACING;  // MFMAs between the tile loads a matrix block issues
 constexpr int PREFETCH = MLA_PREFETCH;  // LDS operands in flight ahead of the MFMA using them
 constexpr int KN_BYTES = BN * DN * 2;  // 16 KB
 constexpr int KR_BYTES = BN * DR * 2;  // 8 KB
 constexpr int V_BYTES = BN * DN * 2;   // 16 KB
 constexpr int STAGE_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
+constexpr int QR_OFFSET = STAGES * STAGE_BYTES;  // Q-rope of the item's rows
+constexpr int QR_BYTES = BM * DR * 2;             // 32 KB
+constexpr int LDS_BYTES = QR_OFFSET + QR_BYTES;   // 152 KB
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -177,7 +187,7 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char *p) {
 template <typename T>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void mla_fwd_kernel(const FwdParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
     typedef typename T::vec8 vec8;
 
     const int tid = threadIdx.x;
@@ -204,81 +214,169 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // The two waves sharing a SIMD (w, w + 4) take adjacent 32-row blocks, so
     // both groups see the same share of diagonal tiles.
-    const int row0 = item.q_row0 + (wave & 3) * 64 + grp * 32;  // first query row of this wave
-    const int qi = row0 + r32;                                  // this lane's query row
-    const int pos = kv_len - q_len + qi;                        // its key position
-    const int wpos0 = kv_len - q_len + row0;                    // key positions of the wave's rows
+    const int lrow0 = (wave & 3) * 64 + grp * 32;   // first row of this wave within the item
+    const int row0 = item.q_row0 + lrow0;           // ... within the sequence
+    const int qi = row0 + r32;                      // this lane's query row
+    const int pos = kv_len - q_len + qi;            // its key position
+    const int wpos0 = kv_len - q_len + row0;        // key positions of the wave's rows
     const int wpos1 = wpos0 + 31;
 
-    // ---- Q^T operand (B of S^T = K . Q^T): lane holds row r32, k-slots g*8..g*8+7.
-    // Rows past the sequence end read as zeros.
-    vec8 qreg[12];
+    // ---- Q-nope^T operand (B of S^T = K . Q^T) in VGPRs: lane holds row r32,
+    // k-slots g*8..g*8+7 of each 16-wide k-step. Rows past the end read as 0.
+    vec8 qreg[8];
     {
         const int rows = max(0, min(32, q_len - row0));
         const int64_t tok = (int64_t)seq.q_off + row0;
         const i32x4 rq = make_rsrc(static_cast<const unsigned char *>(p.q) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
-        const i32x4 rqr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
-                                    (uint32_t)rows * H * DR * 2);
         const uint32_t qo = (uint32_t)r32 * H * DN * 2 + g * 16;
-        const uint32_t qro = (uint32_t)r32 * H * DR * 2 + g * 16;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
             qreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rq, qo + ks * 32, 0, 0));
+    }
+    // ---- Q-rope of the item's 256 rows -> LDS (DMA), rows swizzled by 16-byte
+    // chunk: chunk c of row r sits at c ^ ((r >> 1) & 7).
+    {
+        const int rows = max(0, min(BM, q_len - item.q_row0));
+        const int64_t tok = (int64_t)seq.q_off + item.q_row0;
+        const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
+                                   (uint32_t)rows * H * DR * 2);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qreg[8 + ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rqr, qro + ks * 32, 0, 0));
+        for (int u = 0; u < QR_BYTES / (NT * 16); ++u) {
+            const int slot = tid + NT * u;
+            const int r = slot >> 3;
+            const uint32_t src = (uint32_t)r * H * DR * 2 + ((((slot & 7) ^ ((r >> 1) & 7))) << 4);
+            mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(smem + QR_OFFSET + u * NT * 16 + wave * 64 * 16), 16, src,
+                                    0, 0, 0);
+        }
     }
 
-    // ---- K / V tile streaming (LDS-DMA). Tile kt -> ring stage kt % 3.
+    // ---- K / V tile streaming. Tile kt lives in ring stage kt % 3.
+    //  * K-nope and K-rope go HBM -> LDS by DMA. Row m of the K tile holds key
+    //    perm(m), perm swapping bits 2 and 3 of the key index, so that after
+    //    S^T = K . Q^T each lane's probabilities of a 16-key step are 8
+    //    consecutive keys (what the V^T operand read below needs).
+    //  * V goes HBM -> VGPRs (two 16-byte rows pieces per thread) and is
+    //    written transposed, V^T[d][key], into LDS one interval later.
     const unsigned char *kbase = static_cast<const unsigned char *>(p.k);
     const unsigned char *krbase = static_cast<const unsigned char *>(p.k_rope);
     const unsigned char *vbase = static_cast<const unsigned char *>(p.v);
     const uint32_t kn_row = (uint32_t)HKV * DN * 2;  // bytes between consecutive keys
     const uint32_t kr_row = (uint32_t)HKV * DR * 2;
-    // per-thread source offsets (fixed across tiles): LDS slot -> (key, swizzled chunk)
-    uint32_t off_kn[2], off_v[2], off_kr;
+    auto perm_key = [](int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); };
+    // The leading group (waves 0-3, threads 0..LT-1) loads every tile, ten
+    // instructions per thread: K-nope in four DMA (slot tid + LT*u: row
+    // slot / 16, chunk slot % 16), K-rope in two (row slot / 8, chunk slot % 8),
+    // V in four loads to registers (keys 2kp and 2kp + 1, 16-byte column
+    // chunks 2dg and 2dg + 1). In the loop they go out one every four MFMAs of
+    // the group's matrix block, so no wave stalls behind a burst of address
+    // work in the texture unit and the trailing group's vector block issues no
+    // memory instruction at all.
+    constexpr int LT = NT / 2;
+    uint32_t off_kn[4], off_kr[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int slot = tid + LT * u;
+        const int m = slot >> 4;
+        off_kn[u] = perm_key(m) * kn_row + (((slot & 15) ^ (m & 15)) << 4);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int slot = tid + NT * u;
-        const int key = slot >> 4;
-        off_kn[u] = key * kn_row + (((slot & 15) ^ (key & 15)) << 4);
-        off_v[u] = key * kn_row + (((slot & 15) ^ ((key & 3) << 2)) << 4);
+        const int slot = tid + LT * u;
+        const int m = slot >> 3;
+        off_kr[u] = perm_key(m) * kr_row + (((slot & 7) ^ ((m >> 1) & 7)) << 4);
     }
-    {
-        const int key = tid >> 3;
-        off_kr = key * kr_row + (((tid & 7) ^ ((key >> 1) & 7)) << 4);
-    }
-    auto issue_tile = [&](int kt) __attribute__((always_inline)) {
-        unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
-        const int64_t rowi = ((int64_t)seq.kv_off + (int64_t)kt * BN) * HKV + hk;  // first key row, this head
-        const uint32_t nvalid = (uint32_t)min(kv_len - kt * BN, BN);
-        const i32x4 rk = make_rsrc(kbase + rowi * (DN * 2), nvalid * kn_row);
-        const i32x4 rr = make_rsrc(krbase + rowi * (DR * 2), nvalid * kr_row);
-        const i32x4 rv = make_rsrc(vbase + rowi * (DN * 2), nvalid * kn_row);
-        const int wofs = wave * 64 * 16;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            mla_raw_buffer_load_lds(rk, (lds_u32_ptr)(st + u * NT * 16 + wofs), 16, off_kn[u], 0, 0, 0);
-        mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(st + KN_BYTES + wofs), 16, off_kr, 0, 0, 0);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            mla_raw_buffer_load_lds(rv, (lds_u32_ptr)(st + KN_BYTES + KR_BYTES + u * NT * 16 + wofs), 16,
-                                    off_v[u], 0, 0, 0);
+    const int kp = tid & 31, dg = (tid >> 5) & 7;
+    // two VGPR offsets (the buffer range check covers the VGPR offset and the
+    // immediate, not the SGPR offset, so the key step must not go there)
+    const uint32_t off_v[2] = {(uint32_t)(2 * kp) * kn_row + dg * 32, (uint32_t)(2 * kp + 1) * kn_row + dg * 32};
+    struct TileLoad {
+        i32x4 rk, rr, rv;
+        unsigned char *st;
     };
-    constexpr int LOADS_PER_TILE = 5;  // DMA instructions per thread and tile
+    auto prep_tile = [&](int kt) __attribute__((always_inline)) -> TileLoad {
+        const int64_t rowi = ((int64_t)seq.kv_off + (int64_t)kt * BN) * HKV + hk;  // first key row, this head
+        const uint32_t nvalid = (uint32_t)max(0, min(kv_len - kt * BN, BN));
+        TileLoad tl;
+        tl.rk = make_rsrc(kbase + rowi * (DN * 2), nvalid * kn_row);
+        tl.rr = make_rsrc(krbase + rowi * (DR * 2), nvalid * kr_row);
+        tl.rv = make_rsrc(vbase + rowi * (DN * 2), nvalid * kn_row);
+        tl.st = smem + (kt % STAGES) * STAGE_BYTES;
+        return tl;
+    };
+    constexpr int LOADS_PER_TILE = 10;
+    // load i of a tile (leading group only); V loads j = i - 6 land in vst[j]:
+    // key 2kp + (j & 1), column chunk 2dg + (j >> 1)
+    auto issue_part = [&](const TileLoad &tl, int i, uint4 *vst) __attribute__((always_inline)) {
+        const int wofs = wave * 64 * 16;
+        if (i < 4) {
+            mla_raw_buffer_load_lds(tl.rk, (lds_u32_ptr)(tl.st + i * LT * 16 + wofs), 16, off_kn[i], 0, 0, 0);
+        } else if (i < 6) {
+            mla_raw_buffer_load_lds(tl.rr, (lds_u32_ptr)(tl.st + KN_BYTES + (i - 4) * LT * 16 + wofs), 16,
+                                    off_kr[i - 4], 0, 0, 0);
+        } else {
+            const int j = i - 6;
+            vst[j] = __builtin_bit_cast(uint4, mla_raw_buffer_load_b128(tl.rv, off_v[j & 1] + (j >> 1) * 16, 0, 0));
+        }
+    };
+    auto issue_tile = [&](int kt, uint4 *vst) __attribute__((always_inline)) {
+        const TileLoad tl = prep_tile(kt);
+#pragma unroll
+        for (int i = 0; i < LOADS_PER_TILE; ++i) issue_part(tl, i, vst);
+    };
+    // V^T region of a stage: row d (128 B = 64 keys), 16-byte chunk c (8 keys)
+    // at position c ^ ((d >> 1) & 7). A leading thread writes the dwords
+    // (key 2kp, 2kp + 1) of rows 16dg .. 16dg + 15: for d = 16dg + 8h + 2dd (+1),
+    // (d >> 1) & 7 = 4h + dd, so the offset is vw_base ^ ((4h + dd) << 4) plus
+    // 1024h + 256dd (+128).
+    const uint32_t vw_base = KN_BYTES + KR_BYTES + dg * 2048 + ((kp >> 2) << 4) + (kp & 3) * 4;
+    auto write_vt = [&](int kt, const uint4 *vst) __attribute__((always_inline)) {
+        unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
+        uint32_t vwb = vw_base;
+        asm volatile("" : "+v"(vwb));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const unsigned a[4] = {vst[2 * h].x, vst[2 * h].y, vst[2 * h].z, vst[2 * h].w};  // key 2kp
+            const unsigned b[4] = {vst[2 * h + 1].x, vst[2 * h + 1].y, vst[2 * h + 1].z, vst[2 * h + 1].w};
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const uint32_t w = (vwb ^ ((4 * h + dd) << 4)) + h * 1024 + dd * 256;
+                *reinterpret_cast<unsigned *>(st + w) = __builtin_amdgcn_perm(b[dd], a[dd], 0x05040100u);
+                *reinterpret_cast<unsigned *>(st + w + 128) = __builtin_amdgcn_perm(b[dd], a[dd], 0x07060302u);
+            }
+        }
+    };
 
-    if (n_kt > 0) issue_tile(0);
-    if (n_kt > 1) issue_tile(1);
+    // Loads of a tile past the last one have no valid rows (they return
+    // zeros) and land in a ring stage no longer read, so the leading group
+    // issues them unconditionally: one code path keeps the V registers in
+    // place across the loop.
+    uint4 vstage[4];
+    if (grp == 0) {
+        uint4 v0[4];
+        issue_tile(0, v0);
+        issue_tile(1, vstage);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE);  // tile 0, Q and Q-rope landed; tile 1 may still fly
+        write_vt(0, v0);
+    } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
+    }
 
-    // A negative scale is folded into Q so the row max can be taken on raw scores.
+    // A negative scale is folded into Q so the row max can be taken on raw
+    // scores: Q-nope is negated in registers, Q-rope in LDS (each thread flips
+    // the chunks its own DMA wrote; the barrier before the schedule publishes them).
     const float c = fabsf(p.scale_log2);
     if (p.scale_log2 < 0.f) {
 #pragma unroll
-        for (int ks = 0; ks < 12; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
             i32x4 w = __builtin_bit_cast(i32x4, qreg[ks]);
             w ^= (int)0x80008000;
             qreg[ks] = __builtin_bit_cast(vec8, w);
+        }
+#pragma unroll
+        for (int u = 0; u < QR_BYTES / (NT * 16); ++u) {
+            i32x4 *q = reinterpret_cast<i32x4 *>(smem + QR_OFFSET + (u * NT + tid) * 16);
+            *q ^= (int)0x80008000;
         }
     }
 
@@ -300,43 +398,31 @@ void mla_fwd_kernel(const FwdParams p) {
         return full;
     };
 
-    // ---- per-lane LDS read offsets: every operand read is one of these lane
-    // offsets plus a compile-time immediate (ring stage, key block, step).
-    // K (A operand of S^T): lane reads key kb*32 + r32, 16-byte chunk 2*ks + g.
-    // With the chunk swizzles c ^ (key & 15) (nope) and c ^ ((key >> 1) & 7)
-    // (rope) and key & 31 == r32, the lane offset depends on ks but not kb.
-    uint32_t k_off[12];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) k_off[ks] = r32 * 256 + (((2 * ks + g) ^ (r32 & 15)) << 4);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) k_off[8 + ks] = KN_BYTES + r32 * 128 + (((2 * ks + g) ^ ((r32 >> 1) & 7)) << 4);
-    // V^T (A operand of O^T, transposing read): within a 16-lane group, lane sl
-    // points at 4 consecutive columns of key 4*(group/2) + sl/4; the chunk
-    // swizzle c ^ ((key & 3) << 2) then depends on the column block db only.
-    uint32_t v_off[4];
-    {
-        const int lg = lane >> 4, sl = lane & 15;
-        const int vk = 4 * (lg >> 1) + (sl >> 2);
-        const int vcl = 2 * (lg & 1) + ((sl & 3) >> 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            v_off[db] = KN_BYTES + KR_BYTES + vk * 256 + (((db * 4 + vcl) ^ ((vk & 3) << 2)) << 4) + (sl & 1) * 8;
-    }
+    // ---- per-lane LDS read offsets. With the XOR swizzles, the offset of
+    // step k (k-step, or 16-key step for V^T) is base ^ (k << 5) for one base
+    // per operand kind; the key block / column block adds a multiple of 4 KB
+    // or 8 KB. Each matrix block forms its addresses from an opaque copy of
+    // the bases (one VALU op per read) instead of keeping 24 of them live.
+    //  K-nope (A of S^T): tile row kb*32 + r32, chunk 2*ks + g, swizzle ^ (row & 15)
+    //  K-rope:            row kb*32 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
+    //  Q-rope (B):        item row lrow0 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
+    //  V^T (A of O^T):    row d = 32*db + r32, chunk 2*st4 + g, swizzle ^ ((d >> 1) & 7)
+    const uint32_t kn_base = r32 * 256 + ((g ^ (r32 & 15)) << 4);
+    const uint32_t kr_base = KN_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
+    const uint32_t qr_base = QR_OFFSET + (lrow0 + r32) * 128 + ((g ^ (((lrow0 + r32) >> 1) & 7)) << 4);
+    const uint32_t vt_base = KN_BYTES + KR_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
+
+    auto lds16 = [](const unsigned char *a) __attribute__((always_inline)) -> vec8 {
+        return __builtin_bit_cast(vec8, *reinterpret_cast<const uint4 *>(a));
+    };
     // operand n of a matrix block: n < 16 -> V^T of (16-key step n/4, column block
     // n%4) from stage sv; n >= 16 -> K of (k-step (n-16)/2, key block (n-16)%2) from sk
-    auto load_operand = [&](const unsigned char *sv, const unsigned char *sk, int n) __attribute__((always_inline))
-        -> vec8 {
-        if (n < 16) {
-            const int st4 = n >> 2, db = n & 3;
-            const i16x4 lo = lds_read_tr16(sv + v_off[db] + st4 * 16 * 256);
-            const i16x4 hi = lds_read_tr16(sv + v_off[db] + st4 * 16 * 256 + 8 * 256);
-            const i16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            return __builtin_bit_cast(vec8, a);
-        }
+    auto load_operand = [&](const unsigned char *sv, const unsigned char *sk, int n, uint32_t knb, uint32_t krb,
+                            uint32_t vtb) __attribute__((always_inline)) -> vec8 {
+        if (n < 16) return lds16(sv + (vtb ^ ((n >> 2) << 5)) + (n & 3) * 32 * 128);
         const int ks = (n - 16) >> 1, kb = (n - 16) & 1;
-        const int row_step = ks < 8 ? 256 : 128;
-        const uint4 u = *reinterpret_cast<const uint4 *>(sk + k_off[ks] + kb * 32 * row_step);
-        return __builtin_bit_cast(vec8, u);
+        if (ks < 8) return lds16(sk + (knb ^ (ks << 5)) + kb * 32 * 256);
+        return lds16(sk + (krb ^ ((ks - 8) << 5)) + kb * 32 * 128);
     };
 
     // ---- softmax state
@@ -347,14 +433,18 @@ void mla_fwd_kernel(const FwdParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
-    f32x16 s[2];  // scores of one tile; element e of block kb is key kb*32 + 8*(e/4) + 4*g + e%4
-    vec8 pb[4];   // P^T operands of the four 16-key steps
+    // scores of one tile; element e of block kb is key
+    // kb*32 + 16*(e/8) + 8*g + (e%8) of the tile (see perm_key)
+    f32x16 s[2];
+    vec8 pb[4];  // P^T operands of the four 16-key steps
 
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
-    // stage sk); either half may be switched off. Operands are read two ahead.
-    auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk)
-        __attribute__((always_inline)) {
+    // stage sk); either half may be switched off. Operands are read ahead.
+    // ISS: issue the loads of tile tl, one every LOAD_SPACING MFMAs
+    auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
+                          const TileLoad &tl) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
+        constexpr bool ISS = decltype(do_iss)::value;
         constexpr int n0 = PV ? 0 : 16, n1 = QK ? 40 : 16;
         if (QK) {
 #pragma unroll
@@ -362,22 +452,36 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
         }
+        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, qrb = qr_base;
+        asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb), "+v"(qrb));
+        // Q-rope operands first: LDS returns in order, so they have landed by
+        // the time the first ring operand is waited for
+        vec8 qr[4];
+        if (QK) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qr[ks] = lds16(smem + (qrb ^ (ks << 5)));
+        }
         vec8 ring[PREFETCH + 1];
 #pragma unroll
         for (int d = 0; d < PREFETCH; ++d)
-            if (n0 + d < n1) ring[d] = load_operand(sv, sk, n0 + d);
+            if (n0 + d < n1) ring[d] = load_operand(sv, sk, n0 + d, knb, krb, vtb);
 #pragma unroll
         for (int n = n0; n < n1; ++n) {
-            if (n + PREFETCH < n1) ring[(n + PREFETCH - n0) % (PREFETCH + 1)] = load_operand(sv, sk, n + PREFETCH);
+            if (n + PREFETCH < n1)
+                ring[(n + PREFETCH - n0) % (PREFETCH + 1)] = load_operand(sv, sk, n + PREFETCH, knb, krb, vtb);
             __builtin_amdgcn_sched_barrier(0);
             const vec8 a = ring[(n - n0) % (PREFETCH + 1)];
             if (n < 16) {
                 o[n & 3] = T::mfma(a, pb[n >> 2], o[n & 3]);
             } else {
                 const int ks = (n - 16) >> 1, kb = (n - 16) & 1;
-                s[kb] = T::mfma(a, qreg[ks], s[kb]);
+                s[kb] = T::mfma(a, ks < 8 ? qreg[ks] : qr[ks - 8], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (ISS && (n - n0) % LOAD_SPACING == 1 && (n - n0) / LOAD_SPACING < LOADS_PER_TILE) {
+                issue_part(tl, (n - n0) / LOAD_SPACING, vstage);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
@@ -400,7 +504,7 @@ void mla_fwd_kernel(const FwdParams p) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int j = key0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const int j = key0 + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
                     float x = s[kb][e];
                     bool vis = j < kv_len;
                     if (causal_like) {
@@ -453,24 +557,23 @@ void mla_fwd_kernel(const FwdParams p) {
 
     const std::integral_constant<bool, true> yes{};
     const std::integral_constant<bool, false> no{};
+    const TileLoad none{};  // placeholder for blocks that issue nothing
     auto stage_ptr = [&](int r) __attribute__((always_inline)) -> const unsigned char * {
         return smem + r * STAGE_BYTES;
     };
+
     // ---- schedule. Interval 0: leading group scores tile 0. Then for each tile
     // j two intervals:
     //   2j+1: leading: vector block j        trailing: PV j-1 + scores j
     //   2j+2: leading: PV j + scores j+1     trailing: vector block j
     // and a last interval in which the trailing group does PV of the last tile.
-    // Tile t's DMA is issued at the start of interval 2t-2 and waited for
-    // before interval 2t, the first that reads it.
+    // Tile t's K DMA and V loads are issued at the start of interval 2t-2 and
+    // waited for at the end of interval 2t-1; V^T is written at the start of
+    // interval 2t; K is first read in interval 2t, V^T in interval 2t+2.
     // A wave's visible tiles are a prefix of the tile range, so a matrix block
     // runs whenever its PV tile is visible; scores it computes for a tile the
     // wave cannot see (or past the last tile) are dropped. Each group runs its
     // own copy of the schedule with the same barrier sequence.
-    if (n_kt > 1)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE);  // tile 0 landed, tile 1 may fly
-    else
-        __builtin_amdgcn_s_waitcnt(0x0F70);
     block_sync();
 
     // one tile's two intervals; R = ring stage of tile j
@@ -481,22 +584,30 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         // interval 2j + 1
         if (lead) {
-            if (wave_active(j)) valu_block(j);
+            // a leading wave past its last visible tile still runs its matrix
+            // blocks (they carry the group's loads), with P = 0
+            if (wave_active(j)) {
+                valu_block(j);
+            } else {
+#pragma unroll
+                for (int st4 = 0; st4 < 4; ++st4) pb[st4] = vec8{};
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // the group's loads of tile j+1 landed
         } else {
-            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes);
+            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none);
         }
-        if (j + 1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70);  // own DMA of tile j+1 landed
         block_sync();
-        // interval 2j + 2
-        if (j + 2 < n_kt) issue_tile(j + 2);
+        // interval 2j + 2: the leading group writes V^T of tile j+1 and sends
+        // out tile j+2's loads during its matrix block
         if (lead) {
-            if (wave_active(j)) mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes);
+            write_vt(j + 1, vstage);
+            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2));
         } else {
             if (wave_active(j)) valu_block(j);
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -506,10 +617,8 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes);
-        if (1 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none);
         block_sync();
-        if (2 < n_kt) issue_tile(2);
         if (wave_active(0)) valu_block(0);
         for (int j = 1; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 1>{}, no);
@@ -519,9 +628,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none);
         }
     } else {
         block_sync();
