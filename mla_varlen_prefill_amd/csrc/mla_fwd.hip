@@ -107,11 +107,6 @@ struct Bf16 {
     static __device__ __forceinline__ pair pack(float a, float b) {
         return pair{static_cast<__bf16>(a), static_cast<__bf16>(b)};
     }
-    // acc + x[0] + x[1], products and sum in fp32
-    static __device__ __forceinline__ float dot2_ones(pair x, float acc) {
-        const pair one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-        return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
-    }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -123,10 +118,6 @@ struct Fp16 {
     typedef _Float16 scalar;
     static __device__ __forceinline__ pair pack(float a, float b) {
         return pair{static_cast<_Float16>(a), static_cast<_Float16>(b)};
-    }
-    static __device__ __forceinline__ float dot2_ones(pair x, float acc) {
-        const pair one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-        return __builtin_amdgcn_fdot2(x, one, acc, false);
     }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -304,25 +295,26 @@ void mla_fwd_kernel(const FwdParams p) {
         tl.st = smem + (kt % STAGES) * STAGE_BYTES;
         return tl;
     };
-    constexpr int LOADS_PER_TILE = 10;
-    // load i of a tile (leading group only); V loads j = i - 6 land in vst[j]:
-    // key 2kp + (j & 1), column chunk 2dg + (j >> 1)
-    auto issue_part = [&](const TileLoad &tl, int i, uint4 *vst) __attribute__((always_inline)) {
+    // A leading thread's loads of a tile: six K DMA (K_LOADS) and four V loads
+    // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
+    // 2dg + (j >> 1).
+    constexpr int K_LOADS = 6, V_LOADS = 4, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
+    auto issue_k = [&](const TileLoad &tl, int i) __attribute__((always_inline)) {
         const int wofs = wave * 64 * 16;
-        if (i < 4) {
+        if (i < 4)
             mla_raw_buffer_load_lds(tl.rk, (lds_u32_ptr)(tl.st + i * LT * 16 + wofs), 16, off_kn[i], 0, 0, 0);
-        } else if (i < 6) {
+        else
             mla_raw_buffer_load_lds(tl.rr, (lds_u32_ptr)(tl.st + KN_BYTES + (i - 4) * LT * 16 + wofs), 16,
                                     off_kr[i - 4], 0, 0, 0);
-        } else {
-            const int j = i - 6;
-            vst[j] = __builtin_bit_cast(uint4, mla_raw_buffer_load_b128(tl.rv, off_v[j & 1] + (j >> 1) * 16, 0, 0));
-        }
     };
-    auto issue_tile = [&](int kt, uint4 *vst) __attribute__((always_inline)) {
-        const TileLoad tl = prep_tile(kt);
-#pragma unroll
-        for (int i = 0; i < LOADS_PER_TILE; ++i) issue_part(tl, i, vst);
+    auto issue_v = [&](const TileLoad &tl, int j, uint4 *vst) __attribute__((always_inline)) {
+        vst[j] = __builtin_bit_cast(uint4, mla_raw_buffer_load_b128(tl.rv, off_v[j & 1] + (j >> 1) * 16, 0, 0));
+    };
+    // load i of a matrix block: V of tile tv first (it has the shorter way to
+    // go), then K of tile tk
+    auto issue_part = [&](const TileLoad &tv, const TileLoad &tk, int i, uint4 *vst) __attribute__((always_inline)) {
+        if (i < V_LOADS) issue_v(tv, i, vst);
+        else issue_k(tk, i - V_LOADS);
     };
     // V^T region of a stage: row d (128 B = 64 keys), 16-byte chunk c (8 keys)
     // at position c ^ ((d >> 1) & 7). A leading thread writes the dwords
@@ -351,12 +343,26 @@ void mla_fwd_kernel(const FwdParams p) {
     // zeros) and land in a ring stage no longer read, so the leading group
     // issues them unconditionally: one code path keeps the V registers in
     // place across the loop.
+    // Tile t's K goes out four intervals before its first scores (a stage's K
+    // region is free once the trailing group has scored the tile before), its V
+    // two intervals before V^T is written (the staging registers are free once
+    // V^T of tile t-1 is written).
     uint4 vstage[4];
     if (grp == 0) {
         uint4 v0[4];
-        issue_tile(0, v0);
-        issue_tile(1, vstage);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_TILE);  // tile 0, Q and Q-rope landed; tile 1 may still fly
+        const TileLoad t0 = prep_tile(0), t1 = prep_tile(1), t2 = prep_tile(2);
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
+#pragma unroll
+        for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j, v0);
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
+#pragma unroll
+        for (int j = 0; j < V_LOADS; ++j) issue_v(t1, j, vstage);
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) issue_k(t2, i);
+        // tile 0, Q and Q-rope landed; K and V of tile 1 and K of tile 2 may still fly
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS + V_LOADS));
         write_vt(0, v0);
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
@@ -440,9 +446,9 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
     // stage sk); either half may be switched off. Operands are read ahead.
-    // ISS: issue the loads of tile tl, one every LOAD_SPACING MFMAs
+    // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING MFMAs
     auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
-                          const TileLoad &tl) __attribute__((always_inline)) {
+                          const TileLoad &tlv, const TileLoad &tlk) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr bool ISS = decltype(do_iss)::value;
         constexpr int n0 = PV ? 0 : 16, n1 = QK ? 40 : 16;
@@ -478,8 +484,8 @@ void mla_fwd_kernel(const FwdParams p) {
                 s[kb] = T::mfma(a, ks < 8 ? qreg[ks] : qr[ks - 8], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ISS && (n - n0) % LOAD_SPACING == 1 && (n - n0) / LOAD_SPACING < LOADS_PER_TILE) {
-                issue_part(tl, (n - n0) / LOAD_SPACING, vstage);
+            if (ISS && (n - n0) % LOAD_SPACING == 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
+                issue_part(tlv, tlk, (n - n0) / LOAD_SPACING, vstage);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -538,9 +544,9 @@ void mla_fwd_kernel(const FwdParams p) {
             m_run = m_new;
         }
         const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        // probabilities, rounded to the input dtype; the row sum is taken over
-        // the rounded values (the ones the PV product uses) with dot2 against
-        // (1, 1), in four independent partial sums
+        // probabilities, rounded to the input dtype for the PV product; the row
+        // sum adds them in fp32 (plain adds: the dot2 instructions would queue
+        // behind the other wave's MFMAs), in four independent partial sums
         float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < 32; t += 2) {
@@ -548,7 +554,7 @@ void mla_fwd_kernel(const FwdParams p) {
             const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
             const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -mc));
             const typename T::pair pr = T::pack(p0, p1);
-            lsum[(t >> 1) & 3] = T::dot2_ones(pr, lsum[(t >> 1) & 3]);
+            lsum[(t >> 1) & 3] += p0 + p1;
             pb[kb * 2 + (e >> 3)][e & 7] = pr[0];
             pb[kb * 2 + (e >> 3)][(e & 7) + 1] = pr[1];
         }
@@ -567,9 +573,12 @@ void mla_fwd_kernel(const FwdParams p) {
     //   2j+1: leading: vector block j        trailing: PV j-1 + scores j
     //   2j+2: leading: PV j + scores j+1     trailing: vector block j
     // and a last interval in which the trailing group does PV of the last tile.
-    // Tile t's K DMA and V loads are issued at the start of interval 2t-2 and
+    // Tile t's K DMA goes out during interval 2t-4 and its V loads during
+    // interval 2t-2 (both from the leading group's matrix block); both are
     // waited for at the end of interval 2t-1; V^T is written at the start of
-    // interval 2t; K is first read in interval 2t, V^T in interval 2t+2.
+    // interval 2t; K is first read in interval 2t, V^T in interval 2t+2. The
+    // K DMA of tile t overwrites only the K half of a stage, whose last reader
+    // (trailing scores of tile t-3) finished in interval 2t-5.
     // A wave's visible tiles are a prefix of the tile range, so a matrix block
     // runs whenever its PV tile is visible; scores it computes for a tile the
     // wave cannot see (or past the last tile) are dropped. Each group runs its
@@ -592,22 +601,24 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int st4 = 0; st4 < 4; ++st4) pb[st4] = vec8{};
             }
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // the group's loads of tile j+1 landed
+            // V of tile j+1 and everything before it landed (K of tile j+1 went
+            // out two intervals earlier); K of tile j+2 may still fly
+            __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
         } else {
-            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none);
+            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none);
         }
         block_sync();
         // interval 2j + 2: the leading group writes V^T of tile j+1 and sends
-        // out tile j+2's loads during its matrix block
+        // out V of tile j+2 and K of tile j+3 during its matrix block
         if (lead) {
             write_vt(j + 1, vstage);
-            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2));
+            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2), prep_tile(j + 3));
         } else {
             if (wave_active(j)) valu_block(j);
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -617,7 +628,7 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none);
         block_sync();
         if (wave_active(0)) valu_block(0);
         for (int j = 1; j < n_kt; j += STAGES) {
@@ -628,9 +639,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none);
         }
     } else {
         block_sync();
