@@ -174,7 +174,23 @@ def cpu_baseline(res, seconds):
                       f"({spent:.1f} s, fp64)"}
 
 
-def bench_gather(steps):
+def _time(fn, steps, stream):
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def bench_paged(steps):
+    """The paged workload: the gather's bandwidth, then attention over the same
+    caches two ways -- fused (mla_prefill_paged reads K/KRope/V through the
+    block table) and two-step (gather, then mla_prefill on the gathered
+    tensors). Queries: qlen = kvlen = context length, causal, 128 heads, bf16."""
     lens, _ = synth.workload_seqlens("paged")
     caches = synth.paged_inputs(lens, device="cuda", with_rope=True)
     total = int(lens.sum())
@@ -184,27 +200,45 @@ def bench_gather(steps):
     rope = torch.empty((total, heads, 64), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
+    def gather():
         mla.paged_cache_load(caches["key_cache"], caches["value_cache"], caches["block_tables"],
                              caches["context_lens"], key, value, None, mla.KV_CACHE_ND, False, False, stream)
         mla.paged_cache_load(caches["rope_cache"], None, caches["block_tables"], caches["context_lens"], rope,
                              None, None, mla.KV_CACHE_ND, False, False, stream)
 
-    step()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    gather_ms = _time(gather, steps, stream)
     nbytes = 2 * total * (key[0].numel() + value[0].numel() + rope[0].numel()) * 2  # read + write
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    del caches, key, value, rope
+    gbs = nbytes / (gather_ms * 1e-3) / 1e9
+    gather_rec = {"workload": "paged", "tokens": total, "bytes_per_step": nbytes, "ms_per_step": gather_ms,
+                  "value": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+
+    qs = ks = np.asarray(lens, np.int32)
+    q = synth._randn((total, heads, 128), torch.bfloat16, 1.0, 4 * 100 + 8, "cuda")
+    qr = synth._randn((total, heads, 64), torch.bfloat16, 1.0, 4 * 100 + 9, "cuda")
+    out = torch.empty((total, heads, 128), dtype=torch.bfloat16, device="cuda")
+    mt = synth.MASK_CAUSAL
+    ws_c = mla.mla_prefill_get_workspace_size(q, qr, key, rope, value, qs, ks, None, heads, synth.QK_SCALE, heads,
+                                              mt, 0, out)
+    ws_p = mla.mla_prefill_paged_get_workspace_size(q, qr, caches["key_cache"], caches["rope_cache"],
+                                                    caches["value_cache"], caches["block_tables"], qs, ks, None,
+                                                    heads, synth.QK_SCALE, heads, mt, out)
+    ws = torch.empty(max(ws_c, ws_p, 1), dtype=torch.uint8, device="cuda")
+    attn_steps = max(1, min(steps, 2))
+    gathered_ms = _time(lambda: mla.mla_prefill(q, qr, key, rope, value, qs, ks, None, heads, synth.QK_SCALE,
+                                                heads, mt, 0, out, ws, stream), attn_steps, stream)
+    fused_ms = _time(lambda: mla.mla_prefill_paged(q, qr, caches["key_cache"], caches["rope_cache"],
+                                                   caches["value_cache"], caches["block_tables"], qs, ks, None,
+                                                   heads, synth.QK_SCALE, heads, mt, out, ws, stream),
+                     attn_steps, stream)
+    flops = FLOP_PER_PAIR * heads * visible_pairs(qs, ks, mt)
+    del caches, key, value, rope, q, qr, out, ws
     torch.cuda.empty_cache()
-    return {"workload": "paged", "tokens": total, "bytes_per_step": nbytes, "ms_per_step": ms,
-            "value": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+    attn_rec = {"workload": "paged", "tokens": total, "heads": heads, "mask": "causal", "block_size":
+                synth.BLOCK_SIZE, "flops_per_step": flops, "fused_ms": fused_ms,
+                "fused_tflops": flops / (fused_ms * 1e-3) / 1e12, "gathered_attention_ms": gathered_ms,
+                "two_step_ms": gather_ms + gathered_ms, "fused_speedup_over_two_step":
+                (gather_ms + gathered_ms) / fused_ms}
+    return gather_rec, attn_rec
 
 
 def main():
@@ -257,7 +291,7 @@ def main():
     }
     if not args.no_gather and args.workload == "single":
         res_t = res.pop("tensors") if args.no_cpu_baseline else None
-        line["gather"] = bench_gather(max(2, min(args.steps, 5)))
+        line["gather"], line["paged_attention"] = bench_paged(max(2, min(args.steps, 5)))
         del res_t
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)

@@ -196,6 +196,47 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
                      const mla_tensor *seq_starts, int8_t kv_cache_cfg,
                      bool is_seq_lens_cumsum_type, bool has_seq_starts, void *stream);
 
+/*
+ * mla_prefill_paged_get_workspace_size / mla_prefill_paged -- "MLA Prefill"
+ * with K, KRope and V read in place from paged caches. The result equals
+ * paged_cache_load ("PagedCacheLoadOperation" page, Members table: ND caches,
+ * plain contextLens, no seqStarts) of K, KRope and V followed by mla_prefill
+ * (cache_mode 0) on the gathered tensors, without materialising them.
+ *
+ *   q, q_rope, q_seqlen, mask, head_num, qk_scale, kv_head_num, mask_type,
+ *   atten_out   as for mla_prefill.
+ *   key_cache     device ND [num_blocks, block_size, kvHeadNum, 128], dtype of q.
+ *   krope_cache   device ND [num_blocks, block_size, kvHeadNum, 64], dtype of q.
+ *   value_cache   device ND [num_blocks, block_size, kvHeadNum, 128], dtype of q.
+ *   block_tables  device int32 [batch, max_blocks]: key t of sequence b is slot
+ *                 t % block_size of block block_tables[b][t / block_size]
+ *                 (every sequence starts at position 0 of its table row).
+ *   kv_seqlen     HOST int32 [batch]: keys (context length) of each sequence.
+ * Supported here: block_size a multiple of MLA_PLAN_KV_COLS (64), at most
+ * MLA_PAGED_MAX_KEYS keys per sequence, num_blocks * block_size < 2^31;
+ * otherwise MLA_ERR_UNSUPPORTED. max_blocks must cover ceil(kv_len /
+ * block_size) for every sequence (else MLA_ERR_SHAPE). Block ids live on the
+ * device and are not checked by the host: a 64-key tile whose block id lies
+ * outside [0, num_blocks) reads as zeros (those keys contribute exp(0 - max)
+ * weight with a zero value row; they are not an error signal). Workspace,
+ * stream and error behaviour as for mla_prefill.
+ */
+#define MLA_PAGED_MAX_KEYS (2048 * 64)
+int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,
+                                         const mla_tensor *key_cache, const mla_tensor *krope_cache,
+                                         const mla_tensor *value_cache, const mla_tensor *block_tables,
+                                         const mla_tensor *q_seqlen, const mla_tensor *kv_seqlen,
+                                         const mla_tensor *mask, int32_t head_num, float qk_scale,
+                                         int32_t kv_head_num, int32_t mask_type,
+                                         const mla_tensor *atten_out, uint64_t *workspace_size);
+int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *key_cache,
+                      const mla_tensor *krope_cache, const mla_tensor *value_cache,
+                      const mla_tensor *block_tables, const mla_tensor *q_seqlen,
+                      const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                      float qk_scale, int32_t kv_head_num, int32_t mask_type,
+                      const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
+                      void *stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char *mla_last_error(void);
 

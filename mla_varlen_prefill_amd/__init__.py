@@ -23,6 +23,7 @@ __all__ = [
     "MASK_UNDEFINED", "MASK_SPEC", "MASK_CAUSAL", "MASK_FREE", "KV_CACHE_NZ", "KV_CACHE_ND",
     "MlaError", "mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load",
     "mla_last_error", "mla_prefill_plan_host", "prefill", "library_path",
+    "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "prefill_paged",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_prefill.so")
@@ -30,6 +31,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_pref
 MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
 KV_CACHE_NZ, KV_CACHE_ND = 0, 1
 PLAN_Q_ROWS, PLAN_KV_COLS = 256, 64
+PAGED_MAX_KEYS = 2048 * 64
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_VALUE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
@@ -77,13 +79,19 @@ def _load():
                                 ctypes.c_void_p]
     lib.paged_cache_load.argtypes = [T, T, T, T, T, T, T, ctypes.c_int8, ctypes.c_bool, ctypes.c_bool,
                                      ctypes.c_void_p]
+    lib.mla_prefill_paged_get_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
+                                                         ctypes.c_int32, ctypes.c_int32, T,
+                                                         ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prefill_paged.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                      ctypes.c_int32, T, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
-    for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host"):
+    for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host",
+               "mla_prefill_paged_get_workspace_size", "mla_prefill_paged"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +181,42 @@ def mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk
                                           _stream_ptr(stream)))
 
 
+def _paged_args(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask, head_num,
+                qk_scale, kv_head_num, mask_type, atten_out, keep):
+    qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)
+    return [_desc(q, keep), _desc(q_rope, keep), _desc(key_cache, keep), _desc(krope_cache, keep),
+            _desc(value_cache, keep), _desc(block_tables, keep), _desc(qs, keep), _desc(ks, keep),
+            _desc(mask, keep), int(head_num), float(qk_scale), int(kv_head_num), int(mask_type),
+            _desc(atten_out, keep)]
+
+
+def mla_prefill_paged_get_workspace_size(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen,
+                                         kv_seqlen, mask, head_num, qk_scale, kv_head_num, mask_type,
+                                         atten_out) -> int:
+    """Bytes of device workspace ``mla_prefill_paged`` needs (host-only planning call)."""
+    lib = _load()
+    keep = []
+    args = _paged_args(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask,
+                       head_num, qk_scale, kv_head_num, mask_type, atten_out, keep)
+    size = ctypes.c_uint64(0)
+    _check("mla_prefill_paged_get_workspace_size",
+           lib.mla_prefill_paged_get_workspace_size(*args, ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask,
+                      head_num, qk_scale, kv_head_num, mask_type, atten_out, workspace, stream=None) -> None:
+    """Enqueue MLA prefill attention reading K, KRope and V through block tables."""
+    lib = _load()
+    keep = []
+    args = _paged_args(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask,
+                       head_num, qk_scale, kv_head_num, mask_type, atten_out, keep)
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_prefill_paged", lib.mla_prefill_paged(*args, ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size),
+                                                      _stream_ptr(stream)))
+
+
 def paged_cache_load(key_cache, value_cache, block_tables, context_lens, key, value, seq_starts=None,
                      kv_cache_cfg=KV_CACHE_ND, is_seq_lens_cumsum_type=False, has_seq_starts=False,
                      stream=None) -> None:
@@ -227,6 +271,23 @@ def prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, head_num, kv_head_num,
     workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
     mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num, mask_type,
                 0, out, workspace, stream)
+    if stream is not None and isinstance(stream, torch.cuda.Stream):
+        workspace.record_stream(stream)
+    return out
+
+
+def prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, head_num,
+                  kv_head_num, qk_scale=1.0, mask_type=MASK_UNDEFINED, mask=None, out=None, stream=None):
+    """Paged form of ``prefill``: allocate output and workspace, run the two-phase pair."""
+    if out is None:
+        d = q.shape[-1] if q.dim() == 3 else q.shape[1] // head_num
+        out = torch.empty((q.shape[0], head_num, d), dtype=q.dtype, device=q.device)
+    ws = mla_prefill_paged_get_workspace_size(q, q_rope, key_cache, krope_cache, value_cache, block_tables,
+                                              q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                                              mask_type, out)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=q.device)
+    mla_prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask,
+                      head_num, qk_scale, kv_head_num, mask_type, out, workspace, stream)
     if stream is not None and isinstance(stream, torch.cuda.Stream):
         workspace.record_stream(stream)
     return out

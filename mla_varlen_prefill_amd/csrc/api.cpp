@@ -24,11 +24,13 @@ using mla::ROPE_DIM;
 using mla::SeqRec;
 using mla::MLA_CUS_PER_XCD;
 using mla::MLA_XCDS;
+using mla::PAGED_MAX_TILES;
 using mla::Task;
 using mla::WorkItem;
 
 static_assert(MLA_PLAN_Q_ROWS == FWD_BM, "plan row count must match the kernel tile");
 static_assert(MLA_PLAN_KV_COLS == FWD_BN, "plan key count must match the kernel tile");
+static_assert(MLA_PAGED_MAX_KEYS == PAGED_MAX_TILES * FWD_BN, "paged key limit must match the kernel table");
 
 namespace {
 
@@ -225,6 +227,80 @@ int validate_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_te
     return MLA_OK;
 }
 
+// Paged K/V: ND caches [num_blocks, block_size, Hkv, dim] and a device block
+// table [batch, max_blocks]. Q, lengths, mask and output are checked as for
+// the contiguous form (through validate_prefill with stand-in K/V
+// descriptors of the packed shape).
+struct PagedProblem {
+    int64_t num_blocks = 0;
+    int64_t block_size = 0;
+    int64_t bt_stride = 0;
+};
+
+int validate_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *key_cache,
+                   const mla_tensor *krope_cache, const mla_tensor *value_cache,
+                   const mla_tensor *block_tables, const mla_tensor *q_seqlen,
+                   const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num, float qk_scale,
+                   int32_t kv_head_num, int32_t mask_type, const mla_tensor *out, Problem *pr,
+                   PagedProblem *pg) {
+    int rc;
+    if ((rc = check_tensor(key_cache, "key_cache", true)) ||
+        (rc = check_tensor(krope_cache, "krope_cache", true)) ||
+        (rc = check_tensor(value_cache, "value_cache", true)) ||
+        (rc = check_tensor(block_tables, "block_tables", true)) ||
+        (rc = check_tensor(kv_seqlen, "kv_seqlen", false)))
+        return rc;
+    if (kv_seqlen->ndim != 1) return fail(MLA_ERR_SHAPE, "kv_seqlen must be [batch]");
+    if (kv_seqlen->dtype != MLA_INT32) return fail(MLA_ERR_DTYPE, "q_seqlen / kv_seqlen must be int32");
+    int64_t sum_kv = 0;
+    for (int64_t b = 0; b < kv_seqlen->shape[0]; ++b) sum_kv += std::max(0, static_cast<const int32_t *>(kv_seqlen->data)[b]);
+    // stand-in descriptors of the packed shape: the shared checks then apply
+    mla_tensor k = *key_cache, kr = *krope_cache, v = *value_cache;
+    k.ndim = kr.ndim = v.ndim = 3;
+    k.shape[0] = kr.shape[0] = v.shape[0] = sum_kv;
+    k.shape[1] = kr.shape[1] = v.shape[1] = kv_head_num;
+    k.shape[2] = key_cache->shape[key_cache->ndim - 1];
+    kr.shape[2] = krope_cache->shape[krope_cache->ndim - 1];
+    v.shape[2] = value_cache->shape[value_cache->ndim - 1];
+    if ((rc = validate_prefill(q, q_rope, &k, &kr, &v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                               mask_type, 0, out, pr)))
+        return rc;
+    if (pr->kv_padded_max_seq != 0) return fail(MLA_ERR_SHAPE, "caches: unexpected shape");
+    const mla_tensor *caches[] = {key_cache, krope_cache, value_cache};
+    const char *names[] = {"key_cache", "krope_cache", "value_cache"};
+    const int64_t dims[] = {HEAD_DIM, ROPE_DIM, HEAD_DIM};
+    for (int i = 0; i < 3; ++i) {
+        const mla_tensor *c = caches[i];
+        if (c->ndim != 4 || c->shape[2] != kv_head_num || c->shape[3] != dims[i] ||
+            c->shape[0] != key_cache->shape[0] || c->shape[1] != key_cache->shape[1])
+            return fail(MLA_ERR_SHAPE, "%s: expected ND [num_blocks, block_size, %d, %lld] like key_cache", names[i],
+                        kv_head_num, (long long)dims[i]);
+    }
+    pg->num_blocks = key_cache->shape[0];
+    pg->block_size = key_cache->shape[1];
+    if (pg->num_blocks <= 0 || pg->block_size <= 0) return fail(MLA_ERR_SHAPE, "caches: empty");
+    if (pg->block_size % FWD_BN != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "block_size %lld: the fused path needs a multiple of %d",
+                    (long long)pg->block_size, FWD_BN);
+    if (pg->num_blocks * pg->block_size > INT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "caches of more than 2^31 - 1 token slots");
+    if (block_tables->dtype != MLA_INT32) return fail(MLA_ERR_DTYPE, "block_tables must be int32");
+    if (block_tables->ndim != 2 || block_tables->shape[0] != pr->batch)
+        return fail(MLA_ERR_SHAPE, "block_tables: expected [batch = %d, max_blocks]", pr->batch);
+    pg->bt_stride = block_tables->shape[1];
+    if (pg->bt_stride > INT32_MAX) return fail(MLA_ERR_SHAPE, "block_tables: too many columns");
+    for (int32_t b = 0; b < pr->batch; ++b) {
+        const int64_t kl = pr->kv_seqlen[b];
+        if ((kl + pg->block_size - 1) / pg->block_size > pg->bt_stride)
+            return fail(MLA_ERR_SHAPE, "block_tables: sequence %d needs %lld blocks, the table has %lld columns", b,
+                        (long long)((kl + pg->block_size - 1) / pg->block_size), (long long)pg->bt_stride);
+        if ((kl + FWD_BN - 1) / FWD_BN > PAGED_MAX_TILES)
+            return fail(MLA_ERR_UNSUPPORTED, "sequence %d: %lld keys exceed the fused path's %d", b, (long long)kl,
+                        PAGED_MAX_TILES * FWD_BN);
+    }
+    return MLA_OK;
+}
+
 // Number of FWD_BN-key tiles (counted from key 0) that query rows
 // [q_row0, q_end) of a sequence can see under mask_type.
 int32_t visible_tiles(int mask_type, int32_t q_len, int32_t kv_len, int32_t q_end) {
@@ -345,6 +421,64 @@ void write_plan(const Plan &p, uint8_t *dst) {
     std::memcpy(dst + tasks_offset(p), p.tasks.data(), p.tasks.size() * sizeof(Task));
 }
 
+// Plan on the host, copy the work list into the workspace, launch. pg and
+// block_tables are null for contiguous K/V.
+int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *block_tables, const mla_tensor *q,
+                    const mla_tensor *q_rope, const void *k, const void *k_rope, const void *v,
+                    const mla_tensor *mask, float qk_scale, const mla_tensor *atten_out, void *workspace,
+                    uint64_t workspace_size, void *stream) {
+    Plan plan;
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
+               &plan);
+    const uint64_t need = plan_bytes(plan);
+    if (need == 0) return ok();  // no query rows: nothing to write
+    if (workspace == nullptr || workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given",
+                    (unsigned long long)need, (unsigned long long)workspace_size);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (plan.tasks.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
+
+    std::vector<uint8_t> host(need);
+    write_plan(plan, host.data());
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipMemcpyAsync: %s", hipGetErrorString(e));
+
+    mla::FwdParams p{};
+    p.q = q->data;
+    p.q_rope = q_rope->data;
+    p.k = k;
+    p.k_rope = k_rope;
+    p.v = v;
+    p.mask = (pr.mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
+    p.out = atten_out->data;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    p.seqs = reinterpret_cast<const SeqRec *>(ws);
+    p.items = reinterpret_cast<const WorkItem *>(ws + items_offset(plan));
+    p.tasks = reinterpret_cast<const Task *>(ws + tasks_offset(plan));
+    p.heads = pr.heads;
+    p.kv_heads = pr.kv_heads;
+    p.group = pr.heads / pr.kv_heads;
+    p.n_tasks = (int32_t)plan.tasks.size();
+    p.mask_type = pr.mask_type;
+    p.mask_is_bf16 = (pr.mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;
+    // A zero (or denormal) scale is replaced by +-1e-30: the kernel divides mask
+    // values by the scale, and the change is below fp32 resolution of the scores.
+    double scale = (double)qk_scale;
+    if (std::fabs(scale) < 1e-30) scale = std::signbit(scale) ? -1e-30 : 1e-30;
+    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    if (pg) {
+        p.block_tables = block_tables;
+        p.bt_stride = (int32_t)pg->bt_stride;
+        p.block_size = (int32_t)pg->block_size;
+        p.num_blocks = (int32_t)pg->num_blocks;
+    }
+    e = mla::launch_mla_fwd(p, pr.dtype, pg != nullptr, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "attention launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -406,50 +540,44 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
     int rc = validate_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
                               kv_head_num, mask_type, cache_mode, atten_out, &pr);
     if (rc) return rc;
+    return plan_and_launch(pr, nullptr, nullptr, q, q_rope, k->data, k_rope->data, v->data, mask, qk_scale,
+                           atten_out, workspace, workspace_size, stream);
+}
+
+int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,
+                                         const mla_tensor *key_cache, const mla_tensor *krope_cache,
+                                         const mla_tensor *value_cache, const mla_tensor *block_tables,
+                                         const mla_tensor *q_seqlen, const mla_tensor *kv_seqlen,
+                                         const mla_tensor *mask, int32_t head_num, float qk_scale,
+                                         int32_t kv_head_num, int32_t mask_type, const mla_tensor *atten_out,
+                                         uint64_t *workspace_size) {
+    if (workspace_size == nullptr) return fail(MLA_ERR_NULL, "workspace_size is NULL");
+    Problem pr;
+    PagedProblem pg;
+    int rc = validate_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen,
+                            mask, head_num, qk_scale, kv_head_num, mask_type, atten_out, &pr, &pg);
+    if (rc) return rc;
     Plan plan;
-    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
-               &plan);
-    const uint64_t need = plan_bytes(plan);
-    if (need == 0) return ok();  // no query rows: nothing to write
-    if (workspace == nullptr || workspace_size < need)
-        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given",
-                    (unsigned long long)need, (unsigned long long)workspace_size);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    if (plan.tasks.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
-
-    std::vector<uint8_t> host(need);
-    write_plan(plan, host.data());
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipMemcpyAsync: %s", hipGetErrorString(e));
-
-    mla::FwdParams p{};
-    p.q = q->data;
-    p.q_rope = q_rope->data;
-    p.k = k->data;
-    p.k_rope = k_rope->data;
-    p.v = v->data;
-    p.mask = (mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
-    p.out = atten_out->data;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    p.seqs = reinterpret_cast<const SeqRec *>(ws);
-    p.items = reinterpret_cast<const WorkItem *>(ws + items_offset(plan));
-    p.tasks = reinterpret_cast<const Task *>(ws + tasks_offset(plan));
-    p.heads = head_num;
-    p.kv_heads = kv_head_num;
-    p.group = head_num / kv_head_num;
-    p.n_tasks = (int32_t)plan.tasks.size();
-    p.mask_type = mask_type;
-    p.mask_is_bf16 = (mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;
-    // A zero (or denormal) scale is replaced by +-1e-30: the kernel divides mask
-    // values by the scale, and the change is below fp32 resolution of the scores.
-    double scale = (double)qk_scale;
-    if (std::fabs(scale) < 1e-30) scale = std::signbit(scale) ? -1e-30 : 1e-30;
-    p.scale_log2 = (float)(scale * 1.4426950408889634);
-    e = mla::launch_mla_fwd(p, pr.dtype, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "attention launch: %s", hipGetErrorString(e));
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, 0, &plan);
+    *workspace_size = plan_bytes(plan);
     return ok();
+}
+
+int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *key_cache,
+                      const mla_tensor *krope_cache, const mla_tensor *value_cache,
+                      const mla_tensor *block_tables, const mla_tensor *q_seqlen,
+                      const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                      float qk_scale, int32_t kv_head_num, int32_t mask_type,
+                      const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
+                      void *stream) {
+    Problem pr;
+    PagedProblem pg;
+    int rc = validate_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen,
+                            mask, head_num, qk_scale, kv_head_num, mask_type, atten_out, &pr, &pg);
+    if (rc) return rc;
+    return plan_and_launch(pr, &pg, static_cast<const int32_t *>(block_tables->data), q, q_rope, key_cache->data,
+                           krope_cache->data, value_cache->data, mask, qk_scale, atten_out, workspace,
+                           workspace_size, stream);
 }
 
 int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,

@@ -62,10 +62,21 @@ struct FwdParams {
     int32_t mask_is_bf16; // dtype of the MASK_FREE tile
     int32_t n_tasks;      // workgroups to launch
     float scale_log2;     // qkScale * log2(e)
+    // Paged K/V (launch_mla_fwd with paged = true): k, k_rope and v point at
+    // ND caches [num_blocks, block_size, Hkv, 128 | 64 | 128]; key t of
+    // sequence b is slot t % block_size of block block_tables[b][t / block_size].
+    const int32_t *block_tables;  // [batch, bt_stride]
+    int32_t bt_stride;
+    int32_t block_size;           // a multiple of FWD_BN
+    int32_t num_blocks;
 };
 
+// Key tiles of one sequence the paged kernel can address (its per-tile table
+// lives in LDS): PAGED_MAX_TILES * FWD_BN keys.
+constexpr int PAGED_MAX_TILES = 2048;
+
 // dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). One workgroup per task.
-hipError_t launch_mla_fwd(const FwdParams &p, int dtype, hipStream_t stream);
+hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream);
 
 struct GatherParams {
     const void *key_cache;

@@ -175,10 +175,15 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-template <typename T>
+// PAGED: K, KRope and V are read from ND caches through the block table; a
+// table of the first cache row of each of the sequence's key tiles sits in
+// the LDS past the ring.
+constexpr int TILE_TABLE_BYTES = PAGED_MAX_TILES * 4;
+
+template <typename T, bool PAGED>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void mla_fwd_kernel(const FwdParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)];
     typedef typename T::vec8 vec8;
 
     const int tid = threadIdx.x;
@@ -242,6 +247,23 @@ void mla_fwd_kernel(const FwdParams p) {
         }
     }
 
+    // ---- paged K/V: first cache row of each key tile of the sequence (block
+    // size is a multiple of the tile, so a tile never straddles two blocks);
+    // -1 for a tile whose block id lies outside the cache, which then reads
+    // as zeros like rows past the sequence end.
+    int32_t *tile_row = reinterpret_cast<int32_t *>(smem + LDS_BYTES);
+    const int n_tiles_seq = min((kv_len + BN - 1) / BN, PAGED_MAX_TILES);
+    if (PAGED) {
+        const int tpb = p.block_size / BN;
+        const int32_t *bt = p.block_tables + (int64_t)item.b * p.bt_stride;
+        for (int i = tid; i < n_tiles_seq; i += NT) {
+            const int bi = i / tpb;
+            const int blk = bt[bi];
+            tile_row[i] = (blk >= 0 && blk < p.num_blocks) ? blk * p.block_size + (i - bi * tpb) * BN : -1;
+        }
+        block_sync();
+    }
+
     // ---- K / V tile streaming. Tile kt lives in ring stage kt % 3.
     //  * K-nope and K-rope go HBM -> LDS by DMA. Row m of the K tile holds key
     //    perm(m), perm swapping bits 2 and 3 of the key index, so that after
@@ -285,9 +307,22 @@ void mla_fwd_kernel(const FwdParams p) {
         i32x4 rk, rr, rv;
         unsigned char *st;
     };
-    auto prep_tile = [&](int kt) __attribute__((always_inline)) -> TileLoad {
-        const int64_t rowi = ((int64_t)seq.kv_off + (int64_t)kt * BN) * HKV + hk;  // first key row, this head
-        const uint32_t nvalid = (uint32_t)max(0, min(kv_len - kt * BN, BN));
+    // paged: first cache row of tile kt (-1: none), read from the LDS table
+    // ahead of prep_tile so the read's latency stays off the matrix block
+    auto cache_row = [&](int kt) __attribute__((always_inline)) -> int {
+        if (!PAGED) return 0;
+        return __builtin_amdgcn_readfirstlane(kt < n_tiles_seq ? tile_row[kt] : -1);
+    };
+    auto prep_tile = [&](int kt, int r) __attribute__((always_inline)) -> TileLoad {
+        int64_t rowi;     // first key row of the tile, this head
+        uint32_t nvalid;  // rows that hold keys of the sequence
+        if (PAGED) {
+            rowi = r >= 0 ? (int64_t)r * HKV + hk : 0;
+            nvalid = r >= 0 ? (uint32_t)max(0, min(kv_len - kt * BN, BN)) : 0u;
+        } else {
+            rowi = ((int64_t)seq.kv_off + (int64_t)kt * BN) * HKV + hk;
+            nvalid = (uint32_t)max(0, min(kv_len - kt * BN, BN));
+        }
         TileLoad tl;
         tl.rk = make_rsrc(kbase + rowi * (DN * 2), nvalid * kn_row);
         tl.rr = make_rsrc(krbase + rowi * (DR * 2), nvalid * kr_row);
@@ -350,7 +385,8 @@ void mla_fwd_kernel(const FwdParams p) {
     uint4 vstage[4];
     if (grp == 0) {
         uint4 v0[4];
-        const TileLoad t0 = prep_tile(0), t1 = prep_tile(1), t2 = prep_tile(2);
+        const TileLoad t0 = prep_tile(0, cache_row(0)), t1 = prep_tile(1, cache_row(1)),
+                       t2 = prep_tile(2, cache_row(2));
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
 #pragma unroll
@@ -592,7 +628,10 @@ void mla_fwd_kernel(const FwdParams p) {
         constexpr int rprev = (r0 + STAGES - 1) % STAGES, rnext = (r0 + 1) % STAGES;
         block_sync();
         // interval 2j + 1
+        int row_v = 0, row_k = 0;  // paged: cache rows of the tiles loaded next interval
         if (lead) {
+            row_v = cache_row(j + 2);
+            row_k = cache_row(j + 3);
             // a leading wave past its last visible tile still runs its matrix
             // blocks (they carry the group's loads), with P = 0
             if (wave_active(j)) {
@@ -612,7 +651,8 @@ void mla_fwd_kernel(const FwdParams p) {
         // out V of tile j+2 and K of tile j+3 during its matrix block
         if (lead) {
             write_vt(j + 1, vstage);
-            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2), prep_tile(j + 3));
+            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2, row_v),
+                       prep_tile(j + 3, row_k));
         } else {
             if (wave_active(j)) valu_block(j);
         }
@@ -670,14 +710,17 @@ void mla_fwd_kernel(const FwdParams p) {
 
 }  // namespace
 
-hipError_t launch_mla_fwd(const FwdParams &p, int dtype, hipStream_t stream) {
+hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream) {
     if (p.n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)p.n_tasks);
     dim3 block(FWD_THREADS);
-    if (dtype == 2)
-        hipLaunchKernelGGL(mla_fwd_kernel<Bf16>, grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL(mla_fwd_kernel<Fp16>, grid, block, 0, stream, p);
+    if (dtype == 2) {
+        if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false>), grid, block, 0, stream, p);
+    } else {
+        if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -11,6 +11,8 @@ it, and it shares no code, tables or helpers with the HIP path.
   Transformer Boost "PagedCacheLoadOperation" page (Members table: keyCache,
   valueCache, blockTables, contextLens, seqStarts, isSeqLensCumsumType,
   hasSeqStarts), ND cache layout.
+* ``paged_attention`` is the composition of the two: gather K, KRope and V
+  out of ND caches, then attention on the gathered tensors.
 
 Mask-type codes (the page names the modes but prints no integer values):
 UNDEFINED 0, SPEC 1, CAUSAL 2, MASK_FREE 3.
@@ -194,3 +196,20 @@ def paged_cache_load(key_cache, value_cache, block_tables, context_lens, seq_sta
         if value is not None:
             value[off:off + n] = value_cache[blocks, slots]
     return key, value
+
+
+def paged_attention(q, qr, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, head_num,
+                    kv_head_num, qk_scale, mask_type, mask=None, lib=None):
+    """MLA prefill attention over K, KRope and V kept in block-paged ND caches.
+
+    By definition the gather of each cache ("PagedCacheLoadOperation" page,
+    Members table: ND layout, plain contextLens = kv_seqlen, every sequence
+    starting at position 0 of its table row) followed by ``attention`` on the
+    packed result ("MLA Prefill" page, Definition). Returns [sum qlen, H, Dv]
+    float64.
+    """
+    k, _ = paged_cache_load(key_cache, None, block_tables, kv_seqlen)
+    kr, _ = paged_cache_load(krope_cache, None, block_tables, kv_seqlen)
+    v, _ = paged_cache_load(value_cache, None, block_tables, kv_seqlen)
+    return attention(q, qr, k, kr, v, q_seqlen, kv_seqlen, head_num, kv_head_num, qk_scale, mask_type, mask,
+                     lib=lib)

@@ -251,3 +251,58 @@ def test_page_contract_values():
     t = tensors()
     t["head_num"] = g["mla_prefill"]["headNum_default"]["value"]
     assert status_of(t) == "MLA_ERR_VALUE"
+
+
+# ------------------------------------------------------------------ paged attention validation
+
+def paged_tensors(qs=(17, 40), ks=(30, 100), h=4, hk=2, bs=64, nb=8, cols=2, dtype=torch.bfloat16):
+    nq = sum(qs)
+    z = lambda *s, dt=dtype: torch.zeros(s, dtype=dt)
+    return dict(q=z(nq, h, 128), q_rope=z(nq, h, 64), key_cache=z(nb, bs, hk, 128),
+                krope_cache=z(nb, bs, hk, 64), value_cache=z(nb, bs, hk, 128),
+                block_tables=torch.zeros((len(qs), cols), dtype=torch.int32),
+                q_seqlen=np.array(qs, np.int32), kv_seqlen=np.array(ks, np.int32), mask=None, head_num=h,
+                qk_scale=0.1, kv_head_num=hk, mask_type=mla.MASK_CAUSAL, atten_out=z(nq, h, 128))
+
+
+def paged_status(t):
+    try:
+        mla.mla_prefill_paged_get_workspace_size(**t)
+        return 0
+    except mla.MlaError as e:
+        return e.code
+
+
+def test_paged_valid_problem_plans_like_the_contiguous_one():
+    t = paged_tensors()
+    size = mla.mla_prefill_paged_get_workspace_size(**t)
+    c = tensors(qs=(17, 40), ks=(30, 100), h=4, hk=2)
+    assert size == ws_size(c) > 0
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(bs=96), -5),                 # block size not a multiple of 64
+    (dict(bs=32, cols=4), -5),
+    (dict(cols=1), -2),                # table too narrow for 100 keys at 64 per block
+    (dict(ks=(30, 2048 * 64 + 1), cols=2100, nb=2100), -5),  # beyond the fused path's key limit
+])
+def test_paged_validation_errors(mutate, status):
+    assert paged_status(paged_tensors(**mutate)) == status
+
+
+def test_paged_cache_shape_and_dtype_errors():
+    t = paged_tensors()
+    t["krope_cache"] = torch.zeros((8, 64, 2, 32), dtype=torch.bfloat16)
+    assert paged_status(t) == -2
+    t = paged_tensors()
+    t["value_cache"] = torch.zeros((8, 64, 2, 128), dtype=torch.float16)
+    assert paged_status(t) == -3
+    t = paged_tensors()
+    t["block_tables"] = torch.zeros((2, 2), dtype=torch.int64)
+    assert paged_status(t) == -3
+    t = paged_tensors()
+    t["block_tables"] = torch.zeros((3, 2), dtype=torch.int32)
+    assert paged_status(t) == -2
+    t = paged_tensors()
+    t["key_cache"] = torch.zeros((8, 128, 2, 128), dtype=torch.bfloat16)  # block size differs between caches
+    assert paged_status(t) == -2

@@ -96,3 +96,38 @@ def test_page_block_table_width_formula():
     width = (max(lens) - 1) // bs + 1
     assert width == 3
     assert all((n - 1) // bs + 1 <= width for n in lens)
+
+
+@pytest.mark.parametrize("block_size", [3, 16])
+def test_paged_attention_equals_attention_on_the_scattered_kv(block_size):
+    # Fused paged attention is, by definition, the gather followed by attention:
+    # scatter contiguous K/KRope/V into a permuted cache whose unused blocks
+    # hold NaN, and the paged result must equal attention on the contiguous
+    # tensors exactly (the same fp64 arithmetic on the same values).
+    rng = np.random.default_rng(3)
+    qlens, kvlens = [5, 9, 0, 4], [7, 9, 3, 11]
+    H, HK, D, R = 4, 2, 8, 4
+    cols = max(-(-n // block_size) for n in kvlens) + 1
+    nb = len(kvlens) * cols + 2
+    table = rng.permutation(nb)[:len(kvlens) * cols].reshape(len(kvlens), cols).astype(np.int32)
+    q = rng.standard_normal((sum(qlens), H, D))
+    qr = rng.standard_normal((sum(qlens), H, R))
+    k = rng.standard_normal((sum(kvlens), HK, D))
+    kr = rng.standard_normal((sum(kvlens), HK, R))
+    v = rng.standard_normal((sum(kvlens), HK, D))
+
+    def cache_of(rows):
+        c = scatter_to_cache(rows, kvlens, table, block_size, nb)
+        used = np.zeros((nb, block_size), bool)
+        for b, n in enumerate(kvlens):
+            for t in range(n):
+                used[table[b][t // block_size], t % block_size] = True
+        c[~used] = np.nan
+        return c
+
+    for mask_type in (oracle.MASK_CAUSAL, oracle.MASK_UNDEFINED):
+        ref = oracle.attention(q, qr, k, kr, v, qlens, kvlens, H, HK, 0.3, mask_type)
+        got = oracle.paged_attention(q, qr, cache_of(k), cache_of(kr), cache_of(v), table, qlens, kvlens, H, HK,
+                                     0.3, mask_type)
+        assert np.isfinite(got).all()
+        assert np.array_equal(got, ref)
