@@ -13,6 +13,9 @@ it, and it shares no code, tables or helpers with the HIP path.
   hasSeqStarts), ND cache layout.
 * ``paged_attention`` is the composition of the two: gather K, KRope and V
   out of ND caches, then attention on the gathered tensors.
+* ``paged_cache_load_nz`` is the same gather for the NZ cache layout of the
+  "PagedCacheLoadOperation" page's dimension table (keyCache / valueCache /
+  key / value rows, NZ column).
 
 Mask-type codes (the page names the modes but prints no integer values):
 UNDEFINED 0, SPEC 1, CAUSAL 2, MASK_FREE 3.
@@ -213,3 +216,32 @@ def paged_attention(q, qr, key_cache, krope_cache, value_cache, block_tables, q_
     v, _ = paged_cache_load(value_cache, None, block_tables, kv_seqlen)
     return attention(q, qr, k, kr, v, q_seqlen, kv_seqlen, head_num, kv_head_num, qk_scale, mask_type, mask,
                      lib=lib)
+
+
+def paged_cache_load_nz(key_cache, value_cache, block_tables, context_lens):
+    """Gather out of block-paged caches in the NZ layout.
+
+    The page's dimension table gives the NZ cache as [num_blocks,
+    num_heads * head_size // E, block_size, E] (E = 32 for int8, else 16) and
+    the gathered tensor as [sum(contextLens), num_heads * head_size]: a token's
+    row is cut into chunks of E elements, and chunk c of the token in slot s of
+    block k sits at cache[k, c, s, :]. Plain lengths only (the page supports
+    seqStarts and cumulative lengths in the ND layout only). Returns
+    (key, value); value is None when value_cache is None.
+    """
+    block_tables = np.asarray(block_tables)
+    batch = block_tables.shape[0]
+    block_size = key_cache.shape[2]
+    spans = sequence_spans(context_lens, batch, False)
+    total = sum(n for _, n in spans)
+
+    def gather(cache):
+        chunks, elems = cache.shape[1], cache.shape[3]
+        out = np.zeros((total, chunks * elems), dtype=cache.dtype)
+        for b, (off, n) in enumerate(spans):
+            for t in range(n):
+                k, s = block_tables[b, t // block_size], t % block_size
+                out[off + t] = cache[k, :, s, :].reshape(-1)
+        return out
+
+    return gather(key_cache), None if value_cache is None else gather(value_cache)

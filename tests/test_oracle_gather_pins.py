@@ -131,3 +131,38 @@ def test_paged_attention_equals_attention_on_the_scattered_kv(block_size):
                                      0.3, mask_type)
         assert np.isfinite(got).all()
         assert np.array_equal(got, ref)
+
+
+def nd_to_nz(cache_nd, elems):
+    """NZ form of an ND cache [nb, bs, H, hs]: each slot's H*hs row cut into
+    chunks of ``elems``, chunk index moved in front of the slot index."""
+    nb, bs, h, hs = cache_nd.shape
+    return cache_nd.reshape(nb, bs, h * hs // elems, elems).transpose(0, 2, 1, 3).copy()
+
+
+@pytest.mark.parametrize("dtype,elems", [(np.int16, 16), (np.int8, 32)])
+def test_nz_gather_equals_nd_gather_reshaped(dtype, elems):
+    rng = np.random.default_rng(7)
+    bs, lens, heads, hs = 8, [5, 17, 0, 9], 4, 32
+    cols = max(-(-n // bs) for n in lens)
+    nb = len(lens) * cols + 1
+    table = rng.permutation(nb)[:len(lens) * cols].reshape(len(lens), cols).astype(np.int32)
+    nd = rng.integers(-100, 100, size=(nb, bs, heads, hs)).astype(dtype)
+    nd_v = rng.integers(-100, 100, size=(nb, bs, heads, hs // 2)).astype(dtype)
+    k_nd, v_nd = oracle.paged_cache_load(nd, nd_v, table, lens)
+    k_nz, v_nz = oracle.paged_cache_load_nz(nd_to_nz(nd, elems), nd_to_nz(nd_v, elems), table, lens)
+    assert np.array_equal(k_nz, k_nd.reshape(len(k_nd), -1))
+    assert np.array_equal(v_nz, v_nd.reshape(len(v_nd), -1))
+
+
+def test_nz_gather_worked_example():
+    # 2 blocks, 2 chunks of 2 elements, block size 2; one sequence of 3 tokens
+    # whose table row is [1, 0]: tokens 0, 1 sit in block 1 slots 0, 1, token 2
+    # in block 0 slot 0. cache[k, c, s, e] = 1000k + 100c + 10s + e.
+    cache = np.array([[[[1000 * k + 100 * c + 10 * s + e for e in range(2)] for s in range(2)] for c in range(2)]
+                      for k in range(2)], dtype=np.int32)
+    key, value = oracle.paged_cache_load_nz(cache, None, [[1, 0]], [3])
+    assert value is None
+    assert key.tolist() == [[1000, 1001, 1100, 1101],
+                            [1010, 1011, 1110, 1111],
+                            [0, 1, 100, 101]]
