@@ -241,6 +241,40 @@ def bench_paged(steps):
     return gather_rec, attn_rec
 
 
+def bench_gather_nz(steps):
+    """The paged workload's gather with the caches in the NZ layout (the same
+    lengths, table and bytes as the ND leg; contents are random bit patterns,
+    which a copy does not look at)."""
+    lens, _ = synth.workload_seqlens("paged")
+    meta = synth.paged_inputs(lens, heads=1, head_size_k=16, head_size_v=16, with_rope=False, device="cuda")
+    table, ctx = meta["block_tables"], meta["context_lens"]
+    nb, bs, heads = meta["key_cache"].shape[0], synth.BLOCK_SIZE, 128
+    del meta
+
+    def nz_cache(head_size):
+        return torch.empty((nb, heads * head_size // 16, bs, 16), dtype=torch.int16,
+                           device="cuda").random_().view(torch.bfloat16)
+
+    kc, vc, rc = nz_cache(128), nz_cache(128), nz_cache(64)
+    total = int(lens.sum())
+    key = torch.empty((total, heads * 128), dtype=torch.bfloat16, device="cuda")
+    value = torch.empty_like(key)
+    rope = torch.empty((total, heads * 64), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def gather():
+        mla.paged_cache_load(kc, vc, table, ctx, key, value, None, mla.KV_CACHE_NZ, False, False, stream)
+        mla.paged_cache_load(rc, None, table, ctx, rope, None, None, mla.KV_CACHE_NZ, False, False, stream)
+
+    ms = _time(gather, steps, stream)
+    nbytes = 2 * total * (key[0].numel() + value[0].numel() + rope[0].numel()) * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del kc, vc, rc, key, value, rope
+    torch.cuda.empty_cache()
+    return {"workload": "paged", "layout": "NZ", "tokens": total, "bytes_per_step": nbytes, "ms_per_step": ms,
+            "value": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +326,7 @@ def main():
     if not args.no_gather and args.workload == "single":
         res_t = res.pop("tensors") if args.no_cpu_baseline else None
         line["gather"], line["paged_attention"] = bench_paged(max(2, min(args.steps, 5)))
+        line["gather_nz"] = bench_gather_nz(max(2, min(args.steps, 5)))
         del res_t
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)

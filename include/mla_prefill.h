@@ -79,8 +79,7 @@ enum mla_mask_type {
 };
 
 /* kvCacheCfg ("PagedCacheLoadOperation" page, Members table): NZ = 0 is the
- * page's default, ND = 1. Only ND is implemented; NZ returns
- * MLA_ERR_UNSUPPORTED. */
+ * page's default, ND = 1. Both layouts are implemented (see paged_cache_load). */
 enum mla_kv_cache_cfg {
     MLA_KV_CACHE_NZ = 0,
     MLA_KV_CACHE_ND = 1
@@ -181,7 +180,14 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
  *   seq_starts    device int32 [batch]: token offset of each sequence inside its
  *                 block table's logical space. Read only when has_seq_starts;
  *                 otherwise every sequence starts at 0 and it may be NULL.
- *   kv_cache_cfg  MLA_KV_CACHE_ND (1). MLA_KV_CACHE_NZ: MLA_ERR_UNSUPPORTED.
+ *   kv_cache_cfg  MLA_KV_CACHE_ND (1), or MLA_KV_CACHE_NZ (0), the layout of the
+ *                 page's dimension table, NZ column: caches
+ *                 [num_blocks, num_heads*head_size / E, block_size, E] with E = 32
+ *                 for int8 and 16 for fp16/bf16 (32-byte chunks), outputs 2-D
+ *                 [num_tokens, num_heads*head_size]; chunk c of the token in
+ *                 slot s of block k is cache[k][c][s]. The page allows seqStarts
+ *                 and cumulative lengths in the ND layout only: with NZ they return
+ *                 MLA_ERR_UNSUPPORTED.
  *
  * Token t of sequence b is logical position s_b + t, found in block
  * block_tables[b][(s_b + t) / block_size] at slot (s_b + t) % block_size. The

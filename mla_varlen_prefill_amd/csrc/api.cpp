@@ -595,9 +595,11 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
     if (value_cache && ((rc = check_tensor(value_cache, "value_cache", true)) ||
                         (rc = check_tensor(value, "value", true))))
         return rc;
-    if (kv_cache_cfg == MLA_KV_CACHE_NZ)
-        return fail(MLA_ERR_UNSUPPORTED, "kvCacheCfg NZ: only the ND cache layout is implemented");
-    if (kv_cache_cfg != MLA_KV_CACHE_ND) return fail(MLA_ERR_VALUE, "kvCacheCfg %d is unknown", kv_cache_cfg);
+    if (kv_cache_cfg != MLA_KV_CACHE_ND && kv_cache_cfg != MLA_KV_CACHE_NZ)
+        return fail(MLA_ERR_VALUE, "kvCacheCfg %d is unknown", kv_cache_cfg);
+    const bool nz = kv_cache_cfg == MLA_KV_CACHE_NZ;
+    if (nz && (is_seq_lens_cumsum_type || has_seq_starts))
+        return fail(MLA_ERR_UNSUPPORTED, "kvCacheCfg NZ: cumulative lengths and seqStarts are ND-only");
 
     const int dt = key_cache->dtype;
     if (!(dt == MLA_FP16 || dt == MLA_BF16 || dt == MLA_INT8))
@@ -608,23 +610,50 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
     if (block_tables->dtype != MLA_INT32 || context_lens->dtype != MLA_INT32)
         return fail(MLA_ERR_DTYPE, "block_tables / context_lens must be int32");
 
-    if (key_cache->ndim != 4) return fail(MLA_ERR_SHAPE, "key_cache: expected ND [num_blocks, block_size, heads, head_size]");
-    const int64_t nb = key_cache->shape[0], bs = key_cache->shape[1], heads = key_cache->shape[2];
-    if (bs <= 0) return fail(MLA_ERR_SHAPE, "key_cache: block_size must be > 0");
-    if (key->ndim != 3 || key->shape[1] != heads || key->shape[2] != key_cache->shape[3])
-        return fail(MLA_ERR_SHAPE, "key: expected [num_tokens, %lld, %lld]", (long long)heads,
-                    (long long)key_cache->shape[3]);
-    const int64_t num_tokens = key->shape[0];
-    if (value_cache) {
-        if (value_cache->ndim != 4 || value_cache->shape[0] != nb || value_cache->shape[1] != bs ||
-            value_cache->shape[2] != heads)
-            return fail(MLA_ERR_SHAPE, "value_cache: expected [%lld, %lld, %lld, head_size_v]", (long long)nb,
-                        (long long)bs, (long long)heads);
-        if (value->ndim != 3 || value->shape[0] != num_tokens || value->shape[1] != heads ||
-            value->shape[2] != value_cache->shape[3])
-            return fail(MLA_ERR_SHAPE, "value: expected [%lld, %lld, %lld]", (long long)num_tokens,
-                        (long long)heads, (long long)value_cache->shape[3]);
+    int64_t nb, bs, heads = 0, chunks_k = 0, chunks_v = 0;
+    if (nz) {
+        // NZ: cache [num_blocks, heads*head_size / E, block_size, E], E = 32 int8 / 16 fp16-bf16
+        // (32 bytes); gathered tensor [num_tokens, heads*head_size]
+        const int64_t e = dt == MLA_INT8 ? 32 : 16;
+        if (key_cache->ndim != 4 || key_cache->shape[3] != e)
+            return fail(MLA_ERR_SHAPE, "key_cache: expected NZ [num_blocks, chunks, block_size, %lld]", (long long)e);
+        nb = key_cache->shape[0];
+        bs = key_cache->shape[2];
+        chunks_k = key_cache->shape[1];
+        if (bs <= 0) return fail(MLA_ERR_SHAPE, "key_cache: block_size must be > 0");
+        if (key->ndim != 2 || key->shape[1] != chunks_k * e)
+            return fail(MLA_ERR_SHAPE, "key: expected [num_tokens, %lld]", (long long)(chunks_k * e));
+        if (value_cache) {
+            if (value_cache->ndim != 4 || value_cache->shape[0] != nb || value_cache->shape[2] != bs ||
+                value_cache->shape[3] != e)
+                return fail(MLA_ERR_SHAPE, "value_cache: expected NZ [%lld, chunks, %lld, %lld]", (long long)nb,
+                            (long long)bs, (long long)e);
+            chunks_v = value_cache->shape[1];
+            if (value->ndim != 2 || value->shape[0] != key->shape[0] || value->shape[1] != chunks_v * e)
+                return fail(MLA_ERR_SHAPE, "value: expected [%lld, %lld]", (long long)key->shape[0],
+                            (long long)(chunks_v * e));
+        }
+    } else {
+        if (key_cache->ndim != 4) return fail(MLA_ERR_SHAPE, "key_cache: expected ND [num_blocks, block_size, heads, head_size]");
+        nb = key_cache->shape[0];
+        bs = key_cache->shape[1];
+        heads = key_cache->shape[2];
+        if (bs <= 0) return fail(MLA_ERR_SHAPE, "key_cache: block_size must be > 0");
+        if (key->ndim != 3 || key->shape[1] != heads || key->shape[2] != key_cache->shape[3])
+            return fail(MLA_ERR_SHAPE, "key: expected [num_tokens, %lld, %lld]", (long long)heads,
+                        (long long)key_cache->shape[3]);
+        if (value_cache) {
+            if (value_cache->ndim != 4 || value_cache->shape[0] != nb || value_cache->shape[1] != bs ||
+                value_cache->shape[2] != heads)
+                return fail(MLA_ERR_SHAPE, "value_cache: expected [%lld, %lld, %lld, head_size_v]", (long long)nb,
+                            (long long)bs, (long long)heads);
+            if (value->ndim != 3 || value->shape[0] != key->shape[0] || value->shape[1] != heads ||
+                value->shape[2] != value_cache->shape[3])
+                return fail(MLA_ERR_SHAPE, "value: expected [%lld, %lld, %lld]", (long long)key->shape[0],
+                            (long long)heads, (long long)value_cache->shape[3]);
+        }
     }
+    const int64_t num_tokens = key->shape[0];
     if (block_tables->ndim != 2) return fail(MLA_ERR_SHAPE, "block_tables: expected [batch, max_blocks]");
     const int64_t batch = block_tables->shape[0];
     if (batch > mla::GATHER_MAX_BATCH)
@@ -654,8 +683,16 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
     p.block_size = bs;
     p.max_blocks = block_tables->shape[1];
     p.num_tokens = num_tokens;
-    p.row_bytes_k = heads * key_cache->shape[3] * (int64_t)elem_size(dt);
-    p.row_bytes_v = value_cache ? heads * value_cache->shape[3] * (int64_t)elem_size(dt) : 0;
+    if (nz) {
+        p.nz = 1;
+        p.chunks_k = chunks_k;
+        p.chunks_v = chunks_v;
+        p.row_bytes_k = chunks_k * 32;
+        p.row_bytes_v = chunks_v * 32;
+    } else {
+        p.row_bytes_k = heads * key_cache->shape[3] * (int64_t)elem_size(dt);
+        p.row_bytes_v = value_cache ? heads * value_cache->shape[3] * (int64_t)elem_size(dt) : 0;
+    }
     p.batch = (int32_t)batch;
     p.ctx_entries = (int32_t)n_ctx;
     p.cumsum = is_seq_lens_cumsum_type ? 1 : 0;

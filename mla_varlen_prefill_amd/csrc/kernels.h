@@ -96,6 +96,11 @@ struct GatherParams {
     int32_t ctx_entries;      // batch or batch + 1
     int32_t cumsum;
     int32_t has_seq_starts;
+    // NZ layout: caches [num_blocks, chunks, block_size, 32 bytes], outputs
+    // [num_tokens, chunks * 32 bytes]; row_bytes_* = chunks_* * 32.
+    int32_t nz;
+    int64_t chunks_k;
+    int64_t chunks_v;
 };
 
 constexpr int GATHER_MAX_BATCH = 8192;  // offsets table in LDS: (batch + 1) * 4 bytes

@@ -17,6 +17,20 @@
 //    a byte copy.
 // Tokens whose output row is past num_tokens, whose table column is past
 // max_blocks or whose block id is outside [0, num_blocks) are skipped.
+//
+// NZ layout (the page's dimension table, NZ column): a token's row is cut into
+// 32-byte chunks (16 fp16/bf16 or 32 int8 elements) and chunk c of slot s of
+// block k sits at cache[k][c][s]. For one chunk, consecutive slots are
+// adjacent; for one token, consecutive chunks are block_size * 32 bytes apart.
+// So the NZ kernel transposes through LDS: a workgroup owns 64 output tokens;
+// for each group of 32 chunks, every read instruction takes one chunk of 32
+// consecutive tokens (one contiguous kilobyte when they share a block), the
+// tile is stored in LDS by token (rows padded by 16 bytes against bank
+// conflicts), and every write instruction then stores one kilobyte of one
+// token's output row. The next group's loads are in flight while a group goes
+// from LDS to the output. (Tiles of 32 x 16, 32 x 32, 64 x 16, 128 x 8,
+// 128 x 16 and 16 x 64 tokens x chunks measured 60-68% of HBM peak against
+// 68-70% for 64 x 32.)
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -48,14 +62,10 @@ __device__ __forceinline__ void copy_row_bytes(const unsigned char *src, unsigne
     for (int64_t c = tid; c < n; c += G_THREADS) dst[c] = src[c];
 }
 
-__global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherParams p) {
-    extern __shared__ int32_t s_off[];  // [batch + 1] output offsets
-    __shared__ int64_t s_src[G_TOKENS];  // source slot (block * block_size + offset), -1 to skip
-    __shared__ int32_t s_partial[G_THREADS];
-    const int tid = threadIdx.x;
+// Output offset of every sequence into s_off[0 .. batch]: a block-wide scan
+// of context_lens, or the running totals as given.
+__device__ void build_offsets(const GatherParams &p, int32_t *s_off, int32_t *s_partial, int tid) {
     const int B = p.batch;
-
-    // ---- output offsets of every sequence
     if (p.cumsum) {
         if (p.ctx_entries == B + 1) {  // [0, c1, c1 + c2, ...]
             for (int i = tid; i <= B; i += G_THREADS) s_off[i] = p.context_lens[i];
@@ -88,6 +98,35 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
         if (hi == B && lo < hi) s_off[B] = run;  // the thread holding the last sequence
         __syncthreads();
     }
+}
+
+// Source slot of output token n (block * block_size + position in the block),
+// or -1 when the token is to be skipped.
+__device__ int64_t source_slot(const GatherParams &p, const int32_t *s_off, int64_t n) {
+    const int B = p.batch;
+    if (n >= p.num_tokens || n >= s_off[B]) return -1;
+    int lo = 0, hi = B;  // last sequence b with s_off[b] <= n: s_off[lo] <= n < s_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= n) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int64_t lpos = n - s_off[b] + (p.has_seq_starts ? p.seq_starts[b] : 0);
+    if (lpos < 0) return -1;
+    const int64_t col = lpos / p.block_size;
+    if (col >= p.max_blocks) return -1;
+    const int64_t blk = p.block_tables[(int64_t)b * p.max_blocks + col];
+    if (blk < 0 || blk >= p.num_blocks) return -1;
+    return blk * p.block_size + lpos % p.block_size;
+}
+
+__global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherParams p) {
+    extern __shared__ int32_t s_off[];  // [batch + 1] output offsets
+    __shared__ int64_t s_src[G_TOKENS];  // source slot (block * block_size + offset), -1 to skip
+    __shared__ int32_t s_partial[G_THREADS];
+    const int tid = threadIdx.x;
+
+    build_offsets(p, s_off, s_partial, tid);
 
     const bool vec = ((p.row_bytes_k | p.row_bytes_v) & 15) == 0 &&
                      ((reinterpret_cast<uintptr_t>(p.key_cache) | reinterpret_cast<uintptr_t>(p.key) |
@@ -102,26 +141,7 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
     for (int64_t n0 = (int64_t)blockIdx.x * G_TOKENS; n0 < total; n0 += (int64_t)gridDim.x * G_TOKENS) {
         // ---- resolve the source rows of tokens n0 .. n0 + G_TOKENS - 1
         if (tid < G_TOKENS) {
-            const int64_t n = n0 + tid;
-            int64_t src = -1;
-            if (n < total && n < s_off[B]) {
-                // last sequence b with s_off[b] <= n
-                int lo = 0, hi = B;  // invariant: s_off[lo] <= n < s_off[hi]
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (s_off[mid] <= n) lo = mid; else hi = mid;
-                }
-                const int b = lo;
-                const int64_t t = n - s_off[b];
-                const int64_t lpos = t + (p.has_seq_starts ? p.seq_starts[b] : 0);
-                if (lpos >= 0) {
-                    const int64_t col = lpos / p.block_size;
-                    if (col < p.max_blocks) {
-                        const int64_t blk = p.block_tables[(int64_t)b * p.max_blocks + col];
-                        if (blk >= 0 && blk < p.num_blocks) src = blk * p.block_size + lpos % p.block_size;
-                    }
-                }
-            }
+            const int64_t src = source_slot(p, s_off, n0 + tid);
             s_src[tid] = src;
         }
         __syncthreads();
@@ -144,10 +164,100 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
     }
 }
 
+
+// ---- NZ layout
+#ifndef MLA_NZ_TOKENS
+#define MLA_NZ_TOKENS 64
+#endif
+#ifndef MLA_NZ_CHUNKS
+#define MLA_NZ_CHUNKS 32
+#endif
+constexpr int NZ_TOKENS = MLA_NZ_TOKENS;      // output tokens per workgroup
+constexpr int NZ_CHUNKS = MLA_NZ_CHUNKS;      // 32-byte chunks per tile
+constexpr int NZ_ROW = NZ_CHUNKS * 32 + 16;   // LDS bytes per token row of the tile
+constexpr int NZ_PER_THREAD = NZ_TOKENS * NZ_CHUNKS * 2 / G_THREADS;  // 16-byte pieces per thread and tile
+
+// One cache (key or value): output token rows n0 .. n0 + 31 of chunks
+// [0, chunks), through LDS tiles of 32 tokens x 32 chunks.
+__global__ __launch_bounds__(G_THREADS) void paged_gather_nz_kernel(const GatherParams p, const void *cache_,
+                                                                    void *out_, int64_t chunks) {
+    extern __shared__ int32_t s_off[];  // [batch + 1] output offsets
+    __shared__ int64_t s_base[NZ_TOKENS];  // byte offset of chunk 0 of each token, -1 to skip
+    __shared__ int32_t s_partial[G_THREADS];
+    __shared__ __attribute__((aligned(16))) unsigned char tile[NZ_TOKENS * NZ_ROW];
+    const int tid = threadIdx.x;
+    const unsigned char *cache = static_cast<const unsigned char *>(cache_);
+    unsigned char *out = static_cast<unsigned char *>(out_);
+
+    build_offsets(p, s_off, s_partial, tid);
+    const int64_t n0 = (int64_t)blockIdx.x * NZ_TOKENS;
+    if (tid < NZ_TOKENS) {
+        const int64_t slot = source_slot(p, s_off, n0 + tid);  // block * block_size + position
+        if (slot < 0) {
+            s_base[tid] = -1;
+        } else {
+            const int64_t blk = slot / p.block_size, pos = slot - blk * p.block_size;
+            s_base[tid] = ((blk * chunks) * p.block_size + pos) * 32;
+        }
+    }
+    __syncthreads();
+    const int64_t chunk_stride = (int64_t)p.block_size * 32;  // bytes between chunk c and c + 1 of one slot
+    const int64_t row_bytes = chunks * 32;
+    // Software pipeline: the loads of chunk group g + 1 are in flight while
+    // group g goes from LDS to the output.
+    u32x4 r[NZ_PER_THREAD];
+    auto load_group = [&](int64_t c0) __attribute__((always_inline)) {
+        // piece q is chunk q / (2 * NZ_TOKENS) of the tile, token (q / 2) % NZ_TOKENS, half q % 2
+#pragma unroll
+        for (int u = 0; u < NZ_PER_THREAD; ++u) {
+            const int q = tid + G_THREADS * u;
+            const int cl = q / (2 * NZ_TOKENS), tok = (q >> 1) % NZ_TOKENS, half = q & 1;
+            const int64_t base = s_base[tok];
+            r[u] = (u32x4){0u, 0u, 0u, 0u};
+            if (base >= 0 && c0 + cl < chunks)
+                r[u] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(cache + base + (c0 + cl) * chunk_stride + half * 16));
+        }
+    };
+    load_group(0);
+    for (int64_t c0 = 0; c0 < chunks; c0 += NZ_CHUNKS) {
+#pragma unroll
+        for (int u = 0; u < NZ_PER_THREAD; ++u) {
+            const int q = tid + G_THREADS * u;
+            const int cl = q / (2 * NZ_TOKENS), tok = (q >> 1) % NZ_TOKENS, half = q & 1;
+            *reinterpret_cast<u32x4 *>(tile + tok * NZ_ROW + cl * 32 + half * 16) = r[u];
+        }
+        __syncthreads();
+        if (c0 + NZ_CHUNKS < chunks) load_group(c0 + NZ_CHUNKS);
+        // LDS -> output: piece q is token q / (2 * NZ_CHUNKS), chunk (q / 2) % NZ_CHUNKS, half q % 2
+#pragma unroll
+        for (int u = 0; u < NZ_PER_THREAD; ++u) {
+            const int q = tid + G_THREADS * u;
+            const int tok = q / (2 * NZ_CHUNKS), cl = (q >> 1) % NZ_CHUNKS, half = q & 1;
+            const int64_t n = n0 + tok;
+            if (s_base[tok] >= 0 && c0 + cl < chunks)
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(tile + tok * NZ_ROW + cl * 32 + half * 16),
+                                            reinterpret_cast<u32x4 *>(out + n * row_bytes + (c0 + cl) * 32 + half * 16));
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream) {
     if (p.num_tokens <= 0 || p.batch <= 0) return hipSuccess;
+    if (p.nz) {
+        const int64_t grid = (p.num_tokens + NZ_TOKENS - 1) / NZ_TOKENS;
+        if (grid > INT32_MAX) return hipErrorInvalidValue;
+        const size_t shmem = sizeof(int32_t) * ((size_t)p.batch + 1);
+        hipLaunchKernelGGL(paged_gather_nz_kernel, dim3((unsigned)grid), dim3(G_THREADS), shmem, stream, p,
+                           p.key_cache, p.key, p.chunks_k);
+        if (p.value_cache)
+            hipLaunchKernelGGL(paged_gather_nz_kernel, dim3((unsigned)grid), dim3(G_THREADS), shmem, stream, p,
+                               p.value_cache, p.value, p.chunks_v);
+        return hipGetLastError();
+    }
     int64_t steps = (p.num_tokens + G_TOKENS - 1) / G_TOKENS;
     int grid = (int)(steps < 8192 ? steps : 8192);
     size_t shmem = sizeof(int32_t) * ((size_t)p.batch + 1);

@@ -152,7 +152,7 @@ def gather_args(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(kv_cache_cfg=mla.KV_CACHE_NZ), "MLA_ERR_UNSUPPORTED"),
+    (dict(kv_cache_cfg=mla.KV_CACHE_NZ), "MLA_ERR_SHAPE"),   # ND-shaped outputs under NZ
     (dict(kv_cache_cfg=5), "MLA_ERR_VALUE"),
     (dict(value=None), "MLA_ERR_NULL"),
     (dict(key=torch.zeros(10, 2, 8, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
@@ -168,6 +168,42 @@ def test_gather_validation_errors(kw, status):
     with pytest.raises(mla.MlaError) as e:
         mla.paged_cache_load(**gather_args(**kw), stream=0)
     assert e.value.status == status
+
+
+def nz_args(**kw):
+    # NZ: caches [num_blocks, chunks, block_size, 32 bytes of elements], outputs [num_tokens, chunks * elems]
+    a = dict(key_cache=torch.zeros(4, 16, 8, 16, dtype=torch.bfloat16),
+             value_cache=torch.zeros(4, 8, 8, 16, dtype=torch.bfloat16),
+             block_tables=torch.zeros(2, 2, dtype=torch.int32), context_lens=torch.zeros(2, dtype=torch.int32),
+             key=torch.zeros(10, 256, dtype=torch.bfloat16), value=torch.zeros(10, 128, dtype=torch.bfloat16),
+             seq_starts=None, kv_cache_cfg=mla.KV_CACHE_NZ, is_seq_lens_cumsum_type=False, has_seq_starts=False)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(is_seq_lens_cumsum_type=True), "MLA_ERR_UNSUPPORTED"),   # the page: ND only
+    (dict(has_seq_starts=True, seq_starts=torch.zeros(2, dtype=torch.int32)), "MLA_ERR_UNSUPPORTED"),
+    (dict(key_cache=torch.zeros(4, 16, 8, 32, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),   # 16-bit: 16 per chunk
+    (dict(key_cache=torch.zeros(4, 8, 8, 16, dtype=torch.int8), key=torch.zeros(10, 128, dtype=torch.int8),
+          value_cache=None, value=None), "MLA_ERR_SHAPE"),                                # int8: 32 per chunk
+    (dict(key=torch.zeros(10, 16, 16, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (dict(value=torch.zeros(9, 128, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),
+    (dict(value_cache=torch.zeros(4, 8, 4, 16, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),   # block size differs
+])
+def test_gather_nz_validation_errors(kw, status):
+    with pytest.raises(mla.MlaError) as e:
+        mla.paged_cache_load(**nz_args(**kw), stream=0)
+    assert e.value.status == status
+
+
+def test_gather_nz_valid_shapes_pass_validation():
+    # zero tokens: validation passes and nothing is launched (no HIP call here)
+    mla.paged_cache_load(**nz_args(key=torch.zeros(0, 256, dtype=torch.bfloat16),
+                                   value=torch.zeros(0, 128, dtype=torch.bfloat16)), stream=0)
+    mla.paged_cache_load(**nz_args(key_cache=torch.zeros(4, 8, 8, 32, dtype=torch.int8),
+                                   key=torch.zeros(0, 256, dtype=torch.int8), value_cache=None, value=None),
+                         stream=0)
 
 
 # ------------------------------------------------------------------ planner
