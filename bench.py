@@ -148,6 +148,39 @@ def bench_attention(name, steps, warmup):
                 launch_ms_min=float(np.min(launch_ms)))
 
 
+def _attention_tflops(t, qs, ks, heads, kv_heads, mask_type, mask, steps):
+    out = torch.empty((t["q"].shape[0], heads, 128), dtype=t["q"].dtype, device="cuda")
+    args = dict(q=t["q"], q_rope=t["q_rope"], k=t["k"], k_rope=t["k_rope"], v=t["v"], q_seqlen=qs, kv_seqlen=ks,
+                mask=mask, head_num=heads, qk_scale=synth.QK_SCALE, kv_head_num=kv_heads, mask_type=mask_type,
+                cache_mode=0, atten_out=out)
+    ws = torch.empty(max(mla.mla_prefill_get_workspace_size(**args), 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = _time(lambda: mla.mla_prefill(**args, workspace=ws, stream=stream), steps, stream)
+    flops = FLOP_PER_PAIR * heads * visible_pairs(qs, ks, mask_type)
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def bench_extras(steps):
+    """Secondary configurations: the chunked workload under MASK_FREE with the
+    causal fp16 tile (the same visible pairs as causal), and one GPU's share of
+    an 8-way split over heads (16 heads) of the single and chunked shapes."""
+    res = {}
+    t, qs, ks, p = synth.workload_inputs("chunked", device="cuda")
+    res["chunked_causal"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_CAUSAL, None, steps)
+    tile = synth.causal_mask_tile(torch.float16, "cuda")
+    res["chunked_mask_free_causal_tile"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_FREE, tile, steps)
+    del t
+    for name in ("single", "chunked"):
+        qs, ks = synth.workload_seqlens(name)
+        w = synth.WORKLOADS[name]
+        t = synth.attention_inputs(qs, ks, 16, 16, w["dtype"], w["sigma"], w["seed"], "cuda")
+        res[f"tp8_share_{name}_16_heads"] = _attention_tflops(t, np.asarray(qs, np.int32), np.asarray(ks, np.int32),
+                                                             16, 16, synth.MASK_CAUSAL, None, steps)
+        del t
+    torch.cuda.empty_cache()
+    return {k: {"ms": round(v["ms"], 4), "tflops": round(v["tflops"], 2)} for k, v in res.items()}
+
+
 def cpu_baseline(res, seconds):
     """The oracle as it stands, on whole heads of the same workload until about
     ``seconds`` of CPU time have been spent (at least one head)."""
@@ -327,6 +360,7 @@ def main():
         res_t = res.pop("tensors") if args.no_cpu_baseline else None
         line["gather"], line["paged_attention"] = bench_paged(max(2, min(args.steps, 5)))
         line["gather_nz"] = bench_gather_nz(max(2, min(args.steps, 5)))
+        line["extras"] = bench_extras(3)
         del res_t
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)

@@ -28,6 +28,10 @@ using mla::PAGED_MAX_TILES;
 using mla::Task;
 using mla::WorkItem;
 
+#ifndef MLA_PLAN_BATCH_TASKS
+#define MLA_PLAN_BATCH_TASKS (2 * MLA_CUS_PER_XCD)
+#endif
+constexpr int PLAN_BATCH_TASKS = MLA_PLAN_BATCH_TASKS;  // minimum tasks per launch-order batch of an XCD queue
 static_assert(MLA_PLAN_Q_ROWS == FWD_BM, "plan row count must match the kernel tile");
 static_assert(MLA_PLAN_KV_COLS == FWD_BN, "plan key count must match the kernel tile");
 static_assert(MLA_PAGED_MAX_KEYS == PAGED_MAX_TILES * FWD_BN, "paged key limit must match the kernel table");
@@ -404,7 +408,7 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         for (const Group &gr : xcd_groups[x]) {
             for (int32_t i = seq_first[gr.b]; i < seq_first[gr.b + 1]; ++i)
                 for (int32_t h = gr.hk * group; h < (gr.hk + 1) * group; ++h) pending.push_back({i, h});
-            if (pending.size() >= 2 * (size_t)MLA_CUS_PER_XCD) flush();
+            if (pending.size() >= (size_t)PLAN_BATCH_TASKS) flush();
         }
         flush();
     }
