@@ -162,8 +162,9 @@ def _attention_tflops(t, qs, ks, heads, kv_heads, mask_type, mask, steps):
 
 def bench_extras(steps):
     """Secondary configurations: the chunked workload under MASK_FREE with the
-    causal fp16 tile (the same visible pairs as causal), and one GPU's share of
-    an 8-way split over heads (16 heads) of the single and chunked shapes."""
+    causal fp16 tile (the same visible pairs as causal); one GPU's share of an
+    8-way split over heads (16 heads) of the single and chunked shapes; and the
+    single shape with its 128 query heads grouped over 16 and over 1 KV heads."""
     res = {}
     t, qs, ks, p = synth.workload_inputs("chunked", device="cuda")
     res["chunked_causal"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_CAUSAL, None, steps)
@@ -176,6 +177,14 @@ def bench_extras(steps):
         t = synth.attention_inputs(qs, ks, 16, 16, w["dtype"], w["sigma"], w["seed"], "cuda")
         res[f"tp8_share_{name}_16_heads"] = _attention_tflops(t, np.asarray(qs, np.int32), np.asarray(ks, np.int32),
                                                              16, 16, synth.MASK_CAUSAL, None, steps)
+        del t
+    qs, ks = synth.workload_seqlens("single")
+    w = synth.WORKLOADS["single"]
+    for hk in (16, 1):
+        t = synth.attention_inputs(qs, ks, 128, hk, w["dtype"], w["sigma"], w["seed"], "cuda")
+        res[f"single_128_heads_{hk}_kv_heads"] = _attention_tflops(t, np.asarray(qs, np.int32),
+                                                                   np.asarray(ks, np.int32), 128, hk,
+                                                                   synth.MASK_CAUSAL, None, steps)
         del t
     torch.cuda.empty_cache()
     return {k: {"ms": round(v["ms"], 4), "tflops": round(v["tflops"], 2)} for k, v in res.items()}

@@ -253,12 +253,15 @@ const char *mla_last_error(void);
  * the start of the workspace, three arrays each starting on a 256-byte
  * boundary:
  *   batch records  {q_offset, kv_offset, q_len, kv_len}  int32 x 4, batch of them
- *   work items     {batch, first_q_row, kv_tiles, 0}    int32 x 4, *n_items of them
- *   tasks          {item, head}                          int32 x 2, *n_tasks of them
- * One work item covers MLA_PLAN_Q_ROWS query rows of a sequence; kv_tiles
- * counts the tiles of MLA_PLAN_KV_COLS keys (from key 0) those rows can see.
- * Task i is the work of workgroup i of the launch (item -1: an empty padding
- * task). kv_padded_max_seq: 0 for packed K/V, else max_seq of the padded
+ *   work items     {batch, first_q_row, kv_tiles, q_rows} int32 x 4, *n_items of them
+ *   tasks          {item, first_head}                      int32 x 2, *n_tasks of them
+ * A task runs P = MLA_PLAN_Q_ROWS / q_rows query heads, first_head ..
+ * first_head + P - 1, which share one KV head: P is the largest power of two
+ * up to 8 that divides head_num / kv_head_num (1 without head grouping). One
+ * work item covers q_rows = MLA_PLAN_Q_ROWS / P query rows of a sequence;
+ * kv_tiles counts the tiles of MLA_PLAN_KV_COLS keys (from key 0) those rows
+ * can see. Task i is the work of workgroup i of the launch (item -1: an empty
+ * padding task). kv_padded_max_seq: 0 for packed K/V, else max_seq of the padded
  * layout. Returns MLA_ERR_WORKSPACE if buf is too small, MLA_ERR_VALUE for bad
  * lengths or head counts.
  */

@@ -233,8 +233,9 @@ def mla_prefill_plan_host(q_seqlen, kv_seqlen, head_num, kv_head_num, mask_type,
     """The work list mla_prefill would copy to its workspace, decoded.
 
     Returns (seqs [batch, 4] int32 = q_offset, kv_offset, q_len, kv_len;
-    items [n, 4] int32 = batch, first_q_row, kv_tiles, 0;
-    tasks [m, 2] int32 = item (-1: padding), head -- task i is workgroup i).
+    items [n, 4] int32 = batch, first_q_row, kv_tiles, q_rows;
+    tasks [m, 2] int32 = item (-1: padding), first head -- task i is
+    workgroup i and runs PLAN_Q_ROWS // q_rows heads from its first head).
     """
     lib = _load()
     qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)

@@ -32,6 +32,10 @@ using mla::WorkItem;
 #define MLA_PLAN_BATCH_TASKS (2 * MLA_CUS_PER_XCD)
 #endif
 constexpr int PLAN_BATCH_TASKS = MLA_PLAN_BATCH_TASKS;  // minimum tasks per launch-order batch of an XCD queue
+#ifndef MLA_MAX_PACK_SHIFT
+#define MLA_MAX_PACK_SHIFT 3
+#endif
+static_assert(MLA_MAX_PACK_SHIFT >= 0 && MLA_MAX_PACK_SHIFT <= mla::FWD_MAX_PACK_SHIFT, "at most 8 heads per task");
 static_assert(MLA_PLAN_Q_ROWS == FWD_BM, "plan row count must match the kernel tile");
 static_assert(MLA_PLAN_KV_COLS == FWD_BN, "plan key count must match the kernel tile");
 static_assert(MLA_PAGED_MAX_KEYS == PAGED_MAX_TILES * FWD_BN, "paged key limit must match the kernel table");
@@ -340,29 +344,48 @@ uint64_t plan_bytes(const Plan &p) {
     return tasks_offset(p) + p.tasks.size() * sizeof(Task);
 }
 
+// log2 of the query heads one task runs: the largest power of two, at most
+// 8, dividing the group size headNum / kvHeadNum. The heads of a task then
+// share one KV head.
+int32_t pack_shift_for(int32_t heads, int32_t kv_heads) {
+    const int32_t group = kv_heads > 0 ? heads / kv_heads : 1;
+    int32_t ps = 0;
+    while (ps < MLA_MAX_PACK_SHIFT && group % (2 << ps) == 0) ++ps;
+    return ps;
+}
+
 // Work list.
-//  * Items: one per FWD_BM query rows of each sequence, with the number of
-//    key tiles its rows can see.
-//  * Tasks: one workgroup each, an item for one query head.
+//  * Items: one per FWD_BM >> pack_shift query rows of each sequence, with the
+//    number of key tiles its rows can see.
+//  * Tasks: one workgroup each, an item for 2^pack_shift consecutive query
+//    heads of one KV head (its rows of each of them).
 //  * Launch order. Tasks that read the same K/V stream (same sequence and KV
 //    head) form a group. Groups are dealt, heaviest first, to the XCD queue
-//    with the least work so far; block i of the launch is taken from queue
-//    i % MLA_XCDS (the hardware hands consecutive workgroups to consecutive
-//    XCDs). Each queue is cut into batches of whole groups holding at least
-//    twice as many tasks as the XCD has CUs, and each batch is ordered
-//    heaviest task first. The tasks of a group thus run together on one XCD
-//    and share its L2 while they stream the same keys, and the heaviest
-//    first order inside a batch keeps the XCD's CUs evenly loaded to the end.
-//    Short queues are padded with empty tasks.
+//    with the least work so far. If that leaves an XCD more than 5% above the
+//    mean (few KV heads, or one long sequence), groups holding more than 1/32
+//    of the launch's work are cut into consecutive pieces of at most that
+//    much and dealt again, so that every XCD gets a share. Block i of the
+//    launch is taken from queue i % MLA_XCDS (the hardware hands consecutive
+//    workgroups to consecutive XCDs). Each queue is cut into batches of whole
+//    groups holding at least twice as many tasks as the XCD has CUs, and
+//    each batch is ordered heaviest task first. The tasks of a
+//    group thus run together on one XCD and share its L2 while they stream
+//    the same keys, and the heaviest first order inside a batch keeps the
+//    XCD's CUs evenly loaded to the end. Short queues are padded with empty
+//    tasks.
 void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int32_t heads,
                 int32_t kv_heads, int mask_type, int64_t kv_padded_max_seq, Plan *plan) {
     plan->seqs.resize(batch);
     plan->items.clear();
     plan->tasks.clear();
     const int32_t group = kv_heads > 0 ? heads / kv_heads : 1;
+    const int32_t ps = pack_shift_for(heads, kv_heads);
+    const int32_t rows = FWD_BM >> ps;
+    const int32_t tasks_per_item = group >> ps;
     struct Group {
         int64_t work;
         int32_t b, hk;
+        int32_t t0, t1;  // tasks [t0, t1) of the group: task t = item t / tasks_per_item, head pack t % tasks_per_item
     };
     std::vector<Group> groups;
     std::vector<int32_t> seq_first(batch + 1, 0);  // items of sequence b: [seq_first[b], seq_first[b+1])
@@ -377,23 +400,55 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         kv_off += s.kv_len;
         seq_first[b] = (int32_t)plan->items.size();
         int64_t seq_work = 0;
-        for (int32_t r = 0; r < s.q_len; r += FWD_BM) {
-            int32_t q_end = std::min(s.q_len, r + FWD_BM);
-            WorkItem it{b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), 0};
+        for (int32_t r = 0; r < s.q_len; r += rows) {
+            int32_t q_end = std::min(s.q_len, r + rows);
+            WorkItem it{b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), rows};
             seq_work += task_work(it);
             plan->items.push_back(it);
         }
+        const int32_t n_tasks = ((int32_t)plan->items.size() - seq_first[b]) * tasks_per_item;
         if (seq_work > 0)
-            for (int32_t hk = 0; hk < kv_heads; ++hk) groups.push_back({seq_work * group, b, hk});
+            for (int32_t hk = 0; hk < kv_heads; ++hk) groups.push_back({seq_work * tasks_per_item, b, hk, 0, n_tasks});
     }
     seq_first[batch] = (int32_t)plan->items.size();
-    std::stable_sort(groups.begin(), groups.end(), [](const Group &x, const Group &y) { return x.work > y.work; });
-    std::vector<std::vector<Group>> xcd_groups(MLA_XCDS);
-    std::vector<int64_t> load(MLA_XCDS, 0);
-    for (const Group &gr : groups) {
-        const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-        load[x] += gr.work;
-        xcd_groups[x].push_back(gr);
+    std::vector<std::vector<Group>> xcd_groups;
+    std::vector<int64_t> load;
+    auto deal = [&]() {
+        std::stable_sort(groups.begin(), groups.end(), [](const Group &x, const Group &y) { return x.work > y.work; });
+        xcd_groups.assign(MLA_XCDS, {});
+        load.assign(MLA_XCDS, 0);
+        for (const Group &gr : groups) {
+            const int x = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+            load[x] += gr.work;
+            xcd_groups[x].push_back(gr);
+        }
+    };
+    deal();
+    int64_t total = 0;
+    for (const Group &gr : groups) total += gr.work;
+    // If some XCD got more than 5% above the mean (few KV streams, or one long
+    // sequence), cut groups heavier than 1/32 of the total into consecutive
+    // pieces and deal again.
+    if (20 * MLA_XCDS * *std::max_element(load.begin(), load.end()) > 21 * total) {
+        const int64_t cap = std::max<int64_t>(1, (total + 4 * MLA_XCDS - 1) / (4 * MLA_XCDS));
+        std::vector<Group> cut;
+        for (const Group &gr : groups) {
+            if (gr.work <= cap) {
+                cut.push_back(gr);
+                continue;
+            }
+            Group piece{0, gr.b, gr.hk, gr.t0, gr.t0};
+            for (int32_t t = gr.t0; t < gr.t1; ++t) {
+                piece.work += task_work(plan->items[seq_first[gr.b] + t / tasks_per_item]);
+                piece.t1 = t + 1;
+                if (piece.work >= cap || t + 1 == gr.t1) {
+                    cut.push_back(piece);
+                    piece = Group{0, gr.b, gr.hk, t + 1, t + 1};
+                }
+            }
+        }
+        groups.swap(cut);
+        deal();
     }
     std::vector<std::vector<Task>> queue(MLA_XCDS);
     std::vector<Task> pending;
@@ -406,8 +461,8 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
             pending.clear();
         };
         for (const Group &gr : xcd_groups[x]) {
-            for (int32_t i = seq_first[gr.b]; i < seq_first[gr.b + 1]; ++i)
-                for (int32_t h = gr.hk * group; h < (gr.hk + 1) * group; ++h) pending.push_back({i, h});
+            for (int32_t t = gr.t0; t < gr.t1; ++t)
+                pending.push_back({seq_first[gr.b] + t / tasks_per_item, gr.hk * group + (t % tasks_per_item) * (1 << ps)});
             if (pending.size() >= (size_t)PLAN_BATCH_TASKS) flush();
         }
         flush();
@@ -464,6 +519,7 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.heads = pr.heads;
     p.kv_heads = pr.kv_heads;
     p.group = pr.heads / pr.kv_heads;
+    p.pack_shift = pack_shift_for(pr.heads, pr.kv_heads);
     p.n_tasks = (int32_t)plan.tasks.size();
     p.mask_type = pr.mask_type;
     p.mask_is_bf16 = (pr.mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;

@@ -23,17 +23,24 @@ struct SeqRec {
     int32_t kv_len;
 };
 
-// One workgroup's work: FWD_BM query rows starting at q_row0 of sequence b,
-// and the number of FWD_BN-key tiles (from key 0) that any of them can see.
+// Query rows of one workgroup's task: FWD_BM / 2^pack_shift rows of each of
+// 2^pack_shift query heads that share one KV head, so every K/V tile staged
+// in LDS serves all of them (pack_shift = 0 without head grouping).
+constexpr int FWD_MAX_PACK_SHIFT = 3;
+
+// One work item: q_rows (= FWD_BM >> pack_shift) query rows starting at
+// q_row0 of sequence b, and the number of FWD_BN-key tiles (from key 0) that
+// any of them can see.
 struct WorkItem {
     int32_t b;
     int32_t q_row0;
     int32_t kv_tiles;
-    int32_t pad;
+    int32_t q_rows;
 };
 
-// One workgroup's task: a work item and a query head. item == -1 marks an
-// empty padding task.
+// One workgroup's task: a work item and its first query head (the task runs
+// heads head .. head + 2^pack_shift - 1). item == -1 marks an empty padding
+// task.
 struct Task {
     int32_t item;
     int32_t head;
@@ -61,6 +68,7 @@ struct FwdParams {
     int32_t mask_type;    // enum mla_mask_type
     int32_t mask_is_bf16; // dtype of the MASK_FREE tile
     int32_t n_tasks;      // workgroups to launch
+    int32_t pack_shift;   // log2 of the query heads one workgroup runs
     float scale_log2;     // qkScale * log2(e)
     // Paged K/V (launch_mla_fwd with paged = true): k, k_rope and v point at
     // ND caches [num_blocks, block_size, Hkv, 128 | 64 | 128]; key t of

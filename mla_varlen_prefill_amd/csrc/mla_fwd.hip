@@ -5,11 +5,14 @@
 // Q, QRope, K, kRope, V, qkScale, Mask, maskType):
 //     S = qkScale * (Q . K^T + QRope . KRope^T) + mask,   O = softmax_rows(S) . V
 //
-// One workgroup = 8 waves = FWD_BM = 256 query rows of one (sequence, head).
+// One workgroup = 8 waves = FWD_BM = 256 query rows: 256 rows of one
+// (sequence, head), or, when several query heads share a KV head (the page's
+// kvHeadNum < headNum), 256 / P rows of each of P = 2, 4 or 8 heads of one
+// group, so that every K/V tile staged in LDS is used by all of them.
 //
-//  * Each wave owns 32 query rows. Their Q (32 x 128) stays in VGPRs as the
-//    B operand of v_mfma_f32_32x32x16 (8 k-steps of 16); QRope of the
-//    workgroup's 256 rows (4 more k-steps) sits in LDS.
+//  * Each wave owns 32 query rows of one head. Their Q (32 x 128) stays in
+//    VGPRs as the B operand of v_mfma_f32_32x32x16 (8 k-steps of 16); QRope
+//    of the workgroup's 256 rows (4 more k-steps) sits in LDS.
 //  * Keys are walked in tiles of FWD_BN = 64 through a 3-stage LDS ring. K-nope
 //    (64 x 128) and K-rope (64 x 64) of a tile are copied HBM -> LDS by the
 //    buffer-load-to-LDS DMA path; V (64 x 128) is loaded to VGPRs and written
@@ -197,10 +200,17 @@ void mla_fwd_kernel(const FwdParams p) {
     // (launch order and XCD placement are chosen there); padding tasks exit.
     const Task task = p.tasks[blockIdx.x];
     if (task.item < 0) return;
-    const int h = task.head;
     const WorkItem item = p.items[task.item];
     const SeqRec seq = p.seqs[item.b];
-    const int hk = h / p.group;
+    // The wave's 32-row slot: slot s holds head task.head + s % P and rows
+    // 32 * (s / P) .. + 31 of the item (P = 2^pack_shift heads per task). The
+    // two waves sharing a SIMD (w, w + 4) take slots 2(w & 3) and 2(w & 3) + 1:
+    // adjacent row blocks, or the same rows of two heads, so both groups see
+    // the same share of diagonal tiles.
+    const int ps = p.pack_shift;
+    const int slot = (wave & 3) * 2 + grp;
+    const int h = task.head + (slot & ((1 << ps) - 1));
+    const int hk = task.head / p.group;
     const int H = p.heads, HKV = p.kv_heads;
     const int q_len = seq.q_len;
     const int kv_len = seq.kv_len;
@@ -208,9 +218,7 @@ void mla_fwd_kernel(const FwdParams p) {
     const int mask_type = p.mask_type;
     const bool causal_like = mask_type != MASK_UNDEFINED && mask_type != MASK_FREE;
 
-    // The two waves sharing a SIMD (w, w + 4) take adjacent 32-row blocks, so
-    // both groups see the same share of diagonal tiles.
-    const int lrow0 = (wave & 3) * 64 + grp * 32;   // first row of this wave within the item
+    const int lrow0 = (slot >> ps) * 32;            // first row of this wave within the item
     const int row0 = item.q_row0 + lrow0;           // ... within the sequence
     const int qi = row0 + r32;                      // this lane's query row
     const int pos = kv_len - q_len + qi;            // its key position
@@ -230,18 +238,24 @@ void mla_fwd_kernel(const FwdParams p) {
         for (int ks = 0; ks < 8; ++ks)
             qreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rq, qo + ks * 32, 0, 0));
     }
-    // ---- Q-rope of the item's 256 rows -> LDS (DMA), rows swizzled by 16-byte
-    // chunk: chunk c of row r sits at c ^ ((r >> 1) & 7).
+    // ---- Q-rope of the workgroup's 256 rows -> LDS (DMA). LDS row 32 s + r
+    // holds row r of slot s; rows are swizzled by 16-byte chunk: chunk c of LDS
+    // row L sits at c ^ ((L >> 1) & 7). Rows past the sequence end read as 0.
     {
-        const int rows = max(0, min(BM, q_len - item.q_row0));
+        const int rows = max(0, min(BM >> ps, q_len - item.q_row0));
         const int64_t tok = (int64_t)seq.q_off + item.q_row0;
-        const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
+        const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) +
+                                       (tok * H + task.head) * (DR * 2),
                                    (uint32_t)rows * H * DR * 2);
 #pragma unroll
         for (int u = 0; u < QR_BYTES / (NT * 16); ++u) {
-            const int slot = tid + NT * u;
-            const int r = slot >> 3;
-            const uint32_t src = (uint32_t)r * H * DR * 2 + ((((slot & 7) ^ ((r >> 1) & 7))) << 4);
+            const int ld = tid + NT * u;  // 16-byte LDS chunk
+            const int r = ld >> 3;        // LDS row
+            const int sl = r >> 5;        // its slot
+            const int src_row = (sl >> ps) * 32 + (r & 31);
+            const int src_head = sl & ((1 << ps) - 1);
+            const uint32_t src = ((uint32_t)src_row * H + src_head) * (DR * 2) +
+                                 ((((ld & 7) ^ ((r >> 1) & 7))) << 4);
             mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(smem + QR_OFFSET + u * NT * 16 + wave * 64 * 16), 16, src,
                                     0, 0, 0);
         }
@@ -447,11 +461,12 @@ void mla_fwd_kernel(const FwdParams p) {
     // the bases (one VALU op per read) instead of keeping 24 of them live.
     //  K-nope (A of S^T): tile row kb*32 + r32, chunk 2*ks + g, swizzle ^ (row & 15)
     //  K-rope:            row kb*32 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
-    //  Q-rope (B):        item row lrow0 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
+    //  Q-rope (B):        LDS row 32*slot + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
     //  V^T (A of O^T):    row d = 32*db + r32, chunk 2*st4 + g, swizzle ^ ((d >> 1) & 7)
     const uint32_t kn_base = r32 * 256 + ((g ^ (r32 & 15)) << 4);
     const uint32_t kr_base = KN_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
-    const uint32_t qr_base = QR_OFFSET + (lrow0 + r32) * 128 + ((g ^ (((lrow0 + r32) >> 1) & 7)) << 4);
+    const int qr_row = slot * 32 + r32;
+    const uint32_t qr_base = QR_OFFSET + qr_row * 128 + ((g ^ ((qr_row >> 1) & 7)) << 4);
     const uint32_t vt_base = KN_BYTES + KR_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
 
     auto lds16 = [](const unsigned char *a) __attribute__((always_inline)) -> vec8 {

@@ -221,35 +221,58 @@ def visible_count(mask_type, ql, kl, i):
     return int(vis.nonzero()[0].max()) + 1 if vis.any() else 0
 
 
+def heads_per_task(heads, kv_heads):
+    # largest power of two up to 8 dividing the group size
+    g, p = heads // kv_heads, 1
+    while p < 8 and g % (2 * p) == 0:
+        p *= 2
+    return p
+
+
 @pytest.mark.parametrize("mask_type", [0, 1, 2, 3])
 @pytest.mark.parametrize("case", [([17, 40], [17, 40], 4, 4), ([300, 1, 0, 129], [1000, 1, 5, 100], 8, 2),
-                                  ([2048] * 3, [16384] * 3, 16, 16), ([700], [100], 2, 1)])
+                                  ([2048] * 3, [16384] * 3, 16, 16), ([700], [100], 2, 1),
+                                  ([100, 33], [100, 260], 12, 4), ([513, 64], [600, 64], 32, 2),
+                                  ([70], [70], 16, 1)])
 def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
     qs, ks, heads, kv_heads = case
+    pack = heads_per_task(heads, kv_heads)
+    rows = mla.PLAN_Q_ROWS // pack
     seqs, items, tasks = mla.mla_prefill_plan_host(qs, ks, heads, kv_heads, mask_type)
     # batch records are prefix sums
     assert (seqs[:, 0] == np.concatenate([[0], np.cumsum(qs)[:-1]])).all()
     assert (seqs[:, 1] == np.concatenate([[0], np.cumsum(ks)[:-1]])).all()
     assert (seqs[:, 2] == qs).all() and (seqs[:, 3] == ks).all()
-    # every (b, q-tile) is one item
-    want = sorted((b, r) for b, n in enumerate(qs) for r in range(0, n, mla.PLAN_Q_ROWS))
+    # every (b, q-tile of PLAN_Q_ROWS / pack rows) is one item
+    assert (items[:, 3] == rows).all()
+    want = sorted((b, r) for b, n in enumerate(qs) for r in range(0, n, rows))
     assert sorted((int(b), int(r)) for b, r, _, _ in items) == want
     # tile range = tiles holding the furthest visible key of any row in the item
     for b, r, nt, _ in items:
         ql, kl = qs[b], ks[b]
-        far = max(visible_count(mask_type, ql, kl, i) for i in range(r, min(ql, r + mla.PLAN_Q_ROWS)))
+        far = max(visible_count(mask_type, ql, kl, i) for i in range(r, min(ql, r + rows)))
         assert nt == -(-far // mla.PLAN_KV_COLS), (b, r)
-    # every (item, head) is exactly one task; the rest is padding
+    # every (item, head) is covered by exactly one task; the heads of a task
+    # share one kv head; the rest is padding
     real = tasks[tasks[:, 0] >= 0]
-    assert sorted(map(tuple, real.tolist())) == sorted((i, h) for i in range(len(items)) for h in range(heads))
+    covered = sorted((i, h0 + k) for i, h0 in real.tolist() for k in range(pack))
+    assert covered == sorted((i, h) for i in range(len(items)) for h in range(heads))
+    g = heads // kv_heads
+    assert all(h0 % pack == 0 and h0 // g == (h0 + pack - 1) // g for _, h0 in real.tolist())
     assert len(tasks) % 8 == 0
-    # the tasks reading one K/V stream (sequence, kv head) sit on one XCD (task index mod 8)
-    xcd_of = {}
+    # the tasks reading one K/V stream (sequence, kv head) sit on one XCD (task
+    # index mod 8), unless the stream holds more than 1/32 of all work
+    stream_work, xcds = {}, {}
     for i, (it, h) in enumerate(tasks.tolist()):
         if it < 0:
             continue
         key = (int(items[it][0]), h // (heads // kv_heads))
-        assert xcd_of.setdefault(key, i % 8) == i % 8
+        stream_work[key] = stream_work.get(key, 0) + items[it][2] + 1
+        xcds.setdefault(key, set()).add(i % 8)
+    total = sum(stream_work.values())
+    for key, w in stream_work.items():
+        if 32 * w <= total:
+            assert len(xcds[key]) == 1, key
 
 
 def test_plan_balances_xcds_on_causal_workload():
@@ -260,6 +283,19 @@ def test_plan_balances_xcds_on_causal_workload():
         if it >= 0:
             work[i % 8] += items[it][2] + 1
     assert work.max() == work.min()
+
+
+@pytest.mark.parametrize("kv_heads", [128, 16, 1])
+def test_plan_balances_xcds_with_few_kv_heads(kv_heads):
+    """4096-token causal prefill, 128 query heads over kv_heads KV heads: a
+    K/V stream holding more than 1/32 of the work is spread over XCDs, so
+    every XCD's work is within 5% of the mean."""
+    seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 128, kv_heads, mla.MASK_CAUSAL)
+    work = np.zeros(8)
+    for i, (it, h) in enumerate(tasks.tolist()):
+        if it >= 0:
+            work[i % 8] += items[it][2] + 1
+    assert work.max() <= 1.05 * work.mean(), work
 
 
 def test_plan_padded_offsets():
