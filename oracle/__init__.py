@@ -16,6 +16,10 @@ it, and it shares no code, tables or helpers with the HIP path.
 * ``paged_cache_load_nz`` is the same gather for the NZ cache layout of the
   "PagedCacheLoadOperation" page's dimension table (keyCache / valueCache /
   key / value rows, NZ column).
+* ``rms_norm``, ``rope_interleaved`` and ``mla_prolog`` follow the "MlaProlog"
+  page (cann-recipes-infer operator notes: formula section, parameter and
+  return lists, constraints), non-quantised: plain numpy in float64, with
+  ``numpy.matmul`` as the only library step.
 
 Mask-type codes (the page names the modes but prints no integer values):
 UNDEFINED 0, SPEC 1, CAUSAL 2, MASK_FREE 3.
@@ -245,3 +249,53 @@ def paged_cache_load_nz(key_cache, value_cache, block_tables, context_lens):
         return out
 
     return gather(key_cache), None if value_cache is None else gather(value_cache)
+
+
+def rms_norm(y, gamma=None, eps=1e-6):
+    """RmsNorm over the last axis ("MlaProlog" page, formula section):
+    y / sqrt(mean(y^2) + eps), times gamma when one is given (the page's second
+    RmsNorm has weight 1). The page prints neither the formula's body nor eps;
+    this is the usual definition, and eps is an argument."""
+    y = np.asarray(y, dtype=np.float64)
+    out = y / np.sqrt(np.mean(y * y, axis=-1, keepdims=True) + eps)
+    return out if gamma is None else out * np.asarray(gamma, dtype=np.float64)
+
+
+def rope_interleaved(x, cos, sin):
+    """Interleaved rotary embedding ("MlaProlog" page, formula section: "inplace
+    interleaved rope" of the last rope_dim values). Elements 2i and 2i + 1
+    form a pair that is rotated:
+        out[2i]     = x[2i]     * cos[2i]     - x[2i + 1] * sin[2i]
+        out[2i + 1] = x[2i + 1] * cos[2i + 1] + x[2i]     * sin[2i + 1]
+    cos and sin hold one value per element (the page's rope_cos / rope_sin are
+    [t, rope_dim]) and broadcast against x."""
+    x = np.asarray(x, dtype=np.float64)
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    partner = np.empty_like(x)
+    partner[..., 0::2] = -x[..., 1::2]
+    partner[..., 1::2] = x[..., 0::2]
+    return x * cos + partner * sin
+
+
+def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, num_heads, eps=1e-6):
+    """The MLA prolog, non-quantised ("MlaProlog" page, formula section; shapes
+    from its parameter and return lists):
+        c^Q = RmsNorm(x . wq_a) * gamma_cq                       [t, q_lora_rank]
+        q   = RmsNorm(c^Q . wq_b), per head over head_dim (weight 1)
+        q[..., -rope_dim:]  = ROPE(q[..., -rope_dim:])           [t, num_heads, head_dim]
+        kv  = RmsNorm(x . wkv) * gamma_ckv
+        kv[..., -rope_dim:] = ROPE(kv[..., -rope_dim:])          [t, head_dim]
+    with rope_dim = rope_cos.shape[1] and head_dim = wkv.shape[1]. Everything
+    in float64; returns (q, kv, c^Q)."""
+    x = np.asarray(token_x, dtype=np.float64)
+    t = x.shape[0]
+    head_dim = wkv.shape[1]
+    rd = rope_cos.shape[1]
+    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), gamma_cq, eps)
+    q = rms_norm((cq @ np.asarray(wq_b, dtype=np.float64)).reshape(t, num_heads, head_dim), None, eps)
+    q[..., head_dim - rd:] = rope_interleaved(q[..., head_dim - rd:], np.asarray(rope_cos)[:, None, :],
+                                              np.asarray(rope_sin)[:, None, :])
+    kv = rms_norm(x @ np.asarray(wkv, dtype=np.float64), gamma_ckv, eps)
+    kv[:, head_dim - rd:] = rope_interleaved(kv[:, head_dim - rd:], rope_cos, rope_sin)
+    return q, kv, cq

@@ -10,6 +10,8 @@ Built by a different route from ``oracle/oracle.c`` on purpose:
 Follows the "MLA Prefill" page's Members table (Q, QRope, K, kRope, V,
 qkScale, Mask, maskType) read as: scale the whole product, then add the mask.
 """
+import math
+
 import numpy as np
 
 TILE = 512
@@ -57,3 +59,49 @@ def attention(q, qr, k, kr, v, q_seqlen, kv_seqlen, heads, kv_heads, scale, mask
         qo += ql
         ko += kl
     return out
+
+
+# ---------------------------------------------------------------- MLA prolog
+# Float64 brute force of the "MlaProlog" page's formulas (formula section),
+# built by another route than oracle.mla_prolog: matrix products as explicit
+# loops, the RmsNorm with math.fsum, and the interleaved rope as a complex
+# multiplication of (x[2i] + i x[2i+1]) by cos + i sin (cos and sin taken from
+# the even element of each pair, which the inputs fill equally).
+
+def _matmul(a, b):
+    n, k = len(a), len(b)
+    m = len(b[0])
+    return [[math.fsum(a[i][kk] * b[kk][j] for kk in range(k)) for j in range(m)] for i in range(n)]
+
+
+def _rms(row, gamma, eps):
+    r = math.sqrt(math.fsum(v * v for v in row) / len(row) + eps)
+    return [row[i] / r * (1.0 if gamma is None else gamma[i]) for i in range(len(row))]
+
+
+def _rope_complex(vals, cos, sin):
+    out = []
+    for i in range(0, len(vals), 2):
+        z = complex(vals[i], vals[i + 1]) * complex(cos[i], sin[i])
+        out += [z.real, z.imag]
+    return out
+
+
+def mla_prolog(x, wq_a, wq_b, wkv, cos, sin, gamma_cq, gamma_ckv, num_heads, eps):
+    x, wq_a, wq_b, wkv = (np.asarray(a).tolist() for a in (x, wq_a, wq_b, wkv))
+    cos, sin = np.asarray(cos).tolist(), np.asarray(sin).tolist()
+    gamma_cq, gamma_ckv = np.asarray(gamma_cq).tolist(), np.asarray(gamma_ckv).tolist()
+    t, hd, rd = len(x), len(wkv[0]), len(cos[0])
+    cq = [_rms(row, gamma_cq, eps) for row in _matmul(x, wq_a)]
+    qf = _matmul(cq, wq_b)
+    q = np.zeros((t, num_heads, hd))
+    for i in range(t):
+        for h in range(num_heads):
+            head = _rms(qf[i][h * hd:(h + 1) * hd], None, eps)
+            q[i, h] = head[:hd - rd] + _rope_complex(head[hd - rd:], cos[i], sin[i])
+    kvf = _matmul(x, wkv)
+    kv = np.zeros((t, hd))
+    for i in range(t):
+        row = _rms(kvf[i], gamma_ckv, eps)
+        kv[i] = row[:hd - rd] + _rope_complex(row[hd - rd:], cos[i], sin[i])
+    return q, kv, np.array(cq)
