@@ -1,7 +1,8 @@
 /*
  * mla_prefill.h -- C ABI of the MI355X (gfx950) MLA varlen-prefill library.
  *
- * Two operations, each defined by one Ascend Transformer Boost C API page:
+ * The operations below, each defined by one page: two Ascend Transformer
+ * Boost C API pages, and the MlaProlog operator notes (further down):
  *
  *   mla_prefill_get_workspace_size / mla_prefill
  *     "MLA Prefill" page, Definition and the AtbMLAPreFillGetWorkspaceSize
@@ -242,6 +243,59 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
                       float qk_scale, int32_t kv_head_num, int32_t mask_type,
                       const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
                       void *stream);
+
+/*
+ * mla_prolog_get_workspace_size / mla_prolog -- the "MlaProlog" operator
+ * (cann-recipes-infer operator notes: formula section, parameter and return
+ * lists, constraints), non-quantised. From hidden states x it computes
+ *     c^Q = RmsNorm(x . wq_a) * gamma_cq
+ *     q   = RmsNorm(c^Q . wq_b), over each head's head_dim values, weight 1
+ *     kv  = RmsNorm(x . wkv) * gamma_ckv
+ * and then rotates the last rope_dim values of every q head and of kv with the
+ * interleaved rope: elements 2i and 2i + 1 of that slice become
+ *     x[2i] cos[2i] - x[2i+1] sin[2i],   x[2i+1] cos[2i+1] + x[2i] sin[2i+1]
+ * with cos / sin taken from the token's row of rope_cos / rope_sin. RmsNorm(y)
+ * = y / sqrt(mean(y^2) + eps). The page documents the int8 variant (int8
+ * wq_b with a per-column scale, int8 c^Q with a per-token scale) and leaves
+ * the non-quantised one to an example: here wq_b is bf16 and the third output
+ * is c^Q in bf16.
+ *
+ *   token_x     device bf16 [t, h]
+ *   wq_a        device bf16 [h, q_lora_rank]                (row-major, "ND")
+ *   wq_b        device bf16 [q_lora_rank, num_heads * head_dim]
+ *   wkv         device bf16 [h, head_dim]
+ *   rope_cos    device bf16 [t, rope_dim]
+ *   rope_sin    device bf16 [t, rope_dim]
+ *   gamma_cq    device bf16 [q_lora_rank]
+ *   gamma_ckv   device bf16 [head_dim]
+ *   eps         RmsNorm epsilon (the page gives none; 1e-6 is customary), > 0
+ *   q_out       device bf16 [t, num_heads, head_dim] or [t, num_heads * head_dim]
+ *   kv_out      device bf16 [t, head_dim]
+ *   qr_out      device bf16 [t, q_lora_rank]: c^Q
+ *   workspace_size  out: bytes of device workspace mla_prolog needs (t *
+ *               q_lora_rank * 4: the fp32 product x . wq_a before its norm).
+ * Supported (the page's constraints fix head_dim 512, h 4096, q_lora_rank
+ * 1024, num_heads 64, rope_dim 64, t up to 64k): head_dim = 512,
+ * rope_dim = 64, h a multiple of 32, q_lora_rank a multiple of 512, any
+ * num_heads >= 1 and t >= 0; other sizes return MLA_ERR_UNSUPPORTED.
+ * num_heads is read from wq_b's width. Outputs are rounded to nearest even
+ * from fp32; products accumulate in fp32; c^Q is rounded to bf16 before it
+ * enters the second product.
+ * mla_prolog enqueues three kernels on stream (x . [wq_a | wkv] with the kv
+ * epilogue, the c^Q norm, c^Q . wq_b with the q epilogue). The workspace
+ * (16-byte aligned, at least the planned size) must stay untouched until they
+ * have run. Errors as for mla_prefill.
+ */
+int mla_prolog_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                                  const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                                  const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps,
+                                  const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
+                                  uint64_t *workspace_size);
+int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+               const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+               const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
+               const mla_tensor *kv_out, const mla_tensor *qr_out, void *workspace, uint64_t workspace_size,
+               void *stream);
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char *mla_last_error(void);

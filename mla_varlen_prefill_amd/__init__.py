@@ -24,6 +24,7 @@ __all__ = [
     "MlaError", "mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load",
     "mla_last_error", "mla_prefill_plan_host", "prefill", "library_path",
     "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "prefill_paged",
+    "mla_prolog_get_workspace_size", "mla_prolog", "prolog",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_prefill.so")
@@ -84,6 +85,10 @@ def _load():
                                                          ctypes.POINTER(ctypes.c_uint64)]
     lib.mla_prefill_paged.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                       ctypes.c_int32, T, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.mla_prolog_get_workspace_size.argtypes = [T] * 8 + [ctypes.c_float, T, T, T,
+                                                             ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prolog.argtypes = [T] * 8 + [ctypes.c_float, T, T, T, ctypes.c_void_p, ctypes.c_uint64,
+                                         ctypes.c_void_p]
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -91,7 +96,8 @@ def _load():
                                           ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
     for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host",
-               "mla_prefill_paged_get_workspace_size", "mla_prefill_paged"):
+               "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "mla_prolog_get_workspace_size",
+               "mla_prolog"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -292,3 +298,51 @@ def prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tables, 
     if stream is not None and isinstance(stream, torch.cuda.Stream):
         workspace.record_stream(stream)
     return out
+
+
+def _prolog_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out, qr_out,
+                 keep):
+    return ([_desc(x, keep) for x in (token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv)]
+            + [ctypes.c_float(eps)] + [_desc(x, keep) for x in (q_out, kv_out, qr_out)])
+
+
+def mla_prolog_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out,
+                                  kv_out, qr_out) -> int:
+    """Bytes of device workspace ``mla_prolog`` needs for these shapes."""
+    lib = _load()
+    keep = []
+    size = ctypes.c_uint64(0)
+    _check("mla_prolog_get_workspace_size", lib.mla_prolog_get_workspace_size(
+        *_prolog_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out, qr_out,
+                      keep), ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out, qr_out,
+               workspace, stream=None) -> None:
+    """Enqueue the non-quantised MLA prolog (q, kv and c^Q from hidden states)."""
+    lib = _load()
+    keep = []
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_prolog", lib.mla_prolog(
+        *_prolog_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out, qr_out,
+                      keep), ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size), _stream_ptr(stream)))
+
+
+def prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps=1e-6, stream=None):
+    """Allocate outputs and workspace with torch and run the prolog. Returns
+    (q [t, num_heads, head_dim], kv [t, head_dim], c^Q [t, q_lora_rank])."""
+    t, hd, r = token_x.shape[0], wkv.shape[1], wq_a.shape[1]
+    heads = wq_b.shape[1] // hd
+    dev = token_x.device
+    q = torch.empty((t, heads, hd), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
+    cq = torch.empty((t, r), dtype=torch.bfloat16, device=dev)
+    ws = mla_prolog_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q,
+                                       kv, cq)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q, kv, cq, workspace, stream)
+    if stream is not None and isinstance(stream, torch.cuda.Stream):
+        workspace.record_stream(stream)
+    return q, kv, cq

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmla_prefill.so")
-SOURCES = ["api.cpp", "mla_fwd.hip", "paged_gather.hip"]
+SOURCES = ["api.cpp", "mla_fwd.hip", "paged_gather.hip", "prolog.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

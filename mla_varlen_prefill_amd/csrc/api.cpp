@@ -539,6 +539,79 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     return ok();
 }
 
+
+// ---- MLA prolog ("MlaProlog" operator notes: parameter and return lists,
+// constraints), non-quantised.
+struct PrologProblem {
+    int64_t t = 0, h = 0, r = 0, heads = 0;
+};
+
+int check_bf16(const mla_tensor *x, const char *name, int ndim) {
+    int rc = check_tensor(x, name, true);
+    if (rc) return rc;
+    if (x->dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "%s must be bf16", name);
+    if (x->ndim != ndim) return fail(MLA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, x->ndim);
+    return MLA_OK;
+}
+
+int validate_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                    const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                    const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
+                    const mla_tensor *kv_out, const mla_tensor *qr_out, PrologProblem *pp) {
+    int rc;
+    if ((rc = check_bf16(token_x, "token_x", 2)) || (rc = check_bf16(wq_a, "wq_a", 2)) ||
+        (rc = check_bf16(wq_b, "wq_b", 2)) || (rc = check_bf16(wkv, "wkv", 2)) ||
+        (rc = check_bf16(rope_cos, "rope_cos", 2)) || (rc = check_bf16(rope_sin, "rope_sin", 2)) ||
+        (rc = check_bf16(gamma_cq, "gamma_cq", 1)) || (rc = check_bf16(gamma_ckv, "gamma_ckv", 1)) ||
+        (rc = check_bf16(kv_out, "kv_out", 2)) || (rc = check_bf16(qr_out, "qr_out", 2)))
+        return rc;
+    if ((rc = check_tensor(q_out, "q_out", true))) return rc;
+    if (q_out->dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "q_out must be bf16");
+    if (!(eps > 0.f) || !std::isfinite(eps)) return fail(MLA_ERR_VALUE, "eps must be finite and > 0");
+    const int64_t t = token_x->shape[0], h = token_x->shape[1];
+    const int64_t r = wq_a->shape[1], hd = wkv->shape[1], rd = rope_cos->shape[1];
+    if (wq_a->shape[0] != h) return fail(MLA_ERR_SHAPE, "wq_a: expected [h = %lld, q_lora_rank]", (long long)h);
+    if (wkv->shape[0] != h) return fail(MLA_ERR_SHAPE, "wkv: expected [h = %lld, head_dim]", (long long)h);
+    if (wq_b->shape[0] != r)
+        return fail(MLA_ERR_SHAPE, "wq_b: expected [q_lora_rank = %lld, num_heads * head_dim]", (long long)r);
+    if (hd <= 0 || wq_b->shape[1] % hd != 0 || wq_b->shape[1] == 0)
+        return fail(MLA_ERR_SHAPE, "wq_b: width %lld is not num_heads * head_dim (%lld)",
+                    (long long)wq_b->shape[1], (long long)hd);
+    const int64_t heads = wq_b->shape[1] / hd;
+    if (rope_cos->shape[0] != t || rope_sin->ndim != 2 || rope_sin->shape[0] != t || rope_sin->shape[1] != rd)
+        return fail(MLA_ERR_SHAPE, "rope_cos / rope_sin: expected [t = %lld, rope_dim] each", (long long)t);
+    if (gamma_cq->shape[0] != r) return fail(MLA_ERR_SHAPE, "gamma_cq: expected [q_lora_rank = %lld]", (long long)r);
+    if (gamma_ckv->shape[0] != hd) return fail(MLA_ERR_SHAPE, "gamma_ckv: expected [head_dim = %lld]", (long long)hd);
+    if (kv_out->shape[0] != t || kv_out->shape[1] != hd)
+        return fail(MLA_ERR_SHAPE, "kv_out: expected [t = %lld, head_dim = %lld]", (long long)t, (long long)hd);
+    if (qr_out->shape[0] != t || qr_out->shape[1] != r)
+        return fail(MLA_ERR_SHAPE, "qr_out: expected [t = %lld, q_lora_rank = %lld]", (long long)t, (long long)r);
+    const bool q3 = q_out->ndim == 3 && q_out->shape[0] == t && q_out->shape[1] == heads && q_out->shape[2] == hd;
+    const bool q2 = q_out->ndim == 2 && q_out->shape[0] == t && q_out->shape[1] == heads * hd;
+    if (!q3 && !q2)
+        return fail(MLA_ERR_SHAPE, "q_out: expected [t, %lld, %lld] or [t, %lld]", (long long)heads, (long long)hd,
+                    (long long)(heads * hd));
+    if (hd != mla::PROLOG_BN) return fail(MLA_ERR_UNSUPPORTED, "head_dim %lld: only 512 is supported", (long long)hd);
+    if (rd != mla::PROLOG_ROPE) return fail(MLA_ERR_UNSUPPORTED, "rope_dim %lld: only 64 is supported", (long long)rd);
+    if (h <= 0 || h % mla::PROLOG_BK != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "h %lld: a positive multiple of %d is required", (long long)h, mla::PROLOG_BK);
+    if (r <= 0 || r % mla::PROLOG_BN != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: a positive multiple of %d is required", (long long)r,
+                    mla::PROLOG_BN);
+    // buffer resources address at most 4 GB from a tile's start; weights and
+    // a 128-row tile of any operand stay far below that in every supported case
+    if (r * heads * hd * 2 >= (int64_t)1 << 31 || h * r * 2 >= (int64_t)1 << 31 ||
+        (int64_t)mla::PROLOG_BM * heads * hd * 2 >= (int64_t)1 << 31 || t > INT32_MAX / 2)
+        return fail(MLA_ERR_UNSUPPORTED, "operand too large for 32-bit tile offsets");
+    pp->t = t;
+    pp->h = h;
+    pp->r = r;
+    pp->heads = heads;
+    return MLA_OK;
+}
+
+uint64_t prolog_workspace_bytes(const PrologProblem &pp) { return align256((uint64_t)pp.t * pp.r * 4); }
+
 }  // namespace
 
 extern "C" {
@@ -759,6 +832,74 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
     p.has_seq_starts = has_seq_starts ? 1 : 0;
     hipError_t e = mla::launch_paged_gather(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "gather launch: %s", hipGetErrorString(e));
+    return ok();
+}
+
+
+int mla_prolog_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                                  const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                                  const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps,
+                                  const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
+                                  uint64_t *workspace_size) {
+    if (workspace_size == nullptr) return fail(MLA_ERR_NULL, "workspace_size is NULL");
+    PrologProblem pp;
+    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                             qr_out, &pp);
+    if (rc) return rc;
+    *workspace_size = prolog_workspace_bytes(pp);
+    return ok();
+}
+
+int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+               const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+               const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
+               const mla_tensor *kv_out, const mla_tensor *qr_out, void *workspace, uint64_t workspace_size,
+               void *stream) {
+    PrologProblem pp;
+    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                             qr_out, &pp);
+    if (rc) return rc;
+    if (pp.t == 0) return ok();
+    const uint64_t need = prolog_workspace_bytes(pp);
+    if (workspace == nullptr || workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given", (unsigned long long)need,
+                    (unsigned long long)workspace_size);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float *y_q = static_cast<float *>(workspace);
+
+    // x . [wq_a | wkv]: the wq_a tiles store fp32 rows for the c^Q norm, the
+    // wkv tile is the kv row (norm * gamma_ckv, rope)
+    mla::PrologGemmParams g1{};
+    g1.a = token_x->data;
+    g1.lda = pp.h;
+    g1.m = (int32_t)pp.t;
+    g1.k = (int32_t)pp.h;
+    g1.seg[0] = {wq_a->data, pp.r, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, y_q, pp.r, nullptr};
+    g1.seg[1] = {wkv->data, mla::PROLOG_BN, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN, gamma_ckv->data};
+    g1.rope_cos = rope_cos->data;
+    g1.rope_sin = rope_sin->data;
+    g1.eps = eps;
+    hipError_t e = mla::launch_prolog_gemm(g1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
+    e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
+                                    s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm: %s", hipGetErrorString(e));
+    // c^Q . wq_b: one tile per head (norm per head, weight 1, rope)
+    mla::PrologGemmParams g2{};
+    g2.a = qr_out->data;
+    g2.lda = pp.r;
+    g2.m = (int32_t)pp.t;
+    g2.k = (int32_t)pp.r;
+    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE, q_out->data,
+                 pp.heads * mla::PROLOG_BN, nullptr};
+    g2.seg[1] = {nullptr, 0, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
+    g2.rope_cos = rope_cos->data;
+    g2.rope_sin = rope_sin->data;
+    g2.eps = eps;
+    e = mla::launch_prolog_gemm(g2, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
     return ok();
 }
 

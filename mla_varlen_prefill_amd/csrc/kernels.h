@@ -115,4 +115,45 @@ constexpr int GATHER_MAX_BATCH = 8192;  // offsets table in LDS: (batch + 1) * 4
 
 hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream);
 
+// ---- MLA prolog (non-quantised): products of bf16 activations [M, K] with
+// bf16 weights [K, N] (both row-major), in output tiles of PROLOG_BN columns x
+// PROLOG_BM rows, with an epilogue per column range.
+constexpr int PROLOG_BN = 512;  // one head / one normalised row per tile
+constexpr int PROLOG_BM = 128;
+constexpr int PROLOG_BK = 32;   // K must be a multiple
+constexpr int PROLOG_ROPE = 64; // rope_dim: the tile's last 64 columns
+
+enum PrologEpilogue : int32_t {
+    PROLOG_STORE_F32 = 0,  // out (fp32) = product
+    PROLOG_NORM_ROPE = 1,  // out (bf16) = rope(RmsNorm over the tile's 512 columns (* gamma))
+};
+
+struct PrologSegment {
+    const void *w;       // bf16 [K, ldw]; this segment's tile j reads columns j*512 .. j*512+511
+    int64_t ldw;         // row stride of w, elements
+    int32_t n_tiles;     // 512-column tiles of this segment
+    int32_t epilogue;    // PrologEpilogue
+    void *out;           // tile j of rows m: out + m * ld_out + j * 512 (elements of the epilogue's type)
+    int64_t ld_out;
+    const void *gamma;   // bf16 [n_tiles * 512] or null (weight 1); PROLOG_NORM_ROPE only
+};
+
+struct PrologGemmParams {
+    const void *a;       // bf16 [M, lda]
+    int64_t lda;
+    int32_t m;           // rows
+    int32_t k;           // a multiple of PROLOG_BK
+    PrologSegment seg[2];  // tiles 0 .. seg[0].n_tiles - 1 from seg[0], the rest from seg[1]
+    const void *rope_cos;  // bf16 [M, 64]
+    const void *rope_sin;
+    float eps;
+};
+
+hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream);
+
+// y fp32 [rows, cols] (row stride ld_y) -> out bf16 [rows, cols] (row stride
+// ld_out) = RmsNorm over each row * gamma; cols a multiple of 256.
+hipError_t launch_prolog_rms_rows(const float *y, int64_t ld_y, const void *gamma, void *out, int64_t ld_out,
+                                  int32_t rows, int32_t cols, float eps, hipStream_t stream);
+
 }  // namespace mla

@@ -1,0 +1,411 @@
+// MLA prolog, non-quantised, for gfx950 (MI355X).
+//
+// The "MlaProlog" operator (cann-recipes-infer notes, formula section) turns
+// hidden states x [t, h] into the attention inputs:
+//     c^Q = RmsNorm(x . wq_a) * gamma_cq                    [t, q_lora_rank]
+//     q   = rope(RmsNorm(c^Q . wq_b)), the norm per head     [t, heads, 512]
+//     kv  = rope(RmsNorm(x . wkv) * gamma_ckv)               [t, 512]
+// where rope rotates adjacent pairs of the last 64 values of each row.
+//
+// Two kernels:
+//  * prolog_gemm_kernel: out = a . w for bf16 a [M, K] and bf16 w [K, N]
+//    (row-major, as the page gives the weights), one workgroup per tile of
+//    512 output columns x 128 rows, fp32 accumulation on
+//    v_mfma_f32_32x32x16_bf16. A 512-column tile is exactly one head of q (or
+//    the kv row), so the tile's epilogue can apply the RmsNorm over its
+//    columns, gamma and the rope, and store bf16; or it stores fp32.
+//  * prolog_rms_rows_kernel: RmsNorm * gamma of the fp32 rows x . wq_a
+//    (q_lora_rank = 1024 columns, two tiles of the product), stored as the
+//    bf16 c^Q that is both an output and the next product's input.
+//
+// Tile kernel design:
+//  * The product is computed transposed, out^T = w^T . a^T: the MFMA A operand
+//    is a 32-column block of w^T, B a 32-row block of a, so each lane of the
+//    accumulator holds one output row and 16 of its columns in runs of 4 --
+//    the rope's adjacent pairs sit in one lane.
+//  * 8 waves = 4 column quarters (128 columns) x 2 row halves (64 rows):
+//    4 x 2 accumulator blocks of 32 x 32 per wave.
+//  * K is walked in stages of 32 through a 4-stage LDS ring (40 KB a stage).
+//    Activation rows go HBM -> LDS by the buffer-load-to-LDS DMA path. Weight
+//    rows are k-major in memory but the operand needs 8 consecutive k per
+//    column, so each thread loads 4 weight rows x 8 columns to registers,
+//    pairs them with v_perm_b32 and writes 8-byte (4 k) pieces of the
+//    transposed tile. Both LDS layouts are XOR-swizzled in 16-byte chunks so
+//    the 16-byte operand reads are conflict-free; the transposed tile also
+//    permutes its rows (row n at n ^ ((n >> 3) & 3)) so the 8-byte writes hit
+//    every bank group.
+//  * Column tiles are spread so that the 32 CUs of an XCD work on the same
+//    weight tile at the same time (it stays in that XCD's L2).
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+constexpr int BN = PROLOG_BN;
+constexpr int BM = PROLOG_BM;
+constexpr int BK = PROLOG_BK;
+constexpr int NT = 512;
+constexpr int STAGES = 4;
+constexpr int X_BYTES = BM * BK * 2;  // 8 KB of activations
+constexpr int W_BYTES = BN * BK * 2;  // 32 KB of transposed weights
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 160 KB
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned int *lds_u32_ptr;
+
+extern "C" __device__ void prolog_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
+                                                      int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+extern "C" __device__ i32x4 prolog_raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+extern "C" __device__ i16x4 prolog_raw_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i16");
+extern "C" __device__ void prolog_raw_buffer_store_b64(i16x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i16");
+extern "C" __device__ void prolog_raw_buffer_store_b128(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+
+// Buffer resource over [base, base + bytes): loads past the end return 0,
+// stores past the end are dropped. Arguments must be wave-uniform.
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Barrier without __syncthreads()'s fence (which would also wait for the
+// LDS-DMA prefetches meant to stay in flight); LDS reads and writes of this
+// thread have completed (lgkmcnt) before it.
+__device__ __forceinline__ void block_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
+    return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
+void prolog_gemm_kernel(const PrologGemmParams p) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wn = wave & 3;   // column quarter: columns 128 wn .. + 127 of the tile
+    const int wt = wave >> 2;  // row half: rows 64 wt .. + 63
+    const int g = lane >> 5;
+    const int r32 = lane & 31;
+
+    // ---- which tile. When the column tiles split evenly over the 8 XCDs,
+    // XCD x takes column tiles x, x + 8, ... one after another, all row
+    // tiles of each: its CUs then share one weight tile in L2.
+    const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
+    const int m_tiles = (p.m + BM - 1) / BM;
+    const int blk = blockIdx.x;
+    int tn, tm;
+    if (n_tiles % 8 == 0) {
+        const int s = blk >> 3;
+        tn = (blk & 7) + 8 * (s / m_tiles);
+        tm = s % m_tiles;
+    } else {
+        tn = blk % n_tiles;
+        tm = blk / n_tiles;
+    }
+    const bool second = tn >= p.seg[0].n_tiles;
+    const int tj = second ? tn - p.seg[0].n_tiles : tn;
+    const unsigned char *w = static_cast<const unsigned char *>(second ? p.seg[1].w : p.seg[0].w);
+    const int64_t ldw = second ? p.seg[1].ldw : p.seg[0].ldw;
+    const int epilogue = second ? p.seg[1].epilogue : p.seg[0].epilogue;
+    void *out_base = second ? p.seg[1].out : p.seg[0].out;
+    const int64_t ld_out = second ? p.seg[1].ld_out : p.seg[0].ld_out;
+    const unsigned char *gamma = static_cast<const unsigned char *>(second ? p.seg[1].gamma : p.seg[0].gamma);
+    const int m0 = tm * BM;
+    const int rows = min(BM, p.m - m0);
+    const int nk = p.k / BK;
+
+    // ---- activation stage: 128 rows x 64 bytes; thread tid fills 16-byte
+    // slot tid = row tid / 4, physical chunk tid % 4, which holds logical
+    // chunk (tid % 4) ^ ((row >> 2) & 3). Rows past the end read as zeros.
+    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * 2,
+                               (uint32_t)rows * (uint32_t)p.lda * 2);
+    const int xr = tid >> 2;
+    const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * 2 + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
+    auto issue_x = [&](int kt) __attribute__((always_inline)) {
+        prolog_raw_buffer_load_lds(ra, (lds_u32_ptr)(smem + (kt % STAGES) * STAGE_BYTES + wave * 64 * 16), 16,
+                                   xoff + (uint32_t)kt * BK * 2, 0, 0, 0);
+    };
+
+    // ---- weight stage: rows 32 kt .. + 31 of w, this tile's 512 columns.
+    // Thread: k quad kq (rows 4 kq .. 4 kq + 3), column chunk nc (columns
+    // 8 nc .. 8 nc + 7). Rows past K read as zeros.
+    const int kq = tid & 7, nc = tid >> 3;
+    const i32x4 rw = make_rsrc(w + (int64_t)tj * BN * 2, (uint32_t)((int64_t)p.k * ldw * 2 - (int64_t)tj * BN * 2));
+    const uint32_t wrow = (uint32_t)ldw * 2;
+    const uint32_t woff = (uint32_t)(4 * kq) * wrow + nc * 16;
+    auto issue_w = [&](int kt, uint4 *wst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            wst[r] = __builtin_bit_cast(uint4, prolog_raw_buffer_load_b128(
+                                                   rw, woff + (uint32_t)r * wrow + (uint32_t)kt * BK * wrow, 0, 0));
+    };
+    // Transposed stage: physical row P = n ^ ((n >> 3) & 3) of column n holds
+    // its 32 k values, 16-byte chunk c (k 8c .. 8c + 7) at position
+    // c ^ ((P >> 2) & 3). For n = 8 nc + i, P = 8 nc + (i ^ (nc & 3)); the
+    // thread's 4 k values go to chunk kq / 2, half kq % 2.
+    auto write_w = [&](int kt, const uint4 *wst) __attribute__((always_inline)) {
+        unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES + X_BYTES;
+        const unsigned r0[4] = {wst[0].x, wst[0].y, wst[0].z, wst[0].w};
+        const unsigned r1[4] = {wst[1].x, wst[1].y, wst[1].z, wst[1].w};
+        const unsigned r2[4] = {wst[2].x, wst[2].y, wst[2].z, wst[2].w};
+        const unsigned r3[4] = {wst[3].x, wst[3].y, wst[3].z, wst[3].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int prow = 8 * nc + (i ^ (nc & 3));
+            const uint32_t addr = prow * 64 + (((kq >> 1) ^ ((prow >> 2) & 3)) << 4) + (kq & 1) * 8;
+            const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
+            uint2 v;
+            v.x = __builtin_amdgcn_perm(r1[i >> 1], r0[i >> 1], sel);
+            v.y = __builtin_amdgcn_perm(r3[i >> 1], r2[i >> 1], sel);
+            *reinterpret_cast<uint2 *>(st + addr) = v;
+        }
+    };
+
+    // ---- operand read offsets (within a stage). Weight column block nb of
+    // the wave: column n = 128 wn + 32 nb + r32, physical row P; k chunk
+    // 2 ks + g. Activation row block tb: row 64 wt + 32 tb + r32, chunk
+    // 2 ks + g. Both are base ^ (ks << 5) plus a multiple of 2 KB.
+    const int n_l = 128 * wn + r32;
+    const int pn = n_l ^ ((n_l >> 3) & 3);
+    const uint32_t wb = X_BYTES + ((uint32_t)(pn * 64) | ((uint32_t)(g ^ ((pn >> 2) & 3)) << 4));
+    const int xrow = 64 * wt + r32;
+    const uint32_t xb = (uint32_t)(xrow * 64) | ((uint32_t)(g ^ ((xrow >> 2) & 3)) << 4);
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[nb][tb][e] = 0.f;
+
+    // ---- pipeline. Issue order: X0 W0 X1 | W1 X2 | then W(kt+2) X(kt+3) in
+    // iteration kt. At the top of iteration kt the weights of stage kt+1 and
+    // everything older have landed (vmcnt(1): only X(kt+2) may fly); they are
+    // transposed into LDS, then stage kt is consumed. The barrier at the end
+    // publishes stage kt+1 and frees stage kt for X(kt+4).
+    uint4 wst[4];
+    issue_x(0);
+    issue_w(0, wst);
+    issue_x(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 1);  // vmcnt(1): X0, W0 landed
+    write_w(0, wst);
+    issue_w(1, wst);
+    issue_x(2);
+    block_sync();
+    for (int kt = 0; kt < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 1);  // W(kt+1) and X(kt+1) landed
+        write_w(kt + 1, wst);
+        issue_w(kt + 2, wst);
+        issue_x(kt + 3);
+        const unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
+        bf16x8 av[2][4], bv[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                av[ks][nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                            st + ((wb ^ (ks << 5)) + nb * 2048)));
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+                bv[ks][tb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                            st + ((xb ^ (ks << 5)) + tb * 2048)));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+                    acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][nb], bv[ks][tb], acc[nb][tb],
+                                                                          0, 0, 0);
+        block_sync();
+    }
+    // drain the prefetches of stages past the end before the LDS is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    block_sync();
+
+    // ---- epilogue. Lane: output row 64 wt + 32 tb + r32 of the tile; element
+    // 4i + j of block nb is column 128 wn + 32 nb + 8i + 4g + j.
+    if (epilogue == PROLOG_STORE_F32) {
+        float *out = static_cast<float *>(out_base);
+        const i32x4 ro = make_rsrc(out + (int64_t)m0 * ld_out + (int64_t)tj * BN,
+                                   (uint32_t)(((int64_t)rows * ld_out - (int64_t)tj * BN) * 4));
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const uint32_t rowoff = (uint32_t)(64 * wt + 32 * tb + r32) * (uint32_t)ld_out * 4;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 128 * wn + 32 * nb + 8 * i + 4 * g;
+                    i32x4 v;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = __float_as_int(acc[nb][tb][4 * i + j]);
+                    prolog_raw_buffer_store_b128(v, ro, rowoff + n * 4, 0, 0);
+                }
+        }
+        return;
+    }
+
+    // RmsNorm over the tile's 512 columns: per-lane partial sums of squares,
+    // the lane pair (l, l ^ 32) of a row, then the 4 column quarters in LDS.
+    float ssq[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                s0 = __builtin_fmaf(acc[nb][tb][e], acc[nb][tb][e], s0);
+                s1 = __builtin_fmaf(acc[nb][tb][e + 1], acc[nb][tb][e + 1], s1);
+            }
+        const float s = s0 + s1;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(s), __float_as_int(s), false, false);
+        ssq[tb] = g == 0 ? __int_as_float(sw[0]) + __int_as_float(sw[1])
+                         : __int_as_float(sw[1]) + __int_as_float(sw[0]);
+    }
+    float *red = reinterpret_cast<float *>(smem);  // [4 quarters][128 rows]
+    if (g == 0) {
+        red[wn * BM + 64 * wt + r32] = ssq[0];
+        red[wn * BM + 64 * wt + 32 + r32] = ssq[1];
+    }
+    block_sync();
+    float inv[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int row = 64 * wt + 32 * tb + r32;
+        const float tot = ((red[row] + red[BM + row]) + red[2 * BM + row]) + red[3 * BM + row];
+        inv[tb] = 1.0f / sqrtf(tot * (1.0f / BN) + p.eps);
+    }
+
+    __bf16 *out = static_cast<__bf16 *>(out_base);
+    const i32x4 ro = make_rsrc(out + (int64_t)m0 * ld_out + (int64_t)tj * BN,
+                               (uint32_t)(((int64_t)rows * ld_out - (int64_t)tj * BN) * 2));
+    const i32x4 rc = make_rsrc(static_cast<const unsigned char *>(p.rope_cos) + (int64_t)m0 * PROLOG_ROPE * 2,
+                               (uint32_t)rows * PROLOG_ROPE * 2);
+    const i32x4 rs = make_rsrc(static_cast<const unsigned char *>(p.rope_sin) + (int64_t)m0 * PROLOG_ROPE * 2,
+                               (uint32_t)rows * PROLOG_ROPE * 2);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int n = 128 * wn + 32 * nb + 8 * i + 4 * g;
+            float gm[4] = {1.f, 1.f, 1.f, 1.f};
+            if (gamma != nullptr) {
+                const uint2 gw = *reinterpret_cast<const uint2 *>(gamma + ((int64_t)tj * BN + n) * 2);
+                gm[0] = bf16_bits_to_float(gw.x & 0xffff);
+                gm[1] = bf16_bits_to_float(gw.x >> 16);
+                gm[2] = bf16_bits_to_float(gw.y & 0xffff);
+                gm[3] = bf16_bits_to_float(gw.y >> 16);
+            }
+            const bool rope = wn == 3 && nb >= 2;  // columns 448 .. 511
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int row = 64 * wt + 32 * tb + r32;
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = acc[nb][tb][4 * i + j] * inv[tb] * gm[j];
+                if (rope) {
+                    const uint32_t co = (uint32_t)(row * PROLOG_ROPE + (n - (BN - PROLOG_ROPE))) * 2;
+                    const i16x4 cb = prolog_raw_buffer_load_b64(rc, co, 0, 0);
+                    const i16x4 sb = prolog_raw_buffer_load_b64(rs, co, 0, 0);
+                    float cs[4], sn[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        cs[j] = bf16_bits_to_float((unsigned short)cb[j]);
+                        sn[j] = bf16_bits_to_float((unsigned short)sb[j]);
+                    }
+                    const float a0 = v[0] * cs[0] - v[1] * sn[0];
+                    const float a1 = v[1] * cs[1] + v[0] * sn[1];
+                    const float a2 = v[2] * cs[2] - v[3] * sn[2];
+                    const float a3 = v[3] * cs[3] + v[2] * sn[3];
+                    v[0] = a0;
+                    v[1] = a1;
+                    v[2] = a2;
+                    v[3] = a3;
+                }
+                bf16x4 o4;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o4[j] = static_cast<__bf16>(v[j]);
+                prolog_raw_buffer_store_b64(__builtin_bit_cast(i16x4, o4), ro,
+                                            (uint32_t)row * (uint32_t)ld_out * 2 + n * 2, 0, 0);
+            }
+        }
+}
+
+// One wave per row: RmsNorm over cols fp32 values, times gamma, to bf16.
+__global__ __launch_bounds__(256) void prolog_rms_rows_kernel(const float *y, int64_t ld_y, const __bf16 *gamma,
+                                                              __bf16 *out, int64_t ld_out, int32_t rows,
+                                                              int32_t cols, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *yr = y + (int64_t)row * ld_y;
+    float s = 0.f;
+    for (int c = lane * 4; c < cols; c += 256) {
+        const float4 v = *reinterpret_cast<const float4 *>(yr + c);
+        s = __builtin_fmaf(v.x, v.x, s);
+        s = __builtin_fmaf(v.y, v.y, s);
+        s = __builtin_fmaf(v.z, v.z, s);
+        s = __builtin_fmaf(v.w, v.w, s);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    const float inv = 1.0f / sqrtf(s / (float)cols + eps);
+    __bf16 *orow = out + (int64_t)row * ld_out;
+    for (int c = lane * 4; c < cols; c += 256) {
+        const float4 v = *reinterpret_cast<const float4 *>(yr + c);
+        const uint2 gw = *reinterpret_cast<const uint2 *>(gamma + c);
+        bf16x4 o4;
+        o4[0] = static_cast<__bf16>(v.x * inv * bf16_bits_to_float(gw.x & 0xffff));
+        o4[1] = static_cast<__bf16>(v.y * inv * bf16_bits_to_float(gw.x >> 16));
+        o4[2] = static_cast<__bf16>(v.z * inv * bf16_bits_to_float(gw.y & 0xffff));
+        o4[3] = static_cast<__bf16>(v.w * inv * bf16_bits_to_float(gw.y >> 16));
+        *reinterpret_cast<bf16x4 *>(orow + c) = o4;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream) {
+    const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
+    const int m_tiles = (p.m + PROLOG_BM - 1) / PROLOG_BM;
+    if (p.m <= 0 || n_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prolog_gemm_kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prolog_rms_rows(const float *y, int64_t ld_y, const void *gamma, void *out, int64_t ld_out,
+                                  int32_t rows, int32_t cols, float eps, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prolog_rms_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, y, ld_y,
+                       static_cast<const __bf16 *>(gamma), static_cast<__bf16 *>(out), ld_out, rows, cols, eps);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -158,3 +158,46 @@ def paged_inputs(context_lens, heads=128, head_size_k=D_NOPE, head_size_v=D_NOPE
         out["rope_cache"] = _randn((num_blocks, block_size, heads, head_size_rope), dtype, 1.0,
                                    base + 7, device)
     return out
+
+
+# ---------------------------------------------------------------- MLA prolog
+# Sizes the "MlaProlog" page's constraints name: hidden size h 4096,
+# q_lora_rank 1024, 64 heads of head_dim 512, rope_dim 64.
+PROLOG_SIZES = dict(h=4096, q_lora_rank=1024, num_heads=64, head_dim=512, rope_dim=64)
+PROLOG_TOKENS = 16384  # tokens of the measured prolog workload (the page allows 1 .. 64k)
+PROLOG_EPS = 1e-6
+
+
+def rope_tables(positions, rope_dim=64, base=10000.0, dtype=torch.bfloat16, device="cpu"):
+    """cos / sin [len(positions), rope_dim]: the pair (2i, 2i + 1) of position
+    p shares the angle p * base^(-2i / rope_dim)."""
+    pos = torch.as_tensor(np.asarray(positions, dtype=np.float64))
+    inv = base ** (-torch.arange(0, rope_dim, 2, dtype=torch.float64) / rope_dim)
+    ang = torch.repeat_interleave(pos[:, None] * inv[None, :], 2, dim=1)
+    return torch.cos(ang).to(dtype).to(device), torch.sin(ang).to(dtype).to(device)
+
+
+def prolog_inputs(t, h=4096, q_lora_rank=1024, num_heads=64, head_dim=512, rope_dim=64, seed=0, device="cpu",
+                  position0=0):
+    """Seeded bf16 prolog inputs. token_x ~ N(0, 1); each weight ~ N(0, 1/fan_in)
+    (random init of the stated shapes; no trained weights); gammas ~ 1 + 0.1 N(0, 1);
+    rope tables for positions position0 .. position0 + t - 1. Values from
+    torch.Generator(seed * 100 + k), k = 10 .. 15."""
+    base = int(seed) * 100
+    d = dict(
+        token_x=_randn((t, h), torch.bfloat16, 1.0, base + 10, device),
+        wq_a=_randn((h, q_lora_rank), torch.bfloat16, 1.0 / math.sqrt(h), base + 11, device),
+        wq_b=_randn((q_lora_rank, num_heads * head_dim), torch.bfloat16, 1.0 / math.sqrt(q_lora_rank), base + 12,
+                    device),
+        wkv=_randn((h, head_dim), torch.bfloat16, 1.0 / math.sqrt(h), base + 13, device),
+    )
+    g1 = _randn((q_lora_rank,), torch.float32, 0.1, base + 14, device)
+    g2 = _randn((head_dim,), torch.float32, 0.1, base + 15, device)
+    d["gamma_cq"] = (1.0 + g1).to(torch.bfloat16)
+    d["gamma_ckv"] = (1.0 + g2).to(torch.bfloat16)
+    d["rope_cos"], d["rope_sin"] = rope_tables(np.arange(position0, position0 + t), rope_dim, device=device)
+    return d
+
+
+PROLOG_FLOP_PER_TOKEN = 2 * (PROLOG_SIZES["h"] * (PROLOG_SIZES["q_lora_rank"] + PROLOG_SIZES["head_dim"])
+                             + PROLOG_SIZES["q_lora_rank"] * PROLOG_SIZES["num_heads"] * PROLOG_SIZES["head_dim"])

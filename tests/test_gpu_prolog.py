@@ -1,0 +1,112 @@
+"""GPU parity of the non-quantised MLA prolog (``mla_prolog``, through the C ABI).
+
+Expected values come from ``oracle.mla_prolog`` (fp64, "MlaProlog" page
+formulas) on the exact bf16 inputs. Tolerance, element by element:
+|gpu - oracle| <= 1e-2 + 2^-8 |oracle|, and mean |gpu - oracle| <= 3e-3 per
+output. The outputs are bf16 (half an ulp is 2^-9 relative) of values with
+unit root mean square; the fp32 products add little, and rounding c^Q to
+bf16 before the second product adds about 2^-9 / sqrt(3) of the row's rms to
+each q value (random-sign sum of 1024 terms).
+Covered: the page's sizes at several t (one token, ragged tails of the
+128-row tile, several tiles), other head counts (the column tiles not a
+multiple of 8, which changes the launch's tile order), a smaller
+q_lora_rank and h, row independence (a row's bits do not depend on the other
+rows), and the measured 16384-token workload on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_varlen_prefill_amd as mla
+from mla_varlen_prefill_amd import synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+ABS, REL, MEAN = 1e-2, 2.0 ** -8, 3e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(d, eps=synth.PROLOG_EPS):
+    q, kv, cq = mla.prolog(d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"],
+                           d["gamma_cq"], d["gamma_ckv"], eps)
+    torch.cuda.synchronize()
+    return q, kv, cq
+
+
+def run_oracle(d, rows=None, eps=synth.PROLOG_EPS):
+    f = lambda x: x.double().cpu().numpy()
+    x, cos, sin = f(d["token_x"]), f(d["rope_cos"]), f(d["rope_sin"])
+    if rows is not None:
+        x, cos, sin = x[rows], cos[rows], sin[rows]
+    heads = d["wq_b"].shape[1] // d["wkv"].shape[1]
+    return oracle.mla_prolog(x, f(d["wq_a"]), f(d["wq_b"]), f(d["wkv"]), cos, sin, f(d["gamma_cq"]),
+                             f(d["gamma_ckv"]), heads, eps)
+
+
+def assert_close(gpu, ref, what):
+    g = gpu.double().cpu().numpy()
+    assert np.isfinite(g).all(), f"{what}: non-finite"
+    err = np.abs(g - ref)
+    bad = err > ABS + REL * np.abs(ref)
+    assert not bad.any(), f"{what}: {bad.sum()} elements out of tolerance, worst {err.max():.3e}"
+    assert err.mean() <= MEAN, f"{what}: mean abs err {err.mean():.3e}"
+    return float(err.max())
+
+
+def check(d, what):
+    q, kv, cq = run_gpu(d)
+    rq, rkv, rcq = run_oracle(d)
+    assert q.shape == rq.shape and kv.shape == rkv.shape and cq.shape == rcq.shape
+    return (assert_close(q, rq, what + " q"), assert_close(kv, rkv, what + " kv"),
+            assert_close(cq, rcq, what + " c^Q"))
+
+
+@pytest.mark.parametrize("t", [1, 37, 128, 300])
+def test_prolog_page_sizes_match_oracle(t):
+    _say(f"[gpu] prolog page sizes t={t}")
+    d = synth.prolog_inputs(t, seed=t, device=DEV, position0=7 * t)
+    check(d, f"t={t}")
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(t=200, h=4096, q_lora_rank=1024, num_heads=3),   # 3 column tiles: plain tile order
+    dict(t=129, h=256, q_lora_rank=512, num_heads=8),      # one fp32 tile of c^Q, small K
+    dict(t=70, h=64, q_lora_rank=1536, num_heads=16),      # three fp32 tiles, K = 64
+], ids=["3-heads", "rank512-h256", "rank1536-h64"])
+def test_prolog_other_sizes_match_oracle(cfg):
+    _say(f"[gpu] prolog {cfg}")
+    t = cfg.pop("t")
+    d = synth.prolog_inputs(t, seed=5, device=DEV, **cfg)
+    check(d, str(cfg))
+
+
+def test_prolog_rows_are_independent():
+    # every output row depends on its own token only: a prefix run gives the
+    # same bits as the full run
+    _say("[gpu] prolog row independence")
+    d = synth.prolog_inputs(300, seed=9, device=DEV)
+    full = run_gpu(d)
+    part = {k: (v[:77].contiguous() if k in ("token_x", "rope_cos", "rope_sin") else v) for k, v in d.items()}
+    pre = run_gpu(part)
+    for a, b in zip(full, pre):
+        assert torch.equal(a[:77], b)
+
+
+def test_prolog_workload_sampled():
+    t = synth.PROLOG_TOKENS
+    _say(f"[gpu] prolog workload t={t}, sampled rows")
+    d = synth.prolog_inputs(t, seed=1, device=DEV)
+    q, kv, cq = run_gpu(d)
+    assert torch.isfinite(q).all() and torch.isfinite(kv).all() and torch.isfinite(cq).all()
+    rng = np.random.default_rng(17)
+    rows = np.array(sorted(set(rng.integers(0, t, size=40).tolist()) | {0, 127, 128, t - 1}), np.int64)
+    rq, rkv, rcq = run_oracle(d, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    assert_close(q[idx], rq, "workload q")
+    assert_close(kv[idx], rkv, "workload kv")
+    assert_close(cq[idx], rcq, "workload c^Q")
