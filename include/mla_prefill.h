@@ -276,7 +276,7 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
  *               q_lora_rank * 4: the fp32 product x . wq_a before its norm).
  * Supported (the page's constraints fix head_dim 512, h 4096, q_lora_rank
  * 1024, num_heads 64, rope_dim 64, t up to 64k): head_dim = 512,
- * rope_dim = 64, h a multiple of 32, q_lora_rank a multiple of 512, any
+ * rope_dim = 64, h a multiple of 128, q_lora_rank a multiple of 512, any
  * num_heads >= 1 and t >= 0; other sizes return MLA_ERR_UNSUPPORTED.
  * num_heads is read from wq_b's width. Outputs are rounded to nearest even
  * from fp32; products accumulate in fp32; c^Q is rounded to bf16 before it

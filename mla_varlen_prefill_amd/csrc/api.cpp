@@ -593,8 +593,9 @@ int validate_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla
                     (long long)(heads * hd));
     if (hd != mla::PROLOG_BN) return fail(MLA_ERR_UNSUPPORTED, "head_dim %lld: only 512 is supported", (long long)hd);
     if (rd != mla::PROLOG_ROPE) return fail(MLA_ERR_UNSUPPORTED, "rope_dim %lld: only 64 is supported", (long long)rd);
-    if (h <= 0 || h % mla::PROLOG_BK != 0)
-        return fail(MLA_ERR_UNSUPPORTED, "h %lld: a positive multiple of %d is required", (long long)h, mla::PROLOG_BK);
+    if (h <= 0 || h % mla::PROLOG_K_MULTIPLE != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "h %lld: a positive multiple of %d is required", (long long)h,
+                    mla::PROLOG_K_MULTIPLE);
     if (r <= 0 || r % mla::PROLOG_BN != 0)
         return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: a positive multiple of %d is required", (long long)r,
                     mla::PROLOG_BN);

@@ -120,7 +120,8 @@ hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream);
 // PROLOG_BM rows, with an epilogue per column range.
 constexpr int PROLOG_BN = 512;  // one head / one normalised row per tile
 constexpr int PROLOG_BM = 128;
-constexpr int PROLOG_BK = 32;   // K must be a multiple
+constexpr int PROLOG_BK = 32;   // k per pipeline stage
+constexpr int PROLOG_K_MULTIPLE = 128;  // K must be a multiple (4 stages)
 constexpr int PROLOG_ROPE = 64; // rope_dim: the tile's last 64 columns
 
 enum PrologEpilogue : int32_t {
@@ -142,7 +143,7 @@ struct PrologGemmParams {
     const void *a;       // bf16 [M, lda]
     int64_t lda;
     int32_t m;           // rows
-    int32_t k;           // a multiple of PROLOG_BK
+    int32_t k;           // a multiple of PROLOG_K_MULTIPLE
     PrologSegment seg[2];  // tiles 0 .. seg[0].n_tiles - 1 from seg[0], the rest from seg[1]
     const void *rope_cos;  // bf16 [M, 64]
     const void *rope_sin;

@@ -25,18 +25,20 @@
 //    the rope's adjacent pairs sit in one lane.
 //  * 8 waves = 4 column quarters (128 columns) x 2 row halves (64 rows):
 //    4 x 2 accumulator blocks of 32 x 32 per wave.
-//  * K is walked in stages of 32 through a 4-stage LDS ring (40 KB a stage).
-//    Activation rows go HBM -> LDS by the buffer-load-to-LDS DMA path. Weight
-//    rows are k-major in memory but the operand needs 8 consecutive k per
-//    column, so each thread loads 4 weight rows x 8 columns to registers,
-//    pairs them with v_perm_b32 and writes 8-byte (4 k) pieces of the
-//    transposed tile. Both LDS layouts are XOR-swizzled in 16-byte chunks so
+//  * K is walked in stages of 32 through a 4-stage LDS ring (40 KB a stage),
+//    loaded three stages ahead through two register sets. Activation rows are
+//    stored as loaded. Weight rows are k-major in memory but the operand
+//    needs 8 consecutive k per column, so each thread loads 4 weight rows x 8
+//    columns, pairs them with v_perm_b32 and writes 8-byte (4 k) pieces of
+//    the transposed tile. Both LDS layouts are XOR-swizzled in 16-byte chunks so
 //    the 16-byte operand reads are conflict-free; the transposed tile also
 //    permutes its rows (row n at n ^ ((n >> 3) & 3)) so the 8-byte writes hit
 //    every bank group.
 //  * Column tiles are spread so that the 32 CUs of an XCD work on the same
 //    weight tile at the same time (it stays in that XCD's L2).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -50,25 +52,18 @@ constexpr int NT = 512;
 constexpr int STAGES = 4;
 constexpr int X_BYTES = BM * BK * 2;  // 8 KB of activations
 constexpr int W_BYTES = BN * BK * 2;  // 32 KB of transposed weights
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES;  // 160 KB
+constexpr int LDS_BYTES = STAGES * (X_BYTES + W_BYTES);  // 160 KB
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) unsigned int *lds_u32_ptr;
 
-extern "C" __device__ void prolog_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
-                                                      int soffset, int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
 extern "C" __device__ i32x4 prolog_raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 extern "C" __device__ i16x4 prolog_raw_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i16");
-extern "C" __device__ void prolog_raw_buffer_store_b64(i16x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.store.v4i16");
 extern "C" __device__ void prolog_raw_buffer_store_b128(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
@@ -84,8 +79,8 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
     return r;
 }
 
-// Barrier without __syncthreads()'s fence (which would also wait for the
-// LDS-DMA prefetches meant to stay in flight); LDS reads and writes of this
+// Barrier without __syncthreads()'s fence (which would make every thread
+// wait for its prefetches still in flight); LDS reads and writes of this
 // thread have completed (lgkmcnt) before it.
 __device__ __forceinline__ void block_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -100,7 +95,8 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void prolog_gemm_kernel(const PrologGemmParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char xs[STAGES * X_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char ws[STAGES * W_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -137,16 +133,20 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const int rows = min(BM, p.m - m0);
     const int nk = p.k / BK;
 
-    // ---- activation stage: 128 rows x 64 bytes; thread tid fills 16-byte
-    // slot tid = row tid / 4, physical chunk tid % 4, which holds logical
-    // chunk (tid % 4) ^ ((row >> 2) & 3). Rows past the end read as zeros.
+    // ---- activation stage: 128 rows x 64 bytes; thread tid loads the 16
+    // bytes of LDS slot tid = row tid / 4, physical chunk tid % 4, which holds
+    // logical chunk (tid % 4) ^ ((row >> 2) & 3). Rows past the end read as
+    // zeros. (Through registers, not the LDS-DMA path: the compiler cannot
+    // tell where a DMA lands and would wait for it before every LDS access.)
     const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * 2,
                                (uint32_t)rows * (uint32_t)p.lda * 2);
     const int xr = tid >> 2;
     const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * 2 + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
-    auto issue_x = [&](int kt) __attribute__((always_inline)) {
-        prolog_raw_buffer_load_lds(ra, (lds_u32_ptr)(smem + (kt % STAGES) * STAGE_BYTES + wave * 64 * 16), 16,
-                                   xoff + (uint32_t)kt * BK * 2, 0, 0, 0);
+    auto issue_x = [&](int kt, uint4 &xst) __attribute__((always_inline)) {
+        xst = __builtin_bit_cast(uint4, prolog_raw_buffer_load_b128(ra, xoff + (uint32_t)kt * BK * 2, 0, 0));
+    };
+    auto write_x = [&](int slot, const uint4 &xst) __attribute__((always_inline)) {
+        *reinterpret_cast<uint4 *>(xs + slot * X_BYTES + tid * 16) = xst;
     };
 
     // ---- weight stage: rows 32 kt .. + 31 of w, this tile's 512 columns.
@@ -166,8 +166,8 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // its 32 k values, 16-byte chunk c (k 8c .. 8c + 7) at position
     // c ^ ((P >> 2) & 3). For n = 8 nc + i, P = 8 nc + (i ^ (nc & 3)); the
     // thread's 4 k values go to chunk kq / 2, half kq % 2.
-    auto write_w = [&](int kt, const uint4 *wst) __attribute__((always_inline)) {
-        unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES + X_BYTES;
+    auto write_w = [&](int slot, const uint4 *wst) __attribute__((always_inline)) {
+        unsigned char *st = ws + slot * W_BYTES;
         const unsigned r0[4] = {wst[0].x, wst[0].y, wst[0].z, wst[0].w};
         const unsigned r1[4] = {wst[1].x, wst[1].y, wst[1].z, wst[1].w};
         const unsigned r2[4] = {wst[2].x, wst[2].y, wst[2].z, wst[2].w};
@@ -190,7 +190,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // 2 ks + g. Both are base ^ (ks << 5) plus a multiple of 2 KB.
     const int n_l = 128 * wn + r32;
     const int pn = n_l ^ ((n_l >> 3) & 3);
-    const uint32_t wb = X_BYTES + ((uint32_t)(pn * 64) | ((uint32_t)(g ^ ((pn >> 2) & 3)) << 4));
+    const uint32_t wb = (uint32_t)(pn * 64) | ((uint32_t)(g ^ ((pn >> 2) & 3)) << 4);
     const int xrow = 64 * wt + r32;
     const uint32_t xb = (uint32_t)(xrow * 64) | ((uint32_t)(g ^ ((xrow >> 2) & 3)) << 4);
 
@@ -202,73 +202,142 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[nb][tb][e] = 0.f;
 
-    // ---- pipeline. Issue order: X0 W0 X1 | W1 X2 | then W(kt+2) X(kt+3) in
-    // iteration kt. At the top of iteration kt the weights of stage kt+1 and
-    // everything older have landed (vmcnt(1): only X(kt+2) may fly); they are
-    // transposed into LDS, then stage kt is consumed. The barrier at the end
-    // publishes stage kt+1 and frees stage kt for X(kt+4).
-    uint4 wst[4];
-    issue_x(0);
-    issue_w(0, wst);
-    issue_x(1);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 1);  // vmcnt(1): X0, W0 landed
-    write_w(0, wst);
-    issue_w(1, wst);
-    issue_x(2);
+    // ---- pipeline. Stage kt lives in ring slot kt % 4; its rows go through
+    // register set kt % 2. Iteration kt sends out the loads of stage kt+3, so
+    // each stage's loads have two iterations to arrive: at the top of
+    // iteration kt only the five loads of stage kt+2 may still fly (vmcnt(5)),
+    // so stage kt+1 has landed. It is stored into its slot, stage kt+3 is
+    // sent out, and slot kt is consumed; the barrier at the end publishes slot
+    // kt+1. The loop is unrolled by the ring depth so every slot and register
+    // set is a compile-time constant.
+    uint4 wst[2][4], xst[2];
+    issue_w(0, wst[0]);
+    issue_x(0, xst[0]);
+    issue_w(1, wst[1]);
+    issue_x(1, xst[1]);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 5);  // stage 0 landed
+    write_w(0, wst[0]);
+    write_x(0, xst[0]);
+    issue_w(2, wst[0]);
+    issue_x(2, xst[0]);
     block_sync();
-    for (int kt = 0; kt < nk; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 1);  // W(kt+1) and X(kt+1) landed
-        write_w(kt + 1, wst);
-        issue_w(kt + 2, wst);
-        issue_x(kt + 3);
-        const unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
-        bf16x8 av[2][4], bv[2][2];
+    auto step = [&](int kt, auto SLOT) __attribute__((always_inline)) {
+        constexpr int sl = decltype(SLOT)::value;
+        constexpr int nx = (sl + 1) % 2;  // register set of stages kt+1 and kt+3
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);  // stage kt+1 landed
+        write_w((sl + 1) % STAGES, wst[nx]);
+        write_x((sl + 1) % STAGES, xst[nx]);
+        issue_w(kt + 3, wst[nx]);
+        issue_x(kt + 3, xst[nx]);
+        const unsigned char *stw = ws + sl * W_BYTES;
+        const unsigned char *stx = xs + sl * X_BYTES;
+        // one k-step of operands at a time keeps 24 operand registers live
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 av[4], bv[2];
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
-                av[ks][nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                            st + ((wb ^ (ks << 5)) + nb * 2048)));
+                av[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                        stw + ((wb ^ (ks << 5)) + nb * 2048)));
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
-                bv[ks][tb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                            st + ((xb ^ (ks << 5)) + tb * 2048)));
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+                bv[tb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
+                                                        stx + ((xb ^ (ks << 5)) + tb * 2048)));
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
-                    acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[ks][nb], bv[ks][tb], acc[nb][tb],
-                                                                          0, 0, 0);
+                    acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         block_sync();
+    };
+    // K is a multiple of 4 stages: every iteration runs all four steps, so
+    // the registers in flight are the same on every path (a merge of paths
+    // with different loads outstanding would copy them, and a copy waits)
+    for (int kt = 0; kt < nk; kt += STAGES) {
+        step(kt, std::integral_constant<int, 0>{});
+        step(kt + 1, std::integral_constant<int, 1>{});
+        step(kt + 2, std::integral_constant<int, 2>{});
+        step(kt + 3, std::integral_constant<int, 3>{});
     }
-    // drain the prefetches of stages past the end before the LDS is reused
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // the loads of stages past the end return into registers nobody reads;
+    // the LDS is free for the epilogue once every wave is past the last stage
     block_sync();
 
     // ---- epilogue. Lane: output row 64 wt + 32 tb + r32 of the tile; element
     // 4i + j of block nb is column 128 wn + 32 nb + 8i + 4g + j.
+    // Output tiles leave through LDS (the weight ring, free now) so that each
+    // store instruction writes whole rows: 16 bytes per lane straight from
+    // the accumulators would touch 32 rows 16 bytes at a time, and the
+    // partial-line writes cost several times the bytes.
     if (epilogue == PROLOG_STORE_F32) {
+        // fp32 rows are 2 KB: two passes of 64 rows (tb = 0, 1). Row lr of a
+        // pass (= 32 wt + r32) holds chunk c (4 columns) at c ^ ((lr & 7) << 1).
         float *out = static_cast<float *>(out_base);
         const i32x4 ro = make_rsrc(out + (int64_t)m0 * ld_out + (int64_t)tj * BN,
                                    (uint32_t)(((int64_t)rows * ld_out - (int64_t)tj * BN) * 4));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
-            const uint32_t rowoff = (uint32_t)(64 * wt + 32 * tb + r32) * (uint32_t)ld_out * 4;
+            if (tb == 1) block_sync();  // the first pass's rows have been read
+            const int lr = 32 * wt + r32;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int n = 128 * wn + 32 * nb + 8 * i + 4 * g;
-                    i32x4 v;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) v[j] = __float_as_int(acc[nb][tb][4 * i + j]);
-                    prolog_raw_buffer_store_b128(v, ro, rowoff + n * 4, 0, 0);
+                    const int c = 32 * wn + 8 * nb + 2 * i + g;
+                    float4 v;
+                    v.x = acc[nb][tb][4 * i];
+                    v.y = acc[nb][tb][4 * i + 1];
+                    v.z = acc[nb][tb][4 * i + 2];
+                    v.w = acc[nb][tb][4 * i + 3];
+                    *reinterpret_cast<float4 *>(ws + lr * 2048 + ((c ^ ((lr & 7) << 1)) << 4)) = v;
                 }
+            block_sync();
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int q = 8 * wave + (u >> 1);        // pass row
+                const int ch = (u & 1) * 64 + lane;       // logical 16-byte chunk
+                const int row = 64 * (q >> 5) + 32 * tb + (q & 31);
+                const i32x4 v = *reinterpret_cast<const i32x4 *>(ws + q * 2048 + ((ch ^ ((q & 7) << 1)) << 4));
+                prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 4 + ch * 16, 0, 0);
+            }
         }
         return;
+    }
+
+    // Every load of the epilogue (gamma, and the rope's cos / sin for the
+    // quarter holding columns 448 .. 511) goes out first: a load placed after
+    // one of the output stores would have to wait for it (they may alias), and
+    // the latency would be paid once per store. They land while the row sums
+    // are reduced.
+    uint2 gw[4][4];  // gamma of columns n .. n + 3 for (nb, i), bf16 pairs
+    if (gamma != nullptr) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                gw[nb][i] = *reinterpret_cast<const uint2 *>(
+                    gamma + ((int64_t)tj * BN + 128 * wn + 32 * nb + 8 * i + 4 * g) * 2);
+    }
+    const bool rope_wave = wn == 3;  // its blocks nb = 2, 3 are columns 448 .. 511
+    i16x4 rcos[2][4][2], rsin[2][4][2];  // [nb - 2][i][tb]
+    if (rope_wave) {
+        const i32x4 rc = make_rsrc(static_cast<const unsigned char *>(p.rope_cos) + (int64_t)m0 * PROLOG_ROPE * 2,
+                                   (uint32_t)rows * PROLOG_ROPE * 2);
+        const i32x4 rs = make_rsrc(static_cast<const unsigned char *>(p.rope_sin) + (int64_t)m0 * PROLOG_ROPE * 2,
+                                   (uint32_t)rows * PROLOG_ROPE * 2);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb) {
+                    const int row = 64 * wt + 32 * tb + r32;
+                    const uint32_t co = (uint32_t)(row * PROLOG_ROPE + 32 * nb + 8 * i + 4 * g) * 2;
+                    rcos[nb][i][tb] = prolog_raw_buffer_load_b64(rc, co, 0, 0);
+                    rsin[nb][i][tb] = prolog_raw_buffer_load_b64(rs, co, 0, 0);
+                }
     }
 
     // RmsNorm over the tile's 512 columns: per-lane partial sums of squares,
@@ -284,12 +353,11 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 s0 = __builtin_fmaf(acc[nb][tb][e], acc[nb][tb][e], s0);
                 s1 = __builtin_fmaf(acc[nb][tb][e + 1], acc[nb][tb][e + 1], s1);
             }
-        const float s = s0 + s1;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(s), __float_as_int(s), false, false);
-        ssq[tb] = g == 0 ? __int_as_float(sw[0]) + __int_as_float(sw[1])
-                         : __int_as_float(sw[1]) + __int_as_float(sw[0]);
+        const float sm = s0 + s1;
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(sm), __float_as_int(sm), false, false);
+        ssq[tb] = __int_as_float(sw[0]) + __int_as_float(sw[1]);
     }
-    float *red = reinterpret_cast<float *>(smem);  // [4 quarters][128 rows]
+    float *red = reinterpret_cast<float *>(xs);  // [4 quarters][128 rows]
     if (g == 0) {
         red[wn * BM + 64 * wt + r32] = ssq[0];
         red[wn * BM + 64 * wt + 32 + r32] = ssq[1];
@@ -306,10 +374,6 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     __bf16 *out = static_cast<__bf16 *>(out_base);
     const i32x4 ro = make_rsrc(out + (int64_t)m0 * ld_out + (int64_t)tj * BN,
                                (uint32_t)(((int64_t)rows * ld_out - (int64_t)tj * BN) * 2));
-    const i32x4 rc = make_rsrc(static_cast<const unsigned char *>(p.rope_cos) + (int64_t)m0 * PROLOG_ROPE * 2,
-                               (uint32_t)rows * PROLOG_ROPE * 2);
-    const i32x4 rs = make_rsrc(static_cast<const unsigned char *>(p.rope_sin) + (int64_t)m0 * PROLOG_ROPE * 2,
-                               (uint32_t)rows * PROLOG_ROPE * 2);
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -317,28 +381,23 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
             const int n = 128 * wn + 32 * nb + 8 * i + 4 * g;
             float gm[4] = {1.f, 1.f, 1.f, 1.f};
             if (gamma != nullptr) {
-                const uint2 gw = *reinterpret_cast<const uint2 *>(gamma + ((int64_t)tj * BN + n) * 2);
-                gm[0] = bf16_bits_to_float(gw.x & 0xffff);
-                gm[1] = bf16_bits_to_float(gw.x >> 16);
-                gm[2] = bf16_bits_to_float(gw.y & 0xffff);
-                gm[3] = bf16_bits_to_float(gw.y >> 16);
+                gm[0] = bf16_bits_to_float(gw[nb][i].x & 0xffff);
+                gm[1] = bf16_bits_to_float(gw[nb][i].x >> 16);
+                gm[2] = bf16_bits_to_float(gw[nb][i].y & 0xffff);
+                gm[3] = bf16_bits_to_float(gw[nb][i].y >> 16);
             }
-            const bool rope = wn == 3 && nb >= 2;  // columns 448 .. 511
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const int row = 64 * wt + 32 * tb + r32;
                 float v[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = acc[nb][tb][4 * i + j] * inv[tb] * gm[j];
-                if (rope) {
-                    const uint32_t co = (uint32_t)(row * PROLOG_ROPE + (n - (BN - PROLOG_ROPE))) * 2;
-                    const i16x4 cb = prolog_raw_buffer_load_b64(rc, co, 0, 0);
-                    const i16x4 sb = prolog_raw_buffer_load_b64(rs, co, 0, 0);
+                if (nb >= 2 && rope_wave) {
                     float cs[4], sn[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        cs[j] = bf16_bits_to_float((unsigned short)cb[j]);
-                        sn[j] = bf16_bits_to_float((unsigned short)sb[j]);
+                        cs[j] = bf16_bits_to_float((unsigned short)rcos[nb - 2][i][tb][j]);
+                        sn[j] = bf16_bits_to_float((unsigned short)rsin[nb - 2][i][tb][j]);
                     }
                     const float a0 = v[0] * cs[0] - v[1] * sn[0];
                     const float a1 = v[1] * cs[1] + v[0] * sn[1];
@@ -352,10 +411,17 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 bf16x4 o4;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o4[j] = static_cast<__bf16>(v[j]);
-                prolog_raw_buffer_store_b64(__builtin_bit_cast(i16x4, o4), ro,
-                                            (uint32_t)row * (uint32_t)ld_out * 2 + n * 2, 0, 0);
+                // tile row r (1 KB) holds 16-byte chunk c (8 columns) at c ^ (r & 15)
+                *reinterpret_cast<bf16x4 *>(ws + row * 1024 + (((n >> 3) ^ (row & 15)) << 4) + g * 8) = o4;
             }
         }
+    block_sync();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int row = 16 * wave + u;
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(ws + row * 1024 + ((lane ^ (row & 15)) << 4));
+        prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 2 + lane * 16, 0, 0);
+    }
 }
 
 // One wave per row: RmsNorm over cols fp32 values, times gamma, to bf16.

@@ -382,7 +382,7 @@ def test_paged_cache_shape_and_dtype_errors():
 
 # ------------------------------------------------------------------ prolog validation
 
-def prolog_args(t=0, h=64, r=512, heads=2, hd=512, rd=64, **over):
+def prolog_args(t=0, h=128, r=512, heads=2, hd=512, rd=64, **over):
     z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)
     a = dict(token_x=z(t, h), wq_a=z(h, r), wq_b=z(r, heads * hd), wkv=z(h, hd), rope_cos=z(t, rd),
              rope_sin=z(t, rd), gamma_cq=z(r), gamma_ckv=z(hd), eps=1e-6, q_out=z(t, heads, hd), kv_out=z(t, hd),
@@ -410,7 +410,7 @@ def test_prolog_validation_errors():
     ERR_SHAPE, ERR_DTYPE, ERR_VALUE, ERR_UNSUP = -2, -3, -4, -5
     assert prolog_status(token_x=torch.zeros(0, 64, dtype=torch.float16)) == ERR_DTYPE
     assert prolog_status(eps=0.0) == ERR_VALUE
-    assert prolog_status(wq_a=torch.zeros(32, 512, dtype=torch.bfloat16)) == ERR_SHAPE
+    assert prolog_status(wq_a=torch.zeros(64, 512, dtype=torch.bfloat16)) == ERR_SHAPE
     assert prolog_status(gamma_ckv=torch.zeros(511, dtype=torch.bfloat16)) == ERR_SHAPE
     assert prolog_status(q_out=torch.zeros(0, 3, 512, dtype=torch.bfloat16)) == ERR_SHAPE
     assert prolog_status(kv_out=torch.zeros(1, 512, dtype=torch.bfloat16)) == ERR_SHAPE
@@ -419,5 +419,6 @@ def test_prolog_validation_errors():
     assert prolog_status(rd=32) == ERR_UNSUP
     assert prolog_status(r=1000) == ERR_UNSUP
     assert prolog_status(h=48) == ERR_UNSUP
+    assert prolog_status(h=192) == ERR_UNSUP
     # 2-D q_out is accepted
     assert prolog_status(q_out=torch.zeros(0, 1024, dtype=torch.bfloat16)) == 0

@@ -76,8 +76,8 @@ def test_prolog_page_sizes_match_oracle(t):
 @pytest.mark.parametrize("cfg", [
     dict(t=200, h=4096, q_lora_rank=1024, num_heads=3),   # 3 column tiles: plain tile order
     dict(t=129, h=256, q_lora_rank=512, num_heads=8),      # one fp32 tile of c^Q, small K
-    dict(t=70, h=64, q_lora_rank=1536, num_heads=16),      # three fp32 tiles, K = 64
-], ids=["3-heads", "rank512-h256", "rank1536-h64"])
+    dict(t=70, h=128, q_lora_rank=1536, num_heads=16),     # three fp32 tiles, K = 128
+], ids=["3-heads", "rank512-h256", "rank1536-h128"])
 def test_prolog_other_sizes_match_oracle(cfg):
     _say(f"[gpu] prolog {cfg}")
     t = cfg.pop("t")
