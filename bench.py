@@ -317,6 +317,33 @@ def bench_gather_nz(steps):
             "value": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": gbs / PEAK_HBM_GBS}
 
 
+def bench_prolog(steps):
+    """The non-quantised MLA prolog (NEXT-4) on its measured workload: 16384
+    tokens at the sizes the MlaProlog page's constraints name (h 4096,
+    q_lora_rank 1024, 64 heads x 512, rope 64); random-init bf16 weights.
+    FLOPs are the three products' 2 * M * N * K; the norms and the rope are
+    not counted."""
+    t = synth.PROLOG_TOKENS
+    d = synth.prolog_inputs(t, seed=1, device="cuda")
+    hd, r = d["wkv"].shape[1], d["wq_a"].shape[1]
+    heads = d["wq_b"].shape[1] // hd
+    q = torch.empty((t, heads, hd), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((t, hd), dtype=torch.bfloat16, device="cuda")
+    cq = torch.empty((t, r), dtype=torch.bfloat16, device="cuda")
+    eps = synth.PROLOG_EPS
+    args = (d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"], d["gamma_cq"],
+            d["gamma_ckv"], eps, q, kv, cq)
+    ws = torch.empty(max(mla.mla_prolog_get_workspace_size(*args), 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = _time(lambda: mla.mla_prolog(*args, ws, stream), steps, stream)
+    flops = synth.PROLOG_FLOP_PER_TOKEN * t
+    tf = flops / (ms * 1e-3) / 1e12
+    del d, q, kv, cq, ws
+    torch.cuda.empty_cache()
+    return {"workload": "prolog", "tokens": t, "sizes": dict(synth.PROLOG_SIZES), "flop_per_step": flops,
+            "ms_per_step": ms, "value": tf, "unit": "TFLOP/s", "peak": PEAK_TFLOPS, "frac": tf / PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -330,6 +357,8 @@ def main():
                     help="run a plain copy of known size first (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                     help="turn FETCH_SIZE / WRITE_SIZE rocprofv3 runs into HBM bytes per launch, then exit")
+    ap.add_argument("--prolog-only", action="store_true",
+                    help="time only the MLA prolog leg and print its JSON object (for profiling it)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -342,6 +371,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.prolog_only:
+        print(json.dumps(bench_prolog(args.steps)), flush=True)
+        return
     if args.calibrate_copy:
         calibration_copy()
     res = bench_attention(args.workload, args.steps, args.warmup)
@@ -370,6 +402,7 @@ def main():
         line["gather"], line["paged_attention"] = bench_paged(max(2, min(args.steps, 5)))
         line["gather_nz"] = bench_gather_nz(max(2, min(args.steps, 5)))
         line["extras"] = bench_extras(3)
+        line["prolog"] = bench_prolog(max(3, min(args.steps, 10)))
         del res_t
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
