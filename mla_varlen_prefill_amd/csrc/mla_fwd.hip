@@ -96,8 +96,8 @@ extern "C" __device__ void mla_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, 
     __asm("llvm.amdgcn.raw.buffer.load.lds");
 extern "C" __device__ i32x4 mla_raw_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
-extern "C" __device__ void mla_raw_buffer_store_b64(i16x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.store.v4i16");
+extern "C" __device__ void mla_raw_buffer_store_b128(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -702,15 +702,24 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
     }
 
-    // ---- epilogue: combine the two lanes' row sums, normalise, round, store
+    // ---- epilogue: combine the two lanes' row sums, normalise, round, store.
+    // The rows leave through LDS so that each store instruction writes whole
+    // 256-byte head slices of 4 rows: straight from the accumulators every
+    // instruction would write 16 bytes into each of 32 rows, and such
+    // partial-line writes cost far more than their bytes. Before the ring is
+    // reused, the leading group's K DMA for tiles past the last one (still in
+    // flight: block_sync waits for LDS reads and writes, not for DMA) must
+    // have landed, and the barrier waits for the trailing group's last P.V,
+    // which may still read the ring.
     const float l_tot = sum_with_partner(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    block_sync();
     {
-        const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)seq.q_off + row0;
-        const i32x4 ro = make_rsrc(static_cast<unsigned char *>(p.out) + (tok * H + h) * (DN * 2),
-                                   (uint32_t)rows * H * DN * 2);
-        const uint32_t base = (uint32_t)r32 * H * DN * 2 + g * 8;
+        // staging row sr = 32 * slot + r32 (256 bytes: d 0..127), 16-byte
+        // chunk c (8 values of d) at c ^ (sr & 15); a wave writes and reads
+        // back only its own 32 rows
+        const int sr = slot * 32 + r32;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -718,8 +727,21 @@ void mla_fwd_kernel(const FwdParams p) {
                 typename T::vec4 v4;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) v4[jj] = static_cast<typename T::scalar>(o[db][4 * i + jj] * inv);
-                mla_raw_buffer_store_b64(__builtin_bit_cast(i16x4, v4), ro, base + (db * 32 + 8 * i) * 2, 0, 0);
+                *reinterpret_cast<typename T::vec4 *>(smem + sr * 256 + (((4 * db + i) ^ (sr & 15)) << 4) + g * 8) =
+                    v4;
             }
+        const int rows = max(0, min(32, q_len - row0));
+        const int64_t tok = (int64_t)seq.q_off + row0;
+        const i32x4 ro = make_rsrc(static_cast<unsigned char *>(p.out) + (tok * H + h) * (DN * 2),
+                                   (uint32_t)rows * H * DN * 2);
+        const int ch = lane & 15;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int r = 4 * k + (lane >> 4);  // row of the wave
+            const int srr = slot * 32 + r;
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + srr * 256 + ((ch ^ (srr & 15)) << 4));
+            mla_raw_buffer_store_b128(v, ro, (uint32_t)r * H * DN * 2 + ch * 16, 0, 0);
+        }
     }
 }
 
