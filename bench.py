@@ -149,22 +149,25 @@ def bench_attention(name, steps, warmup):
 
 
 def _attention_tflops(t, qs, ks, heads, kv_heads, mask_type, mask, steps):
-    out = torch.empty((t["q"].shape[0], heads, 128), dtype=t["q"].dtype, device="cuda")
+    d = t["q"].shape[-1]
+    out = torch.empty((t["q"].shape[0], heads, d), dtype=t["q"].dtype, device="cuda")
     args = dict(q=t["q"], q_rope=t["q_rope"], k=t["k"], k_rope=t["k_rope"], v=t["v"], q_seqlen=qs, kv_seqlen=ks,
                 mask=mask, head_num=heads, qk_scale=synth.QK_SCALE, kv_head_num=kv_heads, mask_type=mask_type,
                 cache_mode=0, atten_out=out)
     ws = torch.empty(max(mla.mla_prefill_get_workspace_size(**args), 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     ms = _time(lambda: mla.mla_prefill(**args, workspace=ws, stream=stream), steps, stream)
-    flops = FLOP_PER_PAIR * heads * visible_pairs(qs, ks, mask_type)
+    # 2 * (D + 64) for the scores and 2 * D for P.V per visible (query, key, head)
+    flops = (4 * d + 2 * 64) * heads * visible_pairs(qs, ks, mask_type)
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
 def bench_extras(steps):
     """Secondary configurations: the chunked workload under MASK_FREE with the
     causal fp16 tile (the same visible pairs as causal); one GPU's share of an
-    8-way split over heads (16 heads) of the single and chunked shapes; and the
-    single shape with its 128 query heads grouped over 16 and over 1 KV heads."""
+    8-way split over heads (16 heads) of the single and chunked shapes; the
+    single shape at head dim 64; and the single shape with its 128 query heads
+    grouped over 16 and over 1 KV heads."""
     res = {}
     t, qs, ks, p = synth.workload_inputs("chunked", device="cuda")
     res["chunked_causal"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_CAUSAL, None, steps)
@@ -180,6 +183,10 @@ def bench_extras(steps):
         del t
     qs, ks = synth.workload_seqlens("single")
     w = synth.WORKLOADS["single"]
+    t = synth.attention_inputs(qs, ks, 128, 128, w["dtype"], w["sigma"], w["seed"], "cuda", d_nope=64)
+    res["single_head_dim_64"] = _attention_tflops(t, np.asarray(qs, np.int32), np.asarray(ks, np.int32), 128, 128,
+                                                  synth.MASK_CAUSAL, None, steps)
+    del t
     for hk in (16, 1):
         t = synth.attention_inputs(qs, ks, 128, hk, w["dtype"], w["sigma"], w["seed"], "cuda")
         res[f"single_128_heads_{hk}_kv_heads"] = _attention_tflops(t, np.asarray(qs, np.int32),

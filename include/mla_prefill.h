@@ -112,7 +112,8 @@ typedef struct mla_tensor {
  *
  * Arguments (the page's Members table, same order):
  *   q          device, [nTokens, headNum*D] or [nTokens, headNum, D], fp16/bf16.
- *              nTokens = sum of q_seqlen. D = embeddimV; this build runs D = 128.
+ *              nTokens = sum of q_seqlen. D = embeddimV: 64 or 128 here (other
+ *              values return MLA_ERR_UNSUPPORTED).
  *   q_rope     device, [nTokens, headNum*64] or [nTokens, headNum, 64], same dtype.
  *   k          device, packed [sum kv_seqlen, kvHeadNum, D], or padded
  *              [batch, max_seq, kvHeadNum*D] (sequence b's keys start at row
@@ -212,9 +213,9 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
  *
  *   q, q_rope, q_seqlen, mask, head_num, qk_scale, kv_head_num, mask_type,
  *   atten_out   as for mla_prefill.
- *   key_cache     device ND [num_blocks, block_size, kvHeadNum, 128], dtype of q.
+ *   key_cache     device ND [num_blocks, block_size, kvHeadNum, D], dtype of q.
  *   krope_cache   device ND [num_blocks, block_size, kvHeadNum, 64], dtype of q.
- *   value_cache   device ND [num_blocks, block_size, kvHeadNum, 128], dtype of q.
+ *   value_cache   device ND [num_blocks, block_size, kvHeadNum, D], dtype of q.
  *   block_tables  device int32 [batch, max_blocks]: key t of sequence b is slot
  *                 t % block_size of block block_tables[b][t / block_size]
  *                 (every sequence starts at position 0 of its table row).

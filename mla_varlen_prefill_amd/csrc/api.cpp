@@ -18,7 +18,6 @@
 
 using mla::FWD_BM;
 using mla::FWD_BN;
-using mla::HEAD_DIM;
 using mla::MASK_TILE;
 using mla::ROPE_DIM;
 using mla::SeqRec;
@@ -116,6 +115,7 @@ struct Problem {
     int64_t kv_padded_max_seq = 0;  // 0: packed
     int mask_type = 0;
     int mask_dtype = 0;
+    int64_t head_dim = 0;  // embeddimV
     const int32_t *q_seqlen = nullptr;
     const int32_t *kv_seqlen = nullptr;
 };
@@ -229,8 +229,9 @@ int validate_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_te
             return fail(MLA_ERR_SHAPE, "mask: expected [512, 512]");
         pr->mask_dtype = mask->dtype;
     }
-    if (dq != HEAD_DIM)
-        return fail(MLA_ERR_UNSUPPORTED, "embeddimV %lld: this build implements 128", (long long)dq);
+    if (dq != 64 && dq != 128)
+        return fail(MLA_ERR_UNSUPPORTED, "embeddimV %lld: the kernel implements 64 and 128", (long long)dq);
+    pr->head_dim = dq;
     if ((int64_t)head_num > 65535) return fail(MLA_ERR_UNSUPPORTED, "headNum above 65535");
     return MLA_OK;
 }
@@ -276,7 +277,7 @@ int validate_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_tens
     if (pr->kv_padded_max_seq != 0) return fail(MLA_ERR_SHAPE, "caches: unexpected shape");
     const mla_tensor *caches[] = {key_cache, krope_cache, value_cache};
     const char *names[] = {"key_cache", "krope_cache", "value_cache"};
-    const int64_t dims[] = {HEAD_DIM, ROPE_DIM, HEAD_DIM};
+    const int64_t dims[] = {pr->head_dim, ROPE_DIM, pr->head_dim};
     for (int i = 0; i < 3; ++i) {
         const mla_tensor *c = caches[i];
         if (c->ndim != 4 || c->shape[2] != kv_head_num || c->shape[3] != dims[i] ||
@@ -520,6 +521,7 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.kv_heads = pr.kv_heads;
     p.group = pr.heads / pr.kv_heads;
     p.pack_shift = pack_shift_for(pr.heads, pr.kv_heads);
+    p.head_dim = (int32_t)pr.head_dim;
     p.n_tasks = (int32_t)plan.tasks.size();
     p.mask_type = pr.mask_type;
     p.mask_is_bf16 = (pr.mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;

@@ -11,7 +11,6 @@ namespace mla {
 constexpr int FWD_BM = 256;
 constexpr int FWD_BN = 64;
 constexpr int FWD_THREADS = 512;
-constexpr int HEAD_DIM = 128;   // embeddimV handled by the kernel
 constexpr int ROPE_DIM = 64;    // rope part, fixed by the operator definition
 constexpr int MASK_TILE = 512;  // side of the MASK_FREE tile
 
@@ -52,13 +51,13 @@ constexpr int MLA_XCDS = 8;
 constexpr int MLA_CUS_PER_XCD = 32;
 
 struct FwdParams {
-    const void *q;        // [nq, H, 128]
+    const void *q;        // [nq, H, D]
     const void *q_rope;   // [nq, H, 64]
-    const void *k;        // rows of Hkv * 128
+    const void *k;        // rows of Hkv * D
     const void *k_rope;   // rows of Hkv * 64
-    const void *v;        // rows of Hkv * 128
+    const void *v;        // rows of Hkv * D
     const void *mask;     // [512, 512] or nullptr
-    void *out;            // [nq, H, 128]
+    void *out;            // [nq, H, D]
     const SeqRec *seqs;
     const WorkItem *items;
     const Task *tasks;
@@ -69,9 +68,10 @@ struct FwdParams {
     int32_t mask_is_bf16; // dtype of the MASK_FREE tile
     int32_t n_tasks;      // workgroups to launch
     int32_t pack_shift;   // log2 of the query heads one workgroup runs
+    int32_t head_dim;     // embeddimV: 64 or 128
     float scale_log2;     // qkScale * log2(e)
     // Paged K/V (launch_mla_fwd with paged = true): k, k_rope and v point at
-    // ND caches [num_blocks, block_size, Hkv, 128 | 64 | 128]; key t of
+    // ND caches [num_blocks, block_size, Hkv, D | 64 | D]; key t of
     // sequence b is slot t % block_size of block block_tables[b][t / block_size].
     const int32_t *block_tables;  // [batch, bt_stride]
     int32_t bt_stride;

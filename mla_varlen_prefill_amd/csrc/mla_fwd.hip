@@ -10,6 +10,8 @@
 // kvHeadNum < headNum), 256 / P rows of each of P = 2, 4 or 8 heads of one
 // group, so that every K/V tile staged in LDS is used by all of them.
 //
+//  * The head dim D (embeddimV) is a template parameter, 64 or 128; the text
+//    below gives sizes for D = 128.
 //  * Each wave owns 32 query rows of one head. Their Q (32 x 128) stays in
 //    VGPRs as the B operand of v_mfma_f32_32x32x16 (8 k-steps of 16); QRope
 //    of the workgroup's 256 rows (4 more k-steps) sits in LDS.
@@ -56,7 +58,6 @@ namespace {
 constexpr int BM = FWD_BM;
 constexpr int BN = FWD_BN;
 constexpr int NT = FWD_THREADS;
-constexpr int DN = HEAD_DIM;
 constexpr int DR = ROPE_DIM;
 constexpr int STAGES = 3;
 #ifndef MLA_PREFETCH
@@ -67,13 +68,26 @@ constexpr int STAGES = 3;
 #endif
 constexpr int LOAD_SPACING = MLA_LOAD_SPACING;  // MFMAs between the tile loads a matrix block issues
 constexpr int PREFETCH = MLA_PREFETCH;  // LDS operands in flight ahead of the MFMA using them
-constexpr int KN_BYTES = BN * DN * 2;  // 16 KB
 constexpr int KR_BYTES = BN * DR * 2;  // 8 KB
-constexpr int V_BYTES = BN * DN * 2;   // 16 KB
-constexpr int STAGE_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
-constexpr int QR_OFFSET = STAGES * STAGE_BYTES;  // Q-rope of the item's rows
-constexpr int QR_BYTES = BM * DR * 2;             // 32 KB
-constexpr int LDS_BYTES = QR_OFFSET + QR_BYTES;   // 152 KB
+constexpr int QR_BYTES = BM * DR * 2;  // 32 KB
+// LDS of a head dim D (embeddimV: 64 or 128). A ring stage holds K-nope
+// (64 keys x D), K-rope (64 x 64) and V^T (D x 64 keys); Q-rope of the
+// workgroup's rows follows the ring. D = 128: 40 KB stages, 152 KB in all.
+template <int D>
+struct Geom {
+    static constexpr int KN_BYTES = BN * D * 2;
+    static constexpr int V_BYTES = BN * D * 2;
+    static constexpr int STAGE_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
+    static constexpr int QR_OFFSET = STAGES * STAGE_BYTES;
+    static constexpr int LDS_BYTES = QR_OFFSET + QR_BYTES;
+};
+// 16-byte chunk swizzle of an LDS row of D * 2 bytes (K-nope rows, output
+// staging rows): chunk c of row r sits at c ^ swz(r), which makes the 16-byte
+// reads of 16 consecutive rows (and 8-byte writes of 32) conflict-free.
+template <int D>
+__device__ __forceinline__ int row_swizzle(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -183,9 +197,19 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char *p) {
 // the LDS past the ring.
 constexpr int TILE_TABLE_BYTES = PAGED_MAX_TILES * 4;
 
-template <typename T, bool PAGED>
+template <typename T, bool PAGED, int DN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void mla_fwd_kernel(const FwdParams p) {
+    constexpr int KN_BYTES = Geom<DN>::KN_BYTES;
+    constexpr int STAGE_BYTES = Geom<DN>::STAGE_BYTES;
+    constexpr int QR_OFFSET = Geom<DN>::QR_OFFSET;
+    constexpr int LDS_BYTES = Geom<DN>::LDS_BYTES;
+    constexpr int KN_ROW = DN * 2;      // LDS bytes of a K-nope row
+    constexpr int NKS = DN / 16;        // k-steps of the nope product
+    constexpr int NDB = DN / 32;        // 32-column blocks of O
+    constexpr int NV = 4 * NDB;         // V^T operands of a matrix block (4 key steps x NDB)
+    constexpr int KN_LOADS = DN / 32;   // K-nope DMA per leading thread and tile
+    constexpr int CPT = DN / 64;        // V column chunk pairs per leading thread
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)];
     typedef typename T::vec8 vec8;
 
@@ -227,7 +251,7 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // ---- Q-nope^T operand (B of S^T = K . Q^T) in VGPRs: lane holds row r32,
     // k-slots g*8..g*8+7 of each 16-wide k-step. Rows past the end read as 0.
-    vec8 qreg[8];
+    vec8 qreg[NKS];
     {
         const int rows = max(0, min(32, q_len - row0));
         const int64_t tok = (int64_t)seq.q_off + row0;
@@ -235,7 +259,7 @@ void mla_fwd_kernel(const FwdParams p) {
                                    (uint32_t)rows * H * DN * 2);
         const uint32_t qo = (uint32_t)r32 * H * DN * 2 + g * 16;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+        for (int ks = 0; ks < NKS; ++ks)
             qreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rq, qo + ks * 32, 0, 0));
     }
     // ---- Q-rope of the workgroup's 256 rows -> LDS (DMA). LDS row 32 s + r
@@ -300,12 +324,12 @@ void mla_fwd_kernel(const FwdParams p) {
     // work in the texture unit and the trailing group's vector block issues no
     // memory instruction at all.
     constexpr int LT = NT / 2;
-    uint32_t off_kn[4], off_kr[2];
+    uint32_t off_kn[KN_LOADS], off_kr[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KN_LOADS; ++u) {
         const int slot = tid + LT * u;
-        const int m = slot >> 4;
-        off_kn[u] = perm_key(m) * kn_row + (((slot & 15) ^ (m & 15)) << 4);
+        const int m = slot / (DN / 8);  // tile row; DN / 8 chunks of 16 bytes each
+        off_kn[u] = perm_key(m) * kn_row + (((slot % (DN / 8)) ^ row_swizzle<DN>(m)) << 4);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -316,7 +340,8 @@ void mla_fwd_kernel(const FwdParams p) {
     const int kp = tid & 31, dg = (tid >> 5) & 7;
     // two VGPR offsets (the buffer range check covers the VGPR offset and the
     // immediate, not the SGPR offset, so the key step must not go there)
-    const uint32_t off_v[2] = {(uint32_t)(2 * kp) * kn_row + dg * 32, (uint32_t)(2 * kp + 1) * kn_row + dg * 32};
+    const uint32_t off_v[2] = {(uint32_t)(2 * kp) * kn_row + dg * CPT * 16,
+                               (uint32_t)(2 * kp + 1) * kn_row + dg * CPT * 16};
     struct TileLoad {
         i32x4 rk, rr, rv;
         unsigned char *st;
@@ -347,14 +372,14 @@ void mla_fwd_kernel(const FwdParams p) {
     // A leading thread's loads of a tile: six K DMA (K_LOADS) and four V loads
     // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
     // 2dg + (j >> 1).
-    constexpr int K_LOADS = 6, V_LOADS = 4, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
+    constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
     auto issue_k = [&](const TileLoad &tl, int i) __attribute__((always_inline)) {
         const int wofs = wave * 64 * 16;
-        if (i < 4)
+        if (i < KN_LOADS)
             mla_raw_buffer_load_lds(tl.rk, (lds_u32_ptr)(tl.st + i * LT * 16 + wofs), 16, off_kn[i], 0, 0, 0);
         else
-            mla_raw_buffer_load_lds(tl.rr, (lds_u32_ptr)(tl.st + KN_BYTES + (i - 4) * LT * 16 + wofs), 16,
-                                    off_kr[i - 4], 0, 0, 0);
+            mla_raw_buffer_load_lds(tl.rr, (lds_u32_ptr)(tl.st + KN_BYTES + (i - KN_LOADS) * LT * 16 + wofs), 16,
+                                    off_kr[i - KN_LOADS], 0, 0, 0);
     };
     auto issue_v = [&](const TileLoad &tl, int j, uint4 *vst) __attribute__((always_inline)) {
         vst[j] = __builtin_bit_cast(uint4, mla_raw_buffer_load_b128(tl.rv, off_v[j & 1] + (j >> 1) * 16, 0, 0));
@@ -370,13 +395,16 @@ void mla_fwd_kernel(const FwdParams p) {
     // (key 2kp, 2kp + 1) of rows 16dg .. 16dg + 15: for d = 16dg + 8h + 2dd (+1),
     // (d >> 1) & 7 = 4h + dd, so the offset is vw_base ^ ((4h + dd) << 4) plus
     // 1024h + 256dd (+128).
-    const uint32_t vw_base = KN_BYTES + KR_BYTES + dg * 2048 + ((kp >> 2) << 4) + (kp & 3) * 4;
+    // (DN = 64: one chunk per thread, d = 8dg + 2dd; (d >> 1) & 7 = 4(dg & 1) + dd,
+    // so the 4(dg & 1) part goes into the base.)
+    const uint32_t vw_base = KN_BYTES + KR_BYTES + dg * (CPT * 1024) +
+                             (((kp >> 2) ^ (CPT == 1 ? 4 * (dg & 1) : 0)) << 4) + (kp & 3) * 4;
     auto write_vt = [&](int kt, const uint4 *vst) __attribute__((always_inline)) {
         unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
         uint32_t vwb = vw_base;
         asm volatile("" : "+v"(vwb));
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < CPT; ++h) {
             const unsigned a[4] = {vst[2 * h].x, vst[2 * h].y, vst[2 * h].z, vst[2 * h].w};  // key 2kp
             const unsigned b[4] = {vst[2 * h + 1].x, vst[2 * h + 1].y, vst[2 * h + 1].z, vst[2 * h + 1].w};
 #pragma unroll
@@ -396,9 +424,9 @@ void mla_fwd_kernel(const FwdParams p) {
     // region is free once the trailing group has scored the tile before), its V
     // two intervals before V^T is written (the staging registers are free once
     // V^T of tile t-1 is written).
-    uint4 vstage[4];
+    uint4 vstage[V_LOADS];
     if (grp == 0) {
-        uint4 v0[4];
+        uint4 v0[V_LOADS];
         const TileLoad t0 = prep_tile(0, cache_row(0)), t1 = prep_tile(1, cache_row(1)),
                        t2 = prep_tile(2, cache_row(2));
 #pragma unroll
@@ -424,7 +452,7 @@ void mla_fwd_kernel(const FwdParams p) {
     const float c = fabsf(p.scale_log2);
     if (p.scale_log2 < 0.f) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < NKS; ++ks) {
             i32x4 w = __builtin_bit_cast(i32x4, qreg[ks]);
             w ^= (int)0x80008000;
             qreg[ks] = __builtin_bit_cast(vec8, w);
@@ -463,7 +491,7 @@ void mla_fwd_kernel(const FwdParams p) {
     //  K-rope:            row kb*32 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
     //  Q-rope (B):        LDS row 32*slot + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
     //  V^T (A of O^T):    row d = 32*db + r32, chunk 2*st4 + g, swizzle ^ ((d >> 1) & 7)
-    const uint32_t kn_base = r32 * 256 + ((g ^ (r32 & 15)) << 4);
+    const uint32_t kn_base = r32 * KN_ROW + ((g ^ row_swizzle<DN>(r32)) << 4);
     const uint32_t kr_base = KN_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
     const int qr_row = slot * 32 + r32;
     const uint32_t qr_base = QR_OFFSET + qr_row * 128 + ((g ^ ((qr_row >> 1) & 7)) << 4);
@@ -472,22 +500,23 @@ void mla_fwd_kernel(const FwdParams p) {
     auto lds16 = [](const unsigned char *a) __attribute__((always_inline)) -> vec8 {
         return __builtin_bit_cast(vec8, *reinterpret_cast<const uint4 *>(a));
     };
-    // operand n of a matrix block: n < 16 -> V^T of (16-key step n/4, column block
-    // n%4) from stage sv; n >= 16 -> K of (k-step (n-16)/2, key block (n-16)%2) from sk
+    // operand n of a matrix block: n < NV -> V^T of (16-key step n / NDB, column
+    // block n % NDB) from stage sv; n >= NV -> K of (k-step (n - NV) / 2, key
+    // block (n - NV) % 2) from sk, the first NKS k-steps nope, the last 4 rope
     auto load_operand = [&](const unsigned char *sv, const unsigned char *sk, int n, uint32_t knb, uint32_t krb,
                             uint32_t vtb) __attribute__((always_inline)) -> vec8 {
-        if (n < 16) return lds16(sv + (vtb ^ ((n >> 2) << 5)) + (n & 3) * 32 * 128);
-        const int ks = (n - 16) >> 1, kb = (n - 16) & 1;
-        if (ks < 8) return lds16(sk + (knb ^ (ks << 5)) + kb * 32 * 256);
-        return lds16(sk + (krb ^ ((ks - 8) << 5)) + kb * 32 * 128);
+        if (n < NV) return lds16(sv + (vtb ^ ((n / NDB) << 5)) + (n % NDB) * 32 * 128);
+        const int ks = (n - NV) >> 1, kb = (n - NV) & 1;
+        if (ks < NKS) return lds16(sk + (knb ^ (ks << 5)) + kb * 32 * KN_ROW);
+        return lds16(sk + (krb ^ ((ks - NKS) << 5)) + kb * 32 * 128);
     };
 
     // ---- softmax state
     float m_run = -INFINITY;  // running row max of raw scores (same in both lanes of a row)
     float l_run = 0.f;        // this lane's share of the running row sum
-    f32x16 o[4];
+    f32x16 o[NDB];
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
     // scores of one tile; element e of block kb is key
@@ -502,7 +531,7 @@ void mla_fwd_kernel(const FwdParams p) {
                           const TileLoad &tlv, const TileLoad &tlk) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr bool ISS = decltype(do_iss)::value;
-        constexpr int n0 = PV ? 0 : 16, n1 = QK ? 40 : 16;
+        constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
         if (QK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -528,11 +557,11 @@ void mla_fwd_kernel(const FwdParams p) {
                 ring[(n + PREFETCH - n0) % (PREFETCH + 1)] = load_operand(sv, sk, n + PREFETCH, knb, krb, vtb);
             __builtin_amdgcn_sched_barrier(0);
             const vec8 a = ring[(n - n0) % (PREFETCH + 1)];
-            if (n < 16) {
-                o[n & 3] = T::mfma(a, pb[n >> 2], o[n & 3]);
+            if (n < NV) {
+                o[n % NDB] = T::mfma(a, pb[n / NDB], o[n % NDB]);
             } else {
-                const int ks = (n - 16) >> 1, kb = (n - 16) & 1;
-                s[kb] = T::mfma(a, ks < 8 ? qreg[ks] : qr[ks - 8], s[kb]);
+                const int ks = (n - NV) >> 1, kb = (n - NV) & 1;
+                s[kb] = T::mfma(a, ks < NKS ? qreg[ks] : qr[ks - NKS], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (ISS && (n - n0) % LOAD_SPACING == 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
@@ -589,7 +618,7 @@ void mla_fwd_kernel(const FwdParams p) {
             const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
             m_run = m_new;
@@ -716,30 +745,32 @@ void mla_fwd_kernel(const FwdParams p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     block_sync();
     {
-        // staging row sr = 32 * slot + r32 (256 bytes: d 0..127), 16-byte
-        // chunk c (8 values of d) at c ^ (sr & 15); a wave writes and reads
-        // back only its own 32 rows
+        // staging row sr = 32 * slot + r32 (DN * 2 bytes), 16-byte chunk c (8
+        // values of d) at c ^ row_swizzle(sr); a wave writes and reads back
+        // only its own 32 rows
         const int sr = slot * 32 + r32;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 typename T::vec4 v4;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) v4[jj] = static_cast<typename T::scalar>(o[db][4 * i + jj] * inv);
-                *reinterpret_cast<typename T::vec4 *>(smem + sr * 256 + (((4 * db + i) ^ (sr & 15)) << 4) + g * 8) =
-                    v4;
+                *reinterpret_cast<typename T::vec4 *>(smem + sr * KN_ROW +
+                                                      (((4 * db + i) ^ row_swizzle<DN>(sr)) << 4) + g * 8) = v4;
             }
         const int rows = max(0, min(32, q_len - row0));
         const int64_t tok = (int64_t)seq.q_off + row0;
         const i32x4 ro = make_rsrc(static_cast<unsigned char *>(p.out) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
-        const int ch = lane & 15;
+        constexpr int CPR = DN / 8;      // 16-byte chunks of a row
+        constexpr int RPI = 64 / CPR;    // rows one instruction stores
+        const int ch = lane % CPR;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int r = 4 * k + (lane >> 4);  // row of the wave
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int r = RPI * k + lane / CPR;  // row of the wave
             const int srr = slot * 32 + r;
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + srr * 256 + ((ch ^ (srr & 15)) << 4));
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + srr * KN_ROW + ((ch ^ row_swizzle<DN>(srr)) << 4));
             mla_raw_buffer_store_b128(v, ro, (uint32_t)r * H * DN * 2 + ch * 16, 0, 0);
         }
     }
@@ -751,12 +782,22 @@ hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t
     if (p.n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)p.n_tasks);
     dim3 block(FWD_THREADS);
-    if (dtype == 2) {
-        if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false>), grid, block, 0, stream, p);
+    if (p.head_dim == 64) {
+        if (dtype == 2) {
+            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true, 64>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false, 64>), grid, block, 0, stream, p);
+        } else {
+            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true, 64>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false, 64>), grid, block, 0, stream, p);
+        }
     } else {
-        if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false>), grid, block, 0, stream, p);
+        if (dtype == 2) {
+            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true, 128>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false, 128>), grid, block, 0, stream, p);
+        } else {
+            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true, 128>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false, 128>), grid, block, 0, stream, p);
+        }
     }
     return hipGetLastError();
 }

@@ -98,8 +98,11 @@ def test_validation_errors(mutate, status):
     assert mla.mla_last_error() != ""
 
 
-def test_unsupported_head_dim_after_shape_checks():
-    assert status_of(tensors(d=64)) == "MLA_ERR_UNSUPPORTED"
+def test_head_dims_64_and_128_only_after_shape_checks():
+    assert status_of(tensors(d=64)) == "MLA_OK"
+    assert status_of(tensors(d=128)) == "MLA_OK"
+    for d in (32, 96, 192, 256):
+        assert status_of(tensors(d=d)) == "MLA_ERR_UNSUPPORTED"
 
 
 def test_mask_ignored_unless_mask_free():
