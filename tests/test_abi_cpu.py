@@ -425,3 +425,4 @@ def test_prolog_validation_errors():
     assert prolog_status(h=192) == ERR_UNSUP
     # 2-D q_out is accepted
     assert prolog_status(q_out=torch.zeros(0, 1024, dtype=torch.bfloat16)) == 0
+
