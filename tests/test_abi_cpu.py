@@ -426,3 +426,16 @@ def test_prolog_validation_errors():
     # 2-D q_out is accepted
     assert prolog_status(q_out=torch.zeros(0, 1024, dtype=torch.bfloat16)) == 0
 
+
+
+def test_gather_batch_limit():
+    # the gather kernel keeps the batch's offsets in LDS: 8192 sequences at most
+    def args(batch):
+        return gather_args(block_tables=torch.zeros(batch, 1, dtype=torch.int32),
+                           context_lens=torch.zeros(batch, dtype=torch.int32),
+                           key=torch.zeros(0, 2, 16, dtype=torch.bfloat16),
+                           value=torch.zeros(0, 2, 16, dtype=torch.bfloat16))
+    mla.paged_cache_load(**args(8192), stream=0)  # valid; zero tokens, nothing launched
+    with pytest.raises(mla.MlaError) as e:
+        mla.paged_cache_load(**args(8193), stream=0)
+    assert e.value.status == "MLA_ERR_UNSUPPORTED"
