@@ -373,6 +373,10 @@ void mla_fwd_kernel(const FwdParams p) {
     // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
     // 2dg + (j >> 1).
     constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
+    // every load of a matrix block has an MFMA slot, and a V^T piece never
+    // reads a staging register after its reload was issued (see mfma_block)
+    static_assert(LOADS_PER_BLOCK * LOAD_SPACING <= NV + 2 * (NKS + 4), "matrix block too short for its loads");
+    static_assert(LOAD_SPACING >= 4, "V loads would overtake the V^T pieces");
     auto issue_k = [&](const TileLoad &tl, int i) __attribute__((always_inline)) {
         const int wofs = wave * 64 * 16;
         if (i < KN_LOADS)
@@ -399,21 +403,24 @@ void mla_fwd_kernel(const FwdParams p) {
     // so the 4(dg & 1) part goes into the base.)
     const uint32_t vw_base = KN_BYTES + KR_BYTES + dg * (CPT * 1024) +
                              (((kp >> 2) ^ (CPT == 1 ? 4 * (dg & 1) : 0)) << 4) + (kp & 3) * 4;
+    // piece q = 4h + dd of the V^T write: dword dd of chunk pair h, keys
+    // 2kp (vst[2h]) and 2kp + 1 (vst[2h + 1]) -> two V^T rows
+    constexpr int VT_PIECES = 4 * CPT;
+    auto write_vt_piece = [&](unsigned char *st, uint32_t vwb, int q, const uint4 *vst)
+                              __attribute__((always_inline)) {
+        const int h = q >> 2, dd = q & 3;
+        const unsigned a = reinterpret_cast<const unsigned *>(&vst[2 * h])[dd];
+        const unsigned b = reinterpret_cast<const unsigned *>(&vst[2 * h + 1])[dd];
+        const uint32_t w = (vwb ^ ((4 * h + dd) << 4)) + h * 1024 + dd * 256;
+        *reinterpret_cast<unsigned *>(st + w) = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        *reinterpret_cast<unsigned *>(st + w + 128) = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    };
     auto write_vt = [&](int kt, const uint4 *vst) __attribute__((always_inline)) {
         unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
         uint32_t vwb = vw_base;
         asm volatile("" : "+v"(vwb));
 #pragma unroll
-        for (int h = 0; h < CPT; ++h) {
-            const unsigned a[4] = {vst[2 * h].x, vst[2 * h].y, vst[2 * h].z, vst[2 * h].w};  // key 2kp
-            const unsigned b[4] = {vst[2 * h + 1].x, vst[2 * h + 1].y, vst[2 * h + 1].z, vst[2 * h + 1].w};
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd) {
-                const uint32_t w = (vwb ^ ((4 * h + dd) << 4)) + h * 1024 + dd * 256;
-                *reinterpret_cast<unsigned *>(st + w) = __builtin_amdgcn_perm(b[dd], a[dd], 0x05040100u);
-                *reinterpret_cast<unsigned *>(st + w + 128) = __builtin_amdgcn_perm(b[dd], a[dd], 0x07060302u);
-            }
-        }
+        for (int q = 0; q < VT_PIECES; ++q) write_vt_piece(st, vwb, q, vst);
     };
 
     // Loads of a tile past the last one have no valid rows (they return
@@ -527,8 +534,15 @@ void mla_fwd_kernel(const FwdParams p) {
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
     // stage sk); either half may be switched off. Operands are read ahead.
     // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING MFMAs
+    // With ISS the block also writes V^T of the tile staged in vstage into
+    // stage vt_st, one piece after each of its first MFMAs; a burst of these
+    // writes ahead of the block held back its first MFMA. Tile loads go out
+    // after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...: V load 2h, which
+    // refills vstage[2h], then comes after the pieces that read vstage[2h] and
+    // vstage[2h + 1] (the first 4h + 4 MFMAs).
     auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
-                          const TileLoad &tlv, const TileLoad &tlk) __attribute__((always_inline)) {
+                          const TileLoad &tlv, const TileLoad &tlk, unsigned char *vt_st)
+                          __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr bool ISS = decltype(do_iss)::value;
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
@@ -538,8 +552,9 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
         }
-        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, qrb = qr_base;
+        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, qrb = qr_base, vwb = vw_base;
         asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb), "+v"(qrb));
+        if (ISS) asm volatile("" : "+v"(vwb));
         // Q-rope operands first: LDS returns in order, so they have landed by
         // the time the first ring operand is waited for
         vec8 qr[4];
@@ -564,7 +579,11 @@ void mla_fwd_kernel(const FwdParams p) {
                 s[kb] = T::mfma(a, ks < NKS ? qreg[ks] : qr[ks - NKS], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ISS && (n - n0) % LOAD_SPACING == 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
+            if (ISS && n - n0 < VT_PIECES) {
+                write_vt_piece(vt_st, vwb, n - n0, vstage);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (ISS && (n - n0) % LOAD_SPACING == LOAD_SPACING - 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
                 issue_part(tlv, tlk, (n - n0) / LOAD_SPACING, vstage);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -575,13 +594,11 @@ void mla_fwd_kernel(const FwdParams p) {
     // probabilities -> pb, row sums.
     const float inv_c = 1.f / c;
     auto valu_block = [&](int kt) __attribute__((always_inline)) {
-        float mx = -INFINITY;
-        if (wave_full(kt)) {
-            float m4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-            for (int t = 0; t < 32; ++t) m4[t & 3] = fmaxf(m4[t & 3], s[t >> 4][t & 15]);
-            mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
-        } else {
+        // The mask (only on tiles that cut the wave's rows) rewrites the scores
+        // in place; the row max is then common code. With the max inside each
+        // branch the compiler gave the two paths different registers and
+        // copied all 32 scores at the merge.
+        if (!wave_full(kt)) {
             const int key0 = kt * BN;
             const unsigned short *mrow = nullptr;
             if (mask_type == MASK_FREE)
@@ -605,12 +622,13 @@ void mla_fwd_kernel(const FwdParams p) {
                             x += mv * LOG2E * inv_c;
                         }
                     }
-                    x = vis ? x : -INFINITY;
-                    s[kb][e] = x;
-                    mx = fmaxf(mx, x);
+                    s[kb][e] = vis ? x : -INFINITY;
                 }
         }
-        mx = max_with_partner(mx);
+        float m4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+        for (int t = 4; t < 32; ++t) m4[t & 3] = fmaxf(m4[t & 3], s[t >> 4][t & 15]);
+        const float mx = max_with_partner(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
         // move the running max only if some row of the wave rose past the threshold
         const bool need = (mx - m_run) * c > RESCALE_THRESHOLD;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -627,14 +645,15 @@ void mla_fwd_kernel(const FwdParams p) {
         // probabilities, rounded to the input dtype for the PV product; the row
         // sum adds them in fp32 (plain adds: the dot2 instructions would queue
         // behind the other wave's MFMAs), in four independent partial sums
-        float lsum[4] = {0.f, 0.f, 0.f, 0.f};
+        float lsum[4];
 #pragma unroll
         for (int t = 0; t < 32; t += 2) {
             const int kb = t >> 4, e = t & 15;
             const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
             const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -mc));
             const typename T::pair pr = T::pack(p0, p1);
-            lsum[(t >> 1) & 3] += p0 + p1;
+            if (t < 8) lsum[t >> 1] = p0 + p1;
+            else lsum[(t >> 1) & 3] += p0 + p1;
             pb[kb * 2 + (e >> 3)][e & 7] = pr[0];
             pb[kb * 2 + (e >> 3)][(e & 7) + 1] = pr[1];
         }
@@ -655,9 +674,9 @@ void mla_fwd_kernel(const FwdParams p) {
     // and a last interval in which the trailing group does PV of the last tile.
     // Tile t's K DMA goes out during interval 2t-4 and its V loads during
     // interval 2t-2 (both from the leading group's matrix block); both are
-    // waited for at the end of interval 2t-1; V^T is written at the start of
-    // interval 2t; K is first read in interval 2t, V^T in interval 2t+2. The
-    // K DMA of tile t overwrites only the K half of a stage, whose last reader
+    // waited for at the end of interval 2t-1; V^T is written during the leading
+    // group's matrix block of interval 2t; K is first read in interval 2t, V^T
+    // in interval 2t+2. The K DMA of tile t overwrites only the K half of a stage, whose last reader
     // (trailing scores of tile t-3) finished in interval 2t-5.
     // A wave's visible tiles are a prefix of the tile range, so a matrix block
     // runs whenever its PV tile is visible; scores it computes for a tile the
@@ -688,21 +707,20 @@ void mla_fwd_kernel(const FwdParams p) {
             // out two intervals earlier); K of tile j+2 may still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
         } else {
-            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none);
+            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none, nullptr);
         }
         block_sync();
         // interval 2j + 2: the leading group writes V^T of tile j+1 and sends
         // out V of tile j+2 and K of tile j+3 during its matrix block
         if (lead) {
-            write_vt(j + 1, vstage);
             mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2, row_v),
-                       prep_tile(j + 3, row_k));
+                       prep_tile(j + 3, row_k), smem + rnext * STAGE_BYTES);
         } else {
             if (wave_active(j)) valu_block(j);
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -712,7 +730,7 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr);
         block_sync();
         if (wave_active(0)) valu_block(0);
         for (int j = 1; j < n_kt; j += STAGES) {
@@ -723,9 +741,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none, nullptr);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none, nullptr);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none, nullptr);
         }
     } else {
         block_sync();
