@@ -546,6 +546,9 @@ void mla_fwd_kernel(const FwdParams p) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr bool ISS = decltype(do_iss)::value;
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
+        // the wave feeding the matrix core wins issue arbitration against the
+        // other wave of its SIMD, which runs a vector block meanwhile
+        __builtin_amdgcn_s_setprio(1);
         if (QK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -588,6 +591,7 @@ void mla_fwd_kernel(const FwdParams p) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- vector block for tile kt: mask (if needed), row max, lazy rescale,
