@@ -69,17 +69,17 @@ constexpr int STAGES = 3;
 constexpr int LOAD_SPACING = MLA_LOAD_SPACING;  // MFMAs between the tile loads a matrix block issues
 constexpr int PREFETCH = MLA_PREFETCH;  // LDS operands in flight ahead of the MFMA using them
 constexpr int KR_BYTES = BN * DR * 2;  // 8 KB
-constexpr int QR_BYTES = BM * DR * 2;  // 32 KB
 // LDS of a head dim D (embeddimV: 64 or 128). A ring stage holds K-nope
-// (64 keys x D), K-rope (64 x 64) and V^T (D x 64 keys); Q-rope of the
-// workgroup's rows follows the ring. D = 128: 40 KB stages, 152 KB in all.
+// (64 keys x D), K-rope (64 x 64) and V^T (D x 64 keys); two buffers of raw
+// V tiles (64 keys x D, as loaded) follow the ring. D = 128: 40 KB stages,
+// 152 KB in all.
 template <int D>
 struct Geom {
     static constexpr int KN_BYTES = BN * D * 2;
     static constexpr int V_BYTES = BN * D * 2;
     static constexpr int STAGE_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
-    static constexpr int QR_OFFSET = STAGES * STAGE_BYTES;
-    static constexpr int LDS_BYTES = QR_OFFSET + QR_BYTES;
+    static constexpr int VRAW_OFFSET = STAGES * STAGE_BYTES;
+    static constexpr int LDS_BYTES = VRAW_OFFSET + 2 * V_BYTES;
 };
 // 16-byte chunk swizzle of an LDS row of D * 2 bytes (K-nope rows, output
 // staging rows): chunk c of row r sits at c ^ swz(r), which makes the 16-byte
@@ -202,7 +202,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_
 void mla_fwd_kernel(const FwdParams p) {
     constexpr int KN_BYTES = Geom<DN>::KN_BYTES;
     constexpr int STAGE_BYTES = Geom<DN>::STAGE_BYTES;
-    constexpr int QR_OFFSET = Geom<DN>::QR_OFFSET;
+    constexpr int VRAW_OFFSET = Geom<DN>::VRAW_OFFSET;
+    constexpr int V_BYTES = Geom<DN>::V_BYTES;
     constexpr int LDS_BYTES = Geom<DN>::LDS_BYTES;
     constexpr int KN_ROW = DN * 2;      // LDS bytes of a K-nope row
     constexpr int NKS = DN / 16;        // k-steps of the nope product
@@ -210,6 +211,7 @@ void mla_fwd_kernel(const FwdParams p) {
     constexpr int NV = 4 * NDB;         // V^T operands of a matrix block (4 key steps x NDB)
     constexpr int KN_LOADS = DN / 32;   // K-nope DMA per leading thread and tile
     constexpr int CPT = DN / 64;        // V column chunk pairs per leading thread
+    constexpr int V_LOADS_ = 2 * CPT;   // raw V DMA per leading thread and tile
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)];
     typedef typename T::vec8 vec8;
 
@@ -262,27 +264,17 @@ void mla_fwd_kernel(const FwdParams p) {
         for (int ks = 0; ks < NKS; ++ks)
             qreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rq, qo + ks * 32, 0, 0));
     }
-    // ---- Q-rope of the workgroup's 256 rows -> LDS (DMA). LDS row 32 s + r
-    // holds row r of slot s; rows are swizzled by 16-byte chunk: chunk c of LDS
-    // row L sits at c ^ ((L >> 1) & 7). Rows past the sequence end read as 0.
+    // ---- Q-rope^T operand likewise (4 more k-steps of 16)
+    vec8 qrreg[4];
     {
-        const int rows = max(0, min(BM >> ps, q_len - item.q_row0));
-        const int64_t tok = (int64_t)seq.q_off + item.q_row0;
-        const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) +
-                                       (tok * H + task.head) * (DR * 2),
+        const int rows = max(0, min(32, q_len - row0));
+        const int64_t tok = (int64_t)seq.q_off + row0;
+        const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
                                    (uint32_t)rows * H * DR * 2);
+        const uint32_t qo = (uint32_t)r32 * H * DR * 2 + g * 16;
 #pragma unroll
-        for (int u = 0; u < QR_BYTES / (NT * 16); ++u) {
-            const int ld = tid + NT * u;  // 16-byte LDS chunk
-            const int r = ld >> 3;        // LDS row
-            const int sl = r >> 5;        // its slot
-            const int src_row = (sl >> ps) * 32 + (r & 31);
-            const int src_head = sl & ((1 << ps) - 1);
-            const uint32_t src = ((uint32_t)src_row * H + src_head) * (DR * 2) +
-                                 ((((ld & 7) ^ ((r >> 1) & 7))) << 4);
-            mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(smem + QR_OFFSET + u * NT * 16 + wave * 64 * 16), 16, src,
-                                    0, 0, 0);
-        }
+        for (int ks = 0; ks < 4; ++ks)
+            qrreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rr, qo + ks * 32, 0, 0));
     }
 
     // ---- paged K/V: first cache row of each key tile of the sequence (block
@@ -337,14 +329,25 @@ void mla_fwd_kernel(const FwdParams p) {
         const int m = slot >> 3;
         off_kr[u] = perm_key(m) * kr_row + (((slot & 7) ^ ((m >> 1) & 7)) << 4);
     }
-    const int kp = tid & 31, dg = (tid >> 5) & 7;
-    // two VGPR offsets (the buffer range check covers the VGPR offset and the
-    // immediate, not the SGPR offset, so the key step must not go there)
-    const uint32_t off_v[2] = {(uint32_t)(2 * kp) * kn_row + dg * CPT * 16,
-                               (uint32_t)(2 * kp + 1) * kn_row + dg * CPT * 16};
+    // Raw V tiles land by DMA in one of two LDS buffers (tile kt in buffer
+    // kt % 2) in their global row order; 16-byte chunk c of key row m sits at
+    // chunk position c ^ vswz(m), so that the transposing reads below, 16 keys
+    // of one chunk per quarter wave, are conflict-free (D = 128). Load j of a
+    // leading thread fills LDS slot j * LT + tid of the buffer.
+    const int kp = tid & 31, dg = (tid >> 5) & 7;  // V^T writer: keys 2kp, 2kp + 1; column chunks of dg
+    constexpr int CPR = DN / 8;  // 16-byte chunks of a V row
+    auto vswz = [](int m) { return (m >> 1) & (CPR - 1); };
+    uint32_t off_vr[V_LOADS_];
+#pragma unroll
+    for (int u = 0; u < V_LOADS_; ++u) {
+        const int slot = tid + LT * u;
+        const int m = slot / CPR;
+        off_vr[u] = m * kn_row + (((slot % CPR) ^ vswz(m)) << 4);
+    }
     struct TileLoad {
         i32x4 rk, rr, rv;
-        unsigned char *st;
+        unsigned char *st;  // ring stage
+        unsigned char *vr;  // raw V buffer
     };
     // paged: first cache row of tile kt (-1: none), read from the LDS table
     // ahead of prep_tile so the read's latency stays off the matrix block
@@ -367,16 +370,16 @@ void mla_fwd_kernel(const FwdParams p) {
         tl.rr = make_rsrc(krbase + rowi * (DR * 2), nvalid * kr_row);
         tl.rv = make_rsrc(vbase + rowi * (DN * 2), nvalid * kn_row);
         tl.st = smem + (kt % STAGES) * STAGE_BYTES;
+        tl.vr = smem + VRAW_OFFSET + (kt & 1) * V_BYTES;
         return tl;
     };
     // A leading thread's loads of a tile: six K DMA (K_LOADS) and four V loads
     // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
     // 2dg + (j >> 1).
     constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
-    // every load of a matrix block has an MFMA slot, and a V^T piece never
-    // reads a staging register after its reload was issued (see mfma_block)
+    // every load of a matrix block has an MFMA slot
     static_assert(LOADS_PER_BLOCK * LOAD_SPACING <= NV + 2 * (NKS + 4), "matrix block too short for its loads");
-    static_assert(LOAD_SPACING >= 4, "V loads would overtake the V^T pieces");
+    static_assert(V_LOADS * LT * 16 == V_BYTES, "raw V DMA must fill the buffer");
     auto issue_k = [&](const TileLoad &tl, int i) __attribute__((always_inline)) {
         const int wofs = wave * 64 * 16;
         if (i < KN_LOADS)
@@ -385,14 +388,25 @@ void mla_fwd_kernel(const FwdParams p) {
             mla_raw_buffer_load_lds(tl.rr, (lds_u32_ptr)(tl.st + KN_BYTES + (i - KN_LOADS) * LT * 16 + wofs), 16,
                                     off_kr[i - KN_LOADS], 0, 0, 0);
     };
-    auto issue_v = [&](const TileLoad &tl, int j, uint4 *vst) __attribute__((always_inline)) {
-        vst[j] = __builtin_bit_cast(uint4, mla_raw_buffer_load_b128(tl.rv, off_v[j & 1] + (j >> 1) * 16, 0, 0));
+    auto issue_v = [&](const TileLoad &tl, int j) __attribute__((always_inline)) {
+        mla_raw_buffer_load_lds(tl.rv, (lds_u32_ptr)(tl.vr + j * LT * 16 + wave * 64 * 16), 16, off_vr[j], 0, 0,
+                                0);
     };
     // load i of a matrix block: V of tile tv first (it has the shorter way to
     // go), then K of tile tk
-    auto issue_part = [&](const TileLoad &tv, const TileLoad &tk, int i, uint4 *vst) __attribute__((always_inline)) {
-        if (i < V_LOADS) issue_v(tv, i, vst);
+    auto issue_part = [&](const TileLoad &tv, const TileLoad &tk, int i) __attribute__((always_inline)) {
+        if (i < V_LOADS) issue_v(tv, i);
         else issue_k(tk, i - V_LOADS);
+    };
+    // The transposing read: a leading thread (kp, dg) takes the 16-byte chunks
+    // it writes as V^T below from a raw buffer; chunk j is key 2kp + (j & 1),
+    // column chunk CPT dg + (j >> 1).
+    auto read_vraw = [&](const unsigned char *vr, uint4 *vst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < V_LOADS; ++j) {
+            const int m = 2 * kp + (j & 1), cc = CPT * dg + (j >> 1);
+            vst[j] = *reinterpret_cast<const uint4 *>(vr + m * (DN * 2) + ((cc ^ vswz(m)) << 4));
+        }
     };
     // V^T region of a stage: row d (128 B = 64 keys), 16-byte chunk c (8 keys)
     // at position c ^ ((d >> 1) & 7). A leading thread writes the dwords
@@ -424,50 +438,50 @@ void mla_fwd_kernel(const FwdParams p) {
     };
 
     // Loads of a tile past the last one have no valid rows (they return
-    // zeros) and land in a ring stage no longer read, so the leading group
-    // issues them unconditionally: one code path keeps the V registers in
-    // place across the loop.
+    // zeros) and land in a ring stage or raw buffer no longer read, so the
+    // leading group issues them unconditionally.
     // Tile t's K goes out four intervals before its first scores (a stage's K
     // region is free once the trailing group has scored the tile before), its V
-    // two intervals before V^T is written (the staging registers are free once
-    // V^T of tile t-1 is written).
-    uint4 vstage[V_LOADS];
+    // two intervals before V^T is written (raw buffer t % 2 is free once V^T of
+    // tile t-2 is written).
     if (grp == 0) {
-        uint4 v0[V_LOADS];
         const TileLoad t0 = prep_tile(0, cache_row(0)), t1 = prep_tile(1, cache_row(1)),
                        t2 = prep_tile(2, cache_row(2));
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
 #pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j, v0);
+        for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j);
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
 #pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) issue_v(t1, j, vstage);
+        for (int j = 0; j < V_LOADS; ++j) issue_v(t1, j);
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t2, i);
         // tile 0, Q and Q-rope landed; K and V of tile 1 and K of tile 2 may still fly
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS + V_LOADS));
-        write_vt(0, v0);
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
     }
+    // raw V of tile 0 came from other threads' DMA: publish it, then the
+    // leading group writes V^T of tile 0 (the barrier before the schedule
+    // publishes that)
+    block_sync();
+    if (grp == 0) {
+        uint4 v0[V_LOADS];
+        read_vraw(smem + VRAW_OFFSET, v0);
+        write_vt(0, v0);
+    }
 
     // A negative scale is folded into Q so the row max can be taken on raw
-    // scores: Q-nope is negated in registers, Q-rope in LDS (each thread flips
-    // the chunks its own DMA wrote; the barrier before the schedule publishes them).
+    // scores: Q-nope and Q-rope are negated in registers.
     const float c = fabsf(p.scale_log2);
     if (p.scale_log2 < 0.f) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            i32x4 w = __builtin_bit_cast(i32x4, qreg[ks]);
+        for (int ks = 0; ks < NKS + 4; ++ks) {
+            vec8 &q = ks < NKS ? qreg[ks] : qrreg[ks - NKS];
+            i32x4 w = __builtin_bit_cast(i32x4, q);
             w ^= (int)0x80008000;
-            qreg[ks] = __builtin_bit_cast(vec8, w);
-        }
-#pragma unroll
-        for (int u = 0; u < QR_BYTES / (NT * 16); ++u) {
-            i32x4 *q = reinterpret_cast<i32x4 *>(smem + QR_OFFSET + (u * NT + tid) * 16);
-            *q ^= (int)0x80008000;
+            q = __builtin_bit_cast(vec8, w);
         }
     }
 
@@ -496,12 +510,9 @@ void mla_fwd_kernel(const FwdParams p) {
     // the bases (one VALU op per read) instead of keeping 24 of them live.
     //  K-nope (A of S^T): tile row kb*32 + r32, chunk 2*ks + g, swizzle ^ (row & 15)
     //  K-rope:            row kb*32 + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
-    //  Q-rope (B):        LDS row 32*slot + r32, chunk 2*ks + g, swizzle ^ ((row >> 1) & 7)
     //  V^T (A of O^T):    row d = 32*db + r32, chunk 2*st4 + g, swizzle ^ ((d >> 1) & 7)
     const uint32_t kn_base = r32 * KN_ROW + ((g ^ row_swizzle<DN>(r32)) << 4);
     const uint32_t kr_base = KN_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
-    const int qr_row = slot * 32 + r32;
-    const uint32_t qr_base = QR_OFFSET + qr_row * 128 + ((g ^ ((qr_row >> 1) & 7)) << 4);
     const uint32_t vt_base = KN_BYTES + KR_BYTES + r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
 
     auto lds16 = [](const unsigned char *a) __attribute__((always_inline)) -> vec8 {
@@ -533,16 +544,15 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
     // stage sk); either half may be switched off. Operands are read ahead.
-    // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING MFMAs
-    // With ISS the block also writes V^T of the tile staged in vstage into
-    // stage vt_st, one piece after each of its first MFMAs; a burst of these
-    // writes ahead of the block held back its first MFMA. Tile loads go out
-    // after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...: V load 2h, which
-    // refills vstage[2h], then comes after the pieces that read vstage[2h] and
-    // vstage[2h + 1] (the first 4h + 4 MFMAs).
+    // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING
+    // MFMAs (after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...). With ISS
+    // the block also transposes the raw V tile in buffer vt_src into V^T of
+    // stage vt_st: the raw chunks are read ahead of the first MFMA, and the V^T
+    // writes go out one piece after each of the first MFMAs; a burst of these
+    // writes ahead of the block held back its first MFMA.
     auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
-                          const TileLoad &tlv, const TileLoad &tlk, unsigned char *vt_st)
-                          __attribute__((always_inline)) {
+                          const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src,
+                          unsigned char *vt_st) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr bool ISS = decltype(do_iss)::value;
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
@@ -555,16 +565,13 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
         }
-        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, qrb = qr_base, vwb = vw_base;
-        asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb), "+v"(qrb));
+        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, vwb = vw_base;
+        asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb));
         if (ISS) asm volatile("" : "+v"(vwb));
-        // Q-rope operands first: LDS returns in order, so they have landed by
-        // the time the first ring operand is waited for
-        vec8 qr[4];
-        if (QK) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qr[ks] = lds16(smem + (qrb ^ (ks << 5)));
-        }
+        // raw V chunks first: LDS returns in order, so they have landed by the
+        // time the first ring operand is waited for
+        uint4 vst[V_LOADS];
+        if (ISS) read_vraw(vt_src, vst);
         vec8 ring[PREFETCH + 1];
 #pragma unroll
         for (int d = 0; d < PREFETCH; ++d)
@@ -579,15 +586,15 @@ void mla_fwd_kernel(const FwdParams p) {
                 o[n % NDB] = T::mfma(a, pb[n / NDB], o[n % NDB]);
             } else {
                 const int ks = (n - NV) >> 1, kb = (n - NV) & 1;
-                s[kb] = T::mfma(a, ks < NKS ? qreg[ks] : qr[ks - NKS], s[kb]);
+                s[kb] = T::mfma(a, ks < NKS ? qreg[ks] : qrreg[ks - NKS], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (ISS && n - n0 < VT_PIECES) {
-                write_vt_piece(vt_st, vwb, n - n0, vstage);
+                write_vt_piece(vt_st, vwb, n - n0, vst);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (ISS && (n - n0) % LOAD_SPACING == LOAD_SPACING - 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
-                issue_part(tlv, tlk, (n - n0) / LOAD_SPACING, vstage);
+                issue_part(tlv, tlk, (n - n0) / LOAD_SPACING);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -711,20 +718,21 @@ void mla_fwd_kernel(const FwdParams p) {
             // out two intervals earlier); K of tile j+2 may still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
         } else {
-            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none, nullptr);
+            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none, nullptr, nullptr);
         }
         block_sync();
         // interval 2j + 2: the leading group writes V^T of tile j+1 and sends
         // out V of tile j+2 and K of tile j+3 during its matrix block
         if (lead) {
             mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2, row_v),
-                       prep_tile(j + 3, row_k), smem + rnext * STAGE_BYTES);
+                       prep_tile(j + 3, row_k), smem + VRAW_OFFSET + ((j + 1) & 1) * V_BYTES,
+                       smem + rnext * STAGE_BYTES);
         } else {
             if (wave_active(j)) valu_block(j);
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr, nullptr);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -734,7 +742,7 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr, nullptr);
         block_sync();
         if (wave_active(0)) valu_block(0);
         for (int j = 1; j < n_kt; j += STAGES) {
@@ -745,9 +753,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none, nullptr);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none, nullptr);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none, nullptr);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none, nullptr, nullptr);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none, nullptr, nullptr);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none, nullptr, nullptr);
         }
     } else {
         block_sync();
