@@ -429,8 +429,10 @@ void mla_fwd_kernel(const FwdParams p) {
         *reinterpret_cast<unsigned *>(st + w) = __builtin_amdgcn_perm(b, a, 0x05040100u);
         *reinterpret_cast<unsigned *>(st + w + 128) = __builtin_amdgcn_perm(b, a, 0x07060302u);
     };
-    auto write_vt = [&](int kt, const uint4 *vst) __attribute__((always_inline)) {
-        unsigned char *st = smem + (kt % STAGES) * STAGE_BYTES;
+    // the transpose alone, for a trailing wave that runs no matrix block
+    auto transpose_v = [&](const unsigned char *vr, unsigned char *st) __attribute__((always_inline)) {
+        uint4 vst[V_LOADS];
+        read_vraw(vr, vst);
         uint32_t vwb = vw_base;
         asm volatile("" : "+v"(vwb));
 #pragma unroll
@@ -461,15 +463,6 @@ void mla_fwd_kernel(const FwdParams p) {
         __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS + V_LOADS));
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
-    }
-    // raw V of tile 0 came from other threads' DMA: publish it, then the
-    // leading group writes V^T of tile 0 (the barrier before the schedule
-    // publishes that)
-    block_sync();
-    if (grp == 0) {
-        uint4 v0[V_LOADS];
-        read_vraw(smem + VRAW_OFFSET, v0);
-        write_vt(0, v0);
     }
 
     // A negative scale is folded into Q so the row max can be taken on raw
@@ -545,16 +538,16 @@ void mla_fwd_kernel(const FwdParams p) {
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
     // stage sk); either half may be switched off. Operands are read ahead.
     // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING
-    // MFMAs (after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...). With ISS
-    // the block also transposes the raw V tile in buffer vt_src into V^T of
-    // stage vt_st: the raw chunks are read ahead of the first MFMA, and the V^T
-    // writes go out one piece after each of the first MFMAs; a burst of these
-    // writes ahead of the block held back its first MFMA.
+    // MFMAs (after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...). VT:
+    // transpose the raw V tile in buffer vt_src into V^T of stage vt_st: the
+    // raw chunks are read ahead of the first MFMA, and the V^T writes go out
+    // one piece after each of the first MFMAs (a burst of these writes ahead
+    // of the block held back its first MFMA).
     auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
-                          const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src,
+                          auto do_vt, const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src,
                           unsigned char *vt_st) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
-        constexpr bool ISS = decltype(do_iss)::value;
+        constexpr bool ISS = decltype(do_iss)::value, VT = decltype(do_vt)::value;
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
         // the wave feeding the matrix core wins issue arbitration against the
         // other wave of its SIMD, which runs a vector block meanwhile
@@ -567,11 +560,11 @@ void mla_fwd_kernel(const FwdParams p) {
         }
         uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, vwb = vw_base;
         asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb));
-        if (ISS) asm volatile("" : "+v"(vwb));
+        if (VT) asm volatile("" : "+v"(vwb));
         // raw V chunks first: LDS returns in order, so they have landed by the
         // time the first ring operand is waited for
         uint4 vst[V_LOADS];
-        if (ISS) read_vraw(vt_src, vst);
+        if (VT) read_vraw(vt_src, vst);
         vec8 ring[PREFETCH + 1];
 #pragma unroll
         for (int d = 0; d < PREFETCH; ++d)
@@ -589,7 +582,7 @@ void mla_fwd_kernel(const FwdParams p) {
                 s[kb] = T::mfma(a, ks < NKS ? qreg[ks] : qrreg[ks - NKS], s[kb]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (ISS && n - n0 < VT_PIECES) {
+            if (VT && n - n0 < VT_PIECES) {
                 write_vt_piece(vt_st, vwb, n - n0, vst);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -683,12 +676,15 @@ void mla_fwd_kernel(const FwdParams p) {
     //   2j+1: leading: vector block j        trailing: PV j-1 + scores j
     //   2j+2: leading: PV j + scores j+1     trailing: vector block j
     // and a last interval in which the trailing group does PV of the last tile.
-    // Tile t's K DMA goes out during interval 2t-4 and its V loads during
-    // interval 2t-2 (both from the leading group's matrix block); both are
-    // waited for at the end of interval 2t-1; V^T is written during the leading
-    // group's matrix block of interval 2t; K is first read in interval 2t, V^T
-    // in interval 2t+2. The K DMA of tile t overwrites only the K half of a stage, whose last reader
-    // (trailing scores of tile t-3) finished in interval 2t-5.
+    // Tile t's K DMA goes out during interval 2t-4 and its raw V DMA during
+    // interval 2t-2 (both from the leading group's matrix block); the issuing
+    // threads wait for both at the end of interval 2t-1. The trailing group
+    // transposes raw V into V^T of tile t during its matrix block of interval
+    // 2t+1 (tile 0: interval 1). K is first read in interval 2t, V^T in
+    // interval 2t+2. The K DMA of tile t overwrites only the K half of a stage,
+    // whose last reader (trailing scores of tile t-3) finished in interval
+    // 2t-5; the V^T half was last read by P.V of tile t-3 in interval 2t-3;
+    // raw buffer t % 2 is refilled in interval 2t+2, after the transpose.
     // A wave's visible tiles are a prefix of the tile range, so a matrix block
     // runs whenever its PV tile is visible; scores it computes for a tile the
     // wave cannot see (or past the last tile) are dropped. Each group runs its
@@ -718,21 +714,26 @@ void mla_fwd_kernel(const FwdParams p) {
             // out two intervals earlier); K of tile j+2 may still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
         } else {
-            if (wave_active(j - 1)) mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, none, none, nullptr, nullptr);
+            // the trailing group writes V^T of tile j (its raw V landed at the
+            // end of interval 2j-1) with its matrix block, or alone
+            unsigned char *vr = smem + VRAW_OFFSET + (j & 1) * V_BYTES;
+            if (wave_active(j - 1))
+                mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, yes, none, none, vr, smem + r0 * STAGE_BYTES);
+            else
+                transpose_v(vr, smem + r0 * STAGE_BYTES);
         }
         block_sync();
-        // interval 2j + 2: the leading group writes V^T of tile j+1 and sends
-        // out V of tile j+2 and K of tile j+3 during its matrix block
+        // interval 2j + 2: the leading group sends out V of tile j+2 and K of
+        // tile j+3 during its matrix block
         if (lead) {
-            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, prep_tile(j + 2, row_v),
-                       prep_tile(j + 3, row_k), smem + VRAW_OFFSET + ((j + 1) & 1) * V_BYTES,
-                       smem + rnext * STAGE_BYTES);
+            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, no, prep_tile(j + 2, row_v),
+                       prep_tile(j + 3, row_k), nullptr, nullptr);
         } else {
             if (wave_active(j)) valu_block(j);
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr, nullptr);
+        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, no, none, none, nullptr, nullptr);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -742,7 +743,11 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, none, none, nullptr, nullptr);
+        // (and V^T of tile 0, whose raw V the barrier before the schedule published)
+        if (wave_active(0))
+            mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, yes, none, none, smem + VRAW_OFFSET, smem);
+        else
+            transpose_v(smem + VRAW_OFFSET, smem);
         block_sync();
         if (wave_active(0)) valu_block(0);
         for (int j = 1; j < n_kt; j += STAGES) {
@@ -753,9 +758,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, none, none, nullptr, nullptr);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, none, none, nullptr, nullptr);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, none, none, nullptr, nullptr);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, no, none, none, nullptr, nullptr);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, no, none, none, nullptr, nullptr);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, no, none, none, nullptr, nullptr);
         }
     } else {
         block_sync();
