@@ -94,6 +94,9 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MASK_UNDEFINED = 0;
 constexpr int MASK_FREE = 3;
 
+// which tile loads a matrix block issues
+constexpr int ISS_NONE = 0, ISS_K = 1, ISS_V = 2;
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -332,15 +335,16 @@ void mla_fwd_kernel(const FwdParams p) {
     // Raw V tiles land by DMA in one of two LDS buffers (tile kt in buffer
     // kt % 2) in their global row order; 16-byte chunk c of key row m sits at
     // chunk position c ^ vswz(m), so that the transposing reads below, 16 keys
-    // of one chunk per quarter wave, are conflict-free (D = 128). Load j of a
-    // leading thread fills LDS slot j * LT + tid of the buffer.
+    // of one chunk per quarter wave, are conflict-free (D = 128). Either group
+    // issues them: load j of thread i of a group (i = tid % LT) fills LDS slot
+    // j * LT + i of the buffer.
     const int kp = tid & 31, dg = (tid >> 5) & 7;  // V^T writer: keys 2kp, 2kp + 1; column chunks of dg
     constexpr int CPR = DN / 8;  // 16-byte chunks of a V row
     auto vswz = [](int m) { return (m >> 1) & (CPR - 1); };
     uint32_t off_vr[V_LOADS_];
 #pragma unroll
     for (int u = 0; u < V_LOADS_; ++u) {
-        const int slot = tid + LT * u;
+        const int slot = (tid & (LT - 1)) + LT * u;
         const int m = slot / CPR;
         off_vr[u] = m * kn_row + (((slot % CPR) ^ vswz(m)) << 4);
     }
@@ -376,9 +380,10 @@ void mla_fwd_kernel(const FwdParams p) {
     // A leading thread's loads of a tile: six K DMA (K_LOADS) and four V loads
     // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
     // 2dg + (j >> 1).
-    constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT, LOADS_PER_BLOCK = K_LOADS + V_LOADS;
+    constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT;
     // every load of a matrix block has an MFMA slot
-    static_assert(LOADS_PER_BLOCK * LOAD_SPACING <= NV + 2 * (NKS + 4), "matrix block too short for its loads");
+    static_assert(K_LOADS * LOAD_SPACING <= NV + 2 * (NKS + 4), "matrix block too short for its loads");
+    static_assert(V_LOADS * LOAD_SPACING <= 2 * (NKS + 4), "scores-only block too short for the V loads");
     static_assert(V_LOADS * LT * 16 == V_BYTES, "raw V DMA must fill the buffer");
     auto issue_k = [&](const TileLoad &tl, int i) __attribute__((always_inline)) {
         const int wofs = wave * 64 * 16;
@@ -389,14 +394,8 @@ void mla_fwd_kernel(const FwdParams p) {
                                     off_kr[i - KN_LOADS], 0, 0, 0);
     };
     auto issue_v = [&](const TileLoad &tl, int j) __attribute__((always_inline)) {
-        mla_raw_buffer_load_lds(tl.rv, (lds_u32_ptr)(tl.vr + j * LT * 16 + wave * 64 * 16), 16, off_vr[j], 0, 0,
-                                0);
-    };
-    // load i of a matrix block: V of tile tv first (it has the shorter way to
-    // go), then K of tile tk
-    auto issue_part = [&](const TileLoad &tv, const TileLoad &tk, int i) __attribute__((always_inline)) {
-        if (i < V_LOADS) issue_v(tv, i);
-        else issue_k(tk, i - V_LOADS);
+        mla_raw_buffer_load_lds(tl.rv, (lds_u32_ptr)(tl.vr + j * LT * 16 + (wave & 3) * 64 * 16), 16, off_vr[j],
+                                0, 0, 0);
     };
     // The transposing read: a leading thread (kp, dg) takes the 16-byte chunks
     // it writes as V^T below from a raw buffer; chunk j is key 2kp + (j & 1),
@@ -429,23 +428,27 @@ void mla_fwd_kernel(const FwdParams p) {
         *reinterpret_cast<unsigned *>(st + w) = __builtin_amdgcn_perm(b, a, 0x05040100u);
         *reinterpret_cast<unsigned *>(st + w + 128) = __builtin_amdgcn_perm(b, a, 0x07060302u);
     };
-    // the transpose alone, for a trailing wave that runs no matrix block
-    auto transpose_v = [&](const unsigned char *vr, unsigned char *st) __attribute__((always_inline)) {
+    // the transpose and the next raw V loads alone, for a trailing wave that
+    // runs no matrix block
+    auto transpose_v = [&](const unsigned char *vr, unsigned char *st, const TileLoad &tl)
+                           __attribute__((always_inline)) {
         uint4 vst[V_LOADS];
         read_vraw(vr, vst);
         uint32_t vwb = vw_base;
         asm volatile("" : "+v"(vwb));
 #pragma unroll
         for (int q = 0; q < VT_PIECES; ++q) write_vt_piece(st, vwb, q, vst);
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) issue_v(tl, i);
     };
 
     // Loads of a tile past the last one have no valid rows (they return
-    // zeros) and land in a ring stage or raw buffer no longer read, so the
-    // leading group issues them unconditionally.
-    // Tile t's K goes out four intervals before its first scores (a stage's K
-    // region is free once the trailing group has scored the tile before), its V
-    // two intervals before V^T is written (raw buffer t % 2 is free once V^T of
-    // tile t-2 is written).
+    // zeros) and land in a ring stage or raw buffer no longer read, so they
+    // are issued unconditionally.
+    // Tile t's K goes out (leading group) four intervals before its first
+    // scores: a stage's K region is free once the trailing group has scored
+    // the tile before. Its raw V goes out (trailing group) right after the
+    // transpose of tile t-1, two intervals before its own.
     if (grp == 0) {
         const TileLoad t0 = prep_tile(0, cache_row(0)), t1 = prep_tile(1, cache_row(1)),
                        t2 = prep_tile(2, cache_row(2));
@@ -456,11 +459,9 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
 #pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) issue_v(t1, j);
-#pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t2, i);
-        // tile 0, Q and Q-rope landed; K and V of tile 1 and K of tile 2 may still fly
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS + V_LOADS));
+        // tile 0, Q and Q-rope landed; K of tiles 1 and 2 may still fly
+        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS));
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
     }
@@ -537,8 +538,9 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // ---- matrix block: O += P . V (tile in stage sv) then S = K . Q^T (tile in
     // stage sk); either half may be switched off. Operands are read ahead.
-    // ISS: issue V of tile tlv and K of tile tlk, one load every LOAD_SPACING
-    // MFMAs (after MFMAs LOAD_SPACING - 1, 2 LOAD_SPACING - 1, ...). VT:
+    // ISS: ISS_K issues the K loads of tile tlk, ISS_V the raw V loads of tile
+    // tlv, one load every LOAD_SPACING MFMAs (after MFMAs LOAD_SPACING - 1,
+    // 2 LOAD_SPACING - 1, ...). VT:
     // transpose the raw V tile in buffer vt_src into V^T of stage vt_st: the
     // raw chunks are read ahead of the first MFMA, and the V^T writes go out
     // one piece after each of the first MFMAs (a burst of these writes ahead
@@ -547,7 +549,9 @@ void mla_fwd_kernel(const FwdParams p) {
                           auto do_vt, const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src,
                           unsigned char *vt_st) __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
-        constexpr bool ISS = decltype(do_iss)::value, VT = decltype(do_vt)::value;
+        constexpr int ISS = decltype(do_iss)::value;
+        constexpr bool VT = decltype(do_vt)::value;
+        constexpr int NLOADS = ISS == ISS_K ? K_LOADS : (ISS == ISS_V ? V_LOADS : 0);
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
         // the wave feeding the matrix core wins issue arbitration against the
         // other wave of its SIMD, which runs a vector block meanwhile
@@ -586,8 +590,9 @@ void mla_fwd_kernel(const FwdParams p) {
                 write_vt_piece(vt_st, vwb, n - n0, vst);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (ISS && (n - n0) % LOAD_SPACING == LOAD_SPACING - 1 && (n - n0) / LOAD_SPACING < LOADS_PER_BLOCK) {
-                issue_part(tlv, tlk, (n - n0) / LOAD_SPACING);
+            if (NLOADS && (n - n0) % LOAD_SPACING == LOAD_SPACING - 1 && (n - n0) / LOAD_SPACING < NLOADS) {
+                if (ISS == ISS_V) issue_v(tlv, (n - n0) / LOAD_SPACING);
+                else issue_k(tlk, (n - n0) / LOAD_SPACING);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -667,6 +672,9 @@ void mla_fwd_kernel(const FwdParams p) {
     const std::integral_constant<bool, true> yes{};
     const std::integral_constant<bool, false> no{};
     const TileLoad none{};  // placeholder for blocks that issue nothing
+    const std::integral_constant<int, ISS_NONE> iss_none{};
+    const std::integral_constant<int, ISS_K> iss_k{};
+    const std::integral_constant<int, ISS_V> iss_v{};
     auto stage_ptr = [&](int r) __attribute__((always_inline)) -> const unsigned char * {
         return smem + r * STAGE_BYTES;
     };
@@ -676,15 +684,17 @@ void mla_fwd_kernel(const FwdParams p) {
     //   2j+1: leading: vector block j        trailing: PV j-1 + scores j
     //   2j+2: leading: PV j + scores j+1     trailing: vector block j
     // and a last interval in which the trailing group does PV of the last tile.
-    // Tile t's K DMA goes out during interval 2t-4 and its raw V DMA during
-    // interval 2t-2 (both from the leading group's matrix block); the issuing
-    // threads wait for both at the end of interval 2t-1. The trailing group
-    // transposes raw V into V^T of tile t during its matrix block of interval
-    // 2t+1 (tile 0: interval 1). K is first read in interval 2t, V^T in
-    // interval 2t+2. The K DMA of tile t overwrites only the K half of a stage,
-    // whose last reader (trailing scores of tile t-3) finished in interval
-    // 2t-5; the V^T half was last read by P.V of tile t-3 in interval 2t-3;
-    // raw buffer t % 2 is refilled in interval 2t+2, after the transpose.
+    // Tile t's K DMA goes out during interval 2t-4 (leading group's matrix
+    // block) and is waited for at the end of interval 2t-1. Its raw V DMA goes
+    // out during interval 2t-1 (trailing group's matrix block, after the
+    // transpose of tile t-1) and is waited for at the end of interval 2t; the
+    // trailing group transposes it into V^T of tile t in interval 2t+1. (Tile
+    // 0: K and V from the prologue, V^T in interval 1; raw V of tile 1 goes
+    // out in interval 1.) K is first read in interval 2t, V^T in interval
+    // 2t+2. The K DMA of tile t overwrites only the K half of a stage, whose
+    // last reader (trailing scores of tile t-3) finished in interval 2t-5; the
+    // V^T half was last read by P.V of tile t-3 in interval 2t-3; raw buffer
+    // t % 2 last held tile t-2, transposed in interval 2t-3.
     // A wave's visible tiles are a prefix of the tile range, so a matrix block
     // runs whenever its PV tile is visible; scores it computes for a tile the
     // wave cannot see (or past the last tile) are dropped. Each group runs its
@@ -698,9 +708,8 @@ void mla_fwd_kernel(const FwdParams p) {
         constexpr int rprev = (r0 + STAGES - 1) % STAGES, rnext = (r0 + 1) % STAGES;
         block_sync();
         // interval 2j + 1
-        int row_v = 0, row_k = 0;  // paged: cache rows of the tiles loaded next interval
+        int row_k = 0;  // paged: cache row of the tile whose K goes out next interval
         if (lead) {
-            row_v = cache_row(j + 2);
             row_k = cache_row(j + 3);
             // a leading wave past its last visible tile still runs its matrix
             // blocks (they carry the group's loads), with P = 0
@@ -710,30 +719,35 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int st4 = 0; st4 < 4; ++st4) pb[st4] = vec8{};
             }
-            // V of tile j+1 and everything before it landed (K of tile j+1 went
-            // out two intervals earlier); K of tile j+2 may still fly
+            // K of tile j+1 and everything before it landed; K of tile j+2 may
+            // still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
         } else {
             // the trailing group writes V^T of tile j (its raw V landed at the
-            // end of interval 2j-1) with its matrix block, or alone
+            // end of interval 2j) and sends out raw V of tile j+1, with its
+            // matrix block or alone
             unsigned char *vr = smem + VRAW_OFFSET + (j & 1) * V_BYTES;
+            const TileLoad tv = prep_tile(j + 1, cache_row(j + 1));
             if (wave_active(j - 1))
-                mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, no, yes, none, none, vr, smem + r0 * STAGE_BYTES);
+                mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, iss_v, yes, tv, none, vr,
+                           smem + r0 * STAGE_BYTES);
             else
-                transpose_v(vr, smem + r0 * STAGE_BYTES);
+                transpose_v(vr, smem + r0 * STAGE_BYTES, tv);
         }
         block_sync();
-        // interval 2j + 2: the leading group sends out V of tile j+2 and K of
-        // tile j+3 during its matrix block
+        // interval 2j + 2: the leading group sends out K of tile j+3 during its
+        // matrix block
         if (lead) {
-            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, yes, no, prep_tile(j + 2, row_v),
-                       prep_tile(j + 3, row_k), nullptr, nullptr);
+            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k),
+                       nullptr, nullptr);
         } else {
             if (wave_active(j)) valu_block(j);
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile j+1 landed
         }
     };
     if (grp == 0) {
-        if (wave_active(0)) mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, no, none, none, nullptr, nullptr);
+        if (wave_active(0))
+            mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_none, no, none, none, nullptr, nullptr);
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -743,13 +757,18 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (n_kt > 0) {
         // tile 0 peeled: its first interval only scores tile 0
         block_sync();
-        // (and V^T of tile 0, whose raw V the barrier before the schedule published)
-        if (wave_active(0))
-            mfma_block(stage_ptr(0), stage_ptr(0), no, yes, no, yes, none, none, smem + VRAW_OFFSET, smem);
-        else
-            transpose_v(smem + VRAW_OFFSET, smem);
+        // (and V^T of tile 0, whose raw V the barrier before the schedule
+        // published; raw V of tile 1 goes out)
+        {
+            const TileLoad tv = prep_tile(1, cache_row(1));
+            if (wave_active(0))
+                mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_v, yes, tv, none, smem + VRAW_OFFSET, smem);
+            else
+                transpose_v(smem + VRAW_OFFSET, smem, tv);
+        }
         block_sync();
         if (wave_active(0)) valu_block(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile 1 landed
         for (int j = 1; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 1>{}, no);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 2>{}, no);
@@ -758,9 +777,9 @@ void mla_fwd_kernel(const FwdParams p) {
         block_sync();
         if (wave_active(n_kt - 1)) {
             const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, no, no, none, none, nullptr, nullptr);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, no, no, none, none, nullptr, nullptr);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, no, no, none, none, nullptr, nullptr);
+            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, iss_none, no, none, none, nullptr, nullptr);
+            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, iss_none, no, none, none, nullptr, nullptr);
+            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, iss_none, no, none, none, nullptr, nullptr);
         }
     } else {
         block_sync();
