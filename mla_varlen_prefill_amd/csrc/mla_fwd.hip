@@ -12,14 +12,15 @@
 //
 //  * The head dim D (embeddimV) is a template parameter, 64 or 128; the text
 //    below gives sizes for D = 128.
-//  * Each wave owns 32 query rows of one head. Their Q (32 x 128) stays in
-//    VGPRs as the B operand of v_mfma_f32_32x32x16 (8 k-steps of 16); QRope
-//    of the workgroup's 256 rows (4 more k-steps) sits in LDS.
+//  * Each wave owns 32 query rows of one head. Their Q (32 x 128) and QRope
+//    (32 x 64) stay in VGPRs as the B operand of v_mfma_f32_32x32x16 (8 + 4
+//    k-steps of 16).
 //  * Keys are walked in tiles of FWD_BN = 64 through a 3-stage LDS ring. K-nope
 //    (64 x 128) and K-rope (64 x 64) of a tile are copied HBM -> LDS by the
-//    buffer-load-to-LDS DMA path; V (64 x 128) is loaded to VGPRs and written
-//    transposed, V^T (128 x 64), as (key, key + 1) dword pairs. Key rows past
-//    the sequence end fall outside the buffer range and arrive as zeros.
+//    buffer-load-to-LDS DMA path; so is V (64 x 128), into one of two raw
+//    buffers, from which it is transposed LDS -> LDS into the ring stage's
+//    V^T (128 x 64), as (key, key + 1) dword pairs. Key rows past the
+//    sequence end fall outside the buffer range and arrive as zeros.
 //  * LDS rows are XOR-swizzled in 16-byte chunks so that every MFMA operand is
 //    one conflict-free 16-byte read per lane, without padding.
 //  * Scores are computed transposed, S^T = K . Q^T: the accumulator holds one
@@ -35,8 +36,9 @@
 //    block (mask, row max, online-softmax update and probabilities of one
 //    tile), and the roles swap at each barrier. The matrix core of each SIMD
 //    is thus fed by one wave while the other wave's softmax runs on the VALU.
-//    The leading group issues all tile loads, spread over its matrix blocks,
-//    so the vector blocks carry no memory instructions.
+//    The leading group issues the K loads during its matrix blocks, the
+//    trailing group the V loads and the V transpose during its own, so the
+//    vector blocks carry no memory instructions.
 //  * Online softmax in fp32 with exp2 (log2(e) folded into the scale). The
 //    running max is only moved -- and O rescaled -- when a tile raises some
 //    row's max by more than 2^8 in probability units, so most tiles skip the
