@@ -304,22 +304,21 @@ void mla_fwd_kernel(const FwdParams p) {
     //    perm(m), perm swapping bits 2 and 3 of the key index, so that after
     //    S^T = K . Q^T each lane's probabilities of a 16-key step are 8
     //    consecutive keys (what the V^T operand read below needs).
-    //  * V goes HBM -> VGPRs (two 16-byte rows pieces per thread) and is
-    //    written transposed, V^T[d][key], into LDS one interval later.
+    //  * V goes HBM -> LDS by DMA too, into a raw buffer, and is transposed
+    //    into V^T[d][key] of its stage one interval later.
     const unsigned char *kbase = static_cast<const unsigned char *>(p.k);
     const unsigned char *krbase = static_cast<const unsigned char *>(p.k_rope);
     const unsigned char *vbase = static_cast<const unsigned char *>(p.v);
     const uint32_t kn_row = (uint32_t)HKV * DN * 2;  // bytes between consecutive keys
     const uint32_t kr_row = (uint32_t)HKV * DR * 2;
     auto perm_key = [](int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); };
-    // The leading group (waves 0-3, threads 0..LT-1) loads every tile, ten
-    // instructions per thread: K-nope in four DMA (slot tid + LT*u: row
-    // slot / 16, chunk slot % 16), K-rope in two (row slot / 8, chunk slot % 8),
-    // V in four loads to registers (keys 2kp and 2kp + 1, 16-byte column
-    // chunks 2dg and 2dg + 1). In the loop they go out one every four MFMAs of
-    // the group's matrix block, so no wave stalls behind a burst of address
-    // work in the texture unit and the trailing group's vector block issues no
-    // memory instruction at all.
+    // Per tile, the leading group (waves 0-3, threads 0..LT-1) issues the K
+    // DMA, six per thread: K-nope in four (slot tid + LT*u: row slot / 16,
+    // chunk slot % 16), K-rope in two (row slot / 8, chunk slot % 8); the
+    // trailing group issues the raw V DMA (below). In the loop they go out one
+    // every four MFMAs of the group's matrix block, so no wave stalls behind a
+    // burst of address work in the texture unit and the vector blocks issue
+    // no memory instruction at all.
     constexpr int LT = NT / 2;
     uint32_t off_kn[KN_LOADS], off_kr[2];
 #pragma unroll
