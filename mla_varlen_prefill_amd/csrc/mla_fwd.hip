@@ -703,6 +703,10 @@ void mla_fwd_kernel(const FwdParams p) {
     block_sync();
 
     // one tile's two intervals; R = ring stage of tile j
+    // paged, trailing group: cache row of the tile whose raw V goes out next,
+    // read from the LDS table in the vector interval before, like the leading
+    // group's rows, so that the read's latency stays off the matrix block
+    int trail_row_v = 0;
     auto tile_pair = [&](int j, auto R, auto LEAD) __attribute__((always_inline)) {
         constexpr int r0 = decltype(R)::value;
         constexpr bool lead = decltype(LEAD)::value;
@@ -728,7 +732,7 @@ void mla_fwd_kernel(const FwdParams p) {
             // end of interval 2j) and sends out raw V of tile j+1, with its
             // matrix block or alone
             unsigned char *vr = smem + VRAW_OFFSET + (j & 1) * V_BYTES;
-            const TileLoad tv = prep_tile(j + 1, cache_row(j + 1));
+            const TileLoad tv = prep_tile(j + 1, trail_row_v);
             if (wave_active(j - 1))
                 mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, iss_v, yes, tv, none, vr,
                            smem + r0 * STAGE_BYTES);
@@ -742,6 +746,7 @@ void mla_fwd_kernel(const FwdParams p) {
             mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k),
                        nullptr, nullptr);
         } else {
+            trail_row_v = cache_row(j + 2);
             if (wave_active(j)) valu_block(j);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile j+1 landed
         }
@@ -768,6 +773,7 @@ void mla_fwd_kernel(const FwdParams p) {
                 transpose_v(smem + VRAW_OFFSET, smem, tv);
         }
         block_sync();
+        trail_row_v = cache_row(2);
         if (wave_active(0)) valu_block(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile 1 landed
         for (int j = 1; j < n_kt; j += STAGES) {
