@@ -610,20 +610,29 @@ void mla_fwd_kernel(const FwdParams p) {
         // copied all 32 scores at the merge.
         if (!wave_full(kt)) {
             const int key0 = kt * BN;
-            const unsigned short *mrow = nullptr;
-            if (mask_type == MASK_FREE)
-                mrow = static_cast<const unsigned short *>(p.mask) + (pos & (MASK_TILE - 1)) * MASK_TILE;
+            if (mask_type != MASK_FREE) {
+                // Key j is visible iff j <= min(pos, kv_len - 1) (causal modes)
+                // or j <= kv_len - 1 (UNDEFINED). Element e of block kb is key
+                // key0 + 8g + off(kb, e), so one per-lane limit on the constant
+                // offset decides each element with a compare and a select.
+                const int lim = (causal_like ? min(pos, kv_len - 1) : kv_len - 1) - key0 - 8 * g;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int j = key0 + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-                    float x = s[kb][e];
-                    bool vis = j < kv_len;
-                    if (causal_like) {
-                        vis = vis && j <= pos;
-                    } else if (mask_type == MASK_FREE) {
-                        vis = vis && pos >= 0 && (j >> 9) <= (pos >> 9);
+                    for (int e = 0; e < 16; ++e) {
+                        const int off = kb * 32 + 16 * (e >> 3) + (e & 7);
+                        s[kb][e] = off <= lim ? s[kb][e] : -INFINITY;
+                    }
+            } else {
+                const unsigned short *mrow =
+                    static_cast<const unsigned short *>(p.mask) + (pos & (MASK_TILE - 1)) * MASK_TILE;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int j = key0 + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
+                        float x = s[kb][e];
+                        const bool vis = j < kv_len && pos >= 0 && (j >> 9) <= (pos >> 9);
                         if (vis && (j >> 9) == (pos >> 9)) {
                             // tile entry m is added as m * log2(e) / c, so the
                             // fma with c below turns it into m * log2(e)
@@ -631,9 +640,9 @@ void mla_fwd_kernel(const FwdParams p) {
                             const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mbits) : bits_to_float_f16(mbits);
                             x += mv * LOG2E * inv_c;
                         }
+                        s[kb][e] = vis ? x : -INFINITY;
                     }
-                    s[kb][e] = vis ? x : -INFINITY;
-                }
+            }
         }
         float m4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
 #pragma unroll
