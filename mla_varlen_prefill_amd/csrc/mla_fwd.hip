@@ -624,23 +624,46 @@ void mla_fwd_kernel(const FwdParams p) {
                         s[kb][e] = off <= lim ? s[kb][e] : -INFINITY;
                     }
             } else {
-                const unsigned short *mrow =
-                    static_cast<const unsigned short *>(p.mask) + (pos & (MASK_TILE - 1)) * MASK_TILE;
+                // MASK_FREE: a 64-key tile lies inside one 512-key block, so the
+                // block rule gives one limit per lane: keys of an earlier block
+                // are visible (up to kv_len - 1), of a later one not; on the
+                // diagonal block the row of the 512 x 512 tile is added, read as
+                // four runs of 8 entries (the keys 8g + 32kb + 16h + 0..7).
+                const int jb = key0 >> 9, pb = pos >> 9;
+                const int lim = (pos < 0 || jb > pb) ? -1 : kv_len - 1 - key0 - 8 * g;
+                if (pos >= 0 && jb == pb) {
+                    const unsigned short *mrow = static_cast<const unsigned short *>(p.mask) +
+                                                 (pos & (MASK_TILE - 1)) * MASK_TILE + (key0 & (MASK_TILE - 1)) + 8 * g;
+                    const bool vec = (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int kb = q >> 1, hh = q & 1;
+                        const unsigned short *src = mrow + kb * 32 + hh * 16;
+                        unsigned short mb[8];
+                        if (vec) {
+                            const uint4 w = *reinterpret_cast<const uint4 *>(src);
+                            const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) mb[i] = (unsigned short)(ws[i >> 1] >> (16 * (i & 1)));
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) mb[i] = src[i];
+                        }
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            // tile entry m is added as m * log2(e) / c, so the
+                            // fma with c below turns it into m * log2(e)
+                            const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mb[i]) : bits_to_float_f16(mb[i]);
+                            s[kb][8 * hh + i] += mv * LOG2E * inv_c;
+                        }
+                    }
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
-                        const int j = key0 + kb * 32 + 16 * (e >> 3) + 8 * g + (e & 7);
-                        float x = s[kb][e];
-                        const bool vis = j < kv_len && pos >= 0 && (j >> 9) <= (pos >> 9);
-                        if (vis && (j >> 9) == (pos >> 9)) {
-                            // tile entry m is added as m * log2(e) / c, so the
-                            // fma with c below turns it into m * log2(e)
-                            const unsigned short mbits = mrow[j & (MASK_TILE - 1)];
-                            const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mbits) : bits_to_float_f16(mbits);
-                            x += mv * LOG2E * inv_c;
-                        }
-                        s[kb][e] = vis ? x : -INFINITY;
+                        const int off = kb * 32 + 16 * (e >> 3) + (e & 7);
+                        s[kb][e] = off <= lim ? s[kb][e] : -INFINITY;
                     }
             }
         }
