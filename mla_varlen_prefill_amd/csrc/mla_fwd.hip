@@ -628,32 +628,24 @@ void mla_fwd_kernel(const FwdParams p) {
                 // block rule gives one limit per lane: keys of an earlier block
                 // are visible (up to kv_len - 1), of a later one not; on the
                 // diagonal block the row of the 512 x 512 tile is added, read as
-                // four runs of 8 entries (the keys 8g + 32kb + 16h + 0..7).
+                // four 16-byte runs of 8 entries (the keys 8g + 32kb + 16h +
+                // 0..7; the host accepts only 16-byte aligned tiles).
                 const int jb = key0 >> 9, pb = pos >> 9;
                 const int lim = (pos < 0 || jb > pb) ? -1 : kv_len - 1 - key0 - 8 * g;
                 if (pos >= 0 && jb == pb) {
                     const unsigned short *mrow = static_cast<const unsigned short *>(p.mask) +
                                                  (pos & (MASK_TILE - 1)) * MASK_TILE + (key0 & (MASK_TILE - 1)) + 8 * g;
-                    const bool vec = (reinterpret_cast<uintptr_t>(p.mask) & 15) == 0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int kb = q >> 1, hh = q & 1;
-                        const unsigned short *src = mrow + kb * 32 + hh * 16;
-                        unsigned short mb[8];
-                        if (vec) {
-                            const uint4 w = *reinterpret_cast<const uint4 *>(src);
-                            const unsigned ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) mb[i] = (unsigned short)(ws[i >> 1] >> (16 * (i & 1)));
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) mb[i] = src[i];
-                        }
+                        const uint4 w = *reinterpret_cast<const uint4 *>(mrow + kb * 32 + hh * 16);
+                        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
+                            const unsigned short mbits = (unsigned short)(ws[i >> 1] >> (16 * (i & 1)));
                             // tile entry m is added as m * log2(e) / c, so the
                             // fma with c below turns it into m * log2(e)
-                            const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mb[i]) : bits_to_float_f16(mb[i]);
+                            const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mbits) : bits_to_float_f16(mbits);
                             s[kb][8 * hh + i] += mv * LOG2E * inv_c;
                         }
                     }

@@ -89,6 +89,10 @@ def test_valid_problem_plans():
      "MLA_ERR_SHAPE"),
     (lambda t: t.update(mask_type=mla.MASK_FREE, mask=torch.zeros(512, 512, dtype=torch.float32)),
      "MLA_ERR_DTYPE"),
+    # device tensors must be 16-byte aligned (the kernel reads tile rows in 16-byte runs)
+    (lambda t: t.update(mask_type=mla.MASK_FREE,
+                        mask=torch.zeros(512 * 512 + 8, dtype=torch.float16)[1:1 + 512 * 512].view(512, 512)),
+     "MLA_ERR_VALUE"),
     (lambda t: t.update(q=torch.zeros(57, 4, 128, dtype=torch.float32)), "MLA_ERR_DTYPE"),
 ])
 def test_validation_errors(mutate, status):
