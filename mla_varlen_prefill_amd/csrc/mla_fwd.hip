@@ -100,8 +100,6 @@ constexpr int MASK_FREE = 3;
 constexpr int ISS_NONE = 0, ISS_K = 1, ISS_V = 2;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -192,11 +190,6 @@ __device__ __forceinline__ void block_sync() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-__device__ __forceinline__ i16x4 lds_read_tr16(const unsigned char *p) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
-}
-
 // PAGED: K, KRope and V are read from ND caches through the block table; a
 // table of the first cache row of each of the sequence's key tiles sits in
 // the LDS past the ring.
@@ -216,7 +209,7 @@ void mla_fwd_kernel(const FwdParams p) {
     constexpr int NV = 4 * NDB;         // V^T operands of a matrix block (4 key steps x NDB)
     constexpr int KN_LOADS = DN / 32;   // K-nope DMA per leading thread and tile
     constexpr int CPT = DN / 64;        // V column chunk pairs per leading thread
-    constexpr int V_LOADS_ = 2 * CPT;   // raw V DMA per leading thread and tile
+    constexpr int V_LOADS = 2 * CPT;    // raw V DMA per trailing thread and tile
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)];
     typedef typename T::vec8 vec8;
 
@@ -342,9 +335,9 @@ void mla_fwd_kernel(const FwdParams p) {
     const int kp = tid & 31, dg = (tid >> 5) & 7;  // V^T writer: keys 2kp, 2kp + 1; column chunks of dg
     constexpr int CPR = DN / 8;  // 16-byte chunks of a V row
     auto vswz = [](int m) { return (m >> 1) & (CPR - 1); };
-    uint32_t off_vr[V_LOADS_];
+    uint32_t off_vr[V_LOADS];
 #pragma unroll
-    for (int u = 0; u < V_LOADS_; ++u) {
+    for (int u = 0; u < V_LOADS; ++u) {
         const int slot = (tid & (LT - 1)) + LT * u;
         const int m = slot / CPR;
         off_vr[u] = m * kn_row + (((slot % CPR) ^ vswz(m)) << 4);
@@ -381,7 +374,7 @@ void mla_fwd_kernel(const FwdParams p) {
     // A leading thread's loads of a tile: six K DMA (K_LOADS) and four V loads
     // (V_LOADS). V load j lands in vst[j]: key 2kp + (j & 1), column chunk
     // 2dg + (j >> 1).
-    constexpr int K_LOADS = KN_LOADS + 2, V_LOADS = 2 * CPT;
+    constexpr int K_LOADS = KN_LOADS + 2;
     // every load of a matrix block has an MFMA slot
     static_assert(K_LOADS * LOAD_SPACING <= NV + 2 * (NKS + 4), "matrix block too short for its loads");
     static_assert(V_LOADS * LOAD_SPACING <= 2 * (NKS + 4), "scores-only block too short for the V loads");
