@@ -302,11 +302,11 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
 const char *mla_last_error(void);
 
 /*
- * mla_prefill_plan_host -- host-only view of the work list mla_prefill copies
- * into its workspace, for inspection and tests. No HIP call. Writes, into buf
- * (host memory of buf_size bytes), the same bytes mla_prefill would place at
- * the start of the workspace, three arrays each starting on a 256-byte
- * boundary:
+ * mla_prefill_plan_host -- host-only view of the work list mla_prefill builds,
+ * for inspection and tests. No HIP call. (mla_prefill folds each task with its
+ * item and batch record into one 32-byte launch record per workgroup, which
+ * is what its workspace holds.) Writes, into buf (host memory of buf_size
+ * bytes), three arrays each starting on a 256-byte boundary:
  *   batch records  {q_offset, kv_offset, q_len, kv_len}  int32 x 4, batch of them
  *   work items     {batch, first_q_row, kv_tiles, q_rows} int32 x 4, *n_items of them
  *   tasks          {item, first_head}                      int32 x 2, *n_tasks of them

@@ -112,6 +112,27 @@ def _check(fn, rc):
         raise MlaError(fn, rc, mla_last_error())
 
 
+def _on_device(named, stream=None):
+    """Raise ValueError unless every (name, tensor) pair that is not None is a
+    torch tensor in GPU memory, all on one device (the stream's, when a torch
+    stream is given). The C entry points take raw pointers and cannot tell host
+    memory from device memory; a host pointer handed to a kernel faults the
+    GPU, so this is checked before any launching call."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            kind = type(t).__name__ if not isinstance(t, torch.Tensor) else f"tensor on {t.device}"
+            raise ValueError(f"{name} must be a torch tensor in GPU memory (got {kind})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, other device arguments on {dev}")
+    if dev is not None and isinstance(stream, torch.cuda.Stream) and stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {dev}")
+
+
 def _desc(t, keep):
     """mla_tensor descriptor of a torch tensor or numpy array (None -> NULL)."""
     if t is None:
@@ -178,6 +199,8 @@ def mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk
                 mask_type, cache_mode, atten_out, workspace, stream=None) -> None:
     """Enqueue MLA prefill attention on ``stream`` (default: torch's current stream)."""
     lib = _load()
+    _on_device([("q", q), ("q_rope", q_rope), ("k", k), ("k_rope", k_rope), ("v", v), ("atten_out", atten_out),
+                ("mask", mask if mask_type == MASK_FREE else None), ("workspace", workspace)], stream)
     keep = []
     args = _prefill_args(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
                          mask_type, cache_mode, atten_out, keep)
@@ -214,6 +237,9 @@ def mla_prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tabl
                       head_num, qk_scale, kv_head_num, mask_type, atten_out, workspace, stream=None) -> None:
     """Enqueue MLA prefill attention reading K, KRope and V through block tables."""
     lib = _load()
+    _on_device([("q", q), ("q_rope", q_rope), ("key_cache", key_cache), ("krope_cache", krope_cache),
+                ("value_cache", value_cache), ("block_tables", block_tables), ("atten_out", atten_out),
+                ("mask", mask if mask_type == MASK_FREE else None), ("workspace", workspace)], stream)
     keep = []
     args = _paged_args(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask,
                        head_num, qk_scale, kv_head_num, mask_type, atten_out, keep)
@@ -226,8 +252,12 @@ def mla_prefill_paged(q, q_rope, key_cache, krope_cache, value_cache, block_tabl
 def paged_cache_load(key_cache, value_cache, block_tables, context_lens, key, value, seq_starts=None,
                      kv_cache_cfg=KV_CACHE_ND, is_seq_lens_cumsum_type=False, has_seq_starts=False,
                      stream=None) -> None:
-    """Enqueue the paged K/V gather on ``stream`` (default: torch's current stream)."""
+    """Enqueue the paged K/V gather on ``stream`` (default: torch's current stream).
+    Every tensor argument, context_lens and seq_starts included, is device memory."""
     lib = _load()
+    _on_device([("key_cache", key_cache), ("value_cache", value_cache), ("block_tables", block_tables),
+                ("context_lens", context_lens), ("key", key), ("value", value),
+                ("seq_starts", seq_starts if has_seq_starts else None)], stream)
     keep = []
     _check("paged_cache_load", lib.paged_cache_load(
         _desc(key_cache, keep), _desc(value_cache, keep), _desc(block_tables, keep), _desc(context_lens, keep),
@@ -322,6 +352,9 @@ def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv
                workspace, stream=None) -> None:
     """Enqueue the non-quantised MLA prolog (q, kv and c^Q from hidden states)."""
     lib = _load()
+    _on_device([("token_x", token_x), ("wq_a", wq_a), ("wq_b", wq_b), ("wkv", wkv), ("rope_cos", rope_cos),
+                ("rope_sin", rope_sin), ("gamma_cq", gamma_cq), ("gamma_ckv", gamma_ckv), ("q_out", q_out),
+                ("kv_out", kv_out), ("qr_out", qr_out), ("workspace", workspace)], stream)
     keep = []
     ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
     ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0

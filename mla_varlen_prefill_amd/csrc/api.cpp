@@ -337,12 +337,20 @@ struct Plan {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+// Host view of the work list (mla_prefill_plan_host): batch records, items,
+// tasks, each array on a 256-byte boundary.
 uint64_t items_offset(const Plan &p) { return align256(p.seqs.size() * sizeof(SeqRec)); }
 uint64_t tasks_offset(const Plan &p) { return items_offset(p) + align256(p.items.size() * sizeof(WorkItem)); }
 
-uint64_t plan_bytes(const Plan &p) {
+uint64_t view_bytes(const Plan &p) {
     if (p.items.empty()) return 0;
     return tasks_offset(p) + p.tasks.size() * sizeof(Task);
+}
+
+// Device workspace: one LaunchRec per workgroup.
+uint64_t plan_bytes(const Plan &p) {
+    if (p.items.empty()) return 0;
+    return p.tasks.size() * sizeof(mla::LaunchRec);
 }
 
 // log2 of the query heads one task runs: the largest power of two, at most
@@ -475,10 +483,35 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         for (size_t k = 0; k < queue[x].size(); ++k) plan->tasks[k * MLA_XCDS + x] = queue[x][k];
 }
 
-void write_plan(const Plan &p, uint8_t *dst) {
+void write_plan_view(const Plan &p, uint8_t *dst) {
     std::memcpy(dst, p.seqs.data(), p.seqs.size() * sizeof(SeqRec));
     std::memcpy(dst + items_offset(p), p.items.data(), p.items.size() * sizeof(WorkItem));
     std::memcpy(dst + tasks_offset(p), p.tasks.data(), p.tasks.size() * sizeof(Task));
+}
+
+// The launch records the kernel reads: each task with its item and sequence
+// folded in. Paged K/V carry the sequence index (its block-table row) where
+// contiguous K/V carry the sequence's first key row.
+void write_launch(const Plan &p, int32_t group, bool paged, mla::LaunchRec *dst) {
+    for (size_t i = 0; i < p.tasks.size(); ++i) {
+        const Task &t = p.tasks[i];
+        mla::LaunchRec r{};
+        if (t.item < 0) {
+            r.head = -1;
+        } else {
+            const WorkItem &it = p.items[t.item];
+            const SeqRec &sq = p.seqs[it.b];
+            r.q_row0 = it.q_row0;
+            r.kv_tiles = it.kv_tiles;
+            r.head = t.head;
+            r.kv_head = t.head / group;
+            r.q_off = sq.q_off;
+            r.kv_off = paged ? it.b : sq.kv_off;
+            r.q_len = sq.q_len;
+            r.kv_len = sq.kv_len;
+        }
+        dst[i] = r;
+    }
 }
 
 // Plan on the host, copy the work list into the workspace, launch. pg and
@@ -499,8 +532,8 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
         return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     if (plan.tasks.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
 
-    std::vector<uint8_t> host(need);
-    write_plan(plan, host.data());
+    std::vector<mla::LaunchRec> host(plan.tasks.size());
+    write_launch(plan, pr.heads / pr.kv_heads, pg != nullptr, host.data());
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipMemcpyAsync: %s", hipGetErrorString(e));
@@ -513,10 +546,7 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.v = v;
     p.mask = (pr.mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
     p.out = atten_out->data;
-    uint8_t *ws = static_cast<uint8_t *>(workspace);
-    p.seqs = reinterpret_cast<const SeqRec *>(ws);
-    p.items = reinterpret_cast<const WorkItem *>(ws + items_offset(plan));
-    p.tasks = reinterpret_cast<const Task *>(ws + tasks_offset(plan));
+    p.launch = static_cast<const mla::LaunchRec *>(workspace);
     p.heads = pr.heads;
     p.kv_heads = pr.kv_heads;
     p.group = pr.heads / pr.kv_heads;
@@ -638,11 +668,11 @@ int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int
     build_plan(q_seqlen, kv_seqlen, batch, head_num, kv_head_num, mask_type, kv_padded_max_seq, &plan);
     *n_items = (int32_t)plan.items.size();
     *n_tasks = (int32_t)plan.tasks.size();
-    uint64_t need = plan_bytes(plan);
+    uint64_t need = view_bytes(plan);
     if (need > 0) {
         if (buf == nullptr || buf_size < need)
             return fail(MLA_ERR_WORKSPACE, "plan needs %llu bytes", (unsigned long long)need);
-        write_plan(plan, static_cast<uint8_t *>(buf));
+        write_plan_view(plan, static_cast<uint8_t *>(buf));
     }
     return ok();
 }

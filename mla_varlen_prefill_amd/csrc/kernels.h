@@ -50,6 +50,21 @@ struct Task {
 constexpr int MLA_XCDS = 8;
 constexpr int MLA_CUS_PER_XCD = 32;
 
+// What one workgroup of the attention launch runs, flattened so that the
+// kernel reads it with a single scalar load: a work item (q rows of one
+// sequence) for 2^pack_shift query heads from `head`. head == -1 marks an
+// empty padding workgroup.
+struct LaunchRec {
+    int32_t q_row0;    // first query row of the item within its sequence
+    int32_t kv_tiles;  // FWD_BN-key tiles (from key 0) any of its rows can see
+    int32_t head;      // first query head; -1: padding
+    int32_t kv_head;   // the KV head of those query heads
+    int32_t q_off;     // first row of the sequence in Q / attenOut
+    int32_t kv_off;    // contiguous K/V: first key row of the sequence; paged: the sequence index
+    int32_t q_len;
+    int32_t kv_len;
+};
+
 struct FwdParams {
     const void *q;        // [nq, H, D]
     const void *q_rope;   // [nq, H, 64]
@@ -58,9 +73,7 @@ struct FwdParams {
     const void *v;        // rows of Hkv * D
     const void *mask;     // [512, 512] or nullptr
     void *out;            // [nq, H, D]
-    const SeqRec *seqs;
-    const WorkItem *items;
-    const Task *tasks;
+    const LaunchRec *launch;  // one record per workgroup
     int32_t heads;
     int32_t kv_heads;
     int32_t group;        // heads / kv_heads

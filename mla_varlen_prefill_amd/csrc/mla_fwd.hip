@@ -13,8 +13,9 @@
 //  * The head dim D (embeddimV) is a template parameter, 64 or 128; the text
 //    below gives sizes for D = 128.
 //  * Each wave owns 32 query rows of one head. Their Q (32 x 128) and QRope
-//    (32 x 64) stay in VGPRs as the B operand of v_mfma_f32_32x32x16 (8 + 4
-//    k-steps of 16).
+//    (32 x 64) arrive by DMA into LDS, whole rows per instruction, and are
+//    read once into VGPRs, where they stay as the B operand of
+//    v_mfma_f32_32x32x16 (8 + 4 k-steps of 16).
 //  * Keys are walked in tiles of FWD_BN = 64 through a 3-stage LDS ring. K-nope
 //    (64 x 128) and K-rope (64 x 64) of a tile are copied HBM -> LDS by the
 //    buffer-load-to-LDS DMA path; so is V (64 x 128), into one of two raw
@@ -39,7 +40,11 @@
 //    The leading group issues the K loads during its matrix blocks, the
 //    trailing group the V loads and the V transpose during its own, so the
 //    vector blocks carry no memory instructions.
-//  * Online softmax in fp32 with exp2 (log2(e) folded into the scale). The
+//  * The workgroup's work item comes from one 32-byte launch record (one
+//    scalar load); only Q and tile 0 are loaded before the first barrier.
+//  * Online softmax in fp32 with exp2 (log2(e) folded into the scale), its
+//    steps in independent phases (max tree, exponent arguments, exponentials,
+//    packing and row sum) so that no instruction waits on the one before. The
 //    running max is only moved -- and O rescaled -- when a tile raises some
 //    row's max by more than 2^8 in probability units, so most tiles skip the
 //    rescale; probabilities stay <= 256 and are rounded to the input dtype for
@@ -82,7 +87,15 @@ struct Geom {
     static constexpr int STAGE_BYTES = KN_BYTES + KR_BYTES + V_BYTES;
     static constexpr int VRAW_OFFSET = STAGES * STAGE_BYTES;
     static constexpr int LDS_BYTES = VRAW_OFFSET + 2 * V_BYTES;
+    // Q and Q-rope of the 8 waves pass through LDS once, at the start: 32 rows
+    // of D + 64 values per wave. D = 128: in the ring past tile 0's K (stage 0's
+    // V^T and stages 1 and 2, free until the first barrier); D = 64: past
+    // everything else.
+    static constexpr int QSLOT_BYTES = 32 * (D + 64) * 2;
+    static constexpr int QSTAGE_OFFSET = D == 128 ? KN_BYTES + KR_BYTES : LDS_BYTES + PAGED_MAX_TILES * 4;
+    static constexpr int SMEM_MIN = QSTAGE_OFFSET + 8 * QSLOT_BYTES;
 };
+static_assert(Geom<128>::SMEM_MIN <= Geom<128>::VRAW_OFFSET, "Q staging must leave the raw V buffers free");
 // 16-byte chunk swizzle of an LDS row of D * 2 bytes (K-nope rows, output
 // staging rows): chunk c of row r sits at c ^ swz(r), which makes the 16-byte
 // reads of 16 consecutive rows (and 8-byte writes of 32) conflict-free.
@@ -97,7 +110,7 @@ constexpr int MASK_UNDEFINED = 0;
 constexpr int MASK_FREE = 3;
 
 // which tile loads a matrix block issues
-constexpr int ISS_NONE = 0, ISS_K = 1, ISS_V = 2;
+constexpr int ISS_NONE = 0, ISS_K = 1, ISS_V = 2, ISS_K2 = 3;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -166,6 +179,13 @@ __device__ __forceinline__ float bits_to_float_f16(unsigned short b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max of three scores straight from the MFMA (no NaN canonicalisation)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // max of x over lanes l and l ^ 32
 __device__ __forceinline__ float max_with_partner(float x) {
     const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
@@ -210,7 +230,10 @@ void mla_fwd_kernel(const FwdParams p) {
     constexpr int KN_LOADS = DN / 32;   // K-nope DMA per leading thread and tile
     constexpr int CPT = DN / 64;        // V column chunk pairs per leading thread
     constexpr int V_LOADS = 2 * CPT;    // raw V DMA per trailing thread and tile
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)];
+    constexpr int SMEM_BYTES = LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0) > Geom<DN>::SMEM_MIN
+                                   ? LDS_BYTES + (PAGED ? TILE_TABLE_BYTES : 0)
+                                   : Geom<DN>::SMEM_MIN;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM_BYTES];
     typedef typename T::vec8 vec8;
 
     const int tid = threadIdx.x;
@@ -222,10 +245,8 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // The host's task list says which work item and head this workgroup runs
     // (launch order and XCD placement are chosen there); padding tasks exit.
-    const Task task = p.tasks[blockIdx.x];
-    if (task.item < 0) return;
-    const WorkItem item = p.items[task.item];
-    const SeqRec seq = p.seqs[item.b];
+    const LaunchRec task = p.launch[blockIdx.x];
+    if (task.head < 0) return;
     // The wave's 32-row slot: slot s holds head task.head + s % P and rows
     // 32 * (s / P) .. + 31 of the item (P = 2^pack_shift heads per task). The
     // two waves sharing a SIMD (w, w + 4) take slots 2(w & 3) and 2(w & 3) + 1:
@@ -234,46 +255,53 @@ void mla_fwd_kernel(const FwdParams p) {
     const int ps = p.pack_shift;
     const int slot = (wave & 3) * 2 + grp;
     const int h = task.head + (slot & ((1 << ps) - 1));
-    const int hk = task.head / p.group;
+    const int hk = task.kv_head;
     const int H = p.heads, HKV = p.kv_heads;
-    const int q_len = seq.q_len;
-    const int kv_len = seq.kv_len;
-    const int n_kt = item.kv_tiles;
+    const int q_len = task.q_len;
+    const int kv_len = task.kv_len;
+    const int n_kt = task.kv_tiles;
     const int mask_type = p.mask_type;
     const bool causal_like = mask_type != MASK_UNDEFINED && mask_type != MASK_FREE;
 
     const int lrow0 = (slot >> ps) * 32;            // first row of this wave within the item
-    const int row0 = item.q_row0 + lrow0;           // ... within the sequence
+    const int row0 = task.q_row0 + lrow0;           // ... within the sequence
     const int qi = row0 + r32;                      // this lane's query row
     const int pos = kv_len - q_len + qi;            // its key position
     const int wpos0 = kv_len - q_len + row0;        // key positions of the wave's rows
     const int wpos1 = wpos0 + 31;
 
-    // ---- Q-nope^T operand (B of S^T = K . Q^T) in VGPRs: lane holds row r32,
-    // k-slots g*8..g*8+7 of each 16-wide k-step. Rows past the end read as 0.
-    vec8 qreg[NKS];
+    // ---- Q and Q-rope of the wave's 32 rows go HBM -> LDS by DMA, whole rows
+    // per instruction (4 rows of Q-nope, or 8 of Q-rope, per 1 KB), into the
+    // wave's staging slot; they are read back into VGPRs below as the B
+    // operand of S^T = K . Q^T (lane: row r32, k-slots g*8 .. g*8+7 of each
+    // 16-wide k-step). A direct VGPR load would touch 32 rows, 32 bytes each,
+    // per instruction. Chunk c of staged row r sits at c ^ swizzle(r), which
+    // keeps the read-back conflict-free. Rows past the end read as 0.
+    constexpr int QN_INSTR = DN / 16;          // 1 KB DMA instructions for Q-nope
+    constexpr int QN_CPR = DN / 8;             // 16-byte chunks of a Q-nope row
+    unsigned char *qslot = smem + Geom<DN>::QSTAGE_OFFSET + slot * Geom<DN>::QSLOT_BYTES;
     {
         const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)seq.q_off + row0;
+        const int64_t tok = (int64_t)task.q_off + row0;
         const i32x4 rq = make_rsrc(static_cast<const unsigned char *>(p.q) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
-        const uint32_t qo = (uint32_t)r32 * H * DN * 2 + g * 16;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks)
-            qreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rq, qo + ks * 32, 0, 0));
-    }
-    // ---- Q-rope^T operand likewise (4 more k-steps of 16)
-    vec8 qrreg[4];
-    {
-        const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)seq.q_off + row0;
         const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
                                    (uint32_t)rows * H * DR * 2);
-        const uint32_t qo = (uint32_t)r32 * H * DR * 2 + g * 16;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qrreg[ks] = __builtin_bit_cast(vec8, mla_raw_buffer_load_b128(rr, qo + ks * 32, 0, 0));
+        for (int u = 0; u < QN_INSTR; ++u) {
+            const int r = u * (64 / QN_CPR) + lane / QN_CPR, c = (lane % QN_CPR) ^ row_swizzle<DN>(r);
+            mla_raw_buffer_load_lds(rq, (lds_u32_ptr)(qslot + u * 1024), 16, (uint32_t)r * H * DN * 2 + c * 16, 0,
+                                    0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = u * 8 + lane / 8, c = (lane % 8) ^ ((r >> 1) & 7);
+            mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(qslot + 32 * DN * 2 + u * 1024), 16,
+                                    (uint32_t)r * H * DR * 2 + c * 16, 0, 0, 0);
+        }
     }
+    constexpr int Q_LOADS = QN_INSTR + 4;
+    vec8 qreg[NKS], qrreg[4];
 
     // ---- paged K/V: first cache row of each key tile of the sequence (block
     // size is a multiple of the tile, so a tile never straddles two blocks);
@@ -283,7 +311,7 @@ void mla_fwd_kernel(const FwdParams p) {
     const int n_tiles_seq = min((kv_len + BN - 1) / BN, PAGED_MAX_TILES);
     if (PAGED) {
         const int tpb = p.block_size / BN;
-        const int32_t *bt = p.block_tables + (int64_t)item.b * p.bt_stride;
+        const int32_t *bt = p.block_tables + (int64_t)task.kv_off * p.bt_stride;
         for (int i = tid; i < n_tiles_seq; i += NT) {
             const int bi = i / tpb;
             const int blk = bt[bi];
@@ -360,7 +388,7 @@ void mla_fwd_kernel(const FwdParams p) {
             rowi = r >= 0 ? (int64_t)r * HKV + hk : 0;
             nvalid = r >= 0 ? (uint32_t)max(0, min(kv_len - kt * BN, BN)) : 0u;
         } else {
-            rowi = ((int64_t)seq.kv_off + (int64_t)kt * BN) * HKV + hk;
+            rowi = ((int64_t)task.kv_off + (int64_t)kt * BN) * HKV + hk;
             nvalid = (uint32_t)max(0, min(kv_len - kt * BN, BN));
         }
         TileLoad tl;
@@ -443,21 +471,32 @@ void mla_fwd_kernel(const FwdParams p) {
     // scores: a stage's K region is free once the trailing group has scored
     // the tile before. Its raw V goes out (trailing group) right after the
     // transpose of tile t-1, two intervals before its own.
+    // Before the first barrier only what interval 0 needs is loaded: every
+    // wave's Q, and tile 0's K (the leading group scores it); tile 0's raw V
+    // goes out too and is waited for at the end of interval 0. The K of tiles
+    // 1 and 2 goes out during interval 0 (into ring stages that hold the Q
+    // staging until the first barrier).
     if (grp == 0) {
-        const TileLoad t0 = prep_tile(0, cache_row(0)), t1 = prep_tile(1, cache_row(1)),
-                       t2 = prep_tile(2, cache_row(2));
+        const TileLoad t0 = prep_tile(0, cache_row(0));
 #pragma unroll
         for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
 #pragma unroll
         for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j);
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) issue_k(t2, i);
-        // tile 0, Q and Q-rope landed; K of tiles 1 and 2 may still fly
-        __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS));
+        __builtin_amdgcn_s_waitcnt(0x0F70 | V_LOADS);  // Q, Q-rope and K of tile 0 landed
     } else {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
+    }
+    static_assert(Q_LOADS + K_LOADS + V_LOADS <= 63, "vmcnt range");
+    {
+        // Q read back from the wave's own staging slot (its own DMA, landed)
+        const uint32_t qn = (uint32_t)r32 * (DN * 2) + ((g ^ row_swizzle<DN>(r32)) << 4);
+        const uint32_t qr = 32 * DN * 2 + (uint32_t)r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+            qreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const uint4 *>(qslot + (qn ^ (ks << 5))));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qrreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const uint4 *>(qslot + (qr ^ (ks << 5))));
     }
 
     // A negative scale is folded into Q so the row max can be taken on raw
@@ -473,23 +512,31 @@ void mla_fwd_kernel(const FwdParams p) {
         }
     }
 
-    // ---- per-wave tile visibility
+    // ---- per-wave tile visibility. Under every mask mode the tiles some row
+    // of the wave can see, and the tiles every row sees whole, are prefixes of
+    // the item's tile range, so two wave-uniform counts decide both questions
+    // with one compare each.
+    //  * visible: causal modes, key0 <= wpos1; MASK_FREE, the key block (512
+    //    keys) is not after the last row's block; UNDEFINED, every tile.
+    //  * whole: the tile lies inside the sequence (key0 + 64 <= kv_len) and,
+    //    for the causal modes, its last key is <= wpos0; for MASK_FREE its
+    //    512-key block lies before the first row's block.
+    int kt_vis = n_kt, kt_full = kv_len / BN;
+    if (causal_like) {
+        kt_vis = min(n_kt, wpos1 >= 0 ? wpos1 / BN + 1 : 0);
+        kt_full = min(kt_full, max(0, (wpos0 + 1) / BN));
+    } else if (mask_type == MASK_FREE) {
+        kt_vis = min(n_kt, wpos1 >= 0 ? ((wpos1 >> 9) + 1) * (MASK_TILE / BN) : 0);
+        kt_full = min(kt_full, wpos0 >= 0 ? (wpos0 >> 9) * (MASK_TILE / BN) : 0);
+    }
+    kt_vis = __builtin_amdgcn_readfirstlane(kt_vis);
+    kt_full = __builtin_amdgcn_readfirstlane(kt_full);
     // can any of the wave's rows see any key of tile kt?
     auto wave_active = [&](int kt) __attribute__((always_inline)) -> bool {
-        if (kt < 0 || kt >= n_kt) return false;
-        const int key0 = kt * BN;
-        if (causal_like) return key0 <= wpos1;
-        if (mask_type == MASK_FREE) return wpos1 >= 0 && (key0 >> 9) <= (wpos1 >> 9);
-        return true;
+        return (unsigned)kt < (unsigned)kt_vis;
     };
     // does every row of the wave see every key of it (no per-element mask)?
-    auto wave_full = [&](int kt) __attribute__((always_inline)) -> bool {
-        const int key0 = kt * BN;
-        bool full = key0 + BN <= kv_len;
-        if (causal_like) full = full && key0 + BN - 1 <= wpos0;
-        else if (mask_type == MASK_FREE) full = full && wpos0 >= 0 && ((key0 + BN - 1) >> 9) < (wpos0 >> 9);
-        return full;
-    };
+    auto wave_full = [&](int kt) __attribute__((always_inline)) -> bool { return kt < kt_full; };
 
     // ---- per-lane LDS read offsets. With the XOR swizzles, the offset of
     // step k (k-step, or 16-key step for V^T) is base ^ (k << 5) for one base
@@ -545,8 +592,12 @@ void mla_fwd_kernel(const FwdParams p) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr int ISS = decltype(do_iss)::value;
         constexpr bool VT = decltype(do_vt)::value;
-        constexpr int NLOADS = ISS == ISS_K ? K_LOADS : (ISS == ISS_V ? V_LOADS : 0);
+        // ISS_K2 (tile 0's scores only): the K of two tiles, tlv's then tlk's,
+        // one load every other MFMA
+        constexpr int NLOADS = ISS == ISS_K ? K_LOADS : (ISS == ISS_V ? V_LOADS : (ISS == ISS_K2 ? 2 * K_LOADS : 0));
+        constexpr int SPACING = ISS == ISS_K2 ? 2 : LOAD_SPACING;
         constexpr int n0 = PV ? 0 : NV, n1 = QK ? NV + 2 * (NKS + 4) : NV;
+        static_assert(NLOADS * SPACING <= n1 - n0, "matrix block too short for its loads");
         // the wave feeding the matrix core wins issue arbitration against the
         // other wave of its SIMD, which runs a vector block meanwhile
         __builtin_amdgcn_s_setprio(1);
@@ -584,9 +635,12 @@ void mla_fwd_kernel(const FwdParams p) {
                 write_vt_piece(vt_st, vwb, n - n0, vst);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (NLOADS && (n - n0) % LOAD_SPACING == LOAD_SPACING - 1 && (n - n0) / LOAD_SPACING < NLOADS) {
-                if (ISS == ISS_V) issue_v(tlv, (n - n0) / LOAD_SPACING);
-                else issue_k(tlk, (n - n0) / LOAD_SPACING);
+            if (NLOADS && (n - n0) % SPACING == SPACING - 1 && (n - n0) / SPACING < NLOADS) {
+                const int li = (n - n0) / SPACING;
+                if (ISS == ISS_V) issue_v(tlv, li);
+                else if (ISS == ISS_K2 && li < K_LOADS) issue_k(tlv, li);
+                else if (ISS == ISS_K2) issue_k(tlk, li - K_LOADS);
+                else issue_k(tlk, li);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -652,10 +706,20 @@ void mla_fwd_kernel(const FwdParams p) {
                     }
             }
         }
-        float m4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+        // Row max as a tree of three-input maxima on the raw scores (no NaN
+        // canonicalisation: the scores come straight from the MFMA).
+        float mx;
+        {
+            float t[11];
 #pragma unroll
-        for (int t = 4; t < 32; ++t) m4[t & 3] = fmaxf(m4[t & 3], s[t >> 4][t & 15]);
-        const float mx = max_with_partner(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+            for (int i = 0; i < 10; ++i)
+                t[i] = max3f(s[(3 * i) >> 4][(3 * i) & 15], s[(3 * i + 1) >> 4][(3 * i + 1) & 15],
+                             s[(3 * i + 2) >> 4][(3 * i + 2) & 15]);
+            t[10] = max3f(s[1][14], s[1][15], s[1][15]);
+            const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]), u2 = max3f(t[6], t[7], t[8]);
+            const float u3 = max3f(t[9], t[10], u2);
+            mx = max_with_partner(max3f(u0, u1, u3));
+        }
         // move the running max only if some row of the wave rose past the threshold
         const bool need = (mx - m_run) * c > RESCALE_THRESHOLD;
         if (__builtin_amdgcn_ballot_w64(need)) {
@@ -669,22 +733,32 @@ void mla_fwd_kernel(const FwdParams p) {
             m_run = m_new;
         }
         const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-        // probabilities, rounded to the input dtype for the PV product; the row
-        // sum adds them in fp32 (plain adds: the dot2 instructions would queue
-        // behind the other wave's MFMAs), in four independent partial sums
-        float lsum[4];
+        // Probabilities in independent phases -- all exponent arguments, then
+        // all exponentials, then the packing and the row sum -- so that no
+        // instruction waits on the one just before it.
+#pragma unroll
+        for (int t = 0; t < 32; ++t) s[t >> 4][t & 15] = __builtin_fmaf(s[t >> 4][t & 15], c, -mc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 32; ++t) s[t >> 4][t & 15] = fast_exp2(s[t >> 4][t & 15]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 32; t += 2) {
             const int kb = t >> 4, e = t & 15;
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][e], c, -mc));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][e + 1], c, -mc));
-            const typename T::pair pr = T::pack(p0, p1);
-            if (t < 8) lsum[t >> 1] = p0 + p1;
-            else lsum[(t >> 1) & 3] += p0 + p1;
+            const typename T::pair pr = T::pack(s[kb][e], s[kb][e + 1]);
             pb[kb * 2 + (e >> 3)][e & 7] = pr[0];
             pb[kb * 2 + (e >> 3)][(e & 7) + 1] = pr[1];
         }
-        l_run += (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+        {
+            float a[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) a[i] = s[(2 * i) >> 4][(2 * i) & 15] + s[(2 * i + 1) >> 4][(2 * i + 1) & 15];
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int i = 0; i < w; ++i) a[i] += a[i + w];
+            l_run += a[0];
+        }
     };
 
     const std::integral_constant<bool, true> yes{};
@@ -693,6 +767,7 @@ void mla_fwd_kernel(const FwdParams p) {
     const std::integral_constant<int, ISS_NONE> iss_none{};
     const std::integral_constant<int, ISS_K> iss_k{};
     const std::integral_constant<int, ISS_V> iss_v{};
+    const std::integral_constant<int, ISS_K2> iss_k2{};
     auto stage_ptr = [&](int r) __attribute__((always_inline)) -> const unsigned char * {
         return smem + r * STAGE_BYTES;
     };
@@ -769,8 +844,20 @@ void mla_fwd_kernel(const FwdParams p) {
         }
     };
     if (grp == 0) {
-        if (wave_active(0))
-            mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_none, no, none, none, nullptr, nullptr);
+        // interval 0: scores of tile 0, and the K of tiles 1 and 2 goes out;
+        // tile 0's raw V (issued before them) has landed at its end
+        {
+            const TileLoad t1 = prep_tile(1, cache_row(1)), t2 = prep_tile(2, cache_row(2));
+            if (wave_active(0)) {
+                mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_k2, no, t1, t2, nullptr, nullptr);
+            } else {
+#pragma unroll
+                for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
+#pragma unroll
+                for (int i = 0; i < K_LOADS; ++i) issue_k(t2, i);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS));
+        }
         for (int j = 0; j < n_kt; j += STAGES) {
             tile_pair(j, std::integral_constant<int, 0>{}, yes);
             if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
@@ -838,7 +925,7 @@ void mla_fwd_kernel(const FwdParams p) {
                                                       (((4 * db + i) ^ row_swizzle<DN>(sr)) << 4) + g * 8) = v4;
             }
         const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)seq.q_off + row0;
+        const int64_t tok = (int64_t)task.q_off + row0;
         const i32x4 ro = make_rsrc(static_cast<unsigned char *>(p.out) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
         constexpr int CPR = DN / 8;      // 16-byte chunks of a row

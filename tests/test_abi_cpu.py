@@ -130,22 +130,91 @@ def test_two_dimensional_forms_and_padded_kv_accepted():
     assert status_of(t) == "MLA_ERR_SHAPE"
 
 
+# The launching entry points are called here straight through ctypes, with
+# descriptors built the binding's way: the binding itself refuses host memory
+# for device arguments before it reaches the C call (tested below), and these
+# tests are about the C library's own validation, which runs before any HIP
+# call and never dereferences a tensor pointer.
+
+def c_status(rc):
+    return mla.STATUS.get(rc, str(rc))
+
+
+def c_mla_prefill(t, workspace):
+    keep = []
+    args = mla._prefill_args(**t, keep=keep)
+    ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    size = workspace.numel() if workspace is not None else 0
+    return c_status(mla._load().mla_prefill(*args, ctypes.c_void_p(ptr), ctypes.c_uint64(size), None))
+
+
+def c_paged_cache_load(key_cache, value_cache, block_tables, context_lens, key, value, seq_starts, kv_cache_cfg,
+                       is_seq_lens_cumsum_type, has_seq_starts):
+    keep = []
+    d = lambda x: mla._desc(x, keep)
+    return c_status(mla._load().paged_cache_load(d(key_cache), d(value_cache), d(block_tables), d(context_lens),
+                                                 d(key), d(value), d(seq_starts), int(kv_cache_cfg),
+                                                 bool(is_seq_lens_cumsum_type), bool(has_seq_starts), None))
+
+
+def c_mla_prolog(kw, workspace):
+    keep = []
+    args = mla._prolog_args(**kw, keep=keep)
+    return c_status(mla._load().mla_prolog(*args, None, ctypes.c_uint64(0), None))
+
+
 def test_workspace_checks_before_any_launch():
     t = tensors()
     need = ws_size(t)
     small = torch.zeros(need - 1, dtype=torch.uint8)
-    with pytest.raises(mla.MlaError) as e:
-        mla.mla_prefill(**t, workspace=small, stream=0)
-    assert e.value.status == "MLA_ERR_WORKSPACE"
+    assert c_mla_prefill(t, small) == "MLA_ERR_WORKSPACE"
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
 def test_no_device_is_a_runtime_error():
     t = tensors()
     ws = torch.zeros(ws_size(t), dtype=torch.uint8)
-    with pytest.raises(mla.MlaError) as e:
+    assert c_mla_prefill(t, ws) == "MLA_ERR_RUNTIME"
+
+
+# ------------------------------------------------------- binding: device memory
+
+def test_binding_refuses_host_memory_for_device_arguments():
+    """A host pointer given to a kernel faults the GPU: the binding raises
+    ValueError before the C call when a device argument is a numpy array or a
+    CPU tensor (these would otherwise pass the C validation, which reads only
+    shapes and dtypes)."""
+    t = tensors()
+    ws = torch.zeros(ws_size(t), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="q must be a torch tensor in GPU memory"):
         mla.mla_prefill(**t, workspace=ws, stream=0)
-    assert e.value.status == "MLA_ERR_RUNTIME"
+    with pytest.raises(ValueError, match="GPU memory"):
+        mla.prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], t["q_seqlen"], t["kv_seqlen"], 4, 4, 0.1,
+                    mla.MASK_CAUSAL)
+    g = gather_args()
+    g["context_lens"] = np.zeros(2, np.int32)  # host lengths: the gather reads them on the device
+    with pytest.raises(ValueError, match="key_cache must be a torch tensor in GPU memory"):
+        mla.paged_cache_load(**g, stream=0)
+    with pytest.raises(ValueError, match="GPU memory"):
+        mla.mla_prolog(**prolog_args(t=0), workspace=None, stream=0)
+    with pytest.raises(ValueError, match="GPU memory"):
+        mla.mla_prefill_paged(t["q"], t["q_rope"], torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16),
+                              torch.zeros(1, 64, 4, 64, dtype=torch.bfloat16),
+                              torch.zeros(1, 64, 4, 128, dtype=torch.bfloat16), torch.zeros(2, 1, dtype=torch.int32),
+                              t["q_seqlen"], t["kv_seqlen"], None, 4, 0.1, 4, mla.MASK_CAUSAL, t["atten_out"], ws,
+                              stream=0)
+
+
+def test_device_check_names_the_host_argument():
+    class FakeCuda:  # stands in for a device tensor in the check's eyes only
+        pass
+    with pytest.raises(ValueError, match="context_lens must be .* \\(got ndarray\\)"):
+        mla._on_device([("context_lens", np.zeros(2, np.int32))])
+    with pytest.raises(ValueError, match="got tensor on cpu"):
+        mla._on_device([("q", torch.zeros(2))])
+    with pytest.raises(ValueError, match="got FakeCuda"):
+        mla._on_device([("v", FakeCuda())])
+    mla._on_device([("mask", None)])  # absent optional arguments are fine
 
 
 def gather_args(**kw):
@@ -172,9 +241,7 @@ def gather_args(**kw):
     (dict(key_cache=torch.zeros(4, 8, 2, 16, dtype=torch.float32)), "MLA_ERR_DTYPE"),
 ])
 def test_gather_validation_errors(kw, status):
-    with pytest.raises(mla.MlaError) as e:
-        mla.paged_cache_load(**gather_args(**kw), stream=0)
-    assert e.value.status == status
+    assert c_paged_cache_load(**gather_args(**kw)) == status
 
 
 def nz_args(**kw):
@@ -199,18 +266,16 @@ def nz_args(**kw):
     (dict(value_cache=torch.zeros(4, 8, 4, 16, dtype=torch.bfloat16)), "MLA_ERR_SHAPE"),   # block size differs
 ])
 def test_gather_nz_validation_errors(kw, status):
-    with pytest.raises(mla.MlaError) as e:
-        mla.paged_cache_load(**nz_args(**kw), stream=0)
-    assert e.value.status == status
+    assert c_paged_cache_load(**nz_args(**kw)) == status
 
 
 def test_gather_nz_valid_shapes_pass_validation():
     # zero tokens: validation passes and nothing is launched (no HIP call here)
-    mla.paged_cache_load(**nz_args(key=torch.zeros(0, 256, dtype=torch.bfloat16),
-                                   value=torch.zeros(0, 128, dtype=torch.bfloat16)), stream=0)
-    mla.paged_cache_load(**nz_args(key_cache=torch.zeros(4, 8, 8, 32, dtype=torch.int8),
-                                   key=torch.zeros(0, 256, dtype=torch.int8), value_cache=None, value=None),
-                         stream=0)
+    assert c_paged_cache_load(**nz_args(key=torch.zeros(0, 256, dtype=torch.bfloat16),
+                                        value=torch.zeros(0, 128, dtype=torch.bfloat16))) == "MLA_OK"
+    assert c_paged_cache_load(**nz_args(key_cache=torch.zeros(4, 8, 8, 32, dtype=torch.int8),
+                                        key=torch.zeros(0, 256, dtype=torch.int8), value_cache=None,
+                                        value=None)) == "MLA_OK"
 
 
 # ------------------------------------------------------------------ planner
@@ -410,7 +475,7 @@ def test_prolog_workspace_size_and_empty_call():
     assert mla.mla_prolog_get_workspace_size(**prolog_args(t=0)) == 0
     assert mla.mla_prolog_get_workspace_size(**prolog_args(t=3)) == 256 * -(-3 * 512 * 4 // 256)
     # t = 0: valid, nothing to launch (no HIP call)
-    mla.mla_prolog(**prolog_args(t=0), workspace=None, stream=0)
+    assert c_mla_prolog(prolog_args(t=0), None) == "MLA_OK"
 
 
 def test_prolog_validation_errors():
@@ -439,7 +504,5 @@ def test_gather_batch_limit():
                            context_lens=torch.zeros(batch, dtype=torch.int32),
                            key=torch.zeros(0, 2, 16, dtype=torch.bfloat16),
                            value=torch.zeros(0, 2, 16, dtype=torch.bfloat16))
-    mla.paged_cache_load(**args(8192), stream=0)  # valid; zero tokens, nothing launched
-    with pytest.raises(mla.MlaError) as e:
-        mla.paged_cache_load(**args(8193), stream=0)
-    assert e.value.status == "MLA_ERR_UNSUPPORTED"
+    assert c_paged_cache_load(**args(8192)) == "MLA_OK"  # valid; zero tokens, nothing launched
+    assert c_paged_cache_load(**args(8193)) == "MLA_ERR_UNSUPPORTED"
