@@ -555,11 +555,7 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.n_tasks = (int32_t)plan.tasks.size();
     p.mask_type = pr.mask_type;
     p.mask_is_bf16 = (pr.mask_type == MLA_MASK_FREE && mask->dtype == MLA_BF16) ? 1 : 0;
-    // A zero (or denormal) scale is replaced by +-1e-30: the kernel divides mask
-    // values by the scale, and the change is below fp32 resolution of the scores.
-    double scale = (double)qk_scale;
-    if (std::fabs(scale) < 1e-30) scale = std::signbit(scale) ? -1e-30 : 1e-30;
-    p.scale_log2 = (float)(scale * 1.4426950408889634);
+    p.qk_scale = qk_scale;
     if (pg) {
         p.block_tables = block_tables;
         p.bt_stride = (int32_t)pg->bt_stride;

@@ -82,7 +82,7 @@ struct FwdParams {
     int32_t n_tasks;      // workgroups to launch
     int32_t pack_shift;   // log2 of the query heads one workgroup runs
     int32_t head_dim;     // embeddimV: 64 or 128
-    float scale_log2;     // qkScale * log2(e)
+    float qk_scale;       // qkScale as given (any finite value, 0 included)
     // Paged K/V (launch_mla_fwd with paged = true): k, k_rope and v point at
     // ND caches [num_blocks, block_size, Hkv, D | 64 | D]; key t of
     // sequence b is slot t % block_size of block block_tables[b][t / block_size].

@@ -103,7 +103,9 @@ template <int D>
 __device__ __forceinline__ int row_swizzle(int r) {
     return D == 128 ? (r & 15) : ((r >> 1) & 7);
 }
-constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units
+// The running max moves only when a row's max rises by more than this many
+// natural-log units (2^8 in probability), so probabilities stay <= 256.
+constexpr float RESCALE_THRESHOLD = 5.545177444479562f;  // 8 ln 2
 constexpr float LOG2E = 1.4426950408889634f;
 
 constexpr int MASK_UNDEFINED = 0;
@@ -140,6 +142,10 @@ struct Bf16 {
     static __device__ __forceinline__ pair pack(float a, float b) {
         return pair{static_cast<__bf16>(a), static_cast<__bf16>(b)};
     }
+    // sum of the two values of a packed pair, in fp32 (exact widening)
+    static __device__ __forceinline__ float pair_sum(unsigned w) {
+        return __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
+    }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
@@ -151,6 +157,10 @@ struct Fp16 {
     typedef _Float16 scalar;
     static __device__ __forceinline__ pair pack(float a, float b) {
         return pair{static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    }
+    static __device__ __forceinline__ float pair_sum(unsigned w) {
+        const pair x = __builtin_bit_cast(pair, w);
+        return static_cast<float>(x[0]) + static_cast<float>(x[1]);
     }
     static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -215,7 +225,9 @@ __device__ __forceinline__ void block_sync() {
 // the LDS past the ring.
 constexpr int TILE_TABLE_BYTES = PAGED_MAX_TILES * 4;
 
-template <typename T, bool PAGED, int DN>
+// MF: the MASK_FREE instance (the 512 x 512 tile is read on diagonal blocks);
+// the other mask types share the other instance.
+template <typename T, bool PAGED, int DN, bool MF>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void mla_fwd_kernel(const FwdParams p) {
     constexpr int KN_BYTES = Geom<DN>::KN_BYTES;
@@ -260,8 +272,8 @@ void mla_fwd_kernel(const FwdParams p) {
     const int q_len = task.q_len;
     const int kv_len = task.kv_len;
     const int n_kt = task.kv_tiles;
-    const int mask_type = p.mask_type;
-    const bool causal_like = mask_type != MASK_UNDEFINED && mask_type != MASK_FREE;
+    const int mask_type = MF ? MASK_FREE : p.mask_type;
+    const bool causal_like = !MF && mask_type != MASK_UNDEFINED;
 
     const int lrow0 = (slot >> ps) * 32;            // first row of this wave within the item
     const int row0 = task.q_row0 + lrow0;           // ... within the sequence
@@ -452,14 +464,13 @@ void mla_fwd_kernel(const FwdParams p) {
     };
     // the transpose and the next raw V loads alone, for a trailing wave that
     // runs no matrix block
-    auto transpose_v = [&](const unsigned char *vr, unsigned char *st, const TileLoad &tl)
-                           __attribute__((always_inline)) {
+    auto transpose_v = [&](const unsigned char *vr, uint32_t st, const TileLoad &tl) __attribute__((always_inline)) {
         uint4 vst[V_LOADS];
         read_vraw(vr, vst);
-        uint32_t vwb = vw_base;
+        uint32_t vwb = vw_base + st;
         asm volatile("" : "+v"(vwb));
 #pragma unroll
-        for (int q = 0; q < VT_PIECES; ++q) write_vt_piece(st, vwb, q, vst);
+        for (int q = 0; q < VT_PIECES; ++q) write_vt_piece(smem, vwb, q, vst);
 #pragma unroll
         for (int i = 0; i < V_LOADS; ++i) issue_v(tl, i);
     };
@@ -501,8 +512,13 @@ void mla_fwd_kernel(const FwdParams p) {
 
     // A negative scale is folded into Q so the row max can be taken on raw
     // scores: Q-nope and Q-rope are negated in registers.
-    const float c = fabsf(p.scale_log2);
-    if (p.scale_log2 < 0.f) {
+    // natural-log units per unit of the raw dot product, and log2 units. A zero
+    // scale is taken as 1e-30, so that a masked -inf times the scale stays
+    // -inf: every score it yields is then so small that exp2 rounds it to
+    // exactly 1, as 0 would.
+    const float c_nat = fmaxf(fabsf(p.qk_scale), 1e-30f);
+    const float c2 = c_nat * LOG2E;
+    if (p.qk_scale < 0.f) {
 #pragma unroll
         for (int ks = 0; ks < NKS + 4; ++ks) {
             vec8 &q = ks < NKS ? qreg[ks] : qrreg[ks - NKS];
@@ -525,7 +541,7 @@ void mla_fwd_kernel(const FwdParams p) {
     if (causal_like) {
         kt_vis = min(n_kt, wpos1 >= 0 ? wpos1 / BN + 1 : 0);
         kt_full = min(kt_full, max(0, (wpos0 + 1) / BN));
-    } else if (mask_type == MASK_FREE) {
+    } else if (MF) {
         kt_vis = min(n_kt, wpos1 >= 0 ? ((wpos1 >> 9) + 1) * (MASK_TILE / BN) : 0);
         kt_full = min(kt_full, wpos0 >= 0 ? (wpos0 >> 9) * (MASK_TILE / BN) : 0);
     }
@@ -556,16 +572,18 @@ void mla_fwd_kernel(const FwdParams p) {
     // operand n of a matrix block: n < NV -> V^T of (16-key step n / NDB, column
     // block n % NDB) from stage sv; n >= NV -> K of (k-step (n - NV) / 2, key
     // block (n - NV) % 2) from sk, the first NKS k-steps nope, the last 4 rope
-    auto load_operand = [&](const unsigned char *sv, const unsigned char *sk, int n, uint32_t knb, uint32_t krb,
-                            uint32_t vtb) __attribute__((always_inline)) -> vec8 {
-        if (n < NV) return lds16(sv + (vtb ^ ((n / NDB) << 5)) + (n % NDB) * 32 * 128);
+    // The bases passed in carry their stage's byte offset (a multiple of 8 KB,
+    // so it never meets the XOR-ed bits).
+    auto load_operand = [&](int n, uint32_t knb, uint32_t krb, uint32_t vtb) __attribute__((always_inline)) -> vec8 {
+        if (n < NV) return lds16(smem + (vtb ^ ((n / NDB) << 5)) + (n % NDB) * 32 * 128);
         const int ks = (n - NV) >> 1, kb = (n - NV) & 1;
-        if (ks < NKS) return lds16(sk + (knb ^ (ks << 5)) + kb * 32 * KN_ROW);
-        return lds16(sk + (krb ^ ((ks - NKS) << 5)) + kb * 32 * 128);
+        if (ks < NKS) return lds16(smem + (knb ^ (ks << 5)) + kb * 32 * KN_ROW);
+        return lds16(smem + (krb ^ ((ks - NKS) << 5)) + kb * 32 * 128);
     };
+    static_assert(STAGE_BYTES % 8192 == 0 && (KN_BYTES + KR_BYTES) % 8192 == 0, "stage offsets must clear the swizzle bits");
 
     // ---- softmax state
-    float m_run = -INFINITY;  // running row max of raw scores (same in both lanes of a row)
+    float m_run = -INFINITY;  // running row max, natural-log units (same in both lanes of a row)
     float l_run = 0.f;        // this lane's share of the running row sum
     f32x16 o[NDB];
 #pragma unroll
@@ -586,9 +604,9 @@ void mla_fwd_kernel(const FwdParams p) {
     // raw chunks are read ahead of the first MFMA, and the V^T writes go out
     // one piece after each of the first MFMAs (a burst of these writes ahead
     // of the block held back its first MFMA).
-    auto mfma_block = [&](const unsigned char *sv, const unsigned char *sk, auto do_pv, auto do_qk, auto do_iss,
-                          auto do_vt, const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src,
-                          unsigned char *vt_st) __attribute__((always_inline)) {
+    auto mfma_block = [&](uint32_t sv, uint32_t sk, auto do_pv, auto do_qk, auto do_iss, auto do_vt,
+                          const TileLoad &tlv, const TileLoad &tlk, const unsigned char *vt_src, uint32_t vt_st)
+                          __attribute__((always_inline)) {
         constexpr bool PV = decltype(do_pv)::value, QK = decltype(do_qk)::value;
         constexpr int ISS = decltype(do_iss)::value;
         constexpr bool VT = decltype(do_vt)::value;
@@ -607,7 +625,7 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) s[kb][e] = 0.f;
         }
-        uint32_t knb = kn_base, krb = kr_base, vtb = vt_base, vwb = vw_base;
+        uint32_t knb = kn_base + sk, krb = kr_base + sk, vtb = vt_base + sv, vwb = vw_base + vt_st;
         asm volatile("" : "+v"(knb), "+v"(krb), "+v"(vtb));
         if (VT) asm volatile("" : "+v"(vwb));
         // raw V chunks first: LDS returns in order, so they have landed by the
@@ -617,11 +635,11 @@ void mla_fwd_kernel(const FwdParams p) {
         vec8 ring[PREFETCH + 1];
 #pragma unroll
         for (int d = 0; d < PREFETCH; ++d)
-            if (n0 + d < n1) ring[d] = load_operand(sv, sk, n0 + d, knb, krb, vtb);
+            if (n0 + d < n1) ring[d] = load_operand(n0 + d, knb, krb, vtb);
 #pragma unroll
         for (int n = n0; n < n1; ++n) {
             if (n + PREFETCH < n1)
-                ring[(n + PREFETCH - n0) % (PREFETCH + 1)] = load_operand(sv, sk, n + PREFETCH, knb, krb, vtb);
+                ring[(n + PREFETCH - n0) % (PREFETCH + 1)] = load_operand(n + PREFETCH, knb, krb, vtb);
             __builtin_amdgcn_sched_barrier(0);
             const vec8 a = ring[(n - n0) % (PREFETCH + 1)];
             if (n < NV) {
@@ -632,7 +650,7 @@ void mla_fwd_kernel(const FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
             if (VT && n - n0 < VT_PIECES) {
-                write_vt_piece(vt_st, vwb, n - n0, vst);
+                write_vt_piece(smem, vwb, n - n0, vst);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (NLOADS && (n - n0) % SPACING == SPACING - 1 && (n - n0) / SPACING < NLOADS) {
@@ -648,83 +666,92 @@ void mla_fwd_kernel(const FwdParams p) {
     };
 
     // ---- vector block for tile kt: mask (if needed), row max, lazy rescale,
-    // probabilities -> pb, row sums.
-    const float inv_c = 1.f / c;
+    // probabilities -> pb, row sums. The running max m_run is kept in
+    // natural-log units (|qkScale| * dot + tile entry). The scores stay raw dot
+    // products, rewritten in place: the causal and undefined masks set masked
+    // keys to -inf; the row max of the raw scores, scaled, is the tile's max;
+    // the exponent arguments are one fma, s * c2 - m_run * log2(e). A
+    // MASK_FREE tile on the diagonal block takes its max on
+    // fma(s, |qkScale|, entry) over the visible keys and its arguments are
+    // fma(s, c2, (entry - m_run) * log2(e)), -inf where masked: with a zero
+    // entry that is the plain fma bit for bit (so MASK_FREE with a causal tile
+    // equals CAUSAL exactly), a tile entry is never divided by the scale, and
+    // an entry near the largest finite value only meets a running max of its
+    // own size. Every path rewrites the scores in place: with a separate
+    // result per path the compiler copied all 32 scores where they merge.
+    const i32x4 mask_rsrc = make_rsrc(p.mask, MF ? MASK_TILE * MASK_TILE * 2 : 0);
     auto valu_block = [&](int kt) __attribute__((always_inline)) {
-        // The mask (only on tiles that cut the wave's rows) rewrites the scores
-        // in place; the row max is then common code. With the max inside each
-        // branch the compiler gave the two paths different registers and
-        // copied all 32 scores at the merge.
-        if (!wave_full(kt)) {
+        const bool full = wave_full(kt);
+        // Masked tile: element e is key key0 + 8g + off(e), visible iff
+        // off(e) <= lim (one limit per lane). Key j is visible iff j <= min(pos,
+        // kv_len - 1) (causal modes) or j <= kv_len - 1 (UNDEFINED). MASK_FREE:
+        // a 64-key tile lies inside one 512-key block, so the block rule gives
+        // one limit too: keys of an earlier block are visible (up to kv_len - 1),
+        // of a later one not; on the diagonal block the row of the 512 x 512
+        // tile is added, read as four 16-byte runs of 8 entries (the keys
+        // 8g + 32kb + 16h + 0..7; the host accepts only 16-byte aligned tiles).
+        // Lanes off the diagonal block read past the tile's end, which returns
+        // zeros, so the entry is 0 there without a branch.
+        auto off_of = [](int e) { return (e >> 4) * 32 + 16 * ((e & 15) >> 3) + (e & 7); };
+        int lim = 0;
+        uint32_t mw[16];
+        auto entry = [&](int e) __attribute__((always_inline)) -> float {
+            const uint32_t w = mw[e >> 1];
+            const unsigned short b = (unsigned short)(w >> (16 * (e & 1)));
+            return p.mask_is_bf16 ? bits_to_float_bf16(b) : bits_to_float_f16(b);
+        };
+        if (!full) {
             const int key0 = kt * BN;
-            if (mask_type != MASK_FREE) {
-                // Key j is visible iff j <= min(pos, kv_len - 1) (causal modes)
-                // or j <= kv_len - 1 (UNDEFINED). Element e of block kb is key
-                // key0 + 8g + off(kb, e), so one per-lane limit on the constant
-                // offset decides each element with a compare and a select.
-                const int lim = (causal_like ? min(pos, kv_len - 1) : kv_len - 1) - key0 - 8 * g;
+            if (!MF) {
+                lim = (causal_like ? min(pos, kv_len - 1) : kv_len - 1) - key0 - 8 * g;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int off = kb * 32 + 16 * (e >> 3) + (e & 7);
-                        s[kb][e] = off <= lim ? s[kb][e] : -INFINITY;
-                    }
+                for (int e = 0; e < 32; ++e) s[e >> 4][e & 15] = off_of(e) <= lim ? s[e >> 4][e & 15] : -INFINITY;
             } else {
-                // MASK_FREE: a 64-key tile lies inside one 512-key block, so the
-                // block rule gives one limit per lane: keys of an earlier block
-                // are visible (up to kv_len - 1), of a later one not; on the
-                // diagonal block the row of the 512 x 512 tile is added, read as
-                // four 16-byte runs of 8 entries (the keys 8g + 32kb + 16h +
-                // 0..7; the host accepts only 16-byte aligned tiles).
-                const int jb = key0 >> 9, pb = pos >> 9;
-                const int lim = (pos < 0 || jb > pb) ? -1 : kv_len - 1 - key0 - 8 * g;
-                if (pos >= 0 && jb == pb) {
-                    const unsigned short *mrow = static_cast<const unsigned short *>(p.mask) +
-                                                 (pos & (MASK_TILE - 1)) * MASK_TILE + (key0 & (MASK_TILE - 1)) + 8 * g;
+                const int jb = key0 >> 9, pblk = pos >> 9;
+                lim = (pos < 0 || jb > pblk) ? -1 : kv_len - 1 - key0 - 8 * g;
+                int pp = pos;  // formed here: kept live across the loop it would cost registers
+                asm volatile("" : "+v"(pp));
+                const uint32_t mo = (pp >= 0 && jb == pblk)
+                                        ? (uint32_t)(((pp & (MASK_TILE - 1)) * MASK_TILE + (key0 & (MASK_TILE - 1)) +
+                                                      8 * g) * 2)
+                                        : 0x40000000u;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int kb = q >> 1, hh = q & 1;
-                        const uint4 w = *reinterpret_cast<const uint4 *>(mrow + kb * 32 + hh * 16);
-                        const unsigned ws[4] = {w.x, w.y, w.z, w.w};
+                for (int q = 0; q < 4; ++q) {
+                    const i32x4 w = mla_raw_buffer_load_b128(mask_rsrc, mo + (q >> 1) * 64 + (q & 1) * 32, 0, 0);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const unsigned short mbits = (unsigned short)(ws[i >> 1] >> (16 * (i & 1)));
-                            // tile entry m is added as m * log2(e) / c, so the
-                            // fma with c below turns it into m * log2(e)
-                            const float mv = p.mask_is_bf16 ? bits_to_float_bf16(mbits) : bits_to_float_f16(mbits);
-                            s[kb][8 * hh + i] += mv * LOG2E * inv_c;
-                        }
-                    }
+                    for (int i = 0; i < 4; ++i) mw[4 * q + i] = (uint32_t)w[i];
                 }
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int off = kb * 32 + 16 * (e >> 3) + (e & 7);
-                        s[kb][e] = off <= lim ? s[kb][e] : -INFINITY;
-                    }
             }
         }
-        // Row max as a tree of three-input maxima on the raw scores (no NaN
-        // canonicalisation: the scores come straight from the MFMA).
-        float mx;
-        {
+        // Row max as a tree of three-input maxima (no NaN canonicalisation: the
+        // scores come straight from the MFMA), in natural-log units.
+        float lane_max = 0.f;  // this lane's own max (before its partner's), as max_tree takes it
+        auto max_tree = [&](auto val) __attribute__((always_inline)) -> float {
             float t[11];
 #pragma unroll
-            for (int i = 0; i < 10; ++i)
-                t[i] = max3f(s[(3 * i) >> 4][(3 * i) & 15], s[(3 * i + 1) >> 4][(3 * i + 1) & 15],
-                             s[(3 * i + 2) >> 4][(3 * i + 2) & 15]);
-            t[10] = max3f(s[1][14], s[1][15], s[1][15]);
+            for (int i = 0; i < 10; ++i) t[i] = max3f(val(3 * i), val(3 * i + 1), val(3 * i + 2));
+            const float v31 = val(31);
+            t[10] = max3f(val(30), v31, v31);
             const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]), u2 = max3f(t[6], t[7], t[8]);
             const float u3 = max3f(t[9], t[10], u2);
-            mx = max_with_partner(max3f(u0, u1, u3));
+            lane_max = max3f(u0, u1, u3);
+            return max_with_partner(lane_max);
+        };
+        const bool mf_masked = MF && !full;
+        float mx;
+        if (!mf_masked) {
+            // the scale is > 0, so it commutes with the max (and keeps -inf)
+            mx = max_tree([&](int e) { return s[e >> 4][e & 15]; }) * c_nat;
+        } else {
+            mx = max_tree([&](int e) {
+                return off_of(e) <= lim ? __builtin_fmaf(s[e >> 4][e & 15], c_nat, entry(e)) : -INFINITY;
+            });
         }
         // move the running max only if some row of the wave rose past the threshold
-        const bool need = (mx - m_run) * c > RESCALE_THRESHOLD;
+        const bool need = mx - m_run > RESCALE_THRESHOLD;
         if (__builtin_amdgcn_ballot_w64(need)) {
             const float m_new = fmaxf(m_run, mx);
-            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * c);
+            const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2((m_run - m_new) * LOG2E);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
@@ -732,12 +759,27 @@ void mla_fwd_kernel(const FwdParams p) {
                 for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
             m_run = m_new;
         }
-        const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+        const float mr = (m_run == -INFINITY) ? 0.f : m_run;
         // Probabilities in independent phases -- all exponent arguments, then
         // all exponentials, then the packing and the row sum -- so that no
         // instruction waits on the one just before it.
+        const float m2 = mr * LOG2E;
+        float pm_arg;  // exponent argument of the lane's largest probability (for the row sum below)
+        if (!mf_masked) {
+            pm_arg = __builtin_fmaf(lane_max, c2, -m2);
 #pragma unroll
-        for (int t = 0; t < 32; ++t) s[t >> 4][t & 15] = __builtin_fmaf(s[t >> 4][t & 15], c, -mc);
+            for (int t = 0; t < 32; ++t) s[t >> 4][t & 15] = __builtin_fmaf(s[t >> 4][t & 15], c2, -m2);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 32; ++t)
+                s[t >> 4][t & 15] = off_of(t) <= lim
+                                        ? __builtin_fmaf(s[t >> 4][t & 15], c2, (entry(t) - mr) * LOG2E)
+                                        : -INFINITY;
+            // the fma is monotone in the score, so with zero entries this is
+            // the other path's value bit for bit
+            (void)max_tree([&](int e) { return s[e >> 4][e & 15]; });
+            pm_arg = lane_max;
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 32; ++t) s[t >> 4][t & 15] = fast_exp2(s[t >> 4][t & 15]);
@@ -750,6 +792,13 @@ void mla_fwd_kernel(const FwdParams p) {
             pb[kb * 2 + (e >> 3)][(e & 7) + 1] = pr[1];
         }
         {
+            // Row sum in fp32. The P.V product sees each probability rounded to
+            // the input dtype; for the lane's largest one the sum takes the
+            // rounded value too, so a row whose weight sits on one key returns
+            // that key's values whatever the rounding (with bf16 and a large
+            // scale that rounding error, up to 2^-8 of the output, was the
+            // largest one). The other probabilities' rounding errors weigh
+            // with their (smaller) share of the row.
             float a[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) a[i] = s[(2 * i) >> 4][(2 * i) & 15] + s[(2 * i + 1) >> 4][(2 * i + 1) & 15];
@@ -757,6 +806,11 @@ void mla_fwd_kernel(const FwdParams p) {
             for (int w = 8; w >= 1; w >>= 1)
 #pragma unroll
                 for (int i = 0; i < w; ++i) a[i] += a[i + w];
+            {
+                const float pm = fast_exp2(pm_arg);  // that probability, bit for bit
+                const typename T::pair pr = T::pack(pm, 0.f);
+                a[0] += T::pair_sum(__builtin_bit_cast(unsigned, pr)) - pm;
+            }
             l_run += a[0];
         }
     };
@@ -768,9 +822,8 @@ void mla_fwd_kernel(const FwdParams p) {
     const std::integral_constant<int, ISS_K> iss_k{};
     const std::integral_constant<int, ISS_V> iss_v{};
     const std::integral_constant<int, ISS_K2> iss_k2{};
-    auto stage_ptr = [&](int r) __attribute__((always_inline)) -> const unsigned char * {
-        return smem + r * STAGE_BYTES;
-    };
+    // byte offset of ring stage r
+    auto soff = [&](int r) __attribute__((always_inline)) -> uint32_t { return (uint32_t)r * STAGE_BYTES; };
 
     // ---- schedule. Interval 0: leading group scores tile 0. Then for each tile
     // j two intervals:
@@ -794,15 +847,15 @@ void mla_fwd_kernel(const FwdParams p) {
     // own copy of the schedule with the same barrier sequence.
     block_sync();
 
-    // one tile's two intervals; R = ring stage of tile j
+    // one tile's two intervals; r0 = ring stage of tile j (a runtime value, so
+    // that each group's loop holds one copy of its matrix and vector blocks)
     // paged, trailing group: cache row of the tile whose raw V goes out next,
     // read from the LDS table in the vector interval before, like the leading
     // group's rows, so that the read's latency stays off the matrix block
     int trail_row_v = 0;
-    auto tile_pair = [&](int j, auto R, auto LEAD) __attribute__((always_inline)) {
-        constexpr int r0 = decltype(R)::value;
+    auto tile_pair = [&](int j, int r0, auto LEAD) __attribute__((always_inline)) {
         constexpr bool lead = decltype(LEAD)::value;
-        constexpr int rprev = (r0 + STAGES - 1) % STAGES, rnext = (r0 + 1) % STAGES;
+        const int rprev = r0 == 0 ? STAGES - 1 : r0 - 1, rnext = r0 == STAGES - 1 ? 0 : r0 + 1;
         block_sync();
         // interval 2j + 1
         int row_k = 0;  // paged: cache row of the tile whose K goes out next interval
@@ -826,17 +879,15 @@ void mla_fwd_kernel(const FwdParams p) {
             unsigned char *vr = smem + VRAW_OFFSET + (j & 1) * V_BYTES;
             const TileLoad tv = prep_tile(j + 1, trail_row_v);
             if (wave_active(j - 1))
-                mfma_block(stage_ptr(rprev), stage_ptr(r0), yes, yes, iss_v, yes, tv, none, vr,
-                           smem + r0 * STAGE_BYTES);
+                mfma_block(soff(rprev), soff(r0), yes, yes, iss_v, yes, tv, none, vr, soff(r0));
             else
-                transpose_v(vr, smem + r0 * STAGE_BYTES, tv);
+                transpose_v(vr, soff(r0), tv);
         }
         block_sync();
         // interval 2j + 2: the leading group sends out K of tile j+3 during its
         // matrix block
         if (lead) {
-            mfma_block(stage_ptr(r0), stage_ptr(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k),
-                       nullptr, nullptr);
+            mfma_block(soff(r0), soff(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k), nullptr, 0);
         } else {
             trail_row_v = cache_row(j + 2);
             if (wave_active(j)) valu_block(j);
@@ -849,7 +900,7 @@ void mla_fwd_kernel(const FwdParams p) {
         {
             const TileLoad t1 = prep_tile(1, cache_row(1)), t2 = prep_tile(2, cache_row(2));
             if (wave_active(0)) {
-                mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_k2, no, t1, t2, nullptr, nullptr);
+                mfma_block(0, 0, no, yes, iss_k2, no, t1, t2, nullptr, 0);
             } else {
 #pragma unroll
                 for (int i = 0; i < K_LOADS; ++i) issue_k(t1, i);
@@ -858,10 +909,11 @@ void mla_fwd_kernel(const FwdParams p) {
             }
             __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * K_LOADS));
         }
-        for (int j = 0; j < n_kt; j += STAGES) {
-            tile_pair(j, std::integral_constant<int, 0>{}, yes);
-            if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 1>{}, yes);
-            if (j + 2 < n_kt) tile_pair(j + 2, std::integral_constant<int, 2>{}, yes);
+        int r = 0;
+#pragma clang loop unroll(disable)
+        for (int j = 0; j < n_kt; ++j) {
+            tile_pair(j, r, yes);
+            r = r == STAGES - 1 ? 0 : r + 1;
         }
         block_sync();
     } else if (n_kt > 0) {
@@ -872,25 +924,24 @@ void mla_fwd_kernel(const FwdParams p) {
         {
             const TileLoad tv = prep_tile(1, cache_row(1));
             if (wave_active(0))
-                mfma_block(stage_ptr(0), stage_ptr(0), no, yes, iss_v, yes, tv, none, smem + VRAW_OFFSET, smem);
+                mfma_block(0, 0, no, yes, iss_v, yes, tv, none, smem + VRAW_OFFSET, 0);
             else
-                transpose_v(smem + VRAW_OFFSET, smem, tv);
+                transpose_v(smem + VRAW_OFFSET, 0, tv);
         }
         block_sync();
         trail_row_v = cache_row(2);
         if (wave_active(0)) valu_block(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile 1 landed
-        for (int j = 1; j < n_kt; j += STAGES) {
-            tile_pair(j, std::integral_constant<int, 1>{}, no);
-            if (j + 1 < n_kt) tile_pair(j + 1, std::integral_constant<int, 2>{}, no);
-            if (j + 2 < n_kt) tile_pair(j + 2, std::integral_constant<int, 0>{}, no);
+        int r = 1;
+#pragma clang loop unroll(disable)
+        for (int j = 1; j < n_kt; ++j) {
+            tile_pair(j, r, no);
+            r = r == STAGES - 1 ? 0 : r + 1;
         }
         block_sync();
         if (wave_active(n_kt - 1)) {
-            const int r = (n_kt - 1) % STAGES;
-            if (r == 0) mfma_block(stage_ptr(0), stage_ptr(0), yes, no, iss_none, no, none, none, nullptr, nullptr);
-            else if (r == 1) mfma_block(stage_ptr(1), stage_ptr(1), yes, no, iss_none, no, none, none, nullptr, nullptr);
-            else mfma_block(stage_ptr(2), stage_ptr(2), yes, no, iss_none, no, none, none, nullptr, nullptr);
+            const uint32_t sl = soff((n_kt - 1) % STAGES);
+            mfma_block(sl, sl, yes, no, iss_none, no, none, none, nullptr, 0);
         }
     } else {
         block_sync();
@@ -947,23 +998,32 @@ hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t
     if (p.n_tasks <= 0) return hipSuccess;
     dim3 grid((unsigned)p.n_tasks);
     dim3 block(FWD_THREADS);
+    const bool mf = p.mask_type == MASK_FREE;
+#define MLA_LAUNCH(TT, PG, D, M) hipLaunchKernelGGL((mla_fwd_kernel<TT, PG, D, M>), grid, block, 0, stream, p)
+#define MLA_LAUNCH_MF(TT, PG, D) \
+    do {                         \
+        if (mf)                  \
+            MLA_LAUNCH(TT, PG, D, true); \
+        else                     \
+            MLA_LAUNCH(TT, PG, D, false); \
+    } while (0)
+#define MLA_LAUNCH_PAGED(TT, D) \
+    do {                        \
+        if (paged)              \
+            MLA_LAUNCH_MF(TT, true, D); \
+        else                    \
+            MLA_LAUNCH_MF(TT, false, D); \
+    } while (0)
     if (p.head_dim == 64) {
-        if (dtype == 2) {
-            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true, 64>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false, 64>), grid, block, 0, stream, p);
-        } else {
-            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true, 64>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false, 64>), grid, block, 0, stream, p);
-        }
+        if (dtype == 2) MLA_LAUNCH_PAGED(Bf16, 64);
+        else MLA_LAUNCH_PAGED(Fp16, 64);
     } else {
-        if (dtype == 2) {
-            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Bf16, true, 128>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mla_fwd_kernel<Bf16, false, 128>), grid, block, 0, stream, p);
-        } else {
-            if (paged) hipLaunchKernelGGL((mla_fwd_kernel<Fp16, true, 128>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((mla_fwd_kernel<Fp16, false, 128>), grid, block, 0, stream, p);
-        }
+        if (dtype == 2) MLA_LAUNCH_PAGED(Bf16, 128);
+        else MLA_LAUNCH_PAGED(Fp16, 128);
     }
+#undef MLA_LAUNCH_PAGED
+#undef MLA_LAUNCH_MF
+#undef MLA_LAUNCH
     return hipGetLastError();
 }
 

@@ -132,6 +132,31 @@ def random_mask_tile(seed, dtype=torch.float16, device="cpu", p_masked=0.2, scal
     return torch.from_numpy(tile.astype(np.float32)).to(dtype).to(device)
 
 
+def extreme_mask_tile(seed, dtype=torch.bfloat16, device="cpu"):
+    """Seeded 512 x 512 tile with entries at the far ends of the dtype's range,
+    on top of random_mask_tile's pattern: in a quarter of the rows 30% of the
+    entries are the most negative finite value of the dtype (-3e38 for bf16,
+    -65504 for fp16); in another quarter 20% are -1e30 (bf16) or -6e4 (fp16);
+    in an eighth of the rows one entry is +1e30 (bf16) or +6e4 (fp16). Every
+    row keeps its diagonal entry small and finite, so it keeps a visible key of
+    moderate score, and has at most one large positive entry."""
+    rng = np.random.default_rng(seed)
+    tile = rng.standard_normal((MASK_TILE, MASK_TILE)) * 2.0
+    tile[rng.random((MASK_TILE, MASK_TILE)) < 0.2] = -np.inf
+    lowest = -3.0e38 if dtype == torch.bfloat16 else -65504.0
+    big = 1.0e30 if dtype == torch.bfloat16 else 6.0e4
+    for r in range(MASK_TILE):
+        u = rng.random()
+        if u < 0.25:
+            tile[r, rng.random(MASK_TILE) < 0.3] = lowest
+        elif u < 0.5:
+            tile[r, rng.random(MASK_TILE) < 0.2] = -big
+        elif u < 0.625:
+            tile[r, rng.integers(0, MASK_TILE)] = big
+        tile[r, r] = rng.standard_normal()
+    return torch.from_numpy(tile.astype(np.float32)).to(dtype).to(device)
+
+
 def paged_inputs(context_lens, heads=128, head_size_k=D_NOPE, head_size_v=D_NOPE,
                  head_size_rope=D_ROPE, block_size=BLOCK_SIZE, dtype=torch.bfloat16,
                  seed=4, device="cpu", with_rope=True):

@@ -1,0 +1,151 @@
+"""GPU parity at the edges of qkScale and of the MASK_FREE tile's range.
+
+The "MLA Prefill" page's Members table gives qkScale a default of 1.0. At that
+scale a score on N(0, 1) inputs has a standard deviation near 14, so most rows
+are dominated by a few keys and the kernel's lazy rescale (the running max
+moves only when a row's max rises by more than 8 ln 2) fires on most tiles. A
+zero scale makes every visible key equally likely (the output is the mean of
+the visible value rows); the page allows it (any float). Tile entries near the
+ends of the dtype's range must not overflow when they are added to the
+scores. Same tolerance as every attention test: max |gpu - oracle| <= 2e-2,
+mean <= 2e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_varlen_prefill_amd as mla
+from mla_varlen_prefill_amd import synth
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+MAX_ABS, MEAN_ABS = 2e-2, 2e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run(t, qs, ks, h, hk, scale, mt, mask=None):
+    out = mla.prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], qs, ks, h, hk, scale, mt, mask)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def ref(t, qs, ks, h, hk, scale, mt, mask=None):
+    d = {n: x.double().cpu().numpy() for n, x in t.items()}
+    tile = mask.double().cpu().numpy() if mask is not None else None
+    return oracle.attention(d["q"], d["q_rope"], d["k"], d["k_rope"], d["v"], qs, ks, h, hk, scale, mt, tile)
+
+
+def check(got, want, what):
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, \
+        f"{what}: max {err.max():.3e} mean {err.mean():.3e}"
+    return err.max()
+
+
+DEFAULT_SCALE_CASES = [
+    # name, q_seqlen, kv_seqlen, heads, kv_heads, dtype, mask type, head dim
+    ("causal-bf16", [300, 129, 1000], [300, 129, 1000], 2, 2, torch.bfloat16, synth.MASK_CAUSAL, 128),
+    ("causal-fp16", [300, 700], [300, 700], 2, 2, torch.float16, synth.MASK_CAUSAL, 128),
+    ("undefined-bf16", [65, 400], [900, 130], 2, 2, torch.bfloat16, synth.MASK_UNDEFINED, 128),
+    ("undefined-fp16", [65, 400], [900, 130], 2, 2, torch.float16, synth.MASK_UNDEFINED, 128),
+    ("chunked-causal-bf16", [200, 64], [1300, 700], 2, 2, torch.bfloat16, synth.MASK_CAUSAL, 128),
+    ("grouped-8-over-2-bf16", [500], [500], 8, 2, torch.bfloat16, synth.MASK_CAUSAL, 128),
+    ("grouped-4-over-1-fp16", [333], [333], 4, 1, torch.float16, synth.MASK_CAUSAL, 128),
+    ("head-dim-64-bf16", [400, 90], [400, 90], 2, 2, torch.bfloat16, synth.MASK_CAUSAL, 64),
+    ("head-dim-64-fp16-undefined", [100], [600], 2, 2, torch.float16, synth.MASK_UNDEFINED, 64),
+]
+
+
+@pytest.mark.parametrize("case", DEFAULT_SCALE_CASES, ids=[c[0] for c in DEFAULT_SCALE_CASES])
+def test_page_default_scale_one_matches_oracle(case):
+    name, qs, ks, h, hk, dt, mt, d = case
+    _say(f"[gpu] qkScale 1.0 {name}: q={qs} kv={ks} H={h}/{hk} {dt} mask={mt} D={d}")
+    t = synth.attention_inputs(qs, ks, h, hk, dt, 1.0, 20 + len(name), DEV, d_nope=d)
+    qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
+    check(run(t, qs, ks, h, hk, 1.0, mt), ref(t, qs, ks, h, hk, 1.0, mt), name)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_page_default_scale_one_mask_free_random_tile(dtype):
+    qs, ks = [300, 600], [700, 600]
+    _say(f"[gpu] qkScale 1.0 MASK_FREE random tile {dtype}")
+    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 31, DEV)
+    tile = synth.random_mask_tile(32, dtype, DEV)
+    qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
+    check(run(t, qs, ks, 2, 2, 1.0, synth.MASK_FREE, tile), ref(t, qs, ks, 2, 2, 1.0, synth.MASK_FREE, tile),
+          "mask-free scale 1")
+
+
+def test_default_scale_one_full_single_shape_sampled_rows():
+    """The single-sequence shape (4096 causal) at 16 heads and qkScale 1.0:
+    sampled rows of every head against the oracle's per-head rows."""
+    L, H = 4096, 16
+    _say(f"[gpu] qkScale 1.0 single shape L={L} H={H}, sampled rows")
+    t = synth.attention_inputs([L], [L], H, H, torch.bfloat16, 1.0, 41, DEV)
+    qs = ks = np.array([L], np.int32)
+    got = run(t, qs, ks, H, H, 1.0, synth.MASK_CAUSAL)
+    rng = np.random.default_rng(42)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, L - 1], rng.integers(0, L, 48)]))
+    errs = []
+    for h in range(H):
+        a = [x.double().cpu().numpy() for x in (t["q"][:, h], t["q_rope"][:, h], t["k"][:, h], t["k_rope"][:, h],
+                                                t["v"][:, h])]
+        want = oracle.attention_head(*a, 1.0, synth.MASK_CAUSAL, rows=rows)
+        errs.append(np.abs(got[rows, h] - want))
+    e = np.concatenate(errs)
+    assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS, f"max {e.max():.3e} mean {e.mean():.3e}"
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0])
+@pytest.mark.parametrize("mt", [synth.MASK_CAUSAL, synth.MASK_UNDEFINED, synth.MASK_FREE])
+def test_zero_scale_is_the_mean_of_visible_values(scale, mt):
+    qs, ks = [1, 70, 600], [1, 200, 600]
+    _say(f"[gpu] qkScale {scale} mask={mt}")
+    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 50, DEV)
+    tile = synth.causal_mask_tile(torch.float16, DEV) if mt == synth.MASK_FREE else None
+    qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
+    got = run(t, qs, ks, 2, 2, scale, mt, tile)
+    want = ref(t, qs, ks, 2, 2, scale, mt, tile)
+    check(got, want, f"scale {scale}")
+    # closed form: with every score 0 the weights are uniform over the visible keys
+    v = t["v"].double().cpu().numpy()
+    b, q_off, k_off = 1, int(qs[0]), int(ks[0])
+    for i in (0, 69):
+        p = ks[b] - qs[b] + i
+        n_vis = ks[b] if mt == synth.MASK_UNDEFINED else p + 1
+        mean = v[k_off:k_off + n_vis].mean(axis=0)
+        assert np.abs(got[q_off + i] - mean).max() <= MAX_ABS
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("scale", [synth.QK_SCALE, 0.0])
+def test_mask_free_extreme_tile_entries_match_oracle(dtype, scale):
+    """Tile entries at the far ends of the dtype's range (bf16: -3e38, -1e30,
+    +1e30; fp16: -65504, -6e4, +6e4) are added without overflow: keys under a
+    very negative entry get weight 0 and a row's single very positive entry
+    takes all the weight, as in the fp64 oracle. The tile keeps at most one
+    large positive entry per row: with several, fp64 itself rounds their score
+    differences away."""
+    qs, ks = [300, 530, 900], [700, 530, 900]
+    _say(f"[gpu] MASK_FREE extreme tile {dtype} scale {scale}")
+    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 60, DEV)
+    tile = synth.extreme_mask_tile(61, dtype, DEV)
+    qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
+    check(run(t, qs, ks, 2, 2, scale, synth.MASK_FREE, tile),
+          ref(t, qs, ks, 2, 2, scale, synth.MASK_FREE, tile), "extreme tile")
+
+
+def test_mask_free_causal_tile_still_equals_causal_bit_exact_at_scale_one_and_zero():
+    qs, ks = [600, 1100], [1100, 1100]
+    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 70, DEV)
+    qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
+    for scale in (1.0, 0.0, -0.3):
+        causal = run(t, qs, ks, 2, 2, scale, synth.MASK_CAUSAL)
+        free = run(t, qs, ks, 2, 2, scale, synth.MASK_FREE, synth.causal_mask_tile(torch.bfloat16, DEV))
+        assert np.array_equal(causal, free), scale
