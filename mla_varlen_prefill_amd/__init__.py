@@ -27,7 +27,10 @@ __all__ = [
     "mla_prolog_get_workspace_size", "mla_prolog", "prolog",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_prefill.so")
+# MLA_PREFILL_LIBRARY selects another build of the same library (the host
+# sanitizer build of build.py is run this way).
+LIB_PATH = os.environ.get("MLA_PREFILL_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                                  "libmla_prefill.so")
 
 MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
 KV_CACHE_NZ, KV_CACHE_ND = 0, 1

@@ -46,6 +46,48 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side AddressSanitizer / UndefinedBehaviorSanitizer build: the host code
+# of every source (validation, planning, launch setup) is instrumented, the
+# device code is compiled as usual and not; linked with clang++ against the
+# shared ASan runtime. The CPU test suite runs against it with that runtime
+# preloaded.
+ASAN_LIB = os.path.join(HERE, "_build", "asan", "libmla_prefill_asan.so")
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    out_dir = os.path.dirname(ASAN_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *HIP_FLAGS, "-x", "hip", "-Xarch_host", "-O1", "-Xarch_host", "-g", *HOST_SANITIZE, "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
+    cmd = [CLANGXX, "-shared", "-fsanitize=address,undefined", "-shared-libasan", *objs, "-o", ASAN_LIB,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return ASAN_LIB
+
+
+def asan_runtime() -> str:
+    """The clang ASan runtime that must be preloaded into an uninstrumented
+    Python process using the sanitized library."""
+    out = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"], check=True,
+                         capture_output=True, text=True).stdout.strip()
+    return out
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        build(verbose="-v" in sys.argv)
+        print(LIB)

@@ -34,7 +34,10 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+DEFAULT_LIB = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIBRARY selects another build (the sanitizer build of build_sanitized)
+LIB = os.environ.get("ORACLE_LIBRARY") or DEFAULT_LIB
+ASAN_LIB = os.path.join(HERE, "liboracle_asan.so")
 
 MASK_UNDEFINED, MASK_SPEC, MASK_CAUSAL, MASK_FREE = 0, 1, 2, 3
 MASK_TILE = 512
@@ -42,9 +45,20 @@ MASK_TILE = 512
 _lib = None
 
 
-def build(src: str = SRC, out: str = LIB) -> str:
+def build(src: str = SRC, out: str = DEFAULT_LIB) -> str:
     """Compile the C oracle with gcc (IEEE arithmetic: no fast-math)."""
     cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def build_sanitized(src: str = SRC, out: str = ASAN_LIB) -> str:
+    """The same oracle built with clang under AddressSanitizer and
+    UndefinedBehaviorSanitizer (for the sanitizer run of the CPU tests)."""
+    clang = os.environ.get("CLANG", "/opt/rocm/llvm/bin/clang")
+    cmd = [clang, "-O1", "-g", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-shared-libasan", src, "-o", out, "-lm",
+           "-Wl,-rpath,/opt/rocm/llvm/lib"]
     subprocess.run(cmd, check=True)
     return out
 
@@ -55,6 +69,8 @@ def load(path: str = LIB):
     if path == LIB and _lib is not None:
         return _lib
     if not os.path.exists(path):
+        if path != DEFAULT_LIB:
+            raise RuntimeError(f"{path} is missing")
         build(out=path)
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)

@@ -110,3 +110,21 @@ def test_prolog_workload_sampled():
     assert_close(q[idx], rq, "workload q")
     assert_close(kv[idx], rkv, "workload kv")
     assert_close(cq[idx], rcq, "workload c^Q")
+
+
+def test_prolog_rope_tables_with_unequal_pair_entries():
+    """rope_cos / rope_sin hold one value per element ("MlaProlog" page,
+    parameter list: [t, rope_dim]); with the two entries of every pair set
+    apart (independent random tables) the kernel must read the odd element's
+    own entries, as the oracle does."""
+    t = 37
+    _say(f"[gpu] prolog t={t}, pair-unequal rope tables")
+    d = synth.prolog_inputs(t, seed=9, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(91)
+    d["rope_cos"] = torch.rand((t, 64), generator=g, device=DEV).mul(2).sub(1).to(torch.bfloat16)
+    d["rope_sin"] = torch.rand((t, 64), generator=g, device=DEV).mul(2).sub(1).to(torch.bfloat16)
+    assert (d["rope_cos"][:, 0::2] != d["rope_cos"][:, 1::2]).float().mean() > 0.9
+    q, kv, cq = run_gpu(d)
+    rq, rkv, rcq = run_oracle(d)
+    for got, ref, what in ((q, rq, "q"), (kv, rkv, "kv"), (cq, rcq, "c^Q")):
+        assert_close(got, ref, what)

@@ -7,13 +7,15 @@ rope on the last rope_dim values of q and kv. The pins:
   * RmsNorm: torch's ``rms_norm`` as a library special case, the unit mean
     square it produces, invariance to the input's scale, gamma per element;
   * rope: the complex-number form of a rotation of adjacent pairs, a worked
-    quarter turn, norm preservation and composition of angles;
+    quarter turn, a pair worked by hand whose two cos/sin entries differ,
+    norm preservation and composition of angles;
   * the prolog: a pure-Python brute force (tests/brute.py) on tiny sizes,
     unit norms of every rope'd head, independence of q from the scale of x
     and of gamma_cq (both RmsNorms remove it), no rotation at angle 0.
 The mutants at the end plant plausible mistakes in a private copy of the
 oracle module (rope on split halves, a norm over all heads, a dropped gamma,
-a sign flip, rope on the leading values) and check that some pin fails.
+a sign flip, rope on the leading values, the odd element of a pair reading
+the even element's table entry) and check that some pin fails.
 """
 import importlib.util
 import math
@@ -89,6 +91,15 @@ def rope_pins(mod):
         failed.append("quarter turn")
     if not np.allclose(np.hypot(got[:, 0::2], got[:, 1::2]), np.hypot(x[:, 0::2], x[:, 1::2]), rtol=1e-12):
         failed.append("pair norms")
+    # worked by hand, with the two entries of a pair's cos/sin different (the
+    # page's rope_cos / rope_sin have one value per element): the even element
+    # takes cos[2i], sin[2i], the odd one cos[2i + 1], sin[2i + 1]
+    #   (a, b) = (1, 2), cos = (1/2, 1/4), sin = (3/4, -1/8):
+    #   out[0] = 1 * 1/2 - 2 * 3/4    = -1
+    #   out[1] = 2 * 1/4 + 1 * (-1/8) = 3/8
+    pair = mod.rope_interleaved(np.array([1.0, 2.0]), np.array([0.5, 0.25]), np.array([0.75, -0.125]))
+    if not np.array_equal(pair, [-1.0, 0.375]):
+        failed.append("pair-unequal tables")
     c2, s2 = rope_tables(4, 16, offset=11)
     ang = np.arctan2(sin, cos) + np.arctan2(s2, c2)
     if not np.allclose(mod.rope_interleaved(got, c2, s2), mod.rope_interleaved(x, np.cos(ang), np.sin(ang)),
@@ -162,6 +173,9 @@ MUTANTS = {
                               "q = rms_norm(cq @ np.asarray(wq_b, dtype=np.float64), None, eps).reshape(t, num_heads, head_dim)"),
     "gamma_ckv dropped": ("kv = rms_norm(x @ np.asarray(wkv, dtype=np.float64), gamma_ckv, eps)",
                           "kv = rms_norm(x @ np.asarray(wkv, dtype=np.float64), None, eps)"),
+    "odd element reads the even table entry": ("    return x * cos + partner * sin",
+                                               "    return (x * np.repeat(cos[..., 0::2], 2, axis=-1)\n"
+                                               "            + partner * np.repeat(sin[..., 0::2], 2, axis=-1))"),
     "rope on leading values": ("kv[:, head_dim - rd:] = rope_interleaved(kv[:, head_dim - rd:], rope_cos, rope_sin)",
                                "kv[:, :rd] = rope_interleaved(kv[:, :rd], rope_cos, rope_sin)"),
 }
