@@ -119,29 +119,58 @@ def test_gather_skips_out_of_range_rows():
 
 def test_gather_full_paged_workload_sampled_rows():
     """The paged workload at full size (32 sequences, ctx up to 32768, 128 heads):
-    every output token is checked against the cache slot it must come from on a
-    seeded sample, plus each sequence's first and last token."""
+    seeded output tokens, plus each sequence's first and last token, compared
+    bit for bit with the oracle's gather of those tokens. The oracle is given
+    the cache blocks those tokens live in (copied whole to the host) and, per
+    token, its sequence's table row (renumbered to the copied blocks) with
+    a one-token length and the token's position as the start offset, so the
+    block and slot arithmetic is the oracle's own."""
     lens, _ = synth.workload_seqlens("paged")
-    _say(f"[gpu] full paged gather, total tokens {int(lens.sum())}")
-    caches = synth.paged_inputs(lens, device=DEV, with_rope=True)
     total = int(lens.sum())
+    _say(f"[gpu] full paged gather, total tokens {total}")
+    caches = synth.paged_inputs(lens, device=DEV, with_rope=True)
     key, value = gather_gpu(caches, caches["context_lens"], total)
     rope, _ = gather_gpu(caches, caches["context_lens"], total, with_value=False, key_name="rope_cache")
     table = caches["block_tables"].cpu().numpy()
+    bs = caches["key_cache"].shape[1]
     off = np.concatenate([[0], np.cumsum(lens)])
     rng = np.random.default_rng(7)
-    picks = set(int(x) for x in rng.integers(0, total, size=4096))
+    picks = set(int(x) for x in rng.integers(0, total, size=256))
     for b in range(len(lens)):
         picks |= {int(off[b]), int(off[b + 1] - 1)}
     picks = np.array(sorted(picks))
     b_of = np.searchsorted(off, picks, side="right") - 1
     t_of = picks - off[b_of]
-    blocks = torch.from_numpy(table[b_of, t_of // 128].astype(np.int64)).to(DEV)
-    slots = torch.from_numpy((t_of % 128).astype(np.int64)).to(DEV)
+    used = np.unique(table[b_of, t_of // bs])
+    renum = np.full(caches["key_cache"].shape[0], -1, np.int64)
+    renum[used] = np.arange(len(used))
+    sub_table = renum[table[b_of]]  # one row per picked token: its sequence's row, renumbered
+    sub_table[sub_table < 0] = 0    # blocks no picked token reads
+    ones = np.ones(len(picks), np.int64)
+    blk = torch.from_numpy(used).to(DEV)
     idx = torch.from_numpy(picks).to(DEV)
     for out, cache in ((key, "key_cache"), (value, "value_cache"), (rope, "rope_cache")):
-        want = caches[cache][blocks, slots]
-        assert torch.equal(out[idx].view(torch.int16), want.view(torch.int16))
+        sub_cache = as_bits(caches[cache][blk])
+        want, _ = oracle.paged_cache_load(sub_cache, None, sub_table, ones, seq_starts=t_of, has_seq_starts=True)
+        assert np.array_equal(as_bits(out[idx]), want), cache
+
+
+def test_gather_nd_reduced_paged_workload_bit_exact():
+    """The paged workload's lengths and block table at 8 heads (K, V, KRope
+    caches [8192, 128, 8, 128 | 128 | 64] bf16, ND): every output row compared
+    bit for bit with the oracle."""
+    lens, _ = synth.workload_seqlens("paged")
+    total = int(lens.sum())
+    _say(f"[gpu] ND gather, reduced paged workload, {total} tokens")
+    c = synth.paged_inputs(lens, heads=8, device=DEV, with_rope=True)
+    key, value = gather_gpu(c, c["context_lens"], total)
+    rope, _ = gather_gpu(c, c["context_lens"], total, with_value=False, key_name="rope_cache")
+    rk, rv = oracle_gather(c, lens)
+    assert np.array_equal(as_bits(key), rk)
+    assert np.array_equal(as_bits(value), rv)
+    del rk, rv
+    rr, _ = oracle_gather(c, lens, with_value=False, key_name="rope_cache")
+    assert np.array_equal(as_bits(rope), rr)
 
 
 # ---------------------------------------------------------------- NZ layout

@@ -183,3 +183,47 @@ def test_paged_medium_workload_sampled():
         errs.append(np.abs(got - ref).ravel())
     err = np.concatenate(errs)
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+def test_paged_full_workload_sampled_rows():
+    """Fused paged attention on the full paged workload (32 sequences of 1024 ..
+    32768 keys from the seeded lengths, 128 heads, block size 128, the seeded
+    permuted block table, causal, bf16): seeded (sequence, head, row) samples
+    plus each sequence's first and last row, against the oracle's gather and
+    attention for that head (``oracle.paged_cache_load`` then
+    ``oracle.attention_head``)."""
+    lens, _ = synth.workload_seqlens("paged")
+    total = int(lens.sum())
+    _say(f"[gpu] fused paged attention, full paged workload, {total} tokens x 128 heads")
+    c = synth.paged_inputs(lens, device=DEV, with_rope=True)
+    H = c["key_cache"].shape[2]
+    q = synth._randn((total, H, 128), torch.bfloat16, 1.0, 4 * 100 + 8, DEV)
+    qr = synth._randn((total, H, 64), torch.bfloat16, 1.0, 4 * 100 + 9, DEV)
+    qs = ks = np.asarray(lens, np.int32)
+    td = dict(q=q, q_rope=qr, key_cache=c["key_cache"], krope_cache=c["rope_cache"], value_cache=c["value_cache"],
+              block_tables=c["block_tables"])
+    out = run_paged(td, qs, ks, H, H, synth.MASK_CAUSAL)
+    table = c["block_tables"].cpu().numpy()
+    qoff = np.concatenate([[0], np.cumsum(qs)])
+    rng = np.random.default_rng(31)
+    heads = sorted(set(int(x) for x in rng.integers(0, H, size=4)) | {0, H - 1})
+    errs = []
+    for h in heads:
+        hc = {k: td[k][:, :, h].unsqueeze(2).contiguous().cpu().double().numpy()
+              for k in ("key_cache", "krope_cache", "value_cache")}
+        for b in sorted(set(int(x) for x in rng.integers(0, len(lens), size=6)) | {0, len(lens) - 1}):
+            one = np.array([int(ks[b])], np.int32)
+            kk, _ = oracle.paged_cache_load(hc["key_cache"], None, table[b:b + 1], one)
+            kr, _ = oracle.paged_cache_load(hc["krope_cache"], None, table[b:b + 1], one)
+            vv, _ = oracle.paged_cache_load(hc["value_cache"], None, table[b:b + 1], one)
+            ql = int(qs[b])
+            rows = np.array(sorted(set(int(x) for x in rng.integers(0, ql, size=24)) | {0, 1, ql - 1}), np.int64)
+            sl = slice(int(qoff[b]), int(qoff[b]) + ql)
+            ref = oracle.attention_head(q[sl, h].double().cpu().numpy(), qr[sl, h].double().cpu().numpy(), kk[:, 0],
+                                        kr[:, 0], vv[:, 0], synth.QK_SCALE, synth.MASK_CAUSAL, rows=rows)
+            got = out[int(qoff[b]) + torch.from_numpy(rows).to(DEV), h].double().cpu().numpy()
+            errs.append(np.abs(got - ref).ravel())
+        del hc
+    err = np.concatenate(errs)
+    _say(f"[gpu]   {len(err) // 128} rows compared, max {err.max():.3e} mean {err.mean():.3e}")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
