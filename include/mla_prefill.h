@@ -29,13 +29,16 @@
  *   - Ownership: the caller owns every tensor, the workspace and the stream.
  *     The library allocates and frees no device memory and keeps no pointer
  *     after a call returns. Host arrays are read before the call returns.
+ *     (Exception: mla_prefill_no_alloc's fixed per-GPU work-list array, a
+ *     static device array of the library, looked up once per device.)
  *   - Calls that take a stream only enqueue work on it (hipStream_t passed as
  *     void*; NULL is the default stream) and return without synchronising.
  *   - Return value: MLA_OK (0) or a negative MLA_ERR_* code. Arguments are
  *     validated completely before any HIP call: on an error nothing is
  *     enqueued and no output is touched. mla_last_error() returns a
  *     thread-local message describing the last failure of the calling thread.
- *   - The library holds no state and is safe to call from several threads.
+ *   - The library holds no other state and is safe to call from several
+ *     threads (mla_prefill_no_alloc: see its note on overlapping calls).
  */
 #ifndef MLA_PREFILL_H
 #define MLA_PREFILL_H
@@ -163,6 +166,31 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
                 float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
                 const mla_tensor *atten_out, void *workspace, uint64_t workspace_size,
                 void *stream);
+
+/*
+ * mla_prefill_no_alloc -- mla_prefill for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same first 14 arguments and stream as mla_prefill, and no
+ * workspace: the work list goes into a fixed array in device memory that the
+ * library holds, MLA_NO_ALLOC_WORKSPACE_BYTES (4 MiB = 131072 launch records)
+ * on each GPU it runs on, until the process ends. The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine). A problem whose
+ * planned workspace (mla_prefill_get_workspace_size) is larger returns
+ * MLA_ERR_WORKSPACE before anything is enqueued; at 128 heads the limit is
+ * reached near 256K query rows. The first call on a device looks the array's
+ * address up with that device current (the tensors and the stream must belong
+ * to the current device, as for mla_prefill).
+ * Every call on one GPU uses that GPU's single array, which keeps the last
+ * call's work list: calls on one stream are ordered and safe, but calls that
+ * overlap on one GPU (several streams, or threads without ordering) race and
+ * can compute wrong results. Errors: as mla_prefill.
+ */
+#define MLA_NO_ALLOC_WORKSPACE_BYTES (4u << 20)
+int mla_prefill_no_alloc(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
+                         const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
+                         const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                         float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
+                         const mla_tensor *atten_out, void *stream);
 
 /*
  * paged_cache_load -- "PagedCacheLoadOperation" page (AtbPagedCacheLoad).

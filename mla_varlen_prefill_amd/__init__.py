@@ -81,6 +81,8 @@ def _load():
     lib.mla_prefill.argtypes = [T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
                                 ctypes.c_int32, ctypes.c_uint8, T, ctypes.c_void_p, ctypes.c_uint64,
                                 ctypes.c_void_p]
+    lib.mla_prefill_no_alloc.argtypes = [T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_uint8, T, ctypes.c_void_p]
     lib.paged_cache_load.argtypes = [T, T, T, T, T, T, T, ctypes.c_int8, ctypes.c_bool, ctypes.c_bool,
                                      ctypes.c_void_p]
     lib.mla_prefill_paged_get_workspace_size.argtypes = [T, T, T, T, T, T, T, T, T, ctypes.c_int32, ctypes.c_float,
@@ -98,7 +100,8 @@ def _load():
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
                                           ctypes.c_uint64, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]
-    for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "paged_cache_load", "mla_prefill_plan_host",
+    for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "mla_prefill_no_alloc", "paged_cache_load",
+               "mla_prefill_plan_host",
                "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "mla_prolog_get_workspace_size",
                "mla_prolog"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -211,6 +214,20 @@ def mla_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk
     ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("mla_prefill", lib.mla_prefill(*args, ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size),
                                           _stream_ptr(stream)))
+
+
+def mla_prefill_no_alloc(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                         mask_type, cache_mode, atten_out, stream=None) -> None:
+    """``mla_prefill`` without a workspace: the work list goes into the
+    library's fixed per-GPU array (``MLA_NO_ALLOC_WORKSPACE_BYTES``), so the
+    call allocates no device memory. Calls that overlap on one GPU race."""
+    lib = _load()
+    _on_device([("q", q), ("q_rope", q_rope), ("k", k), ("k_rope", k_rope), ("v", v), ("atten_out", atten_out),
+                ("mask", mask if mask_type == MASK_FREE else None)], stream)
+    keep = []
+    args = _prefill_args(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale, kv_head_num,
+                         mask_type, cache_mode, atten_out, keep)
+    _check("mla_prefill_no_alloc", lib.mla_prefill_no_alloc(*args, _stream_ptr(stream)))
 
 
 def _paged_args(q, q_rope, key_cache, krope_cache, value_cache, block_tables, q_seqlen, kv_seqlen, mask, head_num,

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -514,17 +515,61 @@ void write_launch(const Plan &p, int32_t group, bool paged, mla::LaunchRec *dst)
     }
 }
 
+// Launch records of mla_prefill_no_alloc: a fixed array in device memory, one
+// copy per GPU, held until the process ends. On the host the name `scratch`
+// stands for a host-side stand-in, not a device address: host code only ever
+// uses the address hipGetSymbolAddress returns for the current device.
+static_assert(MLA_NO_ALLOC_WORKSPACE_BYTES % sizeof(mla::LaunchRec) == 0, "whole launch records");
+static __device__ __align__(256) unsigned char scratch[MLA_NO_ALLOC_WORKSPACE_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};  // device address of `scratch`, per device ordinal
+
+// The current device's copy of `scratch`; its address is looked up once per
+// device, with that device current.
+int scratch_on_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+        return fail(MLA_ERR_UNSUPPORTED, "device ordinal %d beyond the %d this library tracks", dev,
+                    SCRATCH_MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        if (ptr == nullptr) return fail(MLA_ERR_RUNTIME, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
 // Plan on the host, copy the work list into the workspace, launch. pg and
-// block_tables are null for contiguous K/V.
+// block_tables are null for contiguous K/V. With use_scratch the workspace
+// arguments are ignored and the work list goes into the current device's
+// `scratch` array instead.
 int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *block_tables, const mla_tensor *q,
                     const mla_tensor *q_rope, const void *k, const void *k_rope, const void *v,
                     const mla_tensor *mask, float qk_scale, const mla_tensor *atten_out, void *workspace,
-                    uint64_t workspace_size, void *stream) {
+                    uint64_t workspace_size, bool use_scratch, void *stream) {
     Plan plan;
     build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
                &plan);
     const uint64_t need = plan_bytes(plan);
     if (need == 0) return ok();  // no query rows: nothing to write
+    if (use_scratch) {
+        if (need > MLA_NO_ALLOC_WORKSPACE_BYTES)
+            return fail(MLA_ERR_WORKSPACE,
+                        "the work list needs %llu bytes (%zu launch records); mla_prefill_no_alloc holds at most "
+                        "%llu bytes: use mla_prefill with a workspace",
+                        (unsigned long long)need, plan.tasks.size(), (unsigned long long)MLA_NO_ALLOC_WORKSPACE_BYTES);
+        int rc = scratch_on_current_device(&workspace);
+        if (rc) return rc;
+        workspace_size = MLA_NO_ALLOC_WORKSPACE_BYTES;
+    }
     if (workspace == nullptr || workspace_size < need)
         return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given",
                     (unsigned long long)need, (unsigned long long)workspace_size);
@@ -703,7 +748,20 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
                               kv_head_num, mask_type, cache_mode, atten_out, &pr);
     if (rc) return rc;
     return plan_and_launch(pr, nullptr, nullptr, q, q_rope, k->data, k_rope->data, v->data, mask, qk_scale,
-                           atten_out, workspace, workspace_size, stream);
+                           atten_out, workspace, workspace_size, false, stream);
+}
+
+int mla_prefill_no_alloc(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
+                         const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
+                         const mla_tensor *kv_seqlen, const mla_tensor *mask, int32_t head_num,
+                         float qk_scale, int32_t kv_head_num, int32_t mask_type, uint8_t cache_mode,
+                         const mla_tensor *atten_out, void *stream) {
+    Problem pr;
+    int rc = validate_prefill(q, q_rope, k, k_rope, v, q_seqlen, kv_seqlen, mask, head_num, qk_scale,
+                              kv_head_num, mask_type, cache_mode, atten_out, &pr);
+    if (rc) return rc;
+    return plan_and_launch(pr, nullptr, nullptr, q, q_rope, k->data, k_rope->data, v->data, mask, qk_scale,
+                           atten_out, nullptr, 0, true, stream);
 }
 
 int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,
@@ -739,7 +797,7 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
     if (rc) return rc;
     return plan_and_launch(pr, &pg, static_cast<const int32_t *>(block_tables->data), q, q_rope, key_cache->data,
                            krope_cache->data, value_cache->data, mask, qk_scale, atten_out, workspace,
-                           workspace_size, stream);
+                           workspace_size, false, stream);
 }
 
 int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,

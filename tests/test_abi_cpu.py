@@ -177,6 +177,57 @@ def test_no_device_is_a_runtime_error():
     assert c_mla_prefill(t, ws) == "MLA_ERR_RUNTIME"
 
 
+# ----------------------------------------------- mla_prefill_no_alloc's limit
+
+NO_ALLOC_BYTES = 4 << 20  # MLA_NO_ALLOC_WORKSPACE_BYTES
+LAUNCH_RECORD_BYTES = 32
+
+
+def c_no_alloc_on_shapes(nq, heads):
+    """mla_prefill_no_alloc on one causal bf16 sequence of nq rows and keys
+    with `heads` query and KV heads, given as descriptors whose data pointers
+    are placeholders: a call that fails validation or the size check returns
+    before any HIP call and reads no tensor memory."""
+    def desc(*shape):
+        d = mla.MlaTensor()
+        d.data = 1 << 20
+        d.dtype = 2  # MLA_BF16
+        d.ndim = len(shape)
+        for i, n in enumerate(shape):
+            d.shape[i] = n
+        return ctypes.pointer(d)
+    lens = np.array([nq], np.int32)
+    keep = []
+    q, qr, out = desc(nq, heads, 128), desc(nq, heads, 64), desc(nq, heads, 128)
+    k, kr, v = desc(nq, heads, 128), desc(nq, heads, 64), desc(nq, heads, 128)
+    rc = mla._load().mla_prefill_no_alloc(q, qr, k, kr, v, mla._desc(lens, keep), mla._desc(lens, keep), None,
+                                          heads, 0.1, heads, mla.MASK_CAUSAL, 0, out, None)
+    return c_status(rc)
+
+
+def launch_records(nq, heads):
+    _, _, tasks = mla.mla_prefill_plan_host([nq], [nq], heads, heads, mla.MASK_CAUSAL)
+    return len(tasks)
+
+
+def test_no_alloc_rejects_work_lists_beyond_its_array():
+    # 128 heads over 1024 items of 256 rows fill the array exactly; one more
+    # item does not fit.
+    assert launch_records(1024 * 256, 128) * LAUNCH_RECORD_BYTES == NO_ALLOC_BYTES
+    assert launch_records(1024 * 256 + 1, 128) * LAUNCH_RECORD_BYTES > NO_ALLOC_BYTES
+    assert c_no_alloc_on_shapes(1024 * 256 + 1, 128) == "MLA_ERR_WORKSPACE"
+    assert "mla_prefill_no_alloc holds at most 4194304 bytes" in mla.mla_last_error()
+    assert c_no_alloc_on_shapes(1024 * 256 + 1, 0) == "MLA_ERR_VALUE"  # validation still comes first
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
+def test_no_alloc_at_its_limit_passes_the_size_check():
+    # A work list of exactly the array's size passes the check and reaches the
+    # device lookup, which fails here for want of a GPU.
+    assert c_no_alloc_on_shapes(1024 * 256, 128) == "MLA_ERR_RUNTIME"
+    assert "hipGetDevice" in mla.mla_last_error() or "hip" in mla.mla_last_error().lower()
+
+
 # ------------------------------------------------------- binding: device memory
 
 def test_binding_refuses_host_memory_for_device_arguments():
@@ -188,6 +239,8 @@ def test_binding_refuses_host_memory_for_device_arguments():
     ws = torch.zeros(ws_size(t), dtype=torch.uint8)
     with pytest.raises(ValueError, match="q must be a torch tensor in GPU memory"):
         mla.mla_prefill(**t, workspace=ws, stream=0)
+    with pytest.raises(ValueError, match="q must be a torch tensor in GPU memory"):
+        mla.mla_prefill_no_alloc(**t, stream=0)
     with pytest.raises(ValueError, match="GPU memory"):
         mla.prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], t["q_seqlen"], t["kv_seqlen"], 4, 4, 0.1,
                     mla.MASK_CAUSAL)
