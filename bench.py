@@ -162,7 +162,7 @@ def _attention_tflops(t, qs, ks, heads, kv_heads, mask_type, mask, steps):
     return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
 
 
-def bench_extras(steps):
+def bench_extras(steps, cpu=True):
     """Secondary configurations: the chunked workload under MASK_FREE with the
     causal fp16 tile (the same visible pairs as causal); one GPU's share of an
     8-way split over heads (16 heads) of the single and chunked shapes; the
@@ -173,6 +173,12 @@ def bench_extras(steps):
     res["chunked_causal"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_CAUSAL, None, steps)
     tile = synth.causal_mask_tile(torch.float16, "cuda")
     res["chunked_mask_free_causal_tile"] = _attention_tflops(t, qs, ks, 128, 128, synth.MASK_FREE, tile, steps)
+    oracle_recs = {}
+    if cpu:
+        seed = synth.WORKLOADS["chunked"]["seed"]
+        oracle_recs["chunked"] = oracle_sampled(t, qs, ks, 128, 128, synth.MASK_CAUSAL, seed)
+        oracle_recs["chunked_mask_free_causal_tile"] = oracle_sampled(t, qs, ks, 128, 128, synth.MASK_FREE, seed,
+                                                                      tile=tile, tile_edge_rows=True)
     del t
     for name in ("single", "chunked"):
         qs, ks = synth.workload_seqlens(name)
@@ -194,7 +200,7 @@ def bench_extras(steps):
                                                                    synth.MASK_CAUSAL, None, steps)
         del t
     torch.cuda.empty_cache()
-    return {k: {"ms": round(v["ms"], 4), "tflops": round(v["tflops"], 2)} for k, v in res.items()}
+    return {k: {"ms": round(v["ms"], 4), "tflops": round(v["tflops"], 2)} for k, v in res.items()}, oracle_recs
 
 
 def cpu_baseline(res, seconds):
@@ -223,6 +229,166 @@ def cpu_baseline(res, seconds):
                       f"({spent:.1f} s, fp64)"}
 
 
+def _visible_keys(ql, kl, i, mask_type):
+    """Keys query row i of a (ql, kl) sequence sees under a causal-like rule
+    (MASK_FREE is only ever timed here with the causal tile)."""
+    if mask_type == synth.MASK_UNDEFINED:
+        return kl
+    return int(min(kl, max(0, kl - ql + i + 1)))
+
+
+def oracle_sampled(t, qs, ks, heads, kv_heads, mask_type, seed, tile=None, paged=None, tile_edge_rows=False,
+                   pairs=256, rows_per_pair=8):
+    """The oracle as it stands on a seeded sample of a workload, with the time
+    of the whole workload extrapolated from it.
+
+    Sample: ``pairs`` (sequence, head) pairs from default_rng(seed + 1000),
+    the sequence drawn with probability proportional to its query rows and the
+    head uniformly, ``rows_per_pair`` uniform rows of each (so every query row
+    of the workload is equally likely); plus, for every sequence, rows 0, 1
+    and qlen - 1 at heads 0 and H - 1; with ``tile_edge_rows``, also the rows
+    whose key position is 0, 1 or 511 modulo 512 (edges of the MASK_FREE tile
+    blocks) at head 0. Only the (sequence, KV head) slices the sample reads are
+    copied to the host. Each row is one oracle call, with the oracle set to
+    one thread. Paged inputs (``paged`` = caches + table) go through the
+    oracle's gather of the sampled sequence and head first, as its paged path
+    does.
+
+    Extrapolation: the oracle scores every key of a sequence for every query
+    row, so its time per row is proportional to the sequence's key count;
+    full time = sampled time per (row x key) x sum over heads and sequences of
+    qlen x kvlen (the paged gather: per (head x key), once per sequence and
+    head)."""
+    import oracle
+    oracle.build()
+    threads = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        return _oracle_sampled(oracle, threads, t, qs, ks, heads, kv_heads, mask_type, seed, tile, paged,
+                               tile_edge_rows, pairs, rows_per_pair)
+    finally:
+        oracle.set_num_threads(threads)
+
+
+def _oracle_sampled(oracle, threads, t, qs, ks, heads, kv_heads, mask_type, seed, tile, paged, tile_edge_rows,
+                    pairs, rows_per_pair):
+    qs, ks = np.asarray(qs, np.int64), np.asarray(ks, np.int64)
+    nb = len(qs)
+    qoff = np.concatenate([[0], np.cumsum(qs)])
+    koff = np.concatenate([[0], np.cumsum(ks)])
+    rng = np.random.default_rng(seed + 1000)
+    groups = {}
+    pb = rng.choice(nb, size=pairs, p=qs / qs.sum())
+    ph = rng.integers(0, heads, size=pairs)
+    for b, h in zip(pb.tolist(), ph.tolist()):
+        groups.setdefault((b, h), set()).update(rng.integers(0, qs[b], size=rows_per_pair).tolist())
+    sampled = sum(len(v) for v in groups.values())
+    for b in range(nb):
+        if qs[b] == 0:
+            continue
+        for h in (0, heads - 1):
+            groups.setdefault((b, h), set()).update({0, min(1, int(qs[b]) - 1), int(qs[b]) - 1})
+        if tile_edge_rows:
+            pos = ks[b] - qs[b] + np.arange(qs[b])
+            edge = np.nonzero(np.isin(pos % synth.MASK_TILE, (0, 1, synth.MASK_TILE - 1)))[0]
+            groups.setdefault((b, 0), set()).update(edge.tolist())
+    tile64 = tile.double().cpu().numpy() if tile is not None else None
+    d = t["q"].shape[-1]
+    flop_pair = 4 * d + 2 * 64
+    t_attn = t_gather = 0.0
+    n_rows = row_keys = gather_keys = 0
+    sample_flops = 0
+    # fp32 on the device, fp64 in numpy: no torch CPU op (whose worker threads
+    # would keep spinning beside the timed oracle calls)
+    host = lambda x: x.contiguous().float().cpu().numpy().astype(np.float64)
+    for (b, h), rows in sorted(groups.items()):
+        hk = oracle.kv_head_of(h, heads, kv_heads)
+        ql, kl = int(qs[b]), int(ks[b])
+        q = host(t["q"][qoff[b]:qoff[b] + ql, h])
+        qr = host(t["q_rope"][qoff[b]:qoff[b] + ql, h])
+        if paged is None:
+            k = host(t["k"][koff[b]:koff[b] + kl, hk])
+            kr = host(t["k_rope"][koff[b]:koff[b] + kl, hk])
+            v = host(t["v"][koff[b]:koff[b] + kl, hk])
+        else:
+            bs = paged["key_cache"].shape[1]
+            nblk = -(-kl // bs)
+            idx = paged["block_tables"][b, :nblk].long()
+            sub = [host(paged[c][:, :, hk][idx]).reshape(nblk, bs, 1, -1)
+                   for c in ("key_cache", "rope_cache", "value_cache")]
+            row = np.arange(nblk, dtype=np.int64)[None]
+            lens = np.array([kl], np.int64)
+            s0 = time.perf_counter()
+            k, _ = oracle.paged_cache_load(sub[0], None, row, lens)
+            kr, _ = oracle.paged_cache_load(sub[1], None, row, lens)
+            v, _ = oracle.paged_cache_load(sub[2], None, row, lens)
+            t_gather += time.perf_counter() - s0
+            gather_keys += kl
+            k, kr, v = k[:, 0], kr[:, 0], v[:, 0]
+        for i in sorted(rows):
+            s0 = time.perf_counter()
+            oracle.attention_head(q, qr, k, kr, v, synth.QK_SCALE, mask_type, mask=tile64,
+                                  rows=np.array([i], np.int64))
+            t_attn += time.perf_counter() - s0
+            n_rows += 1
+            row_keys += kl
+            sample_flops += flop_pair * _visible_keys(ql, kl, i, mask_type)
+    full_row_keys = heads * int((qs * ks).sum())
+    full_flops = flop_pair * heads * visible_pairs(qs, ks, mask_type)
+    est = t_attn / row_keys * full_row_keys
+    if paged is not None:
+        est += t_gather / gather_keys * heads * int(ks.sum())
+    rec = {"value": full_flops / est / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+           "value_is": "extrapolated: the workload's FLOPs over the extrapolated full oracle time",
+           "sample": f"{n_rows} query rows in {len(groups)} (sequence, head) pairs ({sampled} seeded rows in "
+                     f"{pairs} pairs + boundary rows), one row per oracle call, fp64, one core",
+           "sample_seconds": round(t_attn + t_gather, 3), "sample_tflops": sample_flops / (t_attn + t_gather) / 1e12,
+           "extrapolated_full_seconds_one_core": round(est, 1),
+           "extrapolated_full_seconds_ideal_all_cores": round(est / threads, 1), "host_threads": threads}
+    if paged is not None:
+        rec["sample_gather_seconds"] = round(t_gather, 3)
+    return rec
+
+
+def bench_configs(steps, cpu=True):
+    """The varlen (fp16) and tiny workloads: ms per call (host planning,
+    work-list copy and kernel), TFLOP/s and fraction of the bf16/fp16 MFMA
+    peak. The tiny workload is timed with the full oracle beside it; varlen
+    with the sampled oracle."""
+    out = {}
+    for name in ("varlen", "tiny"):
+        t, qs, ks, p = synth.workload_inputs(name, device="cuda")
+        n = steps if name == "varlen" else max(steps, 200)
+        r = _attention_tflops(t, qs, ks, p["head_num"], p["kv_head_num"], p["mask_type"], None, n)
+        w = synth.WORKLOADS[name]
+        rec = {"workload": name, "dtype": "fp16" if w["dtype"] == torch.float16 else "bf16", "batch": len(qs),
+               "heads": p["head_num"], "mask": "causal", "tokens": int(np.sum(qs)), "timed_calls": n,
+               "ms": round(r["ms"], 4), "tflops": round(r["tflops"], 2), "frac": round(r["tflops"] / PEAK_TFLOPS, 4)}
+        if cpu and name == "varlen":
+            rec["cpu_baseline"] = oracle_sampled(t, qs, ks, p["head_num"], p["kv_head_num"], p["mask_type"],
+                                                 w["seed"])
+        elif cpu:
+            rec["cpu_baseline"] = oracle_full(t, qs, ks, p)
+        out[name] = rec
+        del t
+    torch.cuda.empty_cache()
+    return out
+
+
+def oracle_full(t, qs, ks, params):
+    """The oracle on every row and head of a (small) workload."""
+    import oracle
+    oracle.build()
+    h = {k: v.double().cpu().numpy() for k, v in t.items()}
+    s0 = time.perf_counter()
+    oracle.attention(h["q"], h["q_rope"], h["k"], h["k_rope"], h["v"], qs, ks, params["head_num"],
+                     params["kv_head_num"], params["qk_scale"], params["mask_type"])
+    spent = time.perf_counter() - s0
+    flops = FLOP_PER_PAIR * params["head_num"] * visible_pairs(qs, ks, params["mask_type"])
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "the whole workload", "seconds": round(spent, 4)}
+
+
 def _time(fn, steps, stream):
     fn()
     torch.cuda.synchronize()
@@ -235,7 +401,7 @@ def _time(fn, steps, stream):
     return a.elapsed_time(b) / steps
 
 
-def bench_paged(steps):
+def bench_paged(steps, cpu=True):
     """The paged workload: the gather's bandwidth, then attention over the same
     caches two ways -- fused (mla_prefill_paged reads K/KRope/V through the
     block table) and two-step (gather, then mla_prefill on the gathered
@@ -280,14 +446,19 @@ def bench_paged(steps):
                                                    heads, synth.QK_SCALE, heads, mt, out, ws, stream),
                      attn_steps, stream)
     flops = FLOP_PER_PAIR * heads * visible_pairs(qs, ks, mt)
-    del caches, key, value, rope, q, qr, out, ws
+    del key, value, rope, out, ws
+    oracle_rec = None
+    if cpu:
+        oracle_rec = oracle_sampled({"q": q, "q_rope": qr}, qs, ks, heads, heads, mt, synth.WORKLOADS["paged"]["seed"],
+                                    paged=caches, pairs=128, rows_per_pair=16)
+    del caches, q, qr
     torch.cuda.empty_cache()
     attn_rec = {"workload": "paged", "tokens": total, "heads": heads, "mask": "causal", "block_size":
                 synth.BLOCK_SIZE, "flops_per_step": flops, "fused_ms": fused_ms,
                 "fused_tflops": flops / (fused_ms * 1e-3) / 1e12, "gathered_attention_ms": gathered_ms,
                 "two_step_ms": gather_ms + gathered_ms, "fused_speedup_over_two_step":
                 (gather_ms + gathered_ms) / fused_ms}
-    return gather_rec, attn_rec
+    return gather_rec, attn_rec, oracle_rec
 
 
 def bench_gather_nz(steps):
@@ -351,6 +522,10 @@ def bench_prolog(steps):
             "ms_per_step": ms, "value": tf, "unit": "TFLOP/s", "peak": PEAK_TFLOPS, "frac": tf / PEAK_TFLOPS}
 
 
+def _progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +559,7 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     res = bench_attention(args.workload, args.steps, args.warmup)
+    _progress(f"{args.workload}: {res['launch_ms']:.4f} ms per launch")
     flops = res["flops"]
     value = flops / (res["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (res["launch_ms"] * 1e-3) / 1e12
@@ -406,13 +582,27 @@ def main():
     }
     if not args.no_gather and args.workload == "single":
         res_t = res.pop("tensors") if args.no_cpu_baseline else None
-        line["gather"], line["paged_attention"] = bench_paged(max(2, min(args.steps, 5)))
+        cpu = not args.no_cpu_baseline
+        by_config = {}
+        line["configs"] = bench_configs(max(5, min(args.steps, 20)), cpu)
+        for name, rec in line["configs"].items():
+            if "cpu_baseline" in rec:
+                by_config[name] = rec.pop("cpu_baseline")
+        _progress("varlen and tiny done")
+        line["gather"], line["paged_attention"], by_config["paged"] = bench_paged(max(2, min(args.steps, 5)), cpu)
+        _progress("paged done")
         line["gather_nz"] = bench_gather_nz(max(2, min(args.steps, 5)))
-        line["extras"] = bench_extras(3)
+        line["extras"], extra_cpu = bench_extras(max(3, min(args.steps, 10)), cpu)
+        by_config.update(extra_cpu)
+        _progress("extras done")
         line["prolog"] = bench_prolog(max(3, min(args.steps, 10)))
+        _progress("prolog done")
+        if cpu:
+            line["cpu_baseline_by_config"] = by_config
         del res_t
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_seconds)
+        _progress("cpu baseline done")
     print(json.dumps(line), flush=True)
 
 

@@ -80,6 +80,8 @@ def load(path: str = LIB):
                                           ctypes.c_int, dp, lp, ctypes.c_long, dp, dp]
     lib.oracle_attention_head.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_num_threads.restype = None
     if path == LIB:
         _lib = lib
     return lib
@@ -88,6 +90,11 @@ def load(path: str = LIB):
 def num_threads() -> int:
     """Threads the oracle's parallel loops run on (OMP_NUM_THREADS or all cores)."""
     return int(load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the parallel loops the calling thread runs from now on."""
+    load().oracle_set_num_threads(int(n))
 
 
 def _dptr(a: np.ndarray):

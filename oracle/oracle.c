@@ -155,3 +155,16 @@ int oracle_num_threads(void)
     }
     return n;
 }
+
+/* Threads of the parallel regions the calling thread starts from now on (its
+ * OpenMP thread-count setting); n < 1 is ignored. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
