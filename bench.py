@@ -120,6 +120,80 @@ def summarize_pmc(fetch_dir, write_dir, out_json):
     print(json.dumps(rec, indent=1))
 
 
+# Counter passes for the attention kernel's utilisation (each within one
+# rocprofv3 pass: at most 8 SQ and 2 GRBM counters).
+UTIL_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE",
+    "SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS "
+    "SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE",
+)
+SIMDS = 1024          # 256 CUs x 4 SIMDs
+MFMA_FLOP_PER_SIMD_CYCLE = 1024  # bf16/fp16 dense: 2.5 PFLOP/s = 1024 SIMDs x 1024 x ~2.4 GHz
+XCCS = 8              # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+
+
+def summarize_util(workload, out_json, dirs):
+    """Medians over the timed dispatches of mla_fwd_kernel of the counters of
+    the UTIL_PASSES runs in ``dirs`` (``rocprofv3 --kernel-trace --pmc ...
+    --output-format csv``; the first two dispatches, warm-up, are dropped),
+    with the derived figures:
+
+      cycles          GRBM_GUI_ACTIVE / 8 (per XCD)
+      clock_ghz       cycles / dispatch duration
+      mfma_busy       SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)
+      mfma_flop       SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (FLOP issued to the matrix cores)
+      useful          algorithmic FLOP / mfma_flop (masked parts of diagonal tiles are issued but not counted)
+      predicted       mfma_busy x 1024 SIMDs x 1024 FLOP/cycle x clock x useful
+      valu_busy       SQ_ACTIVE_INST_VALU x 4 / (cycles x 1024 SIMDs)
+      lds_conflict    SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS
+    """
+    import collections
+    import csv
+    import glob
+    import statistics as st
+
+    qs, ks = synth.workload_seqlens(workload)
+    heads = synth.WORKLOADS[workload]["heads"]
+    alg = FLOP_PER_PAIR * heads * visible_pairs(qs, ks, synth.MASK_CAUSAL)
+    merged = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        per = collections.defaultdict(dict)
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if "mla_fwd_kernel" not in r["Kernel_Name"]:
+                    continue
+                v = per[int(r["Dispatch_Id"])]
+                v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                v["duration_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        rows = [per[k] for k in sorted(per)][2:]
+        for name in rows[0]:
+            key = name if name not in merged else f"{name}@{os.path.basename(os.path.normpath(d))}"
+            merged[key] = st.median(x[name] for x in rows)
+        merged.setdefault("dispatches", len(rows))
+    cycles = merged["GRBM_GUI_ACTIVE"] / XCCS
+    dur = merged["duration_ns"] * 1e-9
+    clock = cycles / dur
+    busy = merged["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS)
+    mfma_flop = merged["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    useful = alg / mfma_flop
+    predicted = busy * SIMDS * MFMA_FLOP_PER_SIMD_CYCLE * clock * useful
+    rec = {"kernel": "mla_fwd_kernel", "workload": workload, "kernel_source_sha256_16": kernel_source_hash(),
+           "counters_median": merged, "algorithmic_flop": alg, "duration_ms": dur * 1e3,
+           "cycles": cycles, "clock_ghz": clock / 1e9, "mfma_busy": busy, "mfma_flop": mfma_flop,
+           "useful_fraction": useful, "tflops_measured": alg / dur / 1e12,
+           "tflops_from_mfma_counter": mfma_flop / dur / 1e12 * useful,
+           "tflops_predicted_from_busy": predicted / 1e12,
+           "predicted_over_measured": predicted / (alg / dur),
+           "valu_busy": merged.get("SQ_ACTIVE_INST_VALU", 0.0) * 4 / (cycles * SIMDS),
+           "mfma_valu_coexec": merged.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0.0) / (cycles * SIMDS),
+           "lds_bank_conflict_per_lds_active": (merged.get("SQ_LDS_BANK_CONFLICT", 0.0)
+                                                / max(merged.get("SQ_ACTIVE_INST_LDS", 0.0), 1.0))}
+    with open(out_json, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
 def bench_attention(name, steps, warmup):
     t, qs, ks, params = synth.workload_inputs(name, device="cuda")
     H = params["head_num"]
@@ -539,11 +613,17 @@ def main():
                     help="run a plain copy of known size first (for scaling rocprofv3 HBM counters)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT_JSON"),
                     help="turn FETCH_SIZE / WRITE_SIZE rocprofv3 runs into HBM bytes per launch, then exit")
+    ap.add_argument("--summarize-util", nargs="+", metavar="ARG",
+                    help="WORKLOAD OUT_JSON DIR [DIR ...]: medians and derived utilisation of mla_fwd_kernel "
+                         "from rocprofv3 --pmc runs of the UTIL_PASSES counters, then exit")
     ap.add_argument("--prolog-only", action="store_true",
                     help="time only the MLA prolog leg and print its JSON object (for profiling it)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_util:
+        summarize_util(args.summarize_util[0], args.summarize_util[1], args.summarize_util[2:])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
