@@ -201,7 +201,8 @@ int mla_prefill_no_alloc(const mla_tensor *q, const mla_tensor *q_rope, const ml
  *                 dtype, num_blocks and block_size; or NULL to gather keys only
  *                 (then value must be NULL too).
  *   block_tables  device int32 [batch, max_blocks]: block ids of each sequence.
- *   context_lens  device int32. Plain mode: [batch] token counts. Cumulative
+ *   context_lens  device int32. Plain mode: [batch] token counts (their sum
+ *                 may pass 2^31; the device sums them in 64 bits). Cumulative
  *                 mode (is_seq_lens_cumsum_type): running totals, either
  *                 [batch + 1] starting with 0 or [batch] inclusive totals.
  *   key, value    device outputs [num_tokens, num_heads, head_size_k / _v] of the

@@ -124,7 +124,7 @@ struct GatherParams {
     int64_t chunks_v;
 };
 
-constexpr int GATHER_MAX_BATCH = 8192;  // offsets table in LDS: (batch + 1) * 4 bytes
+constexpr int GATHER_MAX_BATCH = 8192;  // offsets table in LDS: (batch + 1) * 8 bytes
 
 hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream);
 

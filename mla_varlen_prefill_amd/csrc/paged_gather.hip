@@ -42,12 +42,23 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int G_THREADS = 256;
 constexpr int G_TOKENS = 4;  // tokens resolved per workgroup step (16 measured 12% slower on 16 KB rows)
+constexpr int G_GRID = 8192;  // at most this many workgroups (they stride over the steps)
 constexpr int G_UNROLL = 8;  // 16-byte loads in flight per thread and row
 
 // Every pass issues all of a thread's loads (up to G_UNROLL) before its first
 // store, also for rows shorter than G_UNROLL * G_THREADS pieces (a 16 KB
 // KRope row is 4 pieces per thread): a load-store loop there keeps only one
 // load per thread in flight.
+//
+// Measured on the paged workload (one call gathers K and V, 32 KB rows each;
+// a second call KRope, 16 KB rows): K+V at 79-81% of the 8 TB/s peak, KRope
+// at 65-68%, where a plain device copy of the KRope bytes (torch copy_) runs
+// at 57-63%, and at any size from 2 to 64 GB. K alone (one stream of 32 KB
+// rows) and two 16 KB caches in one call run at 65-66% too: only two 32 KB
+// rows per token reach 80%. Not faster on KRope, and 2-15% slower on K+V:
+// the eight loads taken across the four tokens of a step; 2, 8 or 16 tokens
+// per step; 2048 to 65536 workgroups; plain instead of non-temporal loads or
+// stores; one wave per row with 16 loads per lane and no workgroup barriers.
 __device__ __forceinline__ void copy_row16(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
                                            int64_t n16, int tid) {
     for (int64_t c = tid; c < n16; c += G_UNROLL * G_THREADS) {
@@ -67,8 +78,10 @@ __device__ __forceinline__ void copy_row_bytes(const unsigned char *src, unsigne
 }
 
 // Output offset of every sequence into s_off[0 .. batch]: a block-wide scan
-// of context_lens, or the running totals as given.
-__device__ void build_offsets(const GatherParams &p, int32_t *s_off, int32_t *s_partial, int tid) {
+// of context_lens, or the running totals as given. The scan is 64-bit: the
+// lengths are device data the host never sees, and their total may pass
+// 2^31 (rows at or past num_tokens are then skipped, not wrapped).
+__device__ void build_offsets(const GatherParams &p, int64_t *s_off, int64_t *s_partial, int tid) {
     const int B = p.batch;
     if (p.cumsum) {
         if (p.ctx_entries == B + 1) {  // [0, c1, c1 + c2, ...]
@@ -81,20 +94,20 @@ __device__ void build_offsets(const GatherParams &p, int32_t *s_off, int32_t *s_
         // block-wide exclusive scan: each thread sums a contiguous chunk
         const int chunk = (B + G_THREADS - 1) / G_THREADS;
         const int lo = tid * chunk, hi = min(B, lo + chunk);
-        int32_t sum = 0;
+        int64_t sum = 0;
         for (int i = lo; i < hi; ++i) sum += p.context_lens[i];
         s_partial[tid] = sum;
         __syncthreads();
         if (tid == 0) {
-            int32_t run = 0;
+            int64_t run = 0;
             for (int t = 0; t < G_THREADS; ++t) {
-                const int32_t x = s_partial[t];
+                const int64_t x = s_partial[t];
                 s_partial[t] = run;
                 run += x;
             }
         }
         __syncthreads();
-        int32_t run = s_partial[tid];
+        int64_t run = s_partial[tid];
         for (int i = lo; i < hi; ++i) {
             s_off[i] = run;
             run += p.context_lens[i];
@@ -106,7 +119,7 @@ __device__ void build_offsets(const GatherParams &p, int32_t *s_off, int32_t *s_
 
 // Source slot of output token n (block * block_size + position in the block),
 // or -1 when the token is to be skipped.
-__device__ int64_t source_slot(const GatherParams &p, const int32_t *s_off, int64_t n) {
+__device__ int64_t source_slot(const GatherParams &p, const int64_t *s_off, int64_t n) {
     const int B = p.batch;
     if (n >= p.num_tokens || n >= s_off[B]) return -1;
     int lo = 0, hi = B;  // last sequence b with s_off[b] <= n: s_off[lo] <= n < s_off[hi]
@@ -125,9 +138,9 @@ __device__ int64_t source_slot(const GatherParams &p, const int32_t *s_off, int6
 }
 
 __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherParams p) {
-    extern __shared__ int32_t s_off[];  // [batch + 1] output offsets
+    extern __shared__ int64_t s_off[];  // [batch + 1] output offsets
     __shared__ int64_t s_src[G_TOKENS];  // source slot (block * block_size + offset), -1 to skip
-    __shared__ int32_t s_partial[G_THREADS];
+    __shared__ int64_t s_partial[G_THREADS];
     const int tid = threadIdx.x;
 
     build_offsets(p, s_off, s_partial, tid);
@@ -145,6 +158,7 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
     for (int64_t n0 = (int64_t)blockIdx.x * G_TOKENS; n0 < total; n0 += (int64_t)gridDim.x * G_TOKENS) {
         // ---- resolve the source rows of tokens n0 .. n0 + G_TOKENS - 1
         if (tid < G_TOKENS) {
+            // source_slot returns -1 past num_tokens, so every token to copy has n < total
             const int64_t src = source_slot(p, s_off, n0 + tid);
             s_src[tid] = src;
         }
@@ -152,7 +166,7 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
         for (int i = 0; i < G_TOKENS; ++i) {
             const int64_t n = n0 + i;
             const int64_t src = s_src[i];
-            if (n >= total || src < 0) continue;
+            if (src < 0) continue;
             if (vec) {
                 copy_row16(reinterpret_cast<const u32x4 *>(kc + src * p.row_bytes_k),
                            reinterpret_cast<u32x4 *>(ko + n * p.row_bytes_k), p.row_bytes_k >> 4, tid);
@@ -185,9 +199,9 @@ constexpr int NZ_PER_THREAD = NZ_TOKENS * NZ_CHUNKS * 2 / G_THREADS;  // 16-byte
 // [0, chunks), through LDS tiles of 32 tokens x 32 chunks.
 __global__ __launch_bounds__(G_THREADS) void paged_gather_nz_kernel(const GatherParams p, const void *cache_,
                                                                     void *out_, int64_t chunks) {
-    extern __shared__ int32_t s_off[];  // [batch + 1] output offsets
+    extern __shared__ int64_t s_off[];  // [batch + 1] output offsets
     __shared__ int64_t s_base[NZ_TOKENS];  // byte offset of chunk 0 of each token, -1 to skip
-    __shared__ int32_t s_partial[G_THREADS];
+    __shared__ int64_t s_partial[G_THREADS];
     __shared__ __attribute__((aligned(16))) unsigned char tile[NZ_TOKENS * NZ_ROW];
     const int tid = threadIdx.x;
     const unsigned char *cache = static_cast<const unsigned char *>(cache_);
@@ -254,7 +268,7 @@ hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream) {
     if (p.nz) {
         const int64_t grid = (p.num_tokens + NZ_TOKENS - 1) / NZ_TOKENS;
         if (grid > INT32_MAX) return hipErrorInvalidValue;
-        const size_t shmem = sizeof(int32_t) * ((size_t)p.batch + 1);
+        const size_t shmem = sizeof(int64_t) * ((size_t)p.batch + 1);
         hipLaunchKernelGGL(paged_gather_nz_kernel, dim3((unsigned)grid), dim3(G_THREADS), shmem, stream, p,
                            p.key_cache, p.key, p.chunks_k);
         if (p.value_cache)
@@ -262,9 +276,9 @@ hipError_t launch_paged_gather(const GatherParams &p, hipStream_t stream) {
                                p.value_cache, p.value, p.chunks_v);
         return hipGetLastError();
     }
+    size_t shmem = sizeof(int64_t) * ((size_t)p.batch + 1);
     int64_t steps = (p.num_tokens + G_TOKENS - 1) / G_TOKENS;
-    int grid = (int)(steps < 8192 ? steps : 8192);
-    size_t shmem = sizeof(int32_t) * ((size_t)p.batch + 1);
+    int grid = (int)(steps < G_GRID ? steps : G_GRID);
     hipLaunchKernelGGL(paged_gather_kernel, dim3(grid), dim3(G_THREADS), shmem, stream, p);
     return hipGetLastError();
 }

@@ -155,6 +155,43 @@ def test_gather_full_paged_workload_sampled_rows():
         assert np.array_equal(as_bits(out[idx]), want), cache
 
 
+def test_gather_total_past_two_to_the_31():
+    """Plain lengths whose total passes 2^31: sequences of 1.2e9 and 1.0e9
+    tokens, rows of one bf16 element, block size 128, the table columns
+    cycling over a seeded permutation of 64 cache blocks. The device sums the
+    lengths in 64 bits, so the rows of the second sequence past 2^31 are
+    written where they belong. Rows around 2^31, at both ends and at random
+    are compared bit for bit with the oracle's gather of those tokens (each
+    given as a one-token sequence whose block table is the window of its own
+    table row that holds it, from a start position inside that window)."""
+    lens = np.array([1_200_000_000, 1_000_000_000], np.int64)
+    total = int(lens.sum())
+    assert total > 2**31
+    _say(f"[gpu] gather, total {total} tokens past 2^31")
+    bs, nb = 128, 64
+    cols = int(-(-lens.max() // bs))
+    rng = np.random.default_rng(12)
+    table = rng.permutation(nb).astype(np.int32)[np.arange(2 * cols) % nb].reshape(2, cols)
+    g = torch.Generator(device=DEV).manual_seed(1200)
+    cache = torch.randn((nb, bs, 1, 1), generator=g, device=DEV).to(torch.bfloat16)
+    caches = {"key_cache": cache, "block_tables": torch.from_numpy(table).to(DEV)}
+    key, _ = gather_gpu(caches, torch.from_numpy(lens.astype(np.int32)).to(DEV), total, with_value=False)
+    off = np.array([0, lens[0], total])
+    picks = {2**31 - 2, 2**31 - 1, 2**31, 2**31 + 1, 0, int(lens[0]) - 1, int(lens[0]), total - 1}
+    picks |= set(int(x) for x in rng.integers(2**31, total, size=24))
+    picks |= set(int(x) for x in rng.integers(0, total, size=24))
+    picks = np.array(sorted(picks))
+    b_of = np.searchsorted(off, picks, side="right") - 1
+    t_of = picks - off[b_of]
+    col = t_of // bs
+    windows = table[b_of, col][:, None]          # the table column holding each token
+    starts = t_of - col * bs                     # its position inside that window
+    want, _ = oracle.paged_cache_load(as_bits(cache), None, windows, np.ones(len(picks), np.int64),
+                                      seq_starts=starts, has_seq_starts=True)
+    got = as_bits(key[torch.from_numpy(picks).to(DEV)])
+    assert np.array_equal(got, want)
+
+
 def test_gather_nd_reduced_paged_workload_bit_exact():
     """The paged workload's lengths and block table at 8 heads (K, V, KRope
     caches [8192, 128, 8, 128 | 128 | 64] bf16, ND): every output row compared
