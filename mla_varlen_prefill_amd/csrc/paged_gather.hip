@@ -22,15 +22,17 @@
 // 32-byte chunks (16 fp16/bf16 or 32 int8 elements) and chunk c of slot s of
 // block k sits at cache[k][c][s]. For one chunk, consecutive slots are
 // adjacent; for one token, consecutive chunks are block_size * 32 bytes apart.
-// So the NZ kernel transposes through LDS: a workgroup owns 64 output tokens;
+// So the NZ kernel transposes through LDS: a workgroup owns 44 output tokens;
 // for each group of 32 chunks, every read instruction takes one chunk of 32
 // consecutive tokens (one contiguous kilobyte when they share a block), the
 // tile is stored in LDS by token (rows padded by 16 bytes against bank
 // conflicts), and every write instruction then stores one kilobyte of one
 // token's output row. The next group's loads are in flight while a group goes
-// from LDS to the output. (Tiles of 32 x 16, 32 x 32, 64 x 16, 128 x 8,
-// 128 x 16 and 16 x 64 tokens x chunks measured 60-68% of HBM peak against
-// 68-70% for 64 x 32.)
+// from LDS to the output. The 44 x 32 tile (45 KB of LDS, three workgroups
+// per CU) measured 71-74% of the HBM peak for the paged workload's K+V and
+// 71-72% for its KRope, against 67-69% for 64 x 32 (66 KB, two per CU);
+// 36, 40 and 48 tokens were within a point or two of 44, and 32 x 16, 32 x 32,
+// 64 x 16, 64 x 24, 48 x 40, 128 x 8, 128 x 16 and 16 x 64 lower.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(G_THREADS) void paged_gather_kernel(const GatherPar
 
 // ---- NZ layout
 #ifndef MLA_NZ_TOKENS
-#define MLA_NZ_TOKENS 64
+#define MLA_NZ_TOKENS 44
 #endif
 #ifndef MLA_NZ_CHUNKS
 #define MLA_NZ_CHUNKS 32
@@ -194,9 +196,10 @@ constexpr int NZ_TOKENS = MLA_NZ_TOKENS;      // output tokens per workgroup
 constexpr int NZ_CHUNKS = MLA_NZ_CHUNKS;      // 32-byte chunks per tile
 constexpr int NZ_ROW = NZ_CHUNKS * 32 + 16;   // LDS bytes per token row of the tile
 constexpr int NZ_PER_THREAD = NZ_TOKENS * NZ_CHUNKS * 2 / G_THREADS;  // 16-byte pieces per thread and tile
+static_assert(NZ_PER_THREAD * G_THREADS == NZ_TOKENS * NZ_CHUNKS * 2, "whole pieces per thread");
 
-// One cache (key or value): output token rows n0 .. n0 + 31 of chunks
-// [0, chunks), through LDS tiles of 32 tokens x 32 chunks.
+// One cache (key or value): output token rows n0 .. n0 + NZ_TOKENS - 1 of
+// chunks [0, chunks), through LDS tiles of NZ_TOKENS tokens x NZ_CHUNKS chunks.
 __global__ __launch_bounds__(G_THREADS) void paged_gather_nz_kernel(const GatherParams p, const void *cache_,
                                                                     void *out_, int64_t chunks) {
     extern __shared__ int64_t s_off[];  // [batch + 1] output offsets
