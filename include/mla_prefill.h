@@ -302,8 +302,11 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
  *   q_out       device bf16 [t, num_heads, head_dim] or [t, num_heads * head_dim]
  *   kv_out      device bf16 [t, head_dim]
  *   qr_out      device bf16 [t, q_lora_rank]: c^Q
- *   workspace_size  out: bytes of device workspace mla_prolog needs (t *
- *               q_lora_rank * 4: the fp32 product x . wq_a before its norm).
+ *   workspace_size  out: bytes of device workspace mla_prolog needs: the
+ *               fp32 product x . wq_a before its norm (t * q_lora_rank * 4,
+ *               rounded up to 256 bytes), then copies of wq_a, wkv and wq_b
+ *               rearranged for the product kernel (2 bytes per weight); 0
+ *               when t = 0.
  * Supported (the page's constraints fix head_dim 512, h 4096, q_lora_rank
  * 1024, num_heads 64, rope_dim 64, t up to 64k): head_dim = 512,
  * rope_dim = 64, h a multiple of 128, q_lora_rank a multiple of 512, any
@@ -311,8 +314,9 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
  * num_heads is read from wq_b's width. Outputs are rounded to nearest even
  * from fp32; products accumulate in fp32; c^Q is rounded to bf16 before it
  * enters the second product.
- * mla_prolog enqueues three kernels on stream (x . [wq_a | wkv] with the kv
- * epilogue, the c^Q norm, c^Q . wq_b with the q epilogue). The workspace
+ * mla_prolog enqueues six kernels on stream (the rearrangements of wq_a and
+ * of wkv, x . [wq_a | wkv] with the kv epilogue, the c^Q norm, the
+ * rearrangement of wq_b, c^Q . wq_b with the q epilogue). The workspace
  * (16-byte aligned, at least the planned size) must stay untouched until they
  * have run. Errors as for mla_prefill.
  */

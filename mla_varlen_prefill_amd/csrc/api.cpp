@@ -684,7 +684,22 @@ int validate_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla
     return MLA_OK;
 }
 
-uint64_t prolog_workspace_bytes(const PrologProblem &pp) { return align256((uint64_t)pp.t * pp.r * 4); }
+// Workspace of mla_prolog: the fp32 rows of x . wq_a, then the packed copies
+// of wq_a, wkv and wq_b (each 256-byte aligned).
+uint64_t prolog_yq_bytes(const PrologProblem &pp) { return align256((uint64_t)pp.t * pp.r * 4); }
+uint64_t prolog_pack_a_bytes(const PrologProblem &pp) {
+    return align256((uint64_t)mla::prolog_packed_bytes((int32_t)(pp.r / mla::PROLOG_BN), (int32_t)pp.h));
+}
+uint64_t prolog_pack_kv_bytes(const PrologProblem &pp) {
+    return align256((uint64_t)mla::prolog_packed_bytes(1, (int32_t)pp.h));
+}
+uint64_t prolog_pack_b_bytes(const PrologProblem &pp) {
+    return align256((uint64_t)mla::prolog_packed_bytes((int32_t)pp.heads, (int32_t)pp.r));
+}
+uint64_t prolog_workspace_bytes(const PrologProblem &pp) {
+    if (pp.t == 0) return 0;  // nothing to compute
+    return prolog_yq_bytes(pp) + prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp) + prolog_pack_b_bytes(pp);
+}
 
 }  // namespace
 
@@ -954,7 +969,11 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
         return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     hipStream_t s = static_cast<hipStream_t>(stream);
-    float *y_q = static_cast<float *>(workspace);
+    unsigned char *wsb = static_cast<unsigned char *>(workspace);
+    float *y_q = reinterpret_cast<float *>(wsb);
+    unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
+    unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
+    unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
 
     // x . [wq_a | wkv]: the wq_a tiles store fp32 rows for the c^Q norm, the
     // wkv tile is the kv row (norm * gamma_ckv, rope)
@@ -963,12 +982,16 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     g1.lda = pp.h;
     g1.m = (int32_t)pp.t;
     g1.k = (int32_t)pp.h;
-    g1.seg[0] = {wq_a->data, pp.r, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, y_q, pp.r, nullptr};
-    g1.seg[1] = {wkv->data, mla::PROLOG_BN, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN, gamma_ckv->data};
+    g1.seg[0] = {wq_a->data, pp.r, pack_a, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, y_q, pp.r,
+                 nullptr};
+    g1.seg[1] = {wkv->data, mla::PROLOG_BN, pack_kv, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN,
+                 gamma_ckv->data};
     g1.rope_cos = rope_cos->data;
     g1.rope_sin = rope_sin->data;
     g1.eps = eps;
-    hipError_t e = mla::launch_prolog_gemm(g1, s);
+    hipError_t e = mla::launch_prolog_pack(g1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
+    e = mla::launch_prolog_gemm(g1, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
     e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
                                     s);
@@ -979,12 +1002,14 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     g2.lda = pp.r;
     g2.m = (int32_t)pp.t;
     g2.k = (int32_t)pp.r;
-    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE, q_out->data,
-                 pp.heads * mla::PROLOG_BN, nullptr};
-    g2.seg[1] = {nullptr, 0, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
+    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pack_b, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE,
+                 q_out->data, pp.heads * mla::PROLOG_BN, nullptr};
+    g2.seg[1] = {nullptr, 0, nullptr, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
     g2.rope_cos = rope_cos->data;
     g2.rope_sin = rope_sin->data;
     g2.eps = eps;
+    e = mla::launch_prolog_pack(g2, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
     e = mla::launch_prolog_gemm(g2, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
     return ok();

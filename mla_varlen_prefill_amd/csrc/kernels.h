@@ -145,6 +145,7 @@ enum PrologEpilogue : int32_t {
 struct PrologSegment {
     const void *w;       // bf16 [K, ldw]; this segment's tile j reads columns j*512 .. j*512+511
     int64_t ldw;         // row stride of w, elements
+    void *wp;            // packed copy of w (launch_prolog_pack): n_tiles * (K / 32) blocks of 32 KB
     int32_t n_tiles;     // 512-column tiles of this segment
     int32_t epilogue;    // PrologEpilogue
     void *out;           // tile j of rows m: out + m * ld_out + j * 512 (elements of the epilogue's type)
@@ -163,6 +164,16 @@ struct PrologGemmParams {
     float eps;
 };
 
+// Bytes of a segment's packed weights: one 32 KB block per 512-column tile and
+// 32-row stage of K.
+constexpr int64_t PROLOG_PACK_BLOCK = PROLOG_BN * PROLOG_BK * 2;
+inline int64_t prolog_packed_bytes(int32_t n_tiles, int32_t k) {
+    return (int64_t)n_tiles * (k / PROLOG_BK) * PROLOG_PACK_BLOCK;
+}
+
+// Writes seg.wp from seg.w for each segment with tiles: block (j, kt) is the
+// stage image the product kernel reads (see prolog.hip).
+hipError_t launch_prolog_pack(const PrologGemmParams &p, hipStream_t stream);
 hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream);
 
 // y fp32 [rows, cols] (row stride ld_y) -> out bf16 [rows, cols] (row stride

@@ -26,14 +26,24 @@
 //  * 8 waves = 4 column quarters (128 columns) x 2 row halves (64 rows):
 //    4 x 2 accumulator blocks of 32 x 32 per wave.
 //  * K is walked in stages of 32 through a 4-stage LDS ring (40 KB a stage),
-//    loaded three stages ahead through two register sets. Activation rows are
-//    stored as loaded. Weight rows are k-major in memory but the operand
-//    needs 8 consecutive k per column, so each thread loads 4 weight rows x 8
-//    columns, pairs them with v_perm_b32 and writes 8-byte (4 k) pieces of
-//    the transposed tile. Both LDS layouts are XOR-swizzled in 16-byte chunks so
-//    the 16-byte operand reads are conflict-free; the transposed tile also
-//    permutes its rows (row n at n ^ ((n >> 3) & 3)) so the 8-byte writes hit
-//    every bank group.
+//    loaded three stages ahead by DMA (buffer loads straight into LDS, no
+//    register round trip). The operand needs 8 consecutive k per column,
+//    and the weights are k-major in memory, so prolog_pack_kernel first
+//    rewrites each weight into blocks of 32 KB -- one per 512-column tile and
+//    32-row stage -- that are exactly the stage's LDS image: column n, 16-byte
+//    chunk c (k 8c .. 8c + 7) at byte n * 64 + ((c ^ ((n >> 2) & 3)) << 4).
+//    Every weight DMA instruction then reads one contiguous kilobyte. The
+//    activation stage (128 rows x 64 bytes) is DMA'd from the row-major
+//    activations with the same XOR swizzle applied on the global side. Both
+//    swizzles make the 16-byte operand reads conflict-free. (Loading the
+//    weights k-major through registers and transposing them with v_perm
+//    before an LDS write ran at 29% of the bf16 peak on the 16384-token
+//    workload's main product, against 40% for this path: the vector memory
+//    path of a CU moved the 40 KB of a stage too slowly when the lanes of one
+//    load instruction spanned several rows.)
+//  * Each ring slot is an LDS array of its own, so the compiler can tell a
+//    slot being read from the slots the DMA is filling and waits only where
+//    the pipeline says so.
 //  * Column tiles are spread so that the 32 CUs of an XCD work on the same
 //    weight tile at the same time (it stays in that XCD's L2).
 #include <hip/hip_runtime.h>
@@ -64,6 +74,11 @@ extern "C" __device__ i32x4 prolog_raw_buffer_load_b128(i32x4 rsrc, int voffset,
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 extern "C" __device__ i16x4 prolog_raw_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i16");
+typedef __attribute__((address_space(3))) unsigned int *lds_u32_ptr;
+// Buffer load with the LDS-DMA bit: lane l's `size` bytes land at lds + l*size.
+extern "C" __device__ void prolog_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
+                                                      int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
 extern "C" __device__ void prolog_raw_buffer_store_b128(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
@@ -93,10 +108,52 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
     return __uint_as_float(static_cast<unsigned>(b) << 16);
 }
 
+// Packs the weights of one segment tile stage: workgroup (j, kt) reads rows
+// 32 kt .. 32 kt + 31, columns 512 j .. 512 j + 511 of w (coalesced, into LDS
+// k-major) and writes block j * (K / 32) + kt of wp in the stage layout the
+// product kernel reads.
+__global__ __launch_bounds__(256) void prolog_pack_kernel(const unsigned char *w, int64_t ldw, int32_t nk,
+                                                          unsigned char *wp) {
+    constexpr int ROW = BN * 2 + 16;  // LDS bytes per k row (padded)
+    __shared__ __attribute__((aligned(16))) unsigned char t[BK * ROW];
+    const int tid = threadIdx.x;
+    const int j = blockIdx.x / nk, kt = blockIdx.x % nk;
+    const unsigned char *src = w + ((int64_t)kt * BK * ldw + (int64_t)j * BN) * 2;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int q = tid + 256 * u, row = q >> 6, ch = q & 63;  // 64 16-byte chunks per 1 KB row
+        *reinterpret_cast<uint4 *>(t + row * ROW + ch * 16) =
+            *reinterpret_cast<const uint4 *>(src + (int64_t)row * ldw * 2 + ch * 16);
+    }
+    __syncthreads();
+    unsigned char *dst = wp + ((int64_t)j * nk + kt) * PROLOG_PACK_BLOCK;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int s16 = tid + 256 * u;  // 16-byte slot of the block: column n, physical chunk pc
+        const int n = s16 >> 2, pc = s16 & 3, c = pc ^ ((n >> 2) & 3);
+        unsigned short v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const unsigned short *>(t + (8 * c + i) * ROW + n * 2);
+        uint4 o;
+        o.x = v[0] | (unsigned)v[1] << 16;
+        o.y = v[2] | (unsigned)v[3] << 16;
+        o.z = v[4] | (unsigned)v[5] << 16;
+        o.w = v[6] | (unsigned)v[7] << 16;
+        *reinterpret_cast<uint4 *>(dst + s16 * 16) = o;
+    }
+}
+
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void prolog_gemm_kernel(const PrologGemmParams p) {
-    __shared__ __attribute__((aligned(1024))) unsigned char xs[STAGES * X_BYTES];
-    __shared__ __attribute__((aligned(1024))) unsigned char ws[STAGES * W_BYTES];
+    // one array per ring slot (see the design notes above)
+    __shared__ __attribute__((aligned(1024))) unsigned char xs0[X_BYTES], xs1[X_BYTES], xs2[X_BYTES], xs3[X_BYTES];
+    __shared__ __attribute__((aligned(1024))) unsigned char ws0[W_BYTES], ws1[W_BYTES], ws2[W_BYTES], ws3[W_BYTES];
+    auto WS = [&](int i) __attribute__((always_inline)) -> unsigned char * {
+        return i == 0 ? ws0 : i == 1 ? ws1 : i == 2 ? ws2 : ws3;
+    };
+    auto XS = [&](int i) __attribute__((always_inline)) -> unsigned char * {
+        return i == 0 ? xs0 : i == 1 ? xs1 : i == 2 ? xs2 : xs3;
+    };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,8 +180,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     }
     const bool second = tn >= p.seg[0].n_tiles;
     const int tj = second ? tn - p.seg[0].n_tiles : tn;
-    const unsigned char *w = static_cast<const unsigned char *>(second ? p.seg[1].w : p.seg[0].w);
-    const int64_t ldw = second ? p.seg[1].ldw : p.seg[0].ldw;
+    const unsigned char *wpk = static_cast<const unsigned char *>(second ? p.seg[1].wp : p.seg[0].wp);
     const int epilogue = second ? p.seg[1].epilogue : p.seg[0].epilogue;
     void *out_base = second ? p.seg[1].out : p.seg[0].out;
     const int64_t ld_out = second ? p.seg[1].ld_out : p.seg[0].ld_out;
@@ -133,64 +189,34 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const int rows = min(BM, p.m - m0);
     const int nk = p.k / BK;
 
-    // ---- activation stage: 128 rows x 64 bytes; thread tid loads the 16
-    // bytes of LDS slot tid = row tid / 4, physical chunk tid % 4, which holds
-    // logical chunk (tid % 4) ^ ((row >> 2) & 3). Rows past the end read as
-    // zeros. (Through registers, not the LDS-DMA path: the compiler cannot
-    // tell where a DMA lands and would wait for it before every LDS access.)
+    // ---- activation stage: 128 rows x 64 bytes; LDS slot tid (row tid / 4,
+    // physical chunk tid % 4) receives logical chunk (tid % 4) ^ ((row >> 2)
+    // & 3). Rows past the end read as zeros.
     const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * 2,
                                (uint32_t)rows * (uint32_t)p.lda * 2);
     const int xr = tid >> 2;
     const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * 2 + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
-    auto issue_x = [&](int kt, uint4 &xst) __attribute__((always_inline)) {
-        xst = __builtin_bit_cast(uint4, prolog_raw_buffer_load_b128(ra, xoff + (uint32_t)kt * BK * 2, 0, 0));
-    };
-    auto write_x = [&](int slot, const uint4 &xst) __attribute__((always_inline)) {
-        *reinterpret_cast<uint4 *>(xs + slot * X_BYTES + tid * 16) = xst;
-    };
-
-    // ---- weight stage: rows 32 kt .. + 31 of w, this tile's 512 columns.
-    // Thread: k quad kq (rows 4 kq .. 4 kq + 3), column chunk nc (columns
-    // 8 nc .. 8 nc + 7). Rows past K read as zeros.
-    const int kq = tid & 7, nc = tid >> 3;
-    const i32x4 rw = make_rsrc(w + (int64_t)tj * BN * 2, (uint32_t)((int64_t)p.k * ldw * 2 - (int64_t)tj * BN * 2));
-    const uint32_t wrow = (uint32_t)ldw * 2;
-    const uint32_t woff = (uint32_t)(4 * kq) * wrow + nc * 16;
-    auto issue_w = [&](int kt, uint4 *wst) __attribute__((always_inline)) {
+    // ---- weight stage: block kt of this tile's packed weights, 2048 16-byte
+    // slots; load r of a thread takes slot 512 r + tid. Stages past K read
+    // as zeros.
+    const i32x4 rw = make_rsrc(wpk + (int64_t)tj * nk * PROLOG_PACK_BLOCK, (uint32_t)nk * PROLOG_PACK_BLOCK);
+    // DMA of stage kt into ring slot kt % STAGES: lane l's 16 bytes land at
+    // base + 16 l, so a wave's base is its first slot.
+    auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            wst[r] = __builtin_bit_cast(uint4, prolog_raw_buffer_load_b128(
-                                                   rw, woff + (uint32_t)r * wrow + (uint32_t)kt * BK * wrow, 0, 0));
-    };
-    // Transposed stage: physical row P = n ^ ((n >> 3) & 3) of column n holds
-    // its 32 k values, 16-byte chunk c (k 8c .. 8c + 7) at position
-    // c ^ ((P >> 2) & 3). For n = 8 nc + i, P = 8 nc + (i ^ (nc & 3)); the
-    // thread's 4 k values go to chunk kq / 2, half kq % 2.
-    auto write_w = [&](int slot, const uint4 *wst) __attribute__((always_inline)) {
-        unsigned char *st = ws + slot * W_BYTES;
-        const unsigned r0[4] = {wst[0].x, wst[0].y, wst[0].z, wst[0].w};
-        const unsigned r1[4] = {wst[1].x, wst[1].y, wst[1].z, wst[1].w};
-        const unsigned r2[4] = {wst[2].x, wst[2].y, wst[2].z, wst[2].w};
-        const unsigned r3[4] = {wst[3].x, wst[3].y, wst[3].z, wst[3].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int prow = 8 * nc + (i ^ (nc & 3));
-            const uint32_t addr = prow * 64 + (((kq >> 1) ^ ((prow >> 2) & 3)) << 4) + (kq & 1) * 8;
-            const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-            uint2 v;
-            v.x = __builtin_amdgcn_perm(r1[i >> 1], r0[i >> 1], sel);
-            v.y = __builtin_amdgcn_perm(r3[i >> 1], r2[i >> 1], sel);
-            *reinterpret_cast<uint2 *>(st + addr) = v;
-        }
+            prolog_raw_buffer_load_lds(rw, (lds_u32_ptr)(WS(slot) + (r * 512 + wave * 64) * 16), 16,
+                                       (uint32_t)kt * PROLOG_PACK_BLOCK + (uint32_t)(r * 512 + tid) * 16, 0, 0, 0);
+        prolog_raw_buffer_load_lds(ra, (lds_u32_ptr)(XS(slot) + wave * 64 * 16), 16, xoff + (uint32_t)kt * BK * 2,
+                                   0, 0, 0);
     };
 
     // ---- operand read offsets (within a stage). Weight column block nb of
-    // the wave: column n = 128 wn + 32 nb + r32, physical row P; k chunk
-    // 2 ks + g. Activation row block tb: row 64 wt + 32 tb + r32, chunk
-    // 2 ks + g. Both are base ^ (ks << 5) plus a multiple of 2 KB.
+    // the wave: column n = 128 wn + 32 nb + r32; k chunk 2 ks + g. Activation
+    // row block tb: row 64 wt + 32 tb + r32, chunk 2 ks + g. Both are base ^
+    // (ks << 5) plus a multiple of 2 KB.
     const int n_l = 128 * wn + r32;
-    const int pn = n_l ^ ((n_l >> 3) & 3);
-    const uint32_t wb = (uint32_t)(pn * 64) | ((uint32_t)(g ^ ((pn >> 2) & 3)) << 4);
+    const uint32_t wb = (uint32_t)(n_l * 64) | ((uint32_t)(g ^ ((n_l >> 2) & 3)) << 4);
     const int xrow = 64 * wt + r32;
     const uint32_t xb = (uint32_t)(xrow * 64) | ((uint32_t)(g ^ ((xrow >> 2) & 3)) << 4);
 
@@ -202,67 +228,81 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[nb][tb][e] = 0.f;
 
-    // ---- pipeline. Stage kt lives in ring slot kt % 4; its rows go through
-    // register set kt % 2. Iteration kt sends out the loads of stage kt+3, so
-    // each stage's loads have two iterations to arrive: at the top of
-    // iteration kt only the five loads of stage kt+2 may still fly (vmcnt(5)),
-    // so stage kt+1 has landed. It is stored into its slot, stage kt+3 is
-    // sent out, and slot kt is consumed; the barrier at the end publishes slot
-    // kt+1. The loop is unrolled by the ring depth so every slot and register
-    // set is a compile-time constant.
-    uint4 wst[2][4], xst[2];
-    issue_w(0, wst[0]);
-    issue_x(0, xst[0]);
-    issue_w(1, wst[1]);
-    issue_x(1, xst[1]);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 5);  // stage 0 landed
-    write_w(0, wst[0]);
-    write_x(0, xst[0]);
-    issue_w(2, wst[0]);
-    issue_x(2, xst[0]);
+    // Operands of one k-step: av = 4 weight column blocks, bv = 2 activation
+    // row blocks. Operand o < 4 is av[o], o >= 4 is bv[o - 4]. The products of
+    // a k-step run row block first (n -> column block n % 4, row block n / 4),
+    // so each operand is done with early and the next k-step's value is read
+    // into its registers while the remaining products run: bv[0] after product
+    // 3, av[0..2] after products 4..6, av[3] and bv[1] after product 7.
+    bf16x8 av[4], bv[2];
+    auto read_op = [&](int slot, int ks, int o) __attribute__((always_inline)) {
+        if (o < 4)
+            av[o] = __builtin_bit_cast(bf16x8,
+                                       *reinterpret_cast<const uint4 *>(WS(slot) + ((wb ^ (ks << 5)) + o * 2048)));
+        else
+            bv[o - 4] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4 *>(XS(slot) + ((xb ^ (ks << 5)) + (o - 4) * 2048)));
+    };
+    auto product = [&](int n) __attribute__((always_inline)) {
+        const int nb = n & 3, tb = n >> 2;
+        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+    };
+    // operands of the next k-step read after product n of this one
+    auto read_after = [&](int slot, int ks, int n) __attribute__((always_inline)) {
+        if (n == 3) read_op(slot, ks, 4);
+        if (n >= 4) read_op(slot, ks, n - 4);
+        if (n == 7) read_op(slot, ks, 5);
+    };
+
+    // ---- pipeline. Stage kt lives in ring slot kt % 4. Iteration kt sends
+    // out the DMA of stage kt+3 (into the slot of stage kt-1, which every
+    // wave finished reading before the last barrier), so each stage has two
+    // iterations to arrive. Within iteration kt: k-step 0's products, with
+    // k-step 1's operand reads in between; k-step 1's products; the DMA of
+    // stage kt+3; a wait until stage kt+1 has landed (vmcnt(10): only the
+    // loads of stages kt+2 and kt+3 may still fly); the barrier that
+    // publishes it; k-step 0's operand reads of slot kt+1. Every iteration
+    // issues exactly five loads per thread (stages past K read zeros), so
+    // the counts hold on every iteration. The loop is unrolled by the ring
+    // depth so every slot is a compile-time constant.
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 10);  // stage 0 landed (stages 1 and 2 may fly)
     block_sync();
+#pragma unroll
+    for (int o = 0; o < 6; ++o) read_op(0, 0, o);
     auto step = [&](int kt, auto SLOT) __attribute__((always_inline)) {
         constexpr int sl = decltype(SLOT)::value;
-        constexpr int nx = (sl + 1) % 2;  // register set of stages kt+1 and kt+3
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);  // stage kt+1 landed
-        write_w((sl + 1) % STAGES, wst[nx]);
-        write_x((sl + 1) % STAGES, xst[nx]);
-        issue_w(kt + 3, wst[nx]);
-        issue_x(kt + 3, xst[nx]);
-        const unsigned char *stw = ws + sl * W_BYTES;
-        const unsigned char *stx = xs + sl * X_BYTES;
-        // one k-step of operands at a time keeps 24 operand registers live
+        constexpr int ns = (sl + 1) % STAGES;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 av[4], bv[2];
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-                av[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                        stw + ((wb ^ (ks << 5)) + nb * 2048)));
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb)
-                bv[tb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(
-                                                        stx + ((xb ^ (ks << 5)) + tb * 2048)));
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                for (int tb = 0; tb < 2; ++tb)
-                    acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+        for (int n = 0; n < 8; ++n) {
+            product(n);
+            read_after(sl, 1, n);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            product(n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        issue(kt + 3, (sl + 3) % STAGES);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 10);  // stage kt+1 landed: only stages kt+2 and kt+3 may fly
         block_sync();
+#pragma unroll
+        for (int o = 0; o < 6; ++o) read_op(ns, 0, o);
     };
-    // K is a multiple of 4 stages: every iteration runs all four steps, so
-    // the registers in flight are the same on every path (a merge of paths
-    // with different loads outstanding would copy them, and a copy waits)
+    // K is a multiple of 4 stages: every iteration runs all four steps
     for (int kt = 0; kt < nk; kt += STAGES) {
         step(kt, std::integral_constant<int, 0>{});
         step(kt + 1, std::integral_constant<int, 1>{});
         step(kt + 2, std::integral_constant<int, 2>{});
         step(kt + 3, std::integral_constant<int, 3>{});
     }
-    // the loads of stages past the end return into registers nobody reads;
-    // the LDS is free for the epilogue once every wave is past the last stage
+    // The DMA of the three stages past the end (zeros) may still be landing
+    // in the ring, which the epilogue reuses: wait for all of it, then for
+    // every wave to be past the last stage.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     block_sync();
 
     // ---- epilogue. Lane: output row 64 wt + 32 tb + r32 of the tile; element
@@ -291,7 +331,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                     v.y = acc[nb][tb][4 * i + 1];
                     v.z = acc[nb][tb][4 * i + 2];
                     v.w = acc[nb][tb][4 * i + 3];
-                    *reinterpret_cast<float4 *>(ws + lr * 2048 + ((c ^ ((lr & 7) << 1)) << 4)) = v;
+                    *reinterpret_cast<float4 *>(WS(lr >> 4) + (lr & 15) * 2048 + ((c ^ ((lr & 7) << 1)) << 4)) = v;
                 }
             block_sync();
 #pragma unroll
@@ -299,7 +339,8 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 const int q = 8 * wave + (u >> 1);        // pass row
                 const int ch = (u & 1) * 64 + lane;       // logical 16-byte chunk
                 const int row = 64 * (q >> 5) + 32 * tb + (q & 31);
-                const i32x4 v = *reinterpret_cast<const i32x4 *>(ws + q * 2048 + ((ch ^ ((q & 7) << 1)) << 4));
+                const i32x4 v =
+                    *reinterpret_cast<const i32x4 *>(WS(q >> 4) + (q & 15) * 2048 + ((ch ^ ((q & 7) << 1)) << 4));
                 prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 4 + ch * 16, 0, 0);
             }
         }
@@ -357,7 +398,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(sm), __float_as_int(sm), false, false);
         ssq[tb] = __int_as_float(sw[0]) + __int_as_float(sw[1]);
     }
-    float *red = reinterpret_cast<float *>(xs);  // [4 quarters][128 rows]
+    float *red = reinterpret_cast<float *>(xs0);  // [4 quarters][128 rows]
     if (g == 0) {
         red[wn * BM + 64 * wt + r32] = ssq[0];
         red[wn * BM + 64 * wt + 32 + r32] = ssq[1];
@@ -412,14 +453,15 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) o4[j] = static_cast<__bf16>(v[j]);
                 // tile row r (1 KB) holds 16-byte chunk c (8 columns) at c ^ (r & 15)
-                *reinterpret_cast<bf16x4 *>(ws + row * 1024 + (((n >> 3) ^ (row & 15)) << 4) + g * 8) = o4;
+                *reinterpret_cast<bf16x4 *>(WS(row >> 5) + (row & 31) * 1024 + (((n >> 3) ^ (row & 15)) << 4) + g * 8) =
+                    o4;
             }
         }
     block_sync();
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
         const int row = 16 * wave + u;
-        const i32x4 v = *reinterpret_cast<const i32x4 *>(ws + row * 1024 + ((lane ^ (row & 15)) << 4));
+        const i32x4 v = *reinterpret_cast<const i32x4 *>(WS(row >> 5) + (row & 31) * 1024 + ((lane ^ (row & 15)) << 4));
         prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 2 + lane * 16, 0, 0);
     }
 }
@@ -457,6 +499,17 @@ __global__ __launch_bounds__(256) void prolog_rms_rows_kernel(const float *y, in
 }
 
 }  // namespace
+
+hipError_t launch_prolog_pack(const PrologGemmParams &p, hipStream_t stream) {
+    const int32_t nk = p.k / PROLOG_BK;
+    for (int i = 0; i < 2; ++i) {
+        const PrologSegment &sg = p.seg[i];
+        if (sg.n_tiles <= 0) continue;
+        hipLaunchKernelGGL(prolog_pack_kernel, dim3((unsigned)(sg.n_tiles * nk)), dim3(256), 0, stream,
+                           static_cast<const unsigned char *>(sg.w), sg.ldw, nk, static_cast<unsigned char *>(sg.wp));
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream) {
     const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;

@@ -526,7 +526,11 @@ def prolog_status(**kw):
 
 def test_prolog_workspace_size_and_empty_call():
     assert mla.mla_prolog_get_workspace_size(**prolog_args(t=0)) == 0
-    assert mla.mla_prolog_get_workspace_size(**prolog_args(t=3)) == 256 * -(-3 * 512 * 4 // 256)
+    # the fp32 rows of x . wq_a (256-byte aligned), then wq_a, wkv and wq_b
+    # repacked (2 bytes per weight)
+    h, r, heads, hd = 128, 512, 2, 512
+    assert mla.mla_prolog_get_workspace_size(**prolog_args(t=3)) == \
+        256 * -(-3 * r * 4 // 256) + 2 * h * r + 2 * h * hd + 2 * r * heads * hd
     # t = 0: valid, nothing to launch (no HIP call)
     assert c_mla_prolog(prolog_args(t=0), None) == "MLA_OK"
 
