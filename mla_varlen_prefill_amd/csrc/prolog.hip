@@ -36,11 +36,14 @@
 //    activation stage (128 rows x 64 bytes) is DMA'd from the row-major
 //    activations with the same XOR swizzle applied on the global side. Both
 //    swizzles make the 16-byte operand reads conflict-free. (Loading the
-//    weights k-major through registers and transposing them with v_perm
-//    before an LDS write ran at 29% of the bf16 peak on the 16384-token
-//    workload's main product, against 40% for this path: the vector memory
-//    path of a CU moved the 40 KB of a stage too slowly when the lanes of one
-//    load instruction spanned several rows.)
+//    weights k-major through registers, the lanes of one load instruction
+//    spread over eight rows, and transposing them with v_perm before an LDS
+//    write took 1.53 ms for the 16384-token workload's main product, against
+//    1.15-1.29 ms for this path; the whole prolog went from 29% to 34% of the
+//    bf16 peak. Counters on this path: matrix cores busy 49% of the cycles
+//    at 1.85 GHz; a quarter of the LDS cycles are bank conflicts, from the
+//    16-byte DMA writes -- the operand reads measured the same with the
+//    weight rows permuted.)
 //  * Each ring slot is an LDS array of its own, so the compiler can tell a
 //    slot being read from the slots the DMA is filling and waits only where
 //    the pipeline says so.
