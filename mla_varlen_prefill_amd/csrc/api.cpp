@@ -32,6 +32,10 @@ using mla::WorkItem;
 #define MLA_PLAN_BATCH_TASKS (2 * MLA_CUS_PER_XCD)
 #endif
 constexpr int PLAN_BATCH_TASKS = MLA_PLAN_BATCH_TASKS;  // minimum tasks per launch-order batch of an XCD queue
+#ifndef MLA_PLAN_EVEN_BATCH_TASKS
+#define MLA_PLAN_EVEN_BATCH_TASKS (MLA_CUS_PER_XCD / 2)
+#endif
+constexpr int PLAN_EVEN_BATCH_TASKS = MLA_PLAN_EVEN_BATCH_TASKS;  // the same when the tasks are about equal
 #ifndef MLA_MAX_PACK_SHIFT
 #define MLA_MAX_PACK_SHIFT 3
 #endif
@@ -377,8 +381,10 @@ int32_t pack_shift_for(int32_t heads, int32_t kv_heads) {
 //    much and dealt again, so that every XCD gets a share. Block i of the
 //    launch is taken from queue i % MLA_XCDS (the hardware hands consecutive
 //    workgroups to consecutive XCDs). Each queue is cut into batches of whole
-//    groups holding at least twice as many tasks as the XCD has CUs, and
-//    each batch is ordered heaviest task first. The tasks of a
+//    groups holding at least twice as many tasks as the XCD has CUs -- or
+//    half as many when most of the work is in groups whose tasks are within
+//    a factor 2 of each other -- and each batch is ordered heaviest task
+//    first. The tasks of a
 //    group thus run together on one XCD and share its L2 while they stream
 //    the same keys, and the heaviest first order inside a batch keeps the
 //    XCD's CUs evenly loaded to the end. Short queues are padded with empty
@@ -460,6 +466,26 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         groups.swap(cut);
         deal();
     }
+    // Batch size of the launch order (below). Large batches let the
+    // heaviest-first order balance the CUs when a group's tasks differ a lot
+    // in length (causal items over their own keys); when they are about
+    // equal (query rows at the end of a long key range), balance comes by
+    // itself and small batches keep fewer K/V streams in flight per XCD, so
+    // more of them hit in its L2.
+    size_t batch_tasks = PLAN_BATCH_TASKS;
+    {
+        int64_t uneven = 0, even = 0;
+        for (const Group &gr : groups) {
+            int64_t lo = INT64_MAX, hi = 0;
+            for (int32_t t = gr.t0; t < gr.t1; ++t) {
+                const int64_t w = task_work(plan->items[seq_first[gr.b] + t / tasks_per_item]);
+                lo = std::min(lo, w);
+                hi = std::max(hi, w);
+            }
+            if (gr.t1 > gr.t0) (hi > 2 * lo ? uneven : even) += gr.work;
+        }
+        if (even > uneven) batch_tasks = PLAN_EVEN_BATCH_TASKS;
+    }
     std::vector<std::vector<Task>> queue(MLA_XCDS);
     std::vector<Task> pending;
     for (int x = 0; x < MLA_XCDS; ++x) {
@@ -473,7 +499,7 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         for (const Group &gr : xcd_groups[x]) {
             for (int32_t t = gr.t0; t < gr.t1; ++t)
                 pending.push_back({seq_first[gr.b] + t / tasks_per_item, gr.hk * group + (t % tasks_per_item) * (1 << ps)});
-            if (pending.size() >= (size_t)PLAN_BATCH_TASKS) flush();
+            if (pending.size() >= batch_tasks) flush();
         }
         flush();
     }
