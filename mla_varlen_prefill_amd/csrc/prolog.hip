@@ -41,9 +41,10 @@
 //    write took 1.53 ms for the 16384-token workload's main product, against
 //    1.15-1.29 ms for this path; the whole prolog went from 29% to 34% of the
 //    bf16 peak. Counters on this path: matrix cores busy 49% of the cycles
-//    at 1.85 GHz; a quarter of the LDS cycles are bank conflicts, from the
-//    16-byte DMA writes -- the operand reads measured the same with the
-//    weight rows permuted.)
+//    at 1.85 GHz; bank conflicts are a quarter of the LDS-active count, the
+//    same with the weight rows permuted and with 4-byte DMA (which fills 256
+//    contiguous bytes per instruction and ran 6% slower), so they come
+//    from neither the operand reads nor the DMA writes.)
 //  * Each ring slot is an LDS array of its own, so the compiler can tell a
 //    slot being read from the slots the DMA is filling and waits only where
 //    the pipeline says so.
