@@ -60,7 +60,9 @@ constexpr int G_UNROLL = 8;  // 16-byte loads in flight per thread and row
 // rows per token reach 80%. Not faster on KRope, and 2-15% slower on K+V:
 // the eight loads taken across the four tokens of a step; 2, 8 or 16 tokens
 // per step; 2048 to 65536 workgroups; plain instead of non-temporal loads or
-// stores; one wave per row with 16 loads per lane and no workgroup barriers.
+// stores; one wave per row with 16 loads per lane and no workgroup barriers;
+// a KRope-only call taking each step's tokens from both halves of the token
+// range (two read and two write streams, as K+V has).
 __device__ __forceinline__ void copy_row16(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
                                            int64_t n16, int tid) {
     for (int64_t c = tid; c < n16; c += G_UNROLL * G_THREADS) {
