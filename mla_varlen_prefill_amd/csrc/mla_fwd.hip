@@ -88,14 +88,25 @@ struct Geom {
     static constexpr int VRAW_OFFSET = STAGES * STAGE_BYTES;
     static constexpr int LDS_BYTES = VRAW_OFFSET + 2 * V_BYTES;
     // Q and Q-rope of the 8 waves pass through LDS once, at the start: 32 rows
-    // of D + 64 values per wave. D = 128: in the ring past tile 0's K (stage 0's
-    // V^T and stages 1 and 2, free until the first barrier); D = 64: past
-    // everything else.
+    // of D + 64 values per wave (a slot). D = 128, inside the ring: a leading
+    // wave's slot lies in the K half of stage 1 or 2 (tiles 1 and 2's K lands
+    // there after the first barrier, so it is read back before); a trailing
+    // wave's slot lies in the V^T half of a stage or in the second raw V
+    // buffer, which nothing writes before interval 1, so the trailing group
+    // reads its Q back during interval 0 and the first barrier does not wait
+    // for it. Tile 0's K (stage 0's K half) and raw V (first raw buffer) load
+    // meanwhile. D = 64: past everything else.
     static constexpr int QSLOT_BYTES = 32 * (D + 64) * 2;
-    static constexpr int QSTAGE_OFFSET = D == 128 ? KN_BYTES + KR_BYTES : LDS_BYTES + PAGED_MAX_TILES * 4;
-    static constexpr int SMEM_MIN = QSTAGE_OFFSET + 8 * QSLOT_BYTES;
+    static constexpr int QSTAGE_OFFSET = LDS_BYTES + PAGED_MAX_TILES * 4;
+    static constexpr int SMEM_MIN = D == 128 ? 0 : QSTAGE_OFFSET + 8 * QSLOT_BYTES;
+    static constexpr int qslot_offset(int grp, int w) {
+        return D == 128 ? (grp == 0 ? STAGE_BYTES * (1 + (w >> 1)) + (w & 1) * QSLOT_BYTES
+                                    : (w < 3 ? STAGE_BYTES * w + KN_BYTES + KR_BYTES : VRAW_OFFSET + V_BYTES))
+                        : QSTAGE_OFFSET + (2 * w + grp) * QSLOT_BYTES;
+    }
 };
-static_assert(Geom<128>::SMEM_MIN <= Geom<128>::VRAW_OFFSET, "Q staging must leave the raw V buffers free");
+static_assert(2 * Geom<128>::QSLOT_BYTES <= Geom<128>::KN_BYTES + KR_BYTES, "two leading Q slots per K half");
+static_assert(Geom<128>::QSLOT_BYTES <= Geom<128>::V_BYTES, "a trailing Q slot per V^T half or raw buffer");
 // 16-byte chunk swizzle of an LDS row of D * 2 bytes (K-nope rows, output
 // staging rows): chunk c of row r sits at c ^ swz(r), which makes the 16-byte
 // reads of 16 consecutive rows (and 8-byte writes of 32) conflict-free.
@@ -291,7 +302,7 @@ void mla_fwd_kernel(const FwdParams p) {
     // keeps the read-back conflict-free. Rows past the end read as 0.
     constexpr int QN_INSTR = DN / 16;          // 1 KB DMA instructions for Q-nope
     constexpr int QN_CPR = DN / 8;             // 16-byte chunks of a Q-nope row
-    unsigned char *qslot = smem + Geom<DN>::QSTAGE_OFFSET + slot * Geom<DN>::QSLOT_BYTES;
+    unsigned char *qslot = smem + Geom<DN>::qslot_offset(grp, wave & 3);
     {
         const int rows = max(0, min(32, q_len - row0));
         const int64_t tok = (int64_t)task.q_off + row0;
@@ -482,24 +493,10 @@ void mla_fwd_kernel(const FwdParams p) {
     // scores: a stage's K region is free once the trailing group has scored
     // the tile before. Its raw V goes out (trailing group) right after the
     // transpose of tile t-1, two intervals before its own.
-    // Before the first barrier only what interval 0 needs is loaded: every
-    // wave's Q, and tile 0's K (the leading group scores it); tile 0's raw V
-    // goes out too and is waited for at the end of interval 0. The K of tiles
-    // 1 and 2 goes out during interval 0 (into ring stages that hold the Q
-    // staging until the first barrier).
-    if (grp == 0) {
-        const TileLoad t0 = prep_tile(0, cache_row(0));
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
-#pragma unroll
-        for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j);
-        __builtin_amdgcn_s_waitcnt(0x0F70 | V_LOADS);  // Q, Q-rope and K of tile 0 landed
-    } else {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope
-    }
-    static_assert(Q_LOADS + K_LOADS + V_LOADS <= 63, "vmcnt range");
-    {
-        // Q read back from the wave's own staging slot (its own DMA, landed)
+    // Q read back from the wave's own staging slot once its own DMA has
+    // landed. A negative scale is folded into Q so the row max can be taken on
+    // raw scores: Q-nope and Q-rope are negated in registers.
+    auto read_q = [&]() __attribute__((always_inline)) {
         const uint32_t qn = (uint32_t)r32 * (DN * 2) + ((g ^ row_swizzle<DN>(r32)) << 4);
         const uint32_t qr = 32 * DN * 2 + (uint32_t)r32 * 128 + ((g ^ ((r32 >> 1) & 7)) << 4);
 #pragma unroll
@@ -508,25 +505,39 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
             qrreg[ks] = __builtin_bit_cast(vec8, *reinterpret_cast<const uint4 *>(qslot + (qr ^ (ks << 5))));
+        if (p.qk_scale < 0.f) {
+#pragma unroll
+            for (int ks = 0; ks < NKS + 4; ++ks) {
+                vec8 &q = ks < NKS ? qreg[ks] : qrreg[ks - NKS];
+                i32x4 w = __builtin_bit_cast(i32x4, q);
+                w ^= (int)0x80008000;
+                q = __builtin_bit_cast(vec8, w);
+            }
+        }
+    };
+    // Before the first barrier only what interval 0 needs is loaded: the
+    // leading group's Q and tile 0's K (the leading group scores it); tile 0's
+    // raw V goes out too and is waited for at the end of interval 0. The
+    // trailing group waits for its own Q during interval 0. The K of tiles 1
+    // and 2 goes out during interval 0 (into ring stages that hold the leading
+    // group's Q staging until the first barrier).
+    if (grp == 0) {
+        const TileLoad t0 = prep_tile(0, cache_row(0));
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) issue_k(t0, i);
+#pragma unroll
+        for (int j = 0; j < V_LOADS; ++j) issue_v(t0, j);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | V_LOADS);  // Q, Q-rope and K of tile 0 landed
+        read_q();
     }
+    static_assert(Q_LOADS + K_LOADS + V_LOADS <= 63, "vmcnt range");
 
-    // A negative scale is folded into Q so the row max can be taken on raw
-    // scores: Q-nope and Q-rope are negated in registers.
     // natural-log units per unit of the raw dot product, and log2 units. A zero
     // scale is taken as 1e-30, so that a masked -inf times the scale stays
     // -inf: every score it yields is then so small that exp2 rounds it to
     // exactly 1, as 0 would.
     const float c_nat = fmaxf(fabsf(p.qk_scale), 1e-30f);
     const float c2 = c_nat * LOG2E;
-    if (p.qk_scale < 0.f) {
-#pragma unroll
-        for (int ks = 0; ks < NKS + 4; ++ks) {
-            vec8 &q = ks < NKS ? qreg[ks] : qrreg[ks - NKS];
-            i32x4 w = __builtin_bit_cast(i32x4, q);
-            w ^= (int)0x80008000;
-            q = __builtin_bit_cast(vec8, w);
-        }
-    }
 
     // ---- per-wave tile visibility. Under every mask mode the tiles some row
     // of the wave can see, and the tiles every row sees whole, are prefixes of
@@ -846,6 +857,10 @@ void mla_fwd_kernel(const FwdParams p) {
     // wave cannot see (or past the last tile) are dropped. Each group runs its
     // own copy of the schedule with the same barrier sequence.
     block_sync();
+    if (grp != 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // own Q and Q-rope landed
+        read_q();
+    }
 
     // one tile's two intervals; r0 = ring stage of tile j (a runtime value, so
     // that each group's loop holds one copy of its matrix and vector blocks)
@@ -917,7 +932,8 @@ void mla_fwd_kernel(const FwdParams p) {
         }
         block_sync();
     } else if (n_kt > 0) {
-        // tile 0 peeled: its first interval only scores tile 0
+        // tile 0 peeled: in its first interval the leading group scores tile 0
+        // and the trailing group takes its Q into registers
         block_sync();
         // (and V^T of tile 0, whose raw V the barrier before the schedule
         // published; raw V of tile 1 goes out)
@@ -951,20 +967,26 @@ void mla_fwd_kernel(const FwdParams p) {
     // The rows leave through LDS so that each store instruction writes whole
     // 256-byte head slices of 4 rows: straight from the accumulators every
     // instruction would write 16 bytes into each of 32 rows, and such
-    // partial-line writes cost far more than their bytes. Before the ring is
-    // reused, the leading group's K DMA for tiles past the last one (still in
-    // flight: block_sync waits for LDS reads and writes, not for DMA) must
-    // have landed, and the barrier waits for the trailing group's last P.V,
-    // which may still read the ring.
+    // partial-line writes cost far more than their bytes. Each wave stages its
+    // 32 rows (half a V tile of bytes) where no other wave reads or writes any
+    // more, so no barrier is needed and the leading group stores while the
+    // trailing group still runs its last P.V: a leading wave in the raw V
+    // buffers (the last raw V DMA landed and the last transpose ran before the
+    // barrier that ended the loop), a trailing wave in the V^T half of ring
+    // stage n_kt % 3 or (n_kt + 1) % 3 (the last P.V reads stage
+    // (n_kt - 1) % 3; K DMA writes only K halves). The wave's own DMA must have
+    // landed before its LDS is released.
     const float l_tot = sum_with_partner(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    block_sync();
     {
-        // staging row sr = 32 * slot + r32 (DN * 2 bytes), 16-byte chunk c (8
-        // values of d) at c ^ row_swizzle(sr); a wave writes and reads back
-        // only its own 32 rows
-        const int sr = slot * 32 + r32;
+        const int w4 = wave & 3;
+        unsigned char *stg =
+            smem + (grp == 0 ? VRAW_OFFSET + w4 * (V_BYTES / 2)
+                             : ((n_kt + (w4 >> 1)) % STAGES) * STAGE_BYTES + KN_BYTES + KR_BYTES +
+                                   (w4 & 1) * (V_BYTES / 2));
+        // staging row r32 (DN * 2 bytes), 16-byte chunk c (8 values of d) at
+        // c ^ row_swizzle(r32)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -972,8 +994,8 @@ void mla_fwd_kernel(const FwdParams p) {
                 typename T::vec4 v4;
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) v4[jj] = static_cast<typename T::scalar>(o[db][4 * i + jj] * inv);
-                *reinterpret_cast<typename T::vec4 *>(smem + sr * KN_ROW +
-                                                      (((4 * db + i) ^ row_swizzle<DN>(sr)) << 4) + g * 8) = v4;
+                *reinterpret_cast<typename T::vec4 *>(stg + r32 * KN_ROW +
+                                                      (((4 * db + i) ^ row_swizzle<DN>(r32)) << 4) + g * 8) = v4;
             }
         const int rows = max(0, min(32, q_len - row0));
         const int64_t tok = (int64_t)task.q_off + row0;
@@ -985,8 +1007,7 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int k = 0; k < 32 / RPI; ++k) {
             const int r = RPI * k + lane / CPR;  // row of the wave
-            const int srr = slot * 32 + r;
-            const i32x4 v = *reinterpret_cast<const i32x4 *>(smem + srr * KN_ROW + ((ch ^ row_swizzle<DN>(srr)) << 4));
+            const i32x4 v = *reinterpret_cast<const i32x4 *>(stg + r * KN_ROW + ((ch ^ row_swizzle<DN>(r)) << 4));
             mla_raw_buffer_store_b128(v, ro, (uint32_t)r * H * DN * 2 + ch * 16, 0, 0);
         }
     }
