@@ -262,10 +262,12 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // out the DMA of stage kt+3 (into the slot of stage kt-1, which every
     // wave finished reading before the last barrier), so each stage has two
     // iterations to arrive. Within iteration kt: k-step 0's products, with
-    // k-step 1's operand reads in between; k-step 1's products; the DMA of
-    // stage kt+3; a wait until stage kt+1 has landed (vmcnt(10): only the
-    // loads of stages kt+2 and kt+3 may still fly); the barrier that
-    // publishes it; k-step 0's operand reads of slot kt+1. Every iteration
+    // k-step 1's operand reads in between; k-step 1's first five products;
+    // the DMA of stage kt+3; a wait until stage kt+1 has landed (vmcnt(10):
+    // only the loads of stages kt+2 and kt+3 may still fly); the barrier that
+    // publishes it; k-step 1's last three products with k-step 0's operand
+    // reads of slot kt+1 in between, so the matrix core has work while the
+    // first reads after the barrier are in flight. Every iteration
     // issues exactly five loads per thread (stages past K read zeros), so
     // the counts hold on every iteration. The loop is unrolled by the ring
     // depth so every slot is a compile-time constant.
@@ -286,15 +288,25 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
+        for (int n = 0; n < 5; ++n) {
             product(n);
             __builtin_amdgcn_sched_barrier(0);
         }
         issue(kt + 3, (sl + 3) % STAGES);
         __builtin_amdgcn_s_waitcnt(0x0F70 | 10);  // stage kt+1 landed: only stages kt+2 and kt+3 may fly
         block_sync();
+        // k-step 1's last three products need no operand read: the next
+        // slot's k-step 0 operands are read between them (bv[0] and av[0]
+        // are free after product 4)
+        read_op(ns, 0, 4);
+        read_op(ns, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int o = 0; o < 6; ++o) read_op(ns, 0, o);
+        for (int n = 5; n < 8; ++n) {
+            product(n);
+            read_after(ns, 0, n);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
     // K is a multiple of 4 stages: every iteration runs all four steps
     for (int kt = 0; kt < nk; kt += STAGES) {
