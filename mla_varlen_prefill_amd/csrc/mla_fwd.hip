@@ -400,9 +400,13 @@ void mla_fwd_kernel(const FwdParams p) {
     };
     // paged: first cache row of tile kt (-1: none), read from the LDS table
     // ahead of prep_tile so the read's latency stays off the matrix block
+    auto cache_row_ld = [&](int kt) __attribute__((always_inline)) -> int {
+        if (!PAGED) return 0;
+        return kt < n_tiles_seq ? tile_row[kt] : -1;
+    };
     auto cache_row = [&](int kt) __attribute__((always_inline)) -> int {
         if (!PAGED) return 0;
-        return __builtin_amdgcn_readfirstlane(kt < n_tiles_seq ? tile_row[kt] : -1);
+        return __builtin_amdgcn_readfirstlane(cache_row_ld(kt));
     };
     auto prep_tile = [&](int kt, int r) __attribute__((always_inline)) -> TileLoad {
         int64_t rowi;     // first key row of the tile, this head
@@ -875,7 +879,9 @@ void mla_fwd_kernel(const FwdParams p) {
         // interval 2j + 1
         int row_k = 0;  // paged: cache row of the tile whose K goes out next interval
         if (lead) {
-            row_k = cache_row(j + 3);
+            // paged: the table read goes out first and is taken after the
+            // softmax, so its latency does not hold the vector block up
+            const int row_k_ld = cache_row_ld(j + 3);
             // a leading wave past its last visible tile still runs its matrix
             // blocks (they carry the group's loads), with P = 0
             if (wave_active(j)) {
@@ -884,6 +890,7 @@ void mla_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int st4 = 0; st4 < 4; ++st4) pb[st4] = vec8{};
             }
+            if (PAGED) row_k = __builtin_amdgcn_readfirstlane(row_k_ld);
             // K of tile j+1 and everything before it landed; K of tile j+2 may
             // still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
@@ -904,8 +911,9 @@ void mla_fwd_kernel(const FwdParams p) {
         if (lead) {
             mfma_block(soff(r0), soff(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k), nullptr, 0);
         } else {
-            trail_row_v = cache_row(j + 2);
+            const int row_v_ld = cache_row_ld(j + 2);
             if (wave_active(j)) valu_block(j);
+            if (PAGED) trail_row_v = __builtin_amdgcn_readfirstlane(row_v_ld);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile j+1 landed
         }
     };
