@@ -872,12 +872,14 @@ void mla_fwd_kernel(const FwdParams p) {
     // read from the LDS table in the vector interval before, like the leading
     // group's rows, so that the read's latency stays off the matrix block
     int trail_row_v = 0;
+    TileLoad trail_tv{};  // trailing group: raw V load of the next tile, prepared in the vector interval before
     auto tile_pair = [&](int j, int r0, auto LEAD) __attribute__((always_inline)) {
         constexpr bool lead = decltype(LEAD)::value;
         const int rprev = r0 == 0 ? STAGES - 1 : r0 - 1, rnext = r0 == STAGES - 1 ? 0 : r0 + 1;
         block_sync();
         // interval 2j + 1
         int row_k = 0;  // paged: cache row of the tile whose K goes out next interval
+        TileLoad tk{};  // leading group: that K load, prepared here, off the matrix block
         if (lead) {
             // paged: the table read goes out first and is taken after the
             // softmax, so its latency does not hold the vector block up
@@ -891,6 +893,7 @@ void mla_fwd_kernel(const FwdParams p) {
                 for (int st4 = 0; st4 < 4; ++st4) pb[st4] = vec8{};
             }
             if (PAGED) row_k = __builtin_amdgcn_readfirstlane(row_k_ld);
+            tk = prep_tile(j + 3, row_k);
             // K of tile j+1 and everything before it landed; K of tile j+2 may
             // still fly
             __builtin_amdgcn_s_waitcnt(0x0F70 | K_LOADS);
@@ -899,7 +902,7 @@ void mla_fwd_kernel(const FwdParams p) {
             // end of interval 2j) and sends out raw V of tile j+1, with its
             // matrix block or alone
             unsigned char *vr = smem + VRAW_OFFSET + (j & 1) * V_BYTES;
-            const TileLoad tv = prep_tile(j + 1, trail_row_v);
+            const TileLoad tv = trail_tv;
             if (wave_active(j - 1))
                 mfma_block(soff(rprev), soff(r0), yes, yes, iss_v, yes, tv, none, vr, soff(r0));
             else
@@ -909,11 +912,12 @@ void mla_fwd_kernel(const FwdParams p) {
         // interval 2j + 2: the leading group sends out K of tile j+3 during its
         // matrix block
         if (lead) {
-            mfma_block(soff(r0), soff(rnext), yes, yes, iss_k, no, none, prep_tile(j + 3, row_k), nullptr, 0);
+            mfma_block(soff(r0), soff(rnext), yes, yes, iss_k, no, none, tk, nullptr, 0);
         } else {
             const int row_v_ld = cache_row_ld(j + 2);
             if (wave_active(j)) valu_block(j);
             if (PAGED) trail_row_v = __builtin_amdgcn_readfirstlane(row_v_ld);
+            trail_tv = prep_tile(j + 2, trail_row_v);
             __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile j+1 landed
         }
     };
@@ -954,6 +958,7 @@ void mla_fwd_kernel(const FwdParams p) {
         }
         block_sync();
         trail_row_v = cache_row(2);
+        trail_tv = prep_tile(2, trail_row_v);
         if (wave_active(0)) valu_block(0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // raw V of tile 1 landed
         int r = 1;
