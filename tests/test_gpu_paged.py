@@ -27,7 +27,7 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def make_paged(qs, ks, heads, kv_heads, block_size, dtype=torch.bfloat16, seed=0, spare_blocks=3):
+def make_paged(qs, ks, heads, kv_heads, block_size, dtype=torch.bfloat16, seed=0, spare_blocks=3, dim=128):
     """Q/QRope plus ND caches holding each sequence's keys behind a seeded,
     permuted block table; unused blocks (and unused slots) are NaN."""
     rng = np.random.default_rng(seed)
@@ -41,14 +41,14 @@ def make_paged(qs, ks, heads, kv_heads, block_size, dtype=torch.bfloat16, seed=0
         return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
 
     caches = {}
-    for name, dim in (("key_cache", 128), ("krope_cache", 64), ("value_cache", 128)):
-        c = torch.full((nb, block_size, kv_heads, dim), float("nan"), dtype=dtype)
+    for name, d in (("key_cache", dim), ("krope_cache", 64), ("value_cache", dim)):
+        c = torch.full((nb, block_size, kv_heads, d), float("nan"), dtype=dtype)
         for b, n in enumerate(ks):
             for t0 in range(0, int(n), block_size):
                 m = min(block_size, int(n) - t0)
-                c[table[b][t0 // block_size], :m] = randn(m, kv_heads, dim)
+                c[table[b][t0 // block_size], :m] = randn(m, kv_heads, d)
         caches[name] = c
-    q = randn(int(qs.sum()), heads, 128)
+    q = randn(int(qs.sum()), heads, dim)
     qr = randn(int(qs.sum()), heads, 64)
     return dict(q=q, q_rope=qr, block_tables=torch.from_numpy(table), **caches), qs, ks
 
@@ -67,7 +67,7 @@ def run_paged(td, qs, ks, heads, kv_heads, mask_type, mask=None, scale=synth.QK_
 def run_two_step(td, qs, ks, heads, kv_heads, mask_type, mask=None, scale=synth.QK_SCALE):
     n = int(ks.sum())
     ctx = torch.from_numpy(ks).to(DEV)
-    k = torch.empty((n, kv_heads, 128), dtype=td["q"].dtype, device=DEV)
+    k = torch.empty((n, kv_heads, td["q"].shape[-1]), dtype=td["q"].dtype, device=DEV)
     v = torch.empty_like(k)
     kr = torch.empty((n, kv_heads, 64), dtype=td["q"].dtype, device=DEV)
     mla.paged_cache_load(td["key_cache"], td["value_cache"], td["block_tables"], ctx, k, v)
@@ -102,6 +102,17 @@ CASES = [
     ("spec-bs256", [1, 200], [1000, 200], 4, 4, 256, torch.bfloat16, synth.MASK_SPEC),
 ]
 
+# head dim 64 (embeddimV), and the page's default qkScale of 1.0 (scores of
+# standard deviation near 14, so the running max moves often)
+CASES_MORE = [
+    # name, q_seqlen, kv_seqlen, heads, kv_heads, block_size, dtype, mask_type, head dim, scale
+    ("causal-d64-bs64", [1, 63, 130, 300], [1, 63, 130, 300], 2, 2, 64, torch.bfloat16, synth.MASK_CAUSAL, 64,
+     synth.QK_SCALE),
+    ("gqa-d64-fp16-bs128", [100, 33], [700, 260], 8, 2, 128, torch.float16, synth.MASK_CAUSAL, 64, synth.QK_SCALE),
+    ("causal-scale1-bs64", [70, 300], [70, 300], 2, 2, 64, torch.bfloat16, synth.MASK_CAUSAL, 128, 1.0),
+    ("gqa-scale1-fp16-bs128", [100, 33], [700, 260], 8, 2, 128, torch.float16, synth.MASK_UNDEFINED, 128, 1.0),
+]
+
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_paged_matches_oracle_and_two_step(case):
@@ -112,6 +123,17 @@ def test_paged_matches_oracle_and_two_step(case):
     out = run_paged(td, qs, ks, h, hk, mt)
     assert_close(out, oracle_paged(t, qs, ks, h, hk, mt), name)
     assert torch.equal(out, run_two_step(td, qs, ks, h, hk, mt)), f"{name}: fused differs from gather + prefill"
+
+
+@pytest.mark.parametrize("case", CASES_MORE, ids=[c[0] for c in CASES_MORE])
+def test_paged_head_dim_and_scale(case):
+    name, qs, ks, h, hk, bs, dtype, mt, dim, scale = case
+    _say(f"[gpu] paged {name}")
+    t, qs, ks = make_paged(qs, ks, h, hk, bs, dtype, seed=len(name) + 50, dim=dim)
+    td = to_dev(t)
+    out = run_paged(td, qs, ks, h, hk, mt, scale=scale)
+    assert_close(out, oracle_paged(t, qs, ks, h, hk, mt, scale=scale), name)
+    assert torch.equal(out, run_two_step(td, qs, ks, h, hk, mt, scale=scale)), f"{name}: fused differs from gather + prefill"
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
