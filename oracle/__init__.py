@@ -301,6 +301,19 @@ def rope_interleaved(x, cos, sin):
     return x * cos + partner * sin
 
 
+def prolog_kv(token_x, wkv, rope_cos, rope_sin, gamma_ckv, eps=1e-6):
+    """The key-value half of the MLA prolog ("MlaProlog" page, formula
+    section), the same in the plain and the quantised operator:
+        kv = RmsNorm(x . wkv) * gamma_ckv, kv[..., -rope_dim:] = ROPE(kv[..., -rope_dim:])
+    [t, head_dim], float64."""
+    x = np.asarray(token_x, dtype=np.float64)
+    head_dim = wkv.shape[1]
+    rd = rope_cos.shape[1]
+    kv = rms_norm(x @ np.asarray(wkv, dtype=np.float64), gamma_ckv, eps)
+    kv[:, head_dim - rd:] = rope_interleaved(kv[:, head_dim - rd:], rope_cos, rope_sin)
+    return kv
+
+
 def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, num_heads, eps=1e-6):
     """The MLA prolog, non-quantised ("MlaProlog" page, formula section; shapes
     from its parameter and return lists):
@@ -319,6 +332,48 @@ def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv
     q = rms_norm((cq @ np.asarray(wq_b, dtype=np.float64)).reshape(t, num_heads, head_dim), None, eps)
     q[..., head_dim - rd:] = rope_interleaved(q[..., head_dim - rd:], np.asarray(rope_cos)[:, None, :],
                                               np.asarray(rope_sin)[:, None, :])
-    kv = rms_norm(x @ np.asarray(wkv, dtype=np.float64), gamma_ckv, eps)
-    kv[:, head_dim - rd:] = rope_interleaved(kv[:, head_dim - rd:], rope_cos, rope_sin)
+    kv = prolog_kv(x, wkv, rope_cos, rope_sin, gamma_ckv, eps)
     return q, kv, cq
+
+
+def quantize_per_token(c):
+    """Per-token symmetric int8 quantisation of c^Q ("MlaProlog" page,
+    mla_prolog_quant return list: qr_out int8 [t, q_lora_rank] and
+    qr_scale_out float32 [t, 1]). The page names these outputs and their types
+    only. Reading: a row's scale is its largest magnitude over 127, so that
+    c ~ code * scale, and each code is c / scale rounded to the nearest integer
+    with ties to even, which keeps it in [-127, 127]; a row of zeros has scale
+    0 and codes 0. Returns (codes as int64 [t, r], scale as float64 [t])."""
+    c = np.asarray(c, dtype=np.float64)
+    scale = np.max(np.abs(c), axis=-1) / 127.0
+    safe = np.where(scale > 0, scale, 1.0)
+    codes = np.where(scale[:, None] > 0, np.rint(c / safe[:, None]), 0.0)
+    return codes.astype(np.int64), scale
+
+
+def mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, num_heads,
+                     eps=1e-6):
+    """The quantised MLA prolog ("MlaProlog" page, mla_prolog_quant: wq_b is
+    int8 [q_lora_rank, num_heads * head_dim] with the per-channel
+    dequantisation scale wq_b_scale [num_heads * head_dim, 1]; c^Q leaves as
+    int8 codes plus a per-token scale):
+        c^Q      = RmsNorm(x . wq_a) * gamma_cq
+        (qr, s)  = quantize_per_token(c^Q)                       [t, q_lora_rank], [t]
+        q        = RmsNorm((qr . wq_b) * s[t] * wq_b_scale[n]), per head (weight 1)
+        q[..., -rope_dim:] = ROPE(q[..., -rope_dim:])
+        kv       as in mla_prolog
+    The product qr . wq_b is taken exactly, in integers. Returns
+    (q, kv, qr, s), q and kv in float64."""
+    x = np.asarray(token_x, dtype=np.float64)
+    t = x.shape[0]
+    head_dim = wkv.shape[1]
+    rd = rope_cos.shape[1]
+    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), gamma_cq, eps)
+    qr, s = quantize_per_token(cq)
+    acc = qr @ np.asarray(wq_b, dtype=np.int64)
+    y = acc.astype(np.float64) * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)
+    q = rms_norm(y.reshape(t, num_heads, head_dim), None, eps)
+    q[..., head_dim - rd:] = rope_interleaved(q[..., head_dim - rd:], np.asarray(rope_cos)[:, None, :],
+                                              np.asarray(rope_sin)[:, None, :])
+    kv = prolog_kv(x, wkv, rope_cos, rope_sin, gamma_ckv, eps)
+    return q, kv, qr, s

@@ -105,3 +105,35 @@ def mla_prolog(x, wq_a, wq_b, wkv, cos, sin, gamma_cq, gamma_ckv, num_heads, eps
         row = _rms(kvf[i], gamma_ckv, eps)
         kv[i] = row[:hd - rd] + _rope_complex(row[hd - rd:], cos[i], sin[i])
     return q, kv, np.array(cq)
+
+
+# Quantised prolog by the same route: c^Q as above, each code by Python's
+# round() (ties to even) of c / (max|c| / 127), the product as a sum of Python
+# integers, then the dequantisation and the per-head RmsNorm and rope.
+def mla_prolog_quant(x, wq_a, wq_b, wkv, cos, sin, gamma_cq, gamma_ckv, wq_b_scale, num_heads, eps):
+    x, wq_a, wkv = (np.asarray(a).tolist() for a in (x, wq_a, wkv))
+    wq_b = [[int(v) for v in row] for row in np.asarray(wq_b)]
+    wsc = [float(v) for v in np.asarray(wq_b_scale).reshape(-1)]
+    cos, sin = np.asarray(cos).tolist(), np.asarray(sin).tolist()
+    gamma_cq, gamma_ckv = np.asarray(gamma_cq).tolist(), np.asarray(gamma_ckv).tolist()
+    t, hd, rd = len(x), len(wkv[0]), len(cos[0])
+    cq = [_rms(row, gamma_cq, eps) for row in _matmul(x, wq_a)]
+    codes, scales = [], []
+    for row in cq:
+        s = max(abs(v) for v in row) / 127.0
+        scales.append(s)
+        codes.append([round(v / s) if s > 0 else 0 for v in row])
+    n = len(wq_b[0])
+    q = np.zeros((t, num_heads, hd))
+    for i in range(t):
+        acc = [sum(codes[i][k] * wq_b[k][j] for k in range(len(wq_b))) for j in range(n)]
+        y = [acc[j] * scales[i] * wsc[j] for j in range(n)]
+        for h in range(num_heads):
+            head = _rms(y[h * hd:(h + 1) * hd], None, eps)
+            q[i, h] = head[:hd - rd] + _rope_complex(head[hd - rd:], cos[i], sin[i])
+    kvf = _matmul(x, wkv)
+    kv = np.zeros((t, hd))
+    for i in range(t):
+        row = _rms(kvf[i], gamma_ckv, eps)
+        kv[i] = row[:hd - rd] + _rope_complex(row[hd - rd:], cos[i], sin[i])
+    return q, kv, np.array(codes, dtype=np.int64), np.array(scales)

@@ -12,6 +12,13 @@ rope on the last rope_dim values of q and kv. The pins:
   * the prolog: a pure-Python brute force (tests/brute.py) on tiny sizes,
     unit norms of every rope'd head, independence of q from the scale of x
     and of gamma_cq (both RmsNorms remove it), no rotation at angle 0.
+The quantised prolog (``oracle.quantize_per_token``,
+``oracle.mla_prolog_quant``; "MlaProlog" page, mla_prolog_quant) is pinned by
+a row quantised by hand (ties to even, a zero row), the brute force by
+another route (Python's round and integer sums), the code range, q's
+independence of the scale of x and of a head's dequantisation scales, and
+the non-quantised prolog on the dequantised inputs within the bound that
+rounding the codes allows.
 The mutants at the end plant plausible mistakes in a private copy of the
 oracle module (rope on split halves, a norm over all heads, a dropped gamma,
 a sign flip, rope on the leading values, the odd element of a pair reading
@@ -137,6 +144,60 @@ def prolog_pins(mod):
     return failed
 
 
+def quant_problem(seed=1, t=4, r=8, heads=2, hd=8):
+    p = tiny_problem(t=t, r=r, heads=heads, hd=hd, seed=seed)
+    rng = np.random.default_rng(seed + 10)
+    p["wq_b8"] = rng.integers(-127, 128, size=(r, heads * hd))
+    p["wq_b_scale"] = rng.uniform(0.5, 2.0, size=(heads * hd, 1)) / (127 * math.sqrt(r))
+    return p
+
+
+def run_quant(mod, p, eps=1e-6, **over):
+    p = dict(p, **over)
+    return mod.mla_prolog_quant(p["x"], p["wq_a"], p["wq_b8"], p["wkv"], p["cos"], p["sin"], p["gamma_cq"],
+                                p["gamma_ckv"], p["wq_b_scale"], p["heads"], eps)
+
+
+def quant_pins(mod):
+    failed = []
+    # a row worked by hand: max |c| = 254 gives scale 2; -63.5, 2.5 and 1.5
+    # round to the even neighbours -64, 2 and 2; a zero row has scale 0
+    codes, scale = mod.quantize_per_token(np.array([[254.0, -127.0, 5.0, 0.0, 3.0], [0.0] * 5]))
+    if not (np.array_equal(codes, [[127, -64, 2, 0, 2], [0] * 5]) and np.array_equal(scale, [2.0, 0.0])):
+        failed.append("hand quantisation")
+    p = quant_problem()
+    q, kv, qr, sc = run_quant(mod, p)
+    bq, bkv, bqr, bsc = brute.mla_prolog_quant(p["x"], p["wq_a"], p["wq_b8"], p["wkv"], p["cos"], p["sin"],
+                                               p["gamma_cq"], p["gamma_ckv"], p["wq_b_scale"], p["heads"], 1e-6)
+    if not (np.array_equal(qr, bqr) and np.allclose(sc, bsc, rtol=1e-14) and np.allclose(q, bq, atol=1e-12)
+            and np.allclose(kv, bkv, atol=1e-12)):
+        failed.append("quant brute force")
+    if not (np.abs(qr).max() == 127 and (np.abs(qr).max(axis=1) == 127).all()):
+        failed.append("code range")
+    # q does not depend on the scale of x, nor on a common factor of one
+    # head's dequantisation scales (its RmsNorm removes it; eps = 0)
+    w2 = p["wq_b_scale"].copy()
+    w2[:8] *= 3.0
+    q1, _, qr1, _ = run_quant(mod, p, eps=0.0, x=2.0 * p["x"], wq_b_scale=w2)
+    q2, _, qr2, _ = run_quant(mod, p, eps=0.0)
+    if not (np.array_equal(qr1, qr2) and np.allclose(q1, q2, rtol=1e-10, atol=1e-12)):
+        failed.append("quant scale invariance")
+    # against the non-quantised prolog on dequantised weights: the codes
+    # differ from c^Q / s by at most 1/2, so each product entry moves by at
+    # most s * 1/2 * sum_k |wq_b[k, n]| * wq_b_scale[n]
+    wdq = p["wq_b8"] * p["wq_b_scale"].reshape(1, -1)
+    rq, _, cq = run(mod, p, eps=0.0, wq_b=wdq)
+    yq = (qr @ p["wq_b8"]) * sc[:, None] * p["wq_b_scale"].reshape(1, -1)
+    yr = cq @ wdq
+    bound = 0.5 * sc[:, None] * (np.abs(p["wq_b8"]).sum(axis=0) * p["wq_b_scale"].reshape(-1))[None, :]
+    if not (np.abs(yq - yr) <= bound * (1 + 1e-9)).all():
+        failed.append("dequantised product bound")
+    q0, _, _, _ = run_quant(mod, p, eps=0.0)
+    if not np.allclose(q0, rq, atol=0.15):
+        failed.append("close to the non-quantised prolog")
+    return failed
+
+
 def test_rms_norm_pins():
     assert rms_pins(oracle) == []
 
@@ -147,6 +208,10 @@ def test_rope_pins():
 
 def test_prolog_pins():
     assert prolog_pins(oracle) == []
+
+
+def test_quant_prolog_pins():
+    assert quant_pins(oracle) == []
 
 
 def test_prolog_page_sizes_shapes():
@@ -180,6 +245,18 @@ MUTANTS = {
                                "kv[:, :rd] = rope_interleaved(kv[:, :rd], rope_cos, rope_sin)"),
 }
 
+QUANT_MUTANTS = {
+    "ties away from zero": ("np.rint(c / safe[:, None])", "np.sign(c) * np.floor(np.abs(c / safe[:, None]) + 0.5)"),
+    "scale over 128": ("scale = np.max(np.abs(c), axis=-1) / 127.0", "scale = np.max(np.abs(c), axis=-1) / 128.0"),
+    "codes truncated": ("np.rint(c / safe[:, None])", "np.trunc(c / safe[:, None])"),
+    "channel scale dropped": ("acc.astype(np.float64) * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)",
+                              "acc.astype(np.float64) * s[:, None]"),
+    "quantised before gamma": ("    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), gamma_cq, eps)\n    qr, s = quantize_per_token(cq)",
+                               "    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), None, eps)\n    qr, s = quantize_per_token(cq)"),
+    "quant q norm over all heads": ("    q = rms_norm(y.reshape(t, num_heads, head_dim), None, eps)",
+                                    "    q = rms_norm(y, None, eps).reshape(t, num_heads, head_dim)"),
+}
+
 
 def _mutant(tmp_path, old, new):
     src = open(os.path.join(ORACLE_DIR, "__init__.py")).read()
@@ -192,6 +269,16 @@ def _mutant(tmp_path, old, new):
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     return mod
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTANTS))
+def test_quant_prolog_mutant_is_caught(tmp_path, name):
+    mod = _mutant(tmp_path, *QUANT_MUTANTS[name])
+    try:
+        failed = quant_pins(mod)
+    except (ValueError, IndexError) as e:
+        failed = [f"raised {type(e).__name__}"]
+    assert failed, f"mutant {name!r} passed every pin"
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
