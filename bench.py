@@ -33,6 +33,7 @@ from mla_varlen_prefill_amd import synth  # noqa: E402
 METRIC = "MLA prefill attention TFLOP/s at 1 MI355X + % of bf16 MFMA peak"
 PEAK_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 MFMA
 FLOP_PER_PAIR = 2 * (128 + 64) + 2 * 128
 PMC_FILE = os.path.join(ROOT, "profiles", "mla_fwd_single_pmc.json")
 COPY_BYTES = 1 << 30  # plain copy of known size, for scaling the HBM counters
@@ -596,6 +597,38 @@ def bench_prolog(steps):
             "ms_per_step": ms, "value": tf, "unit": "TFLOP/s", "peak": PEAK_TFLOPS, "frac": tf / PEAK_TFLOPS}
 
 
+def bench_prolog_quant(steps):
+    """The quantised MLA prolog (NEXT-4, mla_prolog_quant) on the same
+    16384-token workload: x . [wq_a | wkv] in bf16 and qr . wq_b in int8
+    (int8 weights with per-column scales, synth.prolog_quant_inputs). The
+    roofline is per precision: the least time is the bf16 FLOPs at the bf16
+    peak plus the int8 operations at the int8 peak, and frac is that time over
+    the measured one."""
+    t = synth.PROLOG_TOKENS
+    d = synth.prolog_quant_inputs(t, seed=1, device="cuda")
+    hd, r, h = d["wkv"].shape[1], d["wq_a"].shape[1], d["wq_a"].shape[0]
+    heads = d["wq_b"].shape[1] // hd
+    q = torch.empty((t, heads, hd), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((t, hd), dtype=torch.bfloat16, device="cuda")
+    qr = torch.empty((t, r), dtype=torch.int8, device="cuda")
+    qs = torch.empty((t, 1), dtype=torch.float32, device="cuda")
+    eps = synth.PROLOG_EPS
+    args = (d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"], d["gamma_cq"],
+            d["gamma_ckv"], d["wq_b_scale"], eps, q, kv, qr, qs)
+    ws = torch.empty(max(mla.mla_prolog_quant_get_workspace_size(*args), 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = _time(lambda: mla.mla_prolog_quant(*args, ws, stream), steps, stream)
+    bf16_flops = 2 * t * h * (r + hd)
+    int8_ops = 2 * t * r * heads * hd
+    least_ms = (bf16_flops / (PEAK_TFLOPS * 1e12) + int8_ops / (PEAK_INT8_TOPS * 1e12)) * 1e3
+    del d, q, kv, qr, qs, ws
+    torch.cuda.empty_cache()
+    return {"workload": "prolog_quant", "tokens": t, "sizes": dict(synth.PROLOG_SIZES), "bf16_flop_per_step":
+            bf16_flops, "int8_op_per_step": int8_ops, "ms_per_step": ms,
+            "value": (bf16_flops + int8_ops) / (ms * 1e-3) / 1e12, "unit": "TOP/s (bf16 FLOP + int8 OP)",
+            "least_ms_at_peaks": least_ms, "frac": least_ms / ms}
+
+
 def _progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -616,6 +649,8 @@ def main():
     ap.add_argument("--summarize-util", nargs="+", metavar="ARG",
                     help="WORKLOAD OUT_JSON DIR [DIR ...]: medians and derived utilisation of mla_fwd_kernel "
                          "from rocprofv3 --pmc runs of the UTIL_PASSES counters, then exit")
+    ap.add_argument("--prolog-quant-only", action="store_true",
+                    help="time only the quantised MLA prolog leg and print its JSON object")
     ap.add_argument("--prolog-only", action="store_true",
                     help="time only the MLA prolog leg and print its JSON object (for profiling it)")
     args = ap.parse_args()
@@ -635,6 +670,9 @@ def main():
 
     if args.prolog_only:
         print(json.dumps(bench_prolog(args.steps)), flush=True)
+        return
+    if args.prolog_quant_only:
+        print(json.dumps(bench_prolog_quant(args.steps)), flush=True)
         return
     if args.calibrate_copy:
         calibration_copy()
@@ -676,6 +714,7 @@ def main():
         by_config.update(extra_cpu)
         _progress("extras done")
         line["prolog"] = bench_prolog(max(3, min(args.steps, 10)))
+        line["prolog_quant"] = bench_prolog_quant(max(3, min(args.steps, 10)))
         _progress("prolog done")
         if cpu:
             line["cpu_baseline_by_config"] = by_config

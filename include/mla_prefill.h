@@ -51,12 +51,14 @@ extern "C" {
 #endif
 
 /* Element types. The pages allow float16/bf16 for attention data and
- * float16/bf16/int8 for paged caches; int32 is used for lengths and tables. */
+ * float16/bf16/int8 for paged caches; int32 is used for lengths and tables,
+ * float32 for the quantised prolog's scales. */
 enum mla_dtype {
     MLA_FP16 = 1,
     MLA_BF16 = 2,
     MLA_INT8 = 3,
-    MLA_INT32 = 4
+    MLA_INT32 = 4,
+    MLA_FP32 = 5
 };
 
 /* maskType. The "MLA Prefill" page names the modes (Members table, rows
@@ -330,6 +332,54 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
                const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
                const mla_tensor *kv_out, const mla_tensor *qr_out, void *workspace, uint64_t workspace_size,
                void *stream);
+
+/*
+ * mla_prolog_quant_get_workspace_size / mla_prolog_quant -- the quantised
+ * "MlaProlog" operator (cann-recipes-infer operator notes: the prototype
+ * mla_prolog_quant, formula section, parameter and return lists,
+ * constraints). As mla_prolog, except that wq_b is int8 with a per-column
+ * dequantisation scale and c^Q leaves as int8 codes with a per-token scale:
+ *     c^Q     = RmsNorm(x . wq_a) * gamma_cq                  (fp32)
+ *     s[t]    = max |c^Q[t, :]| / 127
+ *     qr[t,k] = c^Q[t,k] / s[t] rounded to nearest, ties to even (|qr| <= 127)
+ *     q       = RmsNorm((qr . wq_b)[t, n] * s[t] * wq_b_scale[n]), per head, weight 1
+ *     kv      = RmsNorm(x . wkv) * gamma_ckv
+ * then the interleaved rope on the last rope_dim values of every q head and
+ * of kv, as in mla_prolog. The page names qr_out and qr_scale_out and their
+ * types but not the rounding rule or the scale's form: the symmetric
+ * max / 127 scale with c^Q ~ qr_out * qr_scale_out and ties to even is the
+ * reading taken; a row of zeros gets scale 0 and codes 0. qr . wq_b is exact
+ * (int32 accumulation).
+ *
+ *   token_x, wq_a, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps,
+ *   q_out, kv_out     as for mla_prolog
+ *   wq_b          device int8 [q_lora_rank, num_heads * head_dim]
+ *   wq_b_scale    device fp32 [num_heads * head_dim, 1] or [num_heads * head_dim]
+ *   qr_out        device int8 [t, q_lora_rank]: the codes of c^Q
+ *   qr_scale_out  device fp32 [t, 1] or [t]: the per-token scale s
+ *   workspace_size  out: bytes of device workspace mla_prolog_quant needs:
+ *               t * q_lora_rank * 4 for x . wq_a, then the rearranged copies
+ *               of wq_a and wkv (2 bytes per weight) and of wq_b (1 byte per
+ *               weight), each rounded up to 256 bytes; 0 when t = 0.
+ * Supported: as mla_prolog, with q_lora_rank one of 512, 1024, 1536, 2048
+ * (the page fixes 1024). mla_prolog_quant enqueues six kernels on stream
+ * (the rearrangements of wq_a and wkv, x . [wq_a | wkv] with the kv
+ * epilogue, the c^Q norm and quantisation, the rearrangement of wq_b, and
+ * qr . wq_b with the dequantisation, per-head norm and rope epilogue); the
+ * workspace must stay valid until they have run. Errors as for mla_prefill.
+ */
+int mla_prolog_quant_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a,
+                                        const mla_tensor *wq_b, const mla_tensor *wkv,
+                                        const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                                        const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv,
+                                        const mla_tensor *wq_b_scale, float eps, const mla_tensor *q_out,
+                                        const mla_tensor *kv_out, const mla_tensor *qr_out,
+                                        const mla_tensor *qr_scale_out, uint64_t *workspace_size);
+int mla_prolog_quant(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                     const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                     const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale,
+                     float eps, const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
+                     const mla_tensor *qr_scale_out, void *workspace, uint64_t workspace_size, void *stream);
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char *mla_last_error(void);

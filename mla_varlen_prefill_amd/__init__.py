@@ -25,6 +25,7 @@ __all__ = [
     "mla_last_error", "mla_prefill_plan_host", "prefill", "library_path",
     "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "prefill_paged",
     "mla_prolog_get_workspace_size", "mla_prolog", "prolog",
+    "mla_prolog_quant_get_workspace_size", "mla_prolog_quant", "prolog_quant",
 ]
 
 # MLA_PREFILL_LIBRARY selects another build of the same library (the host
@@ -41,8 +42,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -4: "MLA_ERR_VALUE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_WORKSPACE",
           -7: "MLA_ERR_RUNTIME"}
 
-_DTYPE = {torch.float16: 1, torch.bfloat16: 2, torch.int8: 3, torch.int32: 4,
-          np.dtype(np.int32): 4, np.dtype(np.int8): 3, np.dtype(np.float16): 1}
+_DTYPE = {torch.float16: 1, torch.bfloat16: 2, torch.int8: 3, torch.int32: 4, torch.float32: 5,
+          np.dtype(np.int32): 4, np.dtype(np.int8): 3, np.dtype(np.float16): 1, np.dtype(np.float32): 5}
 
 
 class MlaError(RuntimeError):
@@ -94,6 +95,10 @@ def _load():
                                                              ctypes.POINTER(ctypes.c_uint64)]
     lib.mla_prolog.argtypes = [T] * 8 + [ctypes.c_float, T, T, T, ctypes.c_void_p, ctypes.c_uint64,
                                          ctypes.c_void_p]
+    lib.mla_prolog_quant_get_workspace_size.argtypes = [T] * 9 + [ctypes.c_float, T, T, T, T,
+                                                                   ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prolog_quant.argtypes = [T] * 9 + [ctypes.c_float, T, T, T, T, ctypes.c_void_p, ctypes.c_uint64,
+                                               ctypes.c_void_p]
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -103,7 +108,7 @@ def _load():
     for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "mla_prefill_no_alloc", "paged_cache_load",
                "mla_prefill_plan_host",
                "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "mla_prolog_get_workspace_size",
-               "mla_prolog"):
+               "mla_prolog", "mla_prolog_quant_get_workspace_size", "mla_prolog_quant"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -399,3 +404,62 @@ def prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, ep
     if stream is not None and isinstance(stream, torch.cuda.Stream):
         workspace.record_stream(stream)
     return q, kv, cq
+
+
+def _prolog_quant_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q_out,
+                       kv_out, qr_out, qr_scale_out, keep):
+    return ([_desc(x, keep) for x in (token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale)]
+            + [ctypes.c_float(eps)] + [_desc(x, keep) for x in (q_out, kv_out, qr_out, qr_scale_out)])
+
+
+def mla_prolog_quant_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv,
+                                        wq_b_scale, eps, q_out, kv_out, qr_out, qr_scale_out) -> int:
+    """Bytes of device workspace ``mla_prolog_quant`` needs for these shapes."""
+    lib = _load()
+    keep = []
+    size = ctypes.c_uint64(0)
+    _check("mla_prolog_quant_get_workspace_size", lib.mla_prolog_quant_get_workspace_size(
+        *_prolog_quant_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps,
+                            q_out, kv_out, qr_out, qr_scale_out, keep), ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q_out,
+                     kv_out, qr_out, qr_scale_out, workspace, stream=None) -> None:
+    """Enqueue the quantised MLA prolog: int8 wq_b with per-column scales;
+    q, kv, and c^Q as int8 codes with a per-token scale."""
+    lib = _load()
+    _on_device([("token_x", token_x), ("wq_a", wq_a), ("wq_b", wq_b), ("wkv", wkv), ("rope_cos", rope_cos),
+                ("rope_sin", rope_sin), ("gamma_cq", gamma_cq), ("gamma_ckv", gamma_ckv),
+                ("wq_b_scale", wq_b_scale), ("q_out", q_out), ("kv_out", kv_out), ("qr_out", qr_out),
+                ("qr_scale_out", qr_scale_out), ("workspace", workspace)], stream)
+    keep = []
+    ws_ptr = workspace.data_ptr() if workspace is not None and workspace.numel() else None
+    ws_size = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_prolog_quant", lib.mla_prolog_quant(
+        *_prolog_quant_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps,
+                            q_out, kv_out, qr_out, qr_scale_out, keep),
+        ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size), _stream_ptr(stream)))
+
+
+def prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps=1e-6,
+                 stream=None):
+    """Allocate outputs and workspace with torch and run the quantised prolog.
+    Returns (q [t, num_heads, head_dim] bf16, kv [t, head_dim] bf16,
+    c^Q codes [t, q_lora_rank] int8, c^Q scales [t, 1] float32)."""
+    t, hd, r = token_x.shape[0], wkv.shape[1], wq_a.shape[1]
+    heads = wq_b.shape[1] // hd
+    dev = token_x.device
+    q = torch.empty((t, heads, hd), dtype=torch.bfloat16, device=dev)
+    kv = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
+    qr = torch.empty((t, r), dtype=torch.int8, device=dev)
+    qs = torch.empty((t, 1), dtype=torch.float32, device=dev)
+    ws = mla_prolog_quant_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv,
+                                             wq_b_scale, eps, q, kv, qr, qs)
+    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q, kv, qr,
+                     qs, workspace, stream)
+    if stream is not None and isinstance(stream, torch.cuda.Stream):
+        workspace.record_stream(stream)
+    return q, kv, qr, qs
+

@@ -74,7 +74,8 @@ size_t elem_size(int dtype) {
         case MLA_FP16:
         case MLA_BF16: return 2;
         case MLA_INT8: return 1;
-        case MLA_INT32: return 4;
+        case MLA_INT32:
+        case MLA_FP32: return 4;
         default: return 0;
     }
 }
@@ -653,16 +654,37 @@ int check_bf16(const mla_tensor *x, const char *name, int ndim) {
     return MLA_OK;
 }
 
+int check_dtype(const mla_tensor *x, const char *name, int dtype, const char *dname, int ndim) {
+    int rc = check_tensor(x, name, true);
+    if (rc) return rc;
+    if (x->dtype != dtype) return fail(MLA_ERR_DTYPE, "%s must be %s", name, dname);
+    if (x->ndim != ndim) return fail(MLA_ERR_SHAPE, "%s: expected %d dimensions, got %d", name, ndim, x->ndim);
+    return MLA_OK;
+}
+
+// [n, 1] or [n] fp32 (the quantised prolog's scales)
+int check_scale_vector(const mla_tensor *x, const char *name, int64_t n) {
+    int rc = check_tensor(x, name, true);
+    if (rc) return rc;
+    if (x->dtype != MLA_FP32) return fail(MLA_ERR_DTYPE, "%s must be float32", name);
+    const bool ok_shape = (x->ndim == 1 && x->shape[0] == n) || (x->ndim == 2 && x->shape[0] == n && x->shape[1] == 1);
+    if (!ok_shape) return fail(MLA_ERR_SHAPE, "%s: expected [%lld, 1] or [%lld]", name, (long long)n, (long long)n);
+    return MLA_OK;
+}
+
+// quant: wq_b and qr_out are int8 (mla_prolog_quant); the scale tensors are
+// checked by the caller
 int validate_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
                     const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
                     const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
-                    const mla_tensor *kv_out, const mla_tensor *qr_out, PrologProblem *pp) {
+                    const mla_tensor *kv_out, const mla_tensor *qr_out, PrologProblem *pp, bool quant = false) {
     int rc;
     if ((rc = check_bf16(token_x, "token_x", 2)) || (rc = check_bf16(wq_a, "wq_a", 2)) ||
-        (rc = check_bf16(wq_b, "wq_b", 2)) || (rc = check_bf16(wkv, "wkv", 2)) ||
-        (rc = check_bf16(rope_cos, "rope_cos", 2)) || (rc = check_bf16(rope_sin, "rope_sin", 2)) ||
-        (rc = check_bf16(gamma_cq, "gamma_cq", 1)) || (rc = check_bf16(gamma_ckv, "gamma_ckv", 1)) ||
-        (rc = check_bf16(kv_out, "kv_out", 2)) || (rc = check_bf16(qr_out, "qr_out", 2)))
+        (rc = quant ? check_dtype(wq_b, "wq_b", MLA_INT8, "int8", 2) : check_bf16(wq_b, "wq_b", 2)) ||
+        (rc = check_bf16(wkv, "wkv", 2)) || (rc = check_bf16(rope_cos, "rope_cos", 2)) ||
+        (rc = check_bf16(rope_sin, "rope_sin", 2)) || (rc = check_bf16(gamma_cq, "gamma_cq", 1)) ||
+        (rc = check_bf16(gamma_ckv, "gamma_ckv", 1)) || (rc = check_bf16(kv_out, "kv_out", 2)) ||
+        (rc = quant ? check_dtype(qr_out, "qr_out", MLA_INT8, "int8", 2) : check_bf16(qr_out, "qr_out", 2)))
         return rc;
     if ((rc = check_tensor(q_out, "q_out", true))) return rc;
     if (q_out->dtype != MLA_BF16) return fail(MLA_ERR_DTYPE, "q_out must be bf16");
@@ -698,6 +720,9 @@ int validate_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla
     if (r <= 0 || r % mla::PROLOG_BN != 0)
         return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: a positive multiple of %d is required", (long long)r,
                     mla::PROLOG_BN);
+    if (quant && r > mla::PROLOG_QUANT_MAX_COLS)
+        return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: at most %d in the quantised prolog", (long long)r,
+                    mla::PROLOG_QUANT_MAX_COLS);
     // buffer resources address at most 4 GB from a tile's start; weights and
     // a 128-row tile of any operand stay far below that in every supported case
     if (r * heads * hd * 2 >= (int64_t)1 << 31 || h * r * 2 >= (int64_t)1 << 31 ||
@@ -722,9 +747,39 @@ uint64_t prolog_pack_kv_bytes(const PrologProblem &pp) {
 uint64_t prolog_pack_b_bytes(const PrologProblem &pp) {
     return align256((uint64_t)mla::prolog_packed_bytes((int32_t)pp.heads, (int32_t)pp.r));
 }
-uint64_t prolog_workspace_bytes(const PrologProblem &pp) {
+uint64_t prolog_pack_b_i8_bytes(const PrologProblem &pp) {
+    return align256((uint64_t)mla::prolog_packed_bytes((int32_t)pp.heads, (int32_t)pp.r, true));
+}
+uint64_t prolog_workspace_bytes(const PrologProblem &pp, bool quant = false) {
     if (pp.t == 0) return 0;  // nothing to compute
-    return prolog_yq_bytes(pp) + prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp) + prolog_pack_b_bytes(pp);
+    return prolog_yq_bytes(pp) + prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp) +
+           (quant ? prolog_pack_b_i8_bytes(pp) : prolog_pack_b_bytes(pp));
+}
+
+// The first product, x . [wq_a | wkv], shared by both prolog operators: the
+// wq_a tiles store fp32 rows for the c^Q norm, the wkv tile is the kv row
+// (norm * gamma_ckv, rope).
+int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, const mla_tensor *wq_a,
+                         const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                         const mla_tensor *gamma_ckv, float eps, const mla_tensor *kv_out, float *y_q,
+                         unsigned char *pack_a, unsigned char *pack_kv, hipStream_t s) {
+    mla::PrologGemmParams g1{};
+    g1.a = token_x->data;
+    g1.lda = pp.h;
+    g1.m = (int32_t)pp.t;
+    g1.k = (int32_t)pp.h;
+    g1.seg[0] = {wq_a->data, pp.r, pack_a, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, y_q, pp.r,
+                 nullptr};
+    g1.seg[1] = {wkv->data, mla::PROLOG_BN, pack_kv, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN,
+                 gamma_ckv->data};
+    g1.rope_cos = rope_cos->data;
+    g1.rope_sin = rope_sin->data;
+    g1.eps = eps;
+    hipError_t e = mla::launch_prolog_pack(g1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
+    e = mla::launch_prolog_gemm(g1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
+    return MLA_OK;
 }
 
 }  // namespace
@@ -1001,25 +1056,10 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
     unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
 
-    // x . [wq_a | wkv]: the wq_a tiles store fp32 rows for the c^Q norm, the
-    // wkv tile is the kv row (norm * gamma_ckv, rope)
-    mla::PrologGemmParams g1{};
-    g1.a = token_x->data;
-    g1.lda = pp.h;
-    g1.m = (int32_t)pp.t;
-    g1.k = (int32_t)pp.h;
-    g1.seg[0] = {wq_a->data, pp.r, pack_a, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, y_q, pp.r,
-                 nullptr};
-    g1.seg[1] = {wkv->data, mla::PROLOG_BN, pack_kv, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN,
-                 gamma_ckv->data};
-    g1.rope_cos = rope_cos->data;
-    g1.rope_sin = rope_sin->data;
-    g1.eps = eps;
-    hipError_t e = mla::launch_prolog_pack(g1, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
-    e = mla::launch_prolog_gemm(g1, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
-    e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
+    rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
+                              pack_kv, s);
+    if (rc) return rc;
+    hipError_t e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
                                     s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm: %s", hipGetErrorString(e));
     // c^Q . wq_b: one tile per head (norm per head, weight 1, rope)
@@ -1034,6 +1074,80 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     g2.rope_cos = rope_cos->data;
     g2.rope_sin = rope_sin->data;
     g2.eps = eps;
+    e = mla::launch_prolog_pack(g2, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
+    e = mla::launch_prolog_gemm(g2, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int mla_prolog_quant_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a,
+                                        const mla_tensor *wq_b, const mla_tensor *wkv,
+                                        const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                                        const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv,
+                                        const mla_tensor *wq_b_scale, float eps, const mla_tensor *q_out,
+                                        const mla_tensor *kv_out, const mla_tensor *qr_out,
+                                        const mla_tensor *qr_scale_out, uint64_t *workspace_size) {
+    if (workspace_size == nullptr) return fail(MLA_ERR_NULL, "workspace_size is NULL");
+    PrologProblem pp;
+    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                             qr_out, &pp, true);
+    if (rc) return rc;
+    if ((rc = check_scale_vector(wq_b_scale, "wq_b_scale", pp.heads * mla::PROLOG_BN)) ||
+        (rc = check_scale_vector(qr_scale_out, "qr_scale_out", pp.t)))
+        return rc;
+    *workspace_size = prolog_workspace_bytes(pp, true);
+    return ok();
+}
+
+int mla_prolog_quant(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                     const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                     const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale,
+                     float eps, const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
+                     const mla_tensor *qr_scale_out, void *workspace, uint64_t workspace_size, void *stream) {
+    PrologProblem pp;
+    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                             qr_out, &pp, true);
+    if (rc) return rc;
+    if ((rc = check_scale_vector(wq_b_scale, "wq_b_scale", pp.heads * mla::PROLOG_BN)) ||
+        (rc = check_scale_vector(qr_scale_out, "qr_scale_out", pp.t)))
+        return rc;
+    if (pp.t == 0) return ok();
+    const uint64_t need = prolog_workspace_bytes(pp, true);
+    if (workspace == nullptr || workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given", (unsigned long long)need,
+                    (unsigned long long)workspace_size);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char *wsb = static_cast<unsigned char *>(workspace);
+    float *y_q = reinterpret_cast<float *>(wsb);
+    unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
+    unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
+    unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
+
+    rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
+                              pack_kv, s);
+    if (rc) return rc;
+    float *scale = static_cast<float *>(qr_scale_out->data);
+    hipError_t e = mla::launch_prolog_quant_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, scale,
+                                                 (int32_t)pp.t, (int32_t)pp.r, eps, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm and quantisation: %s", hipGetErrorString(e));
+    // qr . wq_b in int8: one tile per head (dequantisation, norm per head, rope)
+    mla::PrologGemmParams g2{};
+    g2.a = qr_out->data;
+    g2.lda = pp.r;
+    g2.m = (int32_t)pp.t;
+    g2.k = (int32_t)pp.r;
+    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pack_b, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE,
+                 q_out->data, pp.heads * mla::PROLOG_BN, nullptr};
+    g2.seg[1] = {nullptr, 0, nullptr, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
+    g2.rope_cos = rope_cos->data;
+    g2.rope_sin = rope_sin->data;
+    g2.eps = eps;
+    g2.int8 = 1;
+    g2.row_scale = scale;
+    g2.col_scale = static_cast<const float *>(wq_b_scale->data);
     e = mla::launch_prolog_pack(g2, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
     e = mla::launch_prolog_gemm(g2, s);

@@ -143,9 +143,9 @@ enum PrologEpilogue : int32_t {
 };
 
 struct PrologSegment {
-    const void *w;       // bf16 [K, ldw]; this segment's tile j reads columns j*512 .. j*512+511
+    const void *w;       // bf16 (int8 with PrologGemmParams::int8) [K, ldw]; tile j reads columns j*512 .. j*512+511
     int64_t ldw;         // row stride of w, elements
-    void *wp;            // packed copy of w (launch_prolog_pack): n_tiles * (K / 32) blocks of 32 KB
+    void *wp;            // packed copy of w (launch_prolog_pack): n_tiles * (K / stage k) blocks of 32 KB
     int32_t n_tiles;     // 512-column tiles of this segment
     int32_t epilogue;    // PrologEpilogue
     void *out;           // tile j of rows m: out + m * ld_out + j * 512 (elements of the epilogue's type)
@@ -154,21 +154,29 @@ struct PrologSegment {
 };
 
 struct PrologGemmParams {
-    const void *a;       // bf16 [M, lda]
+    const void *a;       // bf16 [M, lda], or int8 with int8 set
     int64_t lda;
     int32_t m;           // rows
-    int32_t k;           // a multiple of PROLOG_K_MULTIPLE
+    int32_t k;           // a multiple of PROLOG_K_MULTIPLE (bf16) or PROLOG_K_MULTIPLE_I8 (int8)
     PrologSegment seg[2];  // tiles 0 .. seg[0].n_tiles - 1 from seg[0], the rest from seg[1]
     const void *rope_cos;  // bf16 [M, 64]
     const void *rope_sin;
     float eps;
+    // int8 operands (a and the weights), int32 products: the tile epilogue
+    // first scales product (m, n) by row_scale[m] * col_scale[n] (fp32);
+    // PROLOG_NORM_ROPE only
+    int32_t int8;
+    const float *row_scale;  // [M]
+    const float *col_scale;  // [N], column n of the segment's weights
 };
+// An int8 stage is 64 k: the same 64 bytes per row as a bf16 stage of 32 k.
+constexpr int PROLOG_K_MULTIPLE_I8 = 256;
 
 // Bytes of a segment's packed weights: one 32 KB block per 512-column tile and
 // 32-row stage of K.
 constexpr int64_t PROLOG_PACK_BLOCK = PROLOG_BN * PROLOG_BK * 2;
-inline int64_t prolog_packed_bytes(int32_t n_tiles, int32_t k) {
-    return (int64_t)n_tiles * (k / PROLOG_BK) * PROLOG_PACK_BLOCK;
+inline int64_t prolog_packed_bytes(int32_t n_tiles, int32_t k, bool int8 = false) {
+    return (int64_t)n_tiles * (k / (int8 ? 2 * PROLOG_BK : PROLOG_BK)) * PROLOG_PACK_BLOCK;
 }
 
 // Writes seg.wp from seg.w for each segment with tiles: block (j, kt) is the
@@ -180,5 +188,13 @@ hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream);
 // ld_out) = RmsNorm over each row * gamma; cols a multiple of 256.
 hipError_t launch_prolog_rms_rows(const float *y, int64_t ld_y, const void *gamma, void *out, int64_t ld_out,
                                   int32_t rows, int32_t cols, float eps, hipStream_t stream);
+
+// y fp32 [rows, cols] -> c = RmsNorm over each row * gamma, quantised per row:
+// scale[row] = max |c| / 127 (fp32), codes int8 [rows, cols] (row stride
+// ld_codes) = c / scale rounded to nearest, ties to even (0 for a zero row);
+// cols a multiple of 256, at most PROLOG_QUANT_MAX_COLS.
+constexpr int PROLOG_QUANT_MAX_COLS = 2048;
+hipError_t launch_prolog_quant_rows(const float *y, int64_t ld_y, const void *gamma, void *codes, int64_t ld_codes,
+                                    float *scale, int32_t rows, int32_t cols, float eps, hipStream_t stream);
 
 }  // namespace mla

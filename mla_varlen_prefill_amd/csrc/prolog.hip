@@ -69,6 +69,7 @@ constexpr int W_BYTES = BN * BK * 2;  // 32 KB of transposed weights
 constexpr int LDS_BYTES = STAGES * (X_BYTES + W_BYTES);  // 160 KB
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -78,6 +79,8 @@ extern "C" __device__ i32x4 prolog_raw_buffer_load_b128(i32x4 rsrc, int voffset,
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 extern "C" __device__ i16x4 prolog_raw_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v4i16");
+extern "C" __device__ float prolog_raw_buffer_load_f32(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.f32");
 typedef __attribute__((address_space(3))) unsigned int *lds_u32_ptr;
 // Buffer load with the LDS-DMA bit: lane l's `size` bytes land at lds + l*size.
 extern "C" __device__ void prolog_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
@@ -112,22 +115,28 @@ __device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
     return __uint_as_float(static_cast<unsigned>(b) << 16);
 }
 
-// Packs the weights of one segment tile stage: workgroup (j, kt) reads rows
-// 32 kt .. 32 kt + 31, columns 512 j .. 512 j + 511 of w (coalesced, into LDS
-// k-major) and writes block j * (K / 32) + kt of wp in the stage layout the
-// product kernel reads.
+// Packs the weights of one segment tile stage: workgroup (j, kt) reads the KR
+// k rows of stage kt (32 bf16 or 64 int8 rows), columns 512 j .. 512 j + 511
+// of w (coalesced, into LDS k-major) and writes block j * nk + kt of wp in the
+// stage layout the product kernel reads: column n, 16-byte chunk c (the k
+// values 8c .. 8c + 7 of the stage in bf16, 16c .. 16c + 15 in int8) at byte
+// n * 64 + ((c ^ ((n >> 2) & 3)) << 4).
+template <bool I8>
 __global__ __launch_bounds__(256) void prolog_pack_kernel(const unsigned char *w, int64_t ldw, int32_t nk,
                                                           unsigned char *wp) {
-    constexpr int ROW = BN * 2 + 16;  // LDS bytes per k row (padded)
-    __shared__ __attribute__((aligned(16))) unsigned char t[BK * ROW];
+    constexpr int ESZ = I8 ? 1 : 2;         // bytes per element
+    constexpr int KR = 64 / ESZ;            // k rows per stage
+    constexpr int ROW = BN * ESZ + 16;      // LDS bytes per k row (padded)
+    constexpr int CPR = BN * ESZ / 16;      // 16-byte chunks per k row
+    __shared__ __attribute__((aligned(16))) unsigned char t[KR * ROW];
     const int tid = threadIdx.x;
     const int j = blockIdx.x / nk, kt = blockIdx.x % nk;
-    const unsigned char *src = w + ((int64_t)kt * BK * ldw + (int64_t)j * BN) * 2;
+    const unsigned char *src = w + ((int64_t)kt * KR * ldw + (int64_t)j * BN) * ESZ;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int q = tid + 256 * u, row = q >> 6, ch = q & 63;  // 64 16-byte chunks per 1 KB row
+        const int q = tid + 256 * u, row = q / CPR, ch = q % CPR;
         *reinterpret_cast<uint4 *>(t + row * ROW + ch * 16) =
-            *reinterpret_cast<const uint4 *>(src + (int64_t)row * ldw * 2 + ch * 16);
+            *reinterpret_cast<const uint4 *>(src + (int64_t)row * ldw * ESZ + ch * 16);
     }
     __syncthreads();
     unsigned char *dst = wp + ((int64_t)j * nk + kt) * PROLOG_PACK_BLOCK;
@@ -135,20 +144,36 @@ __global__ __launch_bounds__(256) void prolog_pack_kernel(const unsigned char *w
     for (int u = 0; u < 8; ++u) {
         const int s16 = tid + 256 * u;  // 16-byte slot of the block: column n, physical chunk pc
         const int n = s16 >> 2, pc = s16 & 3, c = pc ^ ((n >> 2) & 3);
-        unsigned short v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const unsigned short *>(t + (8 * c + i) * ROW + n * 2);
         uint4 o;
-        o.x = v[0] | (unsigned)v[1] << 16;
-        o.y = v[2] | (unsigned)v[3] << 16;
-        o.z = v[4] | (unsigned)v[5] << 16;
-        o.w = v[6] | (unsigned)v[7] << 16;
+        if (I8) {
+            unsigned b[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) b[i] = t[(16 * c + i) * ROW + n];
+            o.x = b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24;
+            o.y = b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24;
+            o.z = b[8] | b[9] << 8 | b[10] << 16 | b[11] << 24;
+            o.w = b[12] | b[13] << 8 | b[14] << 16 | b[15] << 24;
+        } else {
+            unsigned short v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = *reinterpret_cast<const unsigned short *>(t + (8 * c + i) * ROW + n * 2);
+            o.x = v[0] | (unsigned)v[1] << 16;
+            o.y = v[2] | (unsigned)v[3] << 16;
+            o.z = v[4] | (unsigned)v[5] << 16;
+            o.w = v[6] | (unsigned)v[7] << 16;
+        }
         *reinterpret_cast<uint4 *>(dst + s16 * 16) = o;
     }
 }
 
+// I8: int8 operands, v_mfma_i32_32x32x32_i8, a stage of 64 k (the same 64
+// bytes per row as a bf16 stage of 32 k, so the ring, the DMA and the operand
+// reads are the same); the epilogue scales the int32 products to fp32 first.
+template <bool I8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2)))
 void prolog_gemm_kernel(const PrologGemmParams p) {
+    constexpr int ESZ = I8 ? 1 : 2;  // bytes per element
     // one array per ring slot (see the design notes above)
     __shared__ __attribute__((aligned(1024))) unsigned char xs0[X_BYTES], xs1[X_BYTES], xs2[X_BYTES], xs3[X_BYTES];
     __shared__ __attribute__((aligned(1024))) unsigned char ws0[W_BYTES], ws1[W_BYTES], ws2[W_BYTES], ws3[W_BYTES];
@@ -191,15 +216,26 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const unsigned char *gamma = static_cast<const unsigned char *>(second ? p.seg[1].gamma : p.seg[0].gamma);
     const int m0 = tm * BM;
     const int rows = min(BM, p.m - m0);
-    const int nk = p.k / BK;
+    const int nk = p.k * ESZ / (BK * 2);  // 64-byte stages
+    // int8: the dequantisation scales go out now and are used by the
+    // epilogue -- thread tid takes the scale of the tile's column tid, a lane
+    // those of its two output rows (rows past the end read 0)
+    float cs_pre = 0.f, rs_pre[2] = {0.f, 0.f};
+    if constexpr (I8) {
+        cs_pre = p.col_scale[(int64_t)tj * BN + tid];
+        const i32x4 rsr = make_rsrc(p.row_scale + m0, (uint32_t)rows * 4);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+            rs_pre[tb] = prolog_raw_buffer_load_f32(rsr, (uint32_t)(64 * wt + 32 * tb + r32) * 4, 0, 0);
+    }
 
     // ---- activation stage: 128 rows x 64 bytes; LDS slot tid (row tid / 4,
     // physical chunk tid % 4) receives logical chunk (tid % 4) ^ ((row >> 2)
     // & 3). Rows past the end read as zeros.
-    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * 2,
-                               (uint32_t)rows * (uint32_t)p.lda * 2);
+    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * ESZ,
+                               (uint32_t)rows * (uint32_t)p.lda * ESZ);
     const int xr = tid >> 2;
-    const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * 2 + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
+    const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * ESZ + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
     // ---- weight stage: block kt of this tile's packed weights, 2048 16-byte
     // slots; load r of a thread takes slot 512 r + tid. Stages past K read
     // as zeros.
@@ -224,13 +260,14 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const int xrow = 64 * wt + r32;
     const uint32_t xb = (uint32_t)(xrow * 64) | ((uint32_t)(g ^ ((xrow >> 2) & 3)) << 4);
 
-    f32x16 acc[4][2];
+    typedef std::conditional_t<I8, i32x16, f32x16> acc_t;
+    acc_t acc[4][2];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[nb][tb][e] = 0.f;
+            for (int e = 0; e < 16; ++e) acc[nb][tb][e] = 0;
 
     // Operands of one k-step: av = 4 weight column blocks, bv = 2 activation
     // row blocks. Operand o < 4 is av[o], o >= 4 is bv[o - 4]. The products of
@@ -249,7 +286,12 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     };
     auto product = [&](int n) __attribute__((always_inline)) {
         const int nb = n & 3, tb = n >> 2;
-        acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
+        if constexpr (I8)
+            acc[nb][tb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, av[nb]),
+                                                                __builtin_bit_cast(i32x4, bv[tb]), acc[nb][tb], 0, 0,
+                                                                0);
+        else
+            acc[nb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[nb], bv[tb], acc[nb][tb], 0, 0, 0);
     };
     // operands of the next k-step read after product n of this one
     auto read_after = [&](int slot, int ks, int n) __attribute__((always_inline)) {
@@ -327,7 +369,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // store instruction writes whole rows: 16 bytes per lane straight from
     // the accumulators would touch 32 rows 16 bytes at a time, and the
     // partial-line writes cost several times the bytes.
-    if (epilogue == PROLOG_STORE_F32) {
+    if (!I8 && epilogue == PROLOG_STORE_F32) {
         // fp32 rows are 2 KB: two passes of 64 rows (tb = 0, 1). Row lr of a
         // pass (= 32 wt + r32) holds chunk c (4 columns) at c ^ ((lr & 7) << 1).
         float *out = static_cast<float *>(out_base);
@@ -369,7 +411,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // the latency would be paid once per store. They land while the row sums
     // are reduced.
     uint2 gw[4][4];  // gamma of columns n .. n + 3 for (nb, i), bf16 pairs
-    if (gamma != nullptr) {
+    if (!I8 && gamma != nullptr) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -397,6 +439,33 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 }
     }
 
+    // int8: the products scaled to fp32 by their row's and column's scales
+    // (the column scales pass through the free ring, so that a lane does not
+    // hold its 64 of them); bf16: as they are.
+    f32x16 fa[4][2];
+    if constexpr (I8) {
+        float *csl = reinterpret_cast<float *>(xs1);  // [512] column scales of the tile
+        csl[tid] = cs_pre;
+        block_sync();
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(csl + 128 * wn + 32 * nb + 8 * i + 4 * g);
+                const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        fa[nb][tb][4 * i + j] = static_cast<float>(acc[nb][tb][4 * i + j]) * (rs_pre[tb] * cj[j]);
+            }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) fa[nb][tb] = acc[nb][tb];
+    }
+
     // RmsNorm over the tile's 512 columns: per-lane partial sums of squares,
     // the lane pair (l, l ^ 32) of a row, then the 4 column quarters in LDS.
     float ssq[2];
@@ -407,8 +476,8 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                s0 = __builtin_fmaf(acc[nb][tb][e], acc[nb][tb][e], s0);
-                s1 = __builtin_fmaf(acc[nb][tb][e + 1], acc[nb][tb][e + 1], s1);
+                s0 = __builtin_fmaf(fa[nb][tb][e], fa[nb][tb][e], s0);
+                s1 = __builtin_fmaf(fa[nb][tb][e + 1], fa[nb][tb][e + 1], s1);
             }
         const float sm = s0 + s1;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(sm), __float_as_int(sm), false, false);
@@ -437,7 +506,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
         for (int i = 0; i < 4; ++i) {
             const int n = 128 * wn + 32 * nb + 8 * i + 4 * g;
             float gm[4] = {1.f, 1.f, 1.f, 1.f};
-            if (gamma != nullptr) {
+            if (!I8 && gamma != nullptr) {
                 gm[0] = bf16_bits_to_float(gw[nb][i].x & 0xffff);
                 gm[1] = bf16_bits_to_float(gw[nb][i].x >> 16);
                 gm[2] = bf16_bits_to_float(gw[nb][i].y & 0xffff);
@@ -448,7 +517,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 const int row = 64 * wt + 32 * tb + r32;
                 float v[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[j] = acc[nb][tb][4 * i + j] * inv[tb] * gm[j];
+                for (int j = 0; j < 4; ++j) v[j] = fa[nb][tb][4 * i + j] * inv[tb] * gm[j];
                 if (nb >= 2 && rope_wave) {
                     float cs[4], sn[4];
 #pragma unroll
@@ -514,15 +583,76 @@ __global__ __launch_bounds__(256) void prolog_rms_rows_kernel(const float *y, in
     }
 }
 
+// One wave per row: c = RmsNorm over the row's cols = 256 NV fp32 values
+// (kept in registers) * gamma, computed as in prolog_rms_rows_kernel; then the
+// row's largest |c|, its scale max / 127, and the int8 codes c / scale
+// rounded to nearest, ties to even (so within [-127, 127]); a zero row gets
+// scale 0 and codes 0.
+template <int NV>
+__global__ __launch_bounds__(256) void prolog_quant_rows_kernel(const float *y, int64_t ld_y, const __bf16 *gamma,
+                                                                signed char *codes, int64_t ld_codes, float *scale,
+                                                                int32_t rows, float eps) {
+    constexpr int COLS = 256 * NV;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *yr = y + (int64_t)row * ld_y;
+    float4 v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        v[u] = *reinterpret_cast<const float4 *>(yr + lane * 4 + 256 * u);
+        s = __builtin_fmaf(v[u].x, v[u].x, s);
+        s = __builtin_fmaf(v[u].y, v[u].y, s);
+        s = __builtin_fmaf(v[u].z, v[u].z, s);
+        s = __builtin_fmaf(v[u].w, v[u].w, s);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    const float inv = 1.0f / sqrtf(s / (float)COLS + eps);
+    float amax = 0.f;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const uint2 gw = *reinterpret_cast<const uint2 *>(gamma + lane * 4 + 256 * u);
+        v[u].x = v[u].x * inv * bf16_bits_to_float(gw.x & 0xffff);
+        v[u].y = v[u].y * inv * bf16_bits_to_float(gw.x >> 16);
+        v[u].z = v[u].z * inv * bf16_bits_to_float(gw.y & 0xffff);
+        v[u].w = v[u].w * inv * bf16_bits_to_float(gw.y >> 16);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float sc = amax / 127.0f;
+    signed char *crow = codes + (int64_t)row * ld_codes;
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+        const float c4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        unsigned packed = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = sc > 0.f ? static_cast<int>(rintf(c4[j] / sc)) : 0;
+            packed |= (static_cast<unsigned>(q) & 0xffu) << (8 * j);
+        }
+        *reinterpret_cast<unsigned *>(crow + lane * 4 + 256 * u) = packed;
+    }
+    if (lane == 0) scale[row] = sc;
+}
+
 }  // namespace
 
 hipError_t launch_prolog_pack(const PrologGemmParams &p, hipStream_t stream) {
-    const int32_t nk = p.k / PROLOG_BK;
+    const int32_t nk = p.k / (p.int8 ? 2 * PROLOG_BK : PROLOG_BK);
     for (int i = 0; i < 2; ++i) {
         const PrologSegment &sg = p.seg[i];
         if (sg.n_tiles <= 0) continue;
-        hipLaunchKernelGGL(prolog_pack_kernel, dim3((unsigned)(sg.n_tiles * nk)), dim3(256), 0, stream,
-                           static_cast<const unsigned char *>(sg.w), sg.ldw, nk, static_cast<unsigned char *>(sg.wp));
+        if (p.int8)
+            hipLaunchKernelGGL(prolog_pack_kernel<true>, dim3((unsigned)(sg.n_tiles * nk)), dim3(256), 0, stream,
+                               static_cast<const unsigned char *>(sg.w), sg.ldw, nk,
+                               static_cast<unsigned char *>(sg.wp));
+        else
+            hipLaunchKernelGGL(prolog_pack_kernel<false>, dim3((unsigned)(sg.n_tiles * nk)), dim3(256), 0, stream,
+                               static_cast<const unsigned char *>(sg.w), sg.ldw, nk,
+                               static_cast<unsigned char *>(sg.wp));
     }
     return hipGetLastError();
 }
@@ -531,7 +661,10 @@ hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream) {
     const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
     const int m_tiles = (p.m + PROLOG_BM - 1) / PROLOG_BM;
     if (p.m <= 0 || n_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(prolog_gemm_kernel, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
+    if (p.int8)
+        hipLaunchKernelGGL(prolog_gemm_kernel<true>, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
+    else
+        hipLaunchKernelGGL(prolog_gemm_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -540,6 +673,35 @@ hipError_t launch_prolog_rms_rows(const float *y, int64_t ld_y, const void *gamm
     if (rows <= 0) return hipSuccess;
     hipLaunchKernelGGL(prolog_rms_rows_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, y, ld_y,
                        static_cast<const __bf16 *>(gamma), static_cast<__bf16 *>(out), ld_out, rows, cols, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_prolog_quant_rows(const float *y, int64_t ld_y, const void *gamma, void *codes, int64_t ld_codes,
+                                    float *scale, int32_t rows, int32_t cols, float eps, hipStream_t stream) {
+    if (rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    const __bf16 *g = static_cast<const __bf16 *>(gamma);
+    signed char *c = static_cast<signed char *>(codes);
+    switch (cols) {
+        case 512:
+            hipLaunchKernelGGL(prolog_quant_rows_kernel<2>, grid, dim3(256), 0, stream, y, ld_y, g, c, ld_codes, scale,
+                               rows, eps);
+            break;
+        case 1024:
+            hipLaunchKernelGGL(prolog_quant_rows_kernel<4>, grid, dim3(256), 0, stream, y, ld_y, g, c, ld_codes, scale,
+                               rows, eps);
+            break;
+        case 1536:
+            hipLaunchKernelGGL(prolog_quant_rows_kernel<6>, grid, dim3(256), 0, stream, y, ld_y, g, c, ld_codes, scale,
+                               rows, eps);
+            break;
+        case 2048:
+            hipLaunchKernelGGL(prolog_quant_rows_kernel<8>, grid, dim3(256), 0, stream, y, ld_y, g, c, ld_codes, scale,
+                               rows, eps);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

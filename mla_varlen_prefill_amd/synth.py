@@ -224,5 +224,24 @@ def prolog_inputs(t, h=4096, q_lora_rank=1024, num_heads=64, head_dim=512, rope_
     return d
 
 
+def prolog_quant_inputs(t, h=4096, q_lora_rank=1024, num_heads=64, head_dim=512, rope_dim=64, seed=0,
+                        device="cpu", position0=0):
+    """Seeded inputs of the quantised prolog: those of prolog_inputs, with wq_b
+    replaced by int8 integers uniform in [-127, 127] and wq_b_scale (float32
+    [num_heads * head_dim, 1]) uniform in [0.75, 1.25] * sqrt(3 / q_lora_rank)
+    / 127, so that wq_b * wq_b_scale has about the variance 1 / q_lora_rank of
+    the plain prolog's weight. Values from torch.Generator(seed * 100 + k),
+    k = 10 .. 17."""
+    d = prolog_inputs(t, h, q_lora_rank, num_heads, head_dim, rope_dim, seed, device, position0)
+    base = int(seed) * 100
+    g = torch.Generator(device="cpu").manual_seed(base + 16)
+    d["wq_b"] = torch.randint(-127, 128, (q_lora_rank, num_heads * head_dim), generator=g,
+                              dtype=torch.int8).to(device)
+    g = torch.Generator(device="cpu").manual_seed(base + 17)
+    u = torch.rand((num_heads * head_dim, 1), generator=g, dtype=torch.float32)
+    d["wq_b_scale"] = ((0.75 + 0.5 * u) * math.sqrt(3.0 / q_lora_rank) / 127.0).to(device)
+    return d
+
+
 PROLOG_FLOP_PER_TOKEN = 2 * (PROLOG_SIZES["h"] * (PROLOG_SIZES["q_lora_rank"] + PROLOG_SIZES["head_dim"])
                              + PROLOG_SIZES["q_lora_rank"] * PROLOG_SIZES["num_heads"] * PROLOG_SIZES["head_dim"])

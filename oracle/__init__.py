@@ -362,16 +362,20 @@ def mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gam
         q        = RmsNorm((qr . wq_b) * s[t] * wq_b_scale[n]), per head (weight 1)
         q[..., -rope_dim:] = ROPE(q[..., -rope_dim:])
         kv       as in mla_prolog
-    The product qr . wq_b is taken exactly, in integers. Returns
-    (q, kv, qr, s), q and kv in float64."""
+    The product qr . wq_b is taken exactly: both factors hold integers of
+    magnitude at most 128, so every partial sum is an integer far below 2^53
+    and a float64 product cannot round. Returns (q, kv, qr, s), q and kv in
+    float64."""
     x = np.asarray(token_x, dtype=np.float64)
     t = x.shape[0]
     head_dim = wkv.shape[1]
     rd = rope_cos.shape[1]
     cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), gamma_cq, eps)
     qr, s = quantize_per_token(cq)
-    acc = qr @ np.asarray(wq_b, dtype=np.int64)
-    y = acc.astype(np.float64) * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)
+    w8 = np.asarray(wq_b, dtype=np.float64)
+    assert qr.shape[1] * 128 * 128 < 2 ** 53 and np.abs(w8).max(initial=0) <= 128
+    acc = qr.astype(np.float64) @ w8
+    y = acc * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)
     q = rms_norm(y.reshape(t, num_heads, head_dim), None, eps)
     q[..., head_dim - rd:] = rope_interleaved(q[..., head_dim - rd:], np.asarray(rope_cos)[:, None, :],
                                               np.asarray(rope_sin)[:, None, :])

@@ -553,6 +553,54 @@ def test_prolog_validation_errors():
     assert prolog_status(q_out=torch.zeros(0, 1024, dtype=torch.bfloat16)) == 0
 
 
+def prolog_quant_args(t=0, h=128, r=512, heads=2, hd=512, rd=64, **over):
+    z = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)
+    a = dict(token_x=z(t, h), wq_a=z(h, r), wq_b=z(r, heads * hd, dt=torch.int8), wkv=z(h, hd), rope_cos=z(t, rd),
+             rope_sin=z(t, rd), gamma_cq=z(r), gamma_ckv=z(hd), wq_b_scale=z(heads * hd, 1, dt=torch.float32),
+             eps=1e-6, q_out=z(t, heads, hd), kv_out=z(t, hd), qr_out=z(t, r, dt=torch.int8),
+             qr_scale_out=z(t, 1, dt=torch.float32))
+    a.update(over)
+    return a
+
+
+def prolog_quant_status(**kw):
+    try:
+        mla.mla_prolog_quant_get_workspace_size(**prolog_quant_args(**kw))
+        return 0
+    except mla.MlaError as e:
+        return e.code
+
+
+def test_prolog_quant_workspace_size():
+    assert mla.mla_prolog_quant_get_workspace_size(**prolog_quant_args(t=0)) == 0
+    # the fp32 rows of x . wq_a, then wq_a and wkv repacked (2 bytes per
+    # weight) and wq_b repacked (1 byte per weight), each 256-byte aligned
+    h, r, heads, hd = 128, 512, 2, 512
+    assert mla.mla_prolog_quant_get_workspace_size(**prolog_quant_args(t=3)) == \
+        256 * -(-3 * r * 4 // 256) + 2 * h * r + 2 * h * hd + r * heads * hd
+    # [n] scales are accepted as well as [n, 1]
+    assert prolog_quant_status(t=2, wq_b_scale=torch.zeros(1024, dtype=torch.float32),
+                               qr_scale_out=torch.zeros(2, dtype=torch.float32)) == 0
+
+
+def test_prolog_quant_validation_errors():
+    ERR_SHAPE, ERR_DTYPE, ERR_UNSUP = -2, -3, -5
+    # wq_b and qr_out must be int8, the scales float32
+    assert prolog_quant_status(wq_b=torch.zeros(512, 1024, dtype=torch.bfloat16)) == ERR_DTYPE
+    assert prolog_quant_status(qr_out=torch.zeros(0, 512, dtype=torch.bfloat16)) == ERR_DTYPE
+    assert prolog_quant_status(wq_b_scale=torch.zeros(1024, 1, dtype=torch.bfloat16)) == ERR_DTYPE
+    assert prolog_quant_status(t=2, qr_scale_out=torch.zeros(2, 1, dtype=torch.float16)) == ERR_DTYPE
+    # one scale per column of wq_b, one per token
+    assert prolog_quant_status(wq_b_scale=torch.zeros(512, 1, dtype=torch.float32)) == ERR_SHAPE
+    assert prolog_quant_status(wq_b_scale=torch.zeros(1024, 2, dtype=torch.float32)) == ERR_SHAPE
+    assert prolog_quant_status(t=2, qr_scale_out=torch.zeros(3, 1, dtype=torch.float32)) == ERR_SHAPE
+    # the plain prolog's checks still apply, and q_lora_rank is at most 2048
+    assert prolog_quant_status(hd=256) == ERR_UNSUP
+    assert prolog_quant_status(r=2560) == ERR_UNSUP
+    assert prolog_status(r=2560) == 0  # the plain prolog has no such limit
+    # the plain entry point still wants bf16 wq_b
+    assert prolog_status(wq_b=torch.zeros(512, 1024, dtype=torch.int8)) == ERR_DTYPE
+
 
 def test_gather_batch_limit():
     # the gather kernel keeps the batch's offsets in LDS: 8192 sequences at most

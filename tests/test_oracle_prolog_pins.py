@@ -249,8 +249,8 @@ QUANT_MUTANTS = {
     "ties away from zero": ("np.rint(c / safe[:, None])", "np.sign(c) * np.floor(np.abs(c / safe[:, None]) + 0.5)"),
     "scale over 128": ("scale = np.max(np.abs(c), axis=-1) / 127.0", "scale = np.max(np.abs(c), axis=-1) / 128.0"),
     "codes truncated": ("np.rint(c / safe[:, None])", "np.trunc(c / safe[:, None])"),
-    "channel scale dropped": ("acc.astype(np.float64) * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)",
-                              "acc.astype(np.float64) * s[:, None]"),
+    "channel scale dropped": ("y = acc * s[:, None] * np.asarray(wq_b_scale, dtype=np.float64).reshape(1, -1)",
+                              "y = acc * s[:, None]"),
     "quantised before gamma": ("    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), gamma_cq, eps)\n    qr, s = quantize_per_token(cq)",
                                "    cq = rms_norm(x @ np.asarray(wq_a, dtype=np.float64), None, eps)\n    qr, s = quantize_per_token(cq)"),
     "quant q norm over all heads": ("    q = rms_norm(y.reshape(t, num_heads, head_dim), None, eps)",
