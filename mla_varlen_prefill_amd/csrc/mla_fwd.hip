@@ -133,6 +133,12 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) unsigned int *lds_u32_ptr;
 
+// Cache policy of a buffer access whose data is used once: non-temporal, so
+// that it leaves L2 early instead of the K/V tiles that the items of a head
+// share. Set on the Q loads and the output stores (single workload: 1.30 ->
+// 1.26 GB of L2 misses per launch, 1.2% faster).
+constexpr int CPOL_NT = 2;
+
 // Buffer load with the LDS-DMA bit: lane l's `size` bytes land at lds + l*size.
 extern "C" __device__ void mla_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr lds, int size, int voffset,
                                                    int soffset, int offset, int aux)
@@ -314,13 +320,13 @@ void mla_fwd_kernel(const FwdParams p) {
         for (int u = 0; u < QN_INSTR; ++u) {
             const int r = u * (64 / QN_CPR) + lane / QN_CPR, c = (lane % QN_CPR) ^ row_swizzle<DN>(r);
             mla_raw_buffer_load_lds(rq, (lds_u32_ptr)(qslot + u * 1024), 16, (uint32_t)r * H * DN * 2 + c * 16, 0,
-                                    0, 0);
+                                    0, CPOL_NT);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int r = u * 8 + lane / 8, c = (lane % 8) ^ ((r >> 1) & 7);
             mla_raw_buffer_load_lds(rr, (lds_u32_ptr)(qslot + 32 * DN * 2 + u * 1024), 16,
-                                    (uint32_t)r * H * DR * 2 + c * 16, 0, 0, 0);
+                                    (uint32_t)r * H * DR * 2 + c * 16, 0, 0, CPOL_NT);
         }
     }
     constexpr int Q_LOADS = QN_INSTR + 4;
@@ -1021,7 +1027,7 @@ void mla_fwd_kernel(const FwdParams p) {
         for (int k = 0; k < 32 / RPI; ++k) {
             const int r = RPI * k + lane / CPR;  // row of the wave
             const i32x4 v = *reinterpret_cast<const i32x4 *>(stg + r * KN_ROW + ((ch ^ row_swizzle<DN>(r)) << 4));
-            mla_raw_buffer_store_b128(v, ro, (uint32_t)r * H * DN * 2 + ch * 16, 0, 0);
+            mla_raw_buffer_store_b128(v, ro, (uint32_t)r * H * DN * 2 + ch * 16, 0, CPOL_NT);
         }
     }
 }
