@@ -89,6 +89,11 @@ extern "C" __device__ void prolog_raw_buffer_load_lds(i32x4 rsrc, lds_u32_ptr ld
 extern "C" __device__ void prolog_raw_buffer_store_b128(i32x4 data, i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 
+// Cache policy of the output stores: non-temporal, since no kernel of the
+// product reads them back and the weight tiles the XCD's CUs share should stay
+// in L2 (16384-token prolog: -2.3%, quantised -3.5%).
+constexpr int CPOL_NT = 2;
+
 // Buffer resource over [base, base + bytes): loads past the end return 0,
 // stores past the end are dropped. Arguments must be wave-uniform.
 __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
@@ -399,7 +404,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 const int row = 64 * (q >> 5) + 32 * tb + (q & 31);
                 const i32x4 v =
                     *reinterpret_cast<const i32x4 *>(WS(q >> 4) + (q & 15) * 2048 + ((ch ^ ((q & 7) << 1)) << 4));
-                prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 4 + ch * 16, 0, 0);
+                prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 4 + ch * 16, 0, CPOL_NT);
             }
         }
         return;
@@ -547,7 +552,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     for (int u = 0; u < 16; ++u) {
         const int row = 16 * wave + u;
         const i32x4 v = *reinterpret_cast<const i32x4 *>(WS(row >> 5) + (row & 31) * 1024 + ((lane ^ (row & 15)) << 4));
-        prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 2 + lane * 16, 0, 0);
+        prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 2 + lane * 16, 0, CPOL_NT);
     }
 }
 
