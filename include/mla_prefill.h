@@ -159,8 +159,15 @@ int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope
  * 16-byte aligned (NULL allowed when the planned size is 0). The call copies
  * a work list built from the host lengths into the workspace and enqueues the
  * attention kernel on stream; the workspace must stay untouched until that
- * work has run. Errors: validation codes as above, MLA_ERR_WORKSPACE,
- * MLA_ERR_RUNTIME when a HIP call fails.
+ * work has run. When the problem holds little work for the GPU's 256 compute
+ * units (few heads or sequences), items longer than an even share of it are
+ * cut into runs of consecutive key tiles, each run a workgroup of its own;
+ * such a workgroup writes its rows over its own keys in fp32 with their
+ * log-sum-exp into the workspace (head_dim * 4 + 4 bytes per row and run),
+ * and a second kernel on the same stream combines the runs of each row. The
+ * result then differs from an unsplit run only by rounding. Errors:
+ * validation codes as above, MLA_ERR_WORKSPACE, MLA_ERR_RUNTIME when a HIP
+ * call fails.
  */
 int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor *k,
                 const mla_tensor *k_rope, const mla_tensor *v, const mla_tensor *q_seqlen,
@@ -176,8 +183,11 @@ int mla_prefill(const mla_tensor *q, const mla_tensor *q_rope, const mla_tensor 
  * workspace: the work list goes into a fixed array in device memory that the
  * library holds, MLA_NO_ALLOC_WORKSPACE_BYTES (4 MiB = 131072 launch records)
  * on each GPU it runs on, until the process ends. The call allocates nothing
- * (no hipMalloc, hipFree or allocating library routine). A problem whose
- * planned workspace (mla_prefill_get_workspace_size) is larger returns
+ * (no hipMalloc, hipFree or allocating library routine). It never splits an
+ * item (mla_prefill may, where little work is spread over many compute
+ * units), so its work list is one 32-byte launch record per workgroup, and
+ * its result can differ from mla_prefill's by rounding where mla_prefill
+ * splits. A problem whose work list is larger than the array returns
  * MLA_ERR_WORKSPACE before anything is enqueued; at 128 heads the limit is
  * reached near 256K query rows. The first call on a device looks the array's
  * address up with that device current (the tensors and the stream must belong
@@ -392,15 +402,17 @@ const char *mla_last_error(void);
  * bytes), three arrays each starting on a 256-byte boundary:
  *   batch records  {q_offset, kv_offset, q_len, kv_len}  int32 x 4, batch of them
  *   work items     {batch, first_q_row, kv_tiles, q_rows} int32 x 4, *n_items of them
- *   tasks          {item, first_head}                      int32 x 2, *n_tasks of them
+ *   tasks          {item, first_head, first_tile, end_tile} int32 x 4, *n_tasks of them
  * A task runs P = MLA_PLAN_Q_ROWS / q_rows query heads, first_head ..
  * first_head + P - 1, which share one KV head: P is the largest power of two
  * up to 8 that divides head_num / kv_head_num (1 without head grouping). One
  * work item covers q_rows = MLA_PLAN_Q_ROWS / P query rows of a sequence;
  * kv_tiles counts the tiles of MLA_PLAN_KV_COLS keys (from key 0) those rows
- * can see. Task i is the work of workgroup i of the launch (item -1: an empty
- * padding task). kv_padded_max_seq: 0 for packed K/V, else max_seq of the padded
- * layout. Returns MLA_ERR_WORKSPACE if buf is too small, MLA_ERR_VALUE for bad
+ * can see. A task covers the item's tiles [first_tile, end_tile): all of
+ * them, or one run of an item that mla_prefill splits (see there). Task i is
+ * the work of workgroup i of the launch (item -1: an empty padding task).
+ * kv_padded_max_seq: 0 for packed K/V, else max_seq of the padded layout.
+ * Returns MLA_ERR_WORKSPACE if buf is too small, MLA_ERR_VALUE for bad
  * lengths or head counts.
  */
 #define MLA_PLAN_Q_ROWS 256

@@ -295,8 +295,10 @@ def mla_prefill_plan_host(q_seqlen, kv_seqlen, head_num, kv_head_num, mask_type,
 
     Returns (seqs [batch, 4] int32 = q_offset, kv_offset, q_len, kv_len;
     items [n, 4] int32 = batch, first_q_row, kv_tiles, q_rows;
-    tasks [m, 2] int32 = item (-1: padding), first head -- task i is
-    workgroup i and runs PLAN_Q_ROWS // q_rows heads from its first head).
+    tasks [m, 4] int32 = item (-1: padding), first head, first tile, end tile
+    -- task i is workgroup i and runs PLAN_Q_ROWS // q_rows heads from its
+    first head over key tiles [first tile, end tile) of the item; an item cut
+    into several such runs is merged after the attention launch).
     """
     lib = _load()
     qs, ks = _host_int32(q_seqlen), _host_int32(kv_seqlen)
@@ -313,12 +315,12 @@ def mla_prefill_plan_host(q_seqlen, kv_seqlen, head_num, kv_head_num, mask_type,
 
     off_items = up(batch * 16)
     off_tasks = off_items + up(n_items.value * 16)
-    buf = np.zeros(max(1, off_tasks + n_tasks.value * 8), dtype=np.uint8)
+    buf = np.zeros(max(1, off_tasks + n_tasks.value * 16), dtype=np.uint8)
     _check("mla_prefill_plan_host", lib.mla_prefill_plan_host(*args, buf.ctypes.data, buf.nbytes,
                                                               ctypes.byref(n_items), ctypes.byref(n_tasks)))
     seqs = buf[:batch * 16].view(np.int32).reshape(batch, 4).copy()
     items = buf[off_items:off_items + n_items.value * 16].view(np.int32).reshape(n_items.value, 4).copy()
-    tasks = buf[off_tasks:off_tasks + n_tasks.value * 8].view(np.int32).reshape(n_tasks.value, 2).copy()
+    tasks = buf[off_tasks:off_tasks + n_tasks.value * 16].view(np.int32).reshape(n_tasks.value, 4).copy()
     return seqs, items, tasks
 
 

@@ -25,6 +25,8 @@ using mla::SeqRec;
 using mla::MLA_CUS_PER_XCD;
 using mla::MLA_XCDS;
 using mla::PAGED_MAX_TILES;
+using mla::MergeRec;
+using mla::PART_ROWS;
 using mla::Task;
 using mla::WorkItem;
 
@@ -36,6 +38,15 @@ constexpr int PLAN_BATCH_TASKS = MLA_PLAN_BATCH_TASKS;  // minimum tasks per lau
 #define MLA_PLAN_EVEN_BATCH_TASKS (MLA_CUS_PER_XCD / 2)
 #endif
 constexpr int PLAN_EVEN_BATCH_TASKS = MLA_PLAN_EVEN_BATCH_TASKS;  // the same when the tasks are about equal
+#ifndef MLA_SPLIT_MIN_TILES
+#define MLA_SPLIT_MIN_TILES 16
+#endif
+constexpr int32_t SPLIT_MIN_TILES = MLA_SPLIT_MIN_TILES;  // no piece of a split item is cut shorter than this
+#ifndef MLA_SPLIT_SHARE_PERCENT
+#define MLA_SPLIT_SHARE_PERCENT 100
+#endif
+constexpr int64_t SPLIT_SHARE_PERCENT = MLA_SPLIT_SHARE_PERCENT;  // longest run, in percent of the even share
+constexpr int64_t TASK_FIXED_TILES = 2;  // a workgroup's fixed work (Q load, pipeline fill, epilogue) in tiles
 #ifndef MLA_MAX_PACK_SHIFT
 #define MLA_MAX_PACK_SHIFT 3
 #endif
@@ -331,32 +342,53 @@ int32_t visible_tiles(int mask_type, int32_t q_len, int32_t kv_len, int32_t q_en
     return (int32_t)((visible + FWD_BN - 1) / FWD_BN);
 }
 
-// Relative cost of a task: its key tiles plus one for the fixed per-workgroup
-// work (Q load, pipeline fill, epilogue).
-int64_t task_work(const WorkItem &it) { return (int64_t)it.kv_tiles + 1; }
+// Relative cost of a task over key tiles [kt0, kt1): its tiles plus one for
+// the fixed per-workgroup work (Q load, pipeline fill, epilogue).
+int64_t tiles_work(int32_t kt0, int32_t kt1) { return (int64_t)(kt1 - kt0) + 1; }
+
+// A run of key tiles [kt0, kt1) of one work item; piece k of n of the item
+// (n = 1: the whole item).
+struct Piece {
+    int32_t item, kt0, kt1, k, n;
+};
 
 struct Plan {
     std::vector<SeqRec> seqs;
     std::vector<WorkItem> items;
     std::vector<Task> tasks;  // one per workgroup, in launch order
+    std::vector<MergeRec> merges;  // one per (split item, head pack)
+    int32_t n_parts = 0;           // partial slots of the split tasks
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // Host view of the work list (mla_prefill_plan_host): batch records, items,
-// tasks, each array on a 256-byte boundary.
+// tasks {item, first head, first tile, end tile}, each array on a 256-byte
+// boundary.
+constexpr uint64_t VIEW_TASK_BYTES = 16;
 uint64_t items_offset(const Plan &p) { return align256(p.seqs.size() * sizeof(SeqRec)); }
 uint64_t tasks_offset(const Plan &p) { return items_offset(p) + align256(p.items.size() * sizeof(WorkItem)); }
 
 uint64_t view_bytes(const Plan &p) {
     if (p.items.empty()) return 0;
-    return tasks_offset(p) + p.tasks.size() * sizeof(Task);
+    return tasks_offset(p) + p.tasks.size() * VIEW_TASK_BYTES;
 }
 
-// Device workspace: one LaunchRec per workgroup.
-uint64_t plan_bytes(const Plan &p) {
+// Device workspace: one LaunchRec per workgroup; with split items, then the
+// merge records, the partial log-sum-exps and the partial rows, each on a
+// 256-byte boundary.
+uint64_t merges_offset(const Plan &p) { return align256(p.tasks.size() * sizeof(mla::LaunchRec)); }
+uint64_t lse_offset(const Plan &p) { return merges_offset(p) + align256(p.merges.size() * sizeof(MergeRec)); }
+uint64_t part_o_offset(const Plan &p) { return lse_offset(p) + align256((uint64_t)p.n_parts * PART_ROWS * 4); }
+// bytes of the records copied from the host
+uint64_t records_bytes(const Plan &p) {
+    if (p.merges.empty()) return p.tasks.size() * sizeof(mla::LaunchRec);
+    return merges_offset(p) + p.merges.size() * sizeof(MergeRec);
+}
+uint64_t plan_bytes(const Plan &p, int64_t head_dim) {
     if (p.items.empty()) return 0;
-    return p.tasks.size() * sizeof(mla::LaunchRec);
+    if (p.n_parts == 0) return records_bytes(p);
+    return part_o_offset(p) + (uint64_t)p.n_parts * PART_ROWS * (uint64_t)head_dim * 4;
 }
 
 // log2 of the query heads one task runs: the largest power of two, at most
@@ -372,8 +404,24 @@ int32_t pack_shift_for(int32_t heads, int32_t kv_heads) {
 // Work list.
 //  * Items: one per FWD_BM >> pack_shift query rows of each sequence, with the
 //    number of key tiles its rows can see.
-//  * Tasks: one workgroup each, an item for 2^pack_shift consecutive query
-//    heads of one KV head (its rows of each of them).
+//  * Split items (contiguous K/V only, allow_split): when the launch holds
+//    little work for the CUs -- few heads, few sequences -- the longest items
+//    would set its duration alone. Let W be the work of all tasks (tiles plus
+//    TASK_FIXED_TILES each) spread evenly over the CUs. If the longest item
+//    has more than 1.5 W tiles, every item with more than
+//    max(W, SPLIT_MIN_TILES) tiles is cut into runs of at most about that
+//    many consecutive key tiles (at multiples of 512 keys under MASK_FREE,
+//    so the tile's blocks stay aligned), each a task of its own. Such a task
+//    writes its rows over its own keys with their log-sum-exp into a partial
+//    slot, and a merge kernel combines the pieces of each (item, head pack)
+//    afterwards. (The part runs at a power-limited clock: once every CU has
+//    work, evening out the tasks mostly trades idle CUs for a lower clock,
+//    and the partial rows and the merge cost more than they save. Measured
+//    at 4096 causal rows: 8 heads 105 -> 80 us, 16 heads 129 -> 124 us, 24
+//    heads 140 -> 170 us, so 24 heads, whose longest item is 1.2 W, is not
+//    split.)
+//  * Tasks: one workgroup each, a piece (or all) of an item for 2^pack_shift
+//    consecutive query heads of one KV head (its rows of each of them).
 //  * Launch order. Tasks that read the same K/V stream (same sequence and KV
 //    head) form a group. Groups are dealt, heaviest first, to the XCD queue
 //    with the least work so far. If that leaves an XCD more than 5% above the
@@ -391,21 +439,17 @@ int32_t pack_shift_for(int32_t heads, int32_t kv_heads) {
 //    XCD's CUs evenly loaded to the end. Short queues are padded with empty
 //    tasks.
 void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch, int32_t heads,
-                int32_t kv_heads, int mask_type, int64_t kv_padded_max_seq, Plan *plan) {
+                int32_t kv_heads, int mask_type, int64_t kv_padded_max_seq, bool allow_split, Plan *plan) {
     plan->seqs.resize(batch);
     plan->items.clear();
     plan->tasks.clear();
+    plan->merges.clear();
+    plan->n_parts = 0;
     const int32_t group = kv_heads > 0 ? heads / kv_heads : 1;
     const int32_t ps = pack_shift_for(heads, kv_heads);
     const int32_t rows = FWD_BM >> ps;
     const int32_t tasks_per_item = group >> ps;
-    struct Group {
-        int64_t work;
-        int32_t b, hk;
-        int32_t t0, t1;  // tasks [t0, t1) of the group: task t = item t / tasks_per_item, head pack t % tasks_per_item
-    };
-    std::vector<Group> groups;
-    std::vector<int32_t> seq_first(batch + 1, 0);  // items of sequence b: [seq_first[b], seq_first[b+1])
+    std::vector<int32_t> seq_item_first(batch + 1, 0);  // items of sequence b: [seq_item_first[b], .. [b + 1])
     int64_t q_off = 0, kv_off = 0;
     for (int32_t b = 0; b < batch; ++b) {
         SeqRec &s = plan->seqs[b];
@@ -415,19 +459,96 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         s.kv_len = kv_seqlen[b];
         q_off += s.q_len;
         kv_off += s.kv_len;
-        seq_first[b] = (int32_t)plan->items.size();
-        int64_t seq_work = 0;
+        seq_item_first[b] = (int32_t)plan->items.size();
         for (int32_t r = 0; r < s.q_len; r += rows) {
             int32_t q_end = std::min(s.q_len, r + rows);
-            WorkItem it{b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), rows};
-            seq_work += task_work(it);
-            plan->items.push_back(it);
+            plan->items.push_back(WorkItem{b, r, visible_tiles(mask_type, s.q_len, s.kv_len, q_end), rows});
         }
-        const int32_t n_tasks = ((int32_t)plan->items.size() - seq_first[b]) * tasks_per_item;
+    }
+    seq_item_first[batch] = (int32_t)plan->items.size();
+    // pieces of each item, in item order (so each sequence's are consecutive)
+    int32_t cap = INT32_MAX;  // longest piece
+    const int32_t gran = mask_type == MLA_MASK_FREE ? MASK_TILE / FWD_BN : 1;
+    if (allow_split) {
+        int64_t total = 0, longest = 0;
+        for (const WorkItem &it : plan->items) {
+            total += ((int64_t)it.kv_tiles + TASK_FIXED_TILES);
+            longest = std::max<int64_t>(longest, it.kv_tiles);
+        }
+        total *= (int64_t)kv_heads * tasks_per_item;
+        const int64_t cus = (int64_t)MLA_XCDS * MLA_CUS_PER_XCD;
+        const int64_t share = (total + cus - 1) / cus;
+        if (2 * longest > 3 * share)
+            cap = (int32_t)std::min<int64_t>(INT32_MAX,
+                                             std::max<int64_t>(SPLIT_MIN_TILES, share * SPLIT_SHARE_PERCENT / 100));
+    }
+    std::vector<Piece> pieces;
+    std::vector<int32_t> seq_piece_first(batch + 1, 0);  // pieces of sequence b: [seq_piece_first[b], .. [b + 1])
+    std::vector<int32_t> item_part_base(plan->items.size(), -1), item_pieces(plan->items.size(), 1);
+    for (int32_t b = 0; b < batch; ++b) {
+        seq_piece_first[b] = (int32_t)pieces.size();
+        for (int32_t i = seq_item_first[b]; i < seq_item_first[b + 1]; ++i) {
+            const int32_t nt = plan->items[i].kv_tiles;
+            // cut points k * nt / n, rounded down to the granularity and kept increasing
+            std::vector<int32_t> cuts{0};
+            const int32_t want = nt > cap ? (nt + cap - 1) / cap : 1;
+            for (int32_t k = 1; k < want; ++k) {
+                const int32_t c = (int32_t)((int64_t)nt * k / want) / gran * gran;
+                if (c > cuts.back() && c < nt) cuts.push_back(c);
+            }
+            cuts.push_back(nt);
+            const int32_t n = (int32_t)cuts.size() - 1;
+            item_pieces[i] = n;
+            if (n > 1) {
+                item_part_base[i] = plan->n_parts;
+                plan->n_parts += n * kv_heads * tasks_per_item;
+            }
+            for (int32_t k = 0; k < n; ++k) pieces.push_back(Piece{i, cuts[k], cuts[k + 1], k, n});
+        }
+    }
+    seq_piece_first[batch] = (int32_t)pieces.size();
+    // merge records: (item, KV head, head pack) in the order of their partial slots
+    for (int32_t i = 0; i < (int32_t)plan->items.size(); ++i) {
+        if (item_part_base[i] < 0) continue;
+        const WorkItem &it = plan->items[i];
+        const SeqRec &sq = plan->seqs[it.b];
+        const int32_t n = item_pieces[i];
+        for (int32_t hk = 0; hk < kv_heads; ++hk)
+            for (int32_t pk = 0; pk < tasks_per_item; ++pk) {
+                MergeRec m{};
+                m.part0 = item_part_base[i] + (hk * tasks_per_item + pk) * n;
+                m.n_parts = n;
+                m.head = hk * group + pk * (1 << ps);
+                m.q_tok0 = sq.q_off + it.q_row0;
+                m.q_left = sq.q_len - it.q_row0;
+                plan->merges.push_back(m);
+            }
+    }
+    // the task of group slot t (t < group's piece count * tasks_per_item)
+    auto make_task = [&](int32_t b, int32_t hk, int32_t t) -> Task {
+        const Piece &pc = pieces[seq_piece_first[b] + t / tasks_per_item];
+        const int32_t pk = t % tasks_per_item;
+        const int32_t part = pc.n > 1 ? item_part_base[pc.item] + (hk * tasks_per_item + pk) * pc.n + pc.k : -1;
+        return Task{pc.item, hk * group + pk * (1 << ps), pc.kt0, pc.kt1, part};
+    };
+    auto slot_work = [&](int32_t b, int32_t t) -> int64_t {
+        const Piece &pc = pieces[seq_piece_first[b] + t / tasks_per_item];
+        return tiles_work(pc.kt0, pc.kt1);
+    };
+    struct Group {
+        int64_t work;
+        int32_t b, hk;
+        int32_t t0, t1;  // tasks [t0, t1) of the group: task t = piece t / tasks_per_item, head pack t % tasks_per_item
+    };
+    std::vector<Group> groups;
+    for (int32_t b = 0; b < batch; ++b) {
+        int64_t seq_work = 0;
+        for (int32_t j = seq_piece_first[b]; j < seq_piece_first[b + 1]; ++j)
+            seq_work += tiles_work(pieces[j].kt0, pieces[j].kt1);
+        const int32_t n_tasks = (seq_piece_first[b + 1] - seq_piece_first[b]) * tasks_per_item;
         if (seq_work > 0)
             for (int32_t hk = 0; hk < kv_heads; ++hk) groups.push_back({seq_work * tasks_per_item, b, hk, 0, n_tasks});
     }
-    seq_first[batch] = (int32_t)plan->items.size();
     std::vector<std::vector<Group>> xcd_groups;
     std::vector<int64_t> load;
     auto deal = [&]() {
@@ -447,18 +568,18 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
     // sequence), cut groups heavier than 1/32 of the total into consecutive
     // pieces and deal again.
     if (20 * MLA_XCDS * *std::max_element(load.begin(), load.end()) > 21 * total) {
-        const int64_t cap = std::max<int64_t>(1, (total + 4 * MLA_XCDS - 1) / (4 * MLA_XCDS));
+        const int64_t gcap = std::max<int64_t>(1, (total + 4 * MLA_XCDS - 1) / (4 * MLA_XCDS));
         std::vector<Group> cut;
         for (const Group &gr : groups) {
-            if (gr.work <= cap) {
+            if (gr.work <= gcap) {
                 cut.push_back(gr);
                 continue;
             }
             Group piece{0, gr.b, gr.hk, gr.t0, gr.t0};
             for (int32_t t = gr.t0; t < gr.t1; ++t) {
-                piece.work += task_work(plan->items[seq_first[gr.b] + t / tasks_per_item]);
+                piece.work += slot_work(gr.b, t);
                 piece.t1 = t + 1;
-                if (piece.work >= cap || t + 1 == gr.t1) {
+                if (piece.work >= gcap || t + 1 == gr.t1) {
                     cut.push_back(piece);
                     piece = Group{0, gr.b, gr.hk, t + 1, t + 1};
                 }
@@ -479,7 +600,7 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         for (const Group &gr : groups) {
             int64_t lo = INT64_MAX, hi = 0;
             for (int32_t t = gr.t0; t < gr.t1; ++t) {
-                const int64_t w = task_work(plan->items[seq_first[gr.b] + t / tasks_per_item]);
+                const int64_t w = slot_work(gr.b, t);
                 lo = std::min(lo, w);
                 hi = std::max(hi, w);
             }
@@ -492,21 +613,20 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
     for (int x = 0; x < MLA_XCDS; ++x) {
         auto flush = [&]() {
             std::stable_sort(pending.begin(), pending.end(), [&](const Task &u, const Task &v) {
-                return task_work(plan->items[u.item]) > task_work(plan->items[v.item]);
+                return tiles_work(u.kt0, u.kt1) > tiles_work(v.kt0, v.kt1);
             });
             queue[x].insert(queue[x].end(), pending.begin(), pending.end());
             pending.clear();
         };
         for (const Group &gr : xcd_groups[x]) {
-            for (int32_t t = gr.t0; t < gr.t1; ++t)
-                pending.push_back({seq_first[gr.b] + t / tasks_per_item, gr.hk * group + (t % tasks_per_item) * (1 << ps)});
+            for (int32_t t = gr.t0; t < gr.t1; ++t) pending.push_back(make_task(gr.b, gr.hk, t));
             if (pending.size() >= batch_tasks) flush();
         }
         flush();
     }
     size_t longest = 0;
     for (const auto &q : queue) longest = std::max(longest, q.size());
-    plan->tasks.assign(longest * MLA_XCDS, Task{-1, 0});
+    plan->tasks.assign(longest * MLA_XCDS, Task{-1, 0, 0, 0, -1});
     for (int x = 0; x < MLA_XCDS; ++x)
         for (size_t k = 0; k < queue[x].size(); ++k) plan->tasks[k * MLA_XCDS + x] = queue[x][k];
 }
@@ -514,29 +634,39 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
 void write_plan_view(const Plan &p, uint8_t *dst) {
     std::memcpy(dst, p.seqs.data(), p.seqs.size() * sizeof(SeqRec));
     std::memcpy(dst + items_offset(p), p.items.data(), p.items.size() * sizeof(WorkItem));
-    std::memcpy(dst + tasks_offset(p), p.tasks.data(), p.tasks.size() * sizeof(Task));
+    int32_t *t = reinterpret_cast<int32_t *>(dst + tasks_offset(p));
+    for (const Task &x : p.tasks) {
+        t[0] = x.item;
+        t[1] = x.head;
+        t[2] = x.kt0;
+        t[3] = x.kt1;
+        t += VIEW_TASK_BYTES / 4;
+    }
 }
 
 // The launch records the kernel reads: each task with its item and sequence
 // folded in. Paged K/V carry the sequence index (its block-table row) where
-// contiguous K/V carry the sequence's first key row.
+// contiguous K/V carry the row of the task's first key (pieces of a split
+// item start at key kt0 * FWD_BN; paged plans are never split).
 void write_launch(const Plan &p, int32_t group, bool paged, mla::LaunchRec *dst) {
     for (size_t i = 0; i < p.tasks.size(); ++i) {
         const Task &t = p.tasks[i];
         mla::LaunchRec r{};
         if (t.item < 0) {
             r.head = -1;
+            r.part = -1;
         } else {
             const WorkItem &it = p.items[t.item];
             const SeqRec &sq = p.seqs[it.b];
-            r.q_row0 = it.q_row0;
-            r.kv_tiles = it.kv_tiles;
+            const int32_t k0 = t.kt0 * FWD_BN;
+            r.q_tok0 = sq.q_off + it.q_row0;
+            r.q_left = sq.q_len - it.q_row0;
+            r.kv_tiles = t.kt1 - t.kt0;
             r.head = t.head;
             r.kv_head = t.head / group;
-            r.q_off = sq.q_off;
-            r.kv_off = paged ? it.b : sq.kv_off;
-            r.q_len = sq.q_len;
-            r.kv_len = sq.kv_len;
+            r.kv_off = paged ? it.b : sq.kv_off + k0;
+            r.kv_len = sq.kv_len - k0;
+            r.part = t.part;
         }
         dst[i] = r;
     }
@@ -582,10 +712,12 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
                     const mla_tensor *q_rope, const void *k, const void *k_rope, const void *v,
                     const mla_tensor *mask, float qk_scale, const mla_tensor *atten_out, void *workspace,
                     uint64_t workspace_size, bool use_scratch, void *stream) {
+    // Items are split only where the workspace is the caller's (not the fixed
+    // array of mla_prefill_no_alloc) and the K/V are contiguous.
     Plan plan;
     build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
-               &plan);
-    const uint64_t need = plan_bytes(plan);
+               !use_scratch && pg == nullptr, &plan);
+    const uint64_t need = plan_bytes(plan, pr.head_dim);
     if (need == 0) return ok();  // no query rows: nothing to write
     if (use_scratch) {
         if (need > MLA_NO_ALLOC_WORKSPACE_BYTES)
@@ -604,11 +736,15 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
         return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     if (plan.tasks.size() > (size_t)INT32_MAX) return fail(MLA_ERR_UNSUPPORTED, "too many work items");
 
-    std::vector<mla::LaunchRec> host(plan.tasks.size());
-    write_launch(plan, pr.heads / pr.kv_heads, pg != nullptr, host.data());
+    const uint64_t rec_bytes = records_bytes(plan);
+    std::vector<uint8_t> host(rec_bytes);
+    write_launch(plan, pr.heads / pr.kv_heads, pg != nullptr, reinterpret_cast<mla::LaunchRec *>(host.data()));
+    if (!plan.merges.empty())
+        std::memcpy(host.data() + merges_offset(plan), plan.merges.data(), plan.merges.size() * sizeof(MergeRec));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(workspace, host.data(), need, hipMemcpyHostToDevice, s);
+    hipError_t e = hipMemcpyAsync(workspace, host.data(), rec_bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "hipMemcpyAsync: %s", hipGetErrorString(e));
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
 
     mla::FwdParams p{};
     p.q = q->data;
@@ -619,6 +755,10 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.mask = (pr.mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
     p.out = atten_out->data;
     p.launch = static_cast<const mla::LaunchRec *>(workspace);
+    if (plan.n_parts > 0) {
+        p.part_lse = reinterpret_cast<float *>(ws + lse_offset(plan));
+        p.part_o = reinterpret_cast<float *>(ws + part_o_offset(plan));
+    }
     p.heads = pr.heads;
     p.kv_heads = pr.kv_heads;
     p.group = pr.heads / pr.kv_heads;
@@ -636,6 +776,19 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     }
     e = mla::launch_mla_fwd(p, pr.dtype, pg != nullptr, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "attention launch: %s", hipGetErrorString(e));
+    if (!plan.merges.empty()) {
+        mla::MergeParams mp{};
+        mp.merges = reinterpret_cast<const MergeRec *>(ws + merges_offset(plan));
+        mp.part_o = p.part_o;
+        mp.part_lse = p.part_lse;
+        mp.out = atten_out->data;
+        mp.n_merges = (int32_t)plan.merges.size();
+        mp.heads = pr.heads;
+        mp.pack_shift = p.pack_shift;
+        mp.head_dim = p.head_dim;
+        e = mla::launch_mla_merge(mp, pr.dtype, s);
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "merge launch: %s", hipGetErrorString(e));
+    }
     return ok();
 }
 
@@ -802,7 +955,7 @@ int mla_prefill_plan_host(const int32_t *q_seqlen, const int32_t *kv_seqlen, int
     for (int32_t b = 0; b < batch; ++b)
         if (q_seqlen[b] < 0 || kv_seqlen[b] < 0) return fail(MLA_ERR_VALUE, "negative length");
     Plan plan;
-    build_plan(q_seqlen, kv_seqlen, batch, head_num, kv_head_num, mask_type, kv_padded_max_seq, &plan);
+    build_plan(q_seqlen, kv_seqlen, batch, head_num, kv_head_num, mask_type, kv_padded_max_seq, true, &plan);
     *n_items = (int32_t)plan.items.size();
     *n_tasks = (int32_t)plan.tasks.size();
     uint64_t need = view_bytes(plan);
@@ -828,8 +981,8 @@ int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope
     if (rc) return rc;
     Plan plan;
     build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
-               &plan);
-    *workspace_size = plan_bytes(plan);
+               true, &plan);
+    *workspace_size = plan_bytes(plan, pr.head_dim);
     return ok();
 }
 
@@ -874,8 +1027,8 @@ int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *
                             mask, head_num, qk_scale, kv_head_num, mask_type, atten_out, &pr, &pg);
     if (rc) return rc;
     Plan plan;
-    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, 0, &plan);
-    *workspace_size = plan_bytes(plan);
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, 0, false, &plan);
+    *workspace_size = plan_bytes(plan, pr.head_dim);
     return ok();
 }
 

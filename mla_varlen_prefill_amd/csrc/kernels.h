@@ -37,12 +37,16 @@ struct WorkItem {
     int32_t q_rows;
 };
 
-// One workgroup's task: a work item and its first query head (the task runs
-// heads head .. head + 2^pack_shift - 1). item == -1 marks an empty padding
-// task.
+// One workgroup's task: key tiles [kt0, kt1) of a work item for its query
+// heads head .. head + 2^pack_shift - 1. A task holding only part of the
+// item's tiles writes a partial result into partial slot `part` (-1: the task
+// holds all of them and writes the output). item == -1 marks an empty
+// padding task.
 struct Task {
     int32_t item;
     int32_t head;
+    int32_t kt0, kt1;
+    int32_t part;
 };
 
 // MI355X: 8 XCDs of 32 CUs; consecutive workgroups of a launch go to
@@ -54,16 +58,40 @@ constexpr int MLA_CUS_PER_XCD = 32;
 // kernel reads it with a single scalar load: a work item (q rows of one
 // sequence) for 2^pack_shift query heads from `head`. head == -1 marks an
 // empty padding workgroup.
+// A task over key tiles [kt0, kt1) of its item is run as the item over the
+// sequence's keys from kt0 * FWD_BN on: kv_off and kv_len are shifted by that
+// many keys, which leaves every row's causal position relative to the keys
+// unchanged (position - k0 = (kv_len - k0) - rows + row), and, since the
+// planner cuts only at multiples of 512 keys under MASK_FREE, its 512-key
+// blocks too.
 struct LaunchRec {
-    int32_t q_row0;    // first query row of the item within its sequence
-    int32_t kv_tiles;  // FWD_BN-key tiles (from key 0) any of its rows can see
+    int32_t q_tok0;    // first query row of the item in Q / attenOut (sequence offset + row in the sequence)
+    int32_t kv_tiles;  // FWD_BN-key tiles (from the task's first key) any of its rows can see
     int32_t head;      // first query head; -1: padding
     int32_t kv_head;   // the KV head of those query heads
-    int32_t q_off;     // first row of the sequence in Q / attenOut
-    int32_t kv_off;    // contiguous K/V: first key row of the sequence; paged: the sequence index
-    int32_t q_len;
-    int32_t kv_len;
+    int32_t q_left;    // query rows of the sequence from the item's first row on
+    int32_t kv_off;    // contiguous K/V: row of the task's first key; paged: the sequence index
+    int32_t kv_len;    // keys of the sequence from the task's first key on
+    int32_t part;      // -1: write attenOut; else the partial slot (normalised fp32 rows and log-sum-exp)
 };
+static_assert(sizeof(LaunchRec) == 32, "one scalar load per workgroup");
+
+// Partial results of tasks holding part of an item's key tiles: slot s holds,
+// for each of the FWD_BM wave rows (wave slot w = 0..7, row r = 0..31, the
+// kernel's row order), the row's attention output over the task's keys
+// alone in fp32 (head_dim values) and the log-sum-exp of its scaled, masked
+// scores over those keys (-inf: no visible key among them). The merge
+// combines the n_parts slots part0.. of one (item, head pack) into attenOut.
+struct MergeRec {
+    int32_t part0;
+    int32_t n_parts;
+    int32_t head;    // first query head
+    int32_t q_tok0;  // as in LaunchRec
+    int32_t q_left;
+    int32_t pad[3];
+};
+static_assert(sizeof(MergeRec) == 32, "merge record size");
+constexpr int PART_ROWS = FWD_BM;
 
 struct FwdParams {
     const void *q;        // [nq, H, D]
@@ -74,6 +102,8 @@ struct FwdParams {
     const void *mask;     // [512, 512] or nullptr
     void *out;            // [nq, H, D]
     const LaunchRec *launch;  // one record per workgroup
+    float *part_o;            // partial rows: [parts, PART_ROWS, head_dim] fp32 (tasks with part >= 0)
+    float *part_lse;          // [parts, PART_ROWS]
     int32_t heads;
     int32_t kv_heads;
     int32_t group;        // heads / kv_heads
@@ -98,6 +128,20 @@ constexpr int PAGED_MAX_TILES = 2048;
 
 // dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). One workgroup per task.
 hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream);
+
+struct MergeParams {
+    const MergeRec *merges;
+    const float *part_o;
+    const float *part_lse;
+    void *out;  // attenOut [nq, heads, head_dim]
+    int32_t n_merges;
+    int32_t heads;
+    int32_t pack_shift;
+    int32_t head_dim;
+};
+
+// Combine the partial results of split tasks into attenOut (dtype as above).
+hipError_t launch_mla_merge(const MergeParams &p, int dtype, hipStream_t stream);
 
 struct GatherParams {
     const void *key_cache;

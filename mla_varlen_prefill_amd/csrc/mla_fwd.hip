@@ -286,17 +286,15 @@ void mla_fwd_kernel(const FwdParams p) {
     const int h = task.head + (slot & ((1 << ps) - 1));
     const int hk = task.kv_head;
     const int H = p.heads, HKV = p.kv_heads;
-    const int q_len = task.q_len;
+    const int q_left = task.q_left;  // rows of the sequence from the item's first row on
     const int kv_len = task.kv_len;
     const int n_kt = task.kv_tiles;
     const int mask_type = MF ? MASK_FREE : p.mask_type;
     const bool causal_like = !MF && mask_type != MASK_UNDEFINED;
 
     const int lrow0 = (slot >> ps) * 32;            // first row of this wave within the item
-    const int row0 = task.q_row0 + lrow0;           // ... within the sequence
-    const int qi = row0 + r32;                      // this lane's query row
-    const int pos = kv_len - q_len + qi;            // its key position
-    const int wpos0 = kv_len - q_len + row0;        // key positions of the wave's rows
+    const int wpos0 = kv_len - q_left + lrow0;      // key positions of the wave's rows
+    const int pos = wpos0 + r32;                    // ... and of this lane's row
     const int wpos1 = wpos0 + 31;
 
     // ---- Q and Q-rope of the wave's 32 rows go HBM -> LDS by DMA, whole rows
@@ -310,8 +308,8 @@ void mla_fwd_kernel(const FwdParams p) {
     constexpr int QN_CPR = DN / 8;             // 16-byte chunks of a Q-nope row
     unsigned char *qslot = smem + Geom<DN>::qslot_offset(grp, wave & 3);
     {
-        const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)task.q_off + row0;
+        const int rows = max(0, min(32, q_left - lrow0));
+        const int64_t tok = (int64_t)task.q_tok0 + lrow0;
         const i32x4 rq = make_rsrc(static_cast<const unsigned char *>(p.q) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
         const i32x4 rr = make_rsrc(static_cast<const unsigned char *>(p.q_rope) + (tok * H + h) * (DR * 2),
@@ -998,6 +996,24 @@ void mla_fwd_kernel(const FwdParams p) {
     const float l_tot = sum_with_partner(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    if (task.part >= 0) {
+        // The task holds part of the item's keys: its rows over those keys in
+        // fp32, and their log-sum-exp (the running max is in natural-log
+        // units and the row sum is taken relative to it), for the merge. Both
+        // lanes of a row hold 4 consecutive values of each 8-value group.
+        const int64_t prow = ((int64_t)task.part * 8 + slot) * 32 + r32;
+        float *po = p.part_o + prow * DN;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 v = {o[db][4 * i] * inv, o[db][4 * i + 1] * inv, o[db][4 * i + 2] * inv,
+                                  o[db][4 * i + 3] * inv};
+                *reinterpret_cast<float4 *>(po + db * 32 + i * 8 + g * 4) = v;
+            }
+        if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + logf(l_tot) : -INFINITY;
+        return;
+    }
     {
         const int w4 = wave & 3;
         unsigned char *stg =
@@ -1016,8 +1032,8 @@ void mla_fwd_kernel(const FwdParams p) {
                 *reinterpret_cast<typename T::vec4 *>(stg + r32 * KN_ROW +
                                                       (((4 * db + i) ^ row_swizzle<DN>(r32)) << 4) + g * 8) = v4;
             }
-        const int rows = max(0, min(32, q_len - row0));
-        const int64_t tok = (int64_t)task.q_off + row0;
+        const int rows = max(0, min(32, q_left - lrow0));
+        const int64_t tok = (int64_t)task.q_tok0 + lrow0;
         const i32x4 ro = make_rsrc(static_cast<unsigned char *>(p.out) + (tok * H + h) * (DN * 2),
                                    (uint32_t)rows * H * DN * 2);
         constexpr int CPR = DN / 8;      // 16-byte chunks of a row
@@ -1032,7 +1048,94 @@ void mla_fwd_kernel(const FwdParams p) {
     }
 }
 
+// ---- merge of split tasks: attenOut row = sum_i w_i O_i / sum_i w_i with
+// w_i = exp(lse_i - max_j lse_j), over the partial results O_i (each
+// normalised over its own keys) of one row; a row no part sees gives 0. The
+// sum is taken in one pass, rescaled whenever a larger lse arrives, so that
+// the loads of several parts can be in flight together. A workgroup takes
+// 256 / (DN / 4) rows of one wave slot of one merge record, DN / 4 lanes per
+// row, 4 values per lane.
+template <int DN>
+struct MergeShape {
+    static constexpr int LPR = DN / 4;          // lanes per row
+    static constexpr int RPB = 256 / LPR;       // rows per workgroup
+    static constexpr int BPS = 32 / RPB;        // workgroups per wave slot
+};
+
+template <typename T, int DN>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_merge_kernel(const MergeParams p) {
+    typedef MergeShape<DN> S;
+    const MergeRec m = p.merges[blockIdx.x / (8 * S::BPS)];
+    const int sub = blockIdx.x % (8 * S::BPS);
+    const int slot = sub / S::BPS;
+    const int ps = p.pack_shift;
+    const int h = m.head + (slot & ((1 << ps) - 1));
+    const int lrow0 = (slot >> ps) * 32;
+    const int r = (sub % S::BPS) * S::RPB + (int)threadIdx.x / S::LPR;  // row of the wave slot
+    if (r >= m.q_left - lrow0) return;
+    const int c = threadIdx.x % S::LPR;
+    const int64_t row0 = ((int64_t)m.part0 * 8 + slot) * 32 + r;  // partial row of part 0
+    constexpr int64_t PSTRIDE = 8 * 32;                          // rows between consecutive parts
+    float mx = -INFINITY, wsum = 0.f;
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+    auto add = [&](float li, float4 v) {
+        if (li > mx) {
+            const float sc = expf(mx - li);  // 0 while mx is -inf
+            wsum *= sc;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[k] *= sc;
+            mx = li;
+        }
+        if (li > -INFINITY) {
+            const float w = expf(li - mx);
+            wsum += w;
+            a[0] += w * v.x;
+            a[1] += w * v.y;
+            a[2] += w * v.z;
+            a[3] += w * v.w;
+        }
+    };
+    int i = 0;
+    for (; i + 4 <= m.n_parts; i += 4) {
+        float li[4];
+        float4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t pr = row0 + (int64_t)(i + k) * PSTRIDE;
+            li[k] = p.part_lse[pr];
+            v[k] = *reinterpret_cast<const float4 *>(p.part_o + pr * DN + 4 * c);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) add(li[k], v[k]);
+    }
+    for (; i < m.n_parts; ++i) {
+        const int64_t pr = row0 + (int64_t)i * PSTRIDE;
+        add(p.part_lse[pr], *reinterpret_cast<const float4 *>(p.part_o + pr * DN + 4 * c));
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    typename T::vec4 o4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o4[k] = static_cast<typename T::scalar>(a[k] * inv);
+    const int64_t tok = (int64_t)m.q_tok0 + lrow0 + r;
+    *reinterpret_cast<typename T::vec4 *>(static_cast<unsigned char *>(p.out) +
+                                          ((tok * p.heads + h) * DN + 4 * c) * 2) = o4;
+}
+
 }  // namespace
+
+hipError_t launch_mla_merge(const MergeParams &p, int dtype, hipStream_t stream) {
+    if (p.n_merges <= 0) return hipSuccess;
+    const unsigned per_rec = 8u * (p.head_dim == 64 ? MergeShape<64>::BPS : MergeShape<128>::BPS);
+    dim3 grid((unsigned)p.n_merges * per_rec), block(256);
+    if (p.head_dim == 64) {
+        if (dtype == 2) hipLaunchKernelGGL((mla_merge_kernel<Bf16, 64>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mla_merge_kernel<Fp16, 64>), grid, block, 0, stream, p);
+    } else {
+        if (dtype == 2) hipLaunchKernelGGL((mla_merge_kernel<Bf16, 128>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((mla_merge_kernel<Fp16, 128>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream) {
     if (p.n_tasks <= 0) return hipSuccess;

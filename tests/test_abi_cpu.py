@@ -354,11 +354,24 @@ def heads_per_task(heads, kv_heads):
     return p
 
 
+def split_cap(items, heads, kv_heads):
+    """Longest run of key tiles a task may hold: an even share W of the work
+    (tiles plus 2 per task) over the 256 compute units, at least 16 tiles;
+    unbounded unless the longest item exceeds 1.5 W."""
+    pack = heads_per_task(heads, kv_heads)
+    total = sum(int(nt) + 2 for _, _, nt, _ in items) * (heads // pack)
+    share = -(-total // 256)
+    if 2 * max(int(nt) for _, _, nt, _ in items) <= 3 * share:
+        return 1 << 40
+    return max(16, share)
+
+
 @pytest.mark.parametrize("mask_type", [0, 1, 2, 3])
 @pytest.mark.parametrize("case", [([17, 40], [17, 40], 4, 4), ([300, 1, 0, 129], [1000, 1, 5, 100], 8, 2),
                                   ([2048] * 3, [16384] * 3, 16, 16), ([700], [100], 2, 1),
                                   ([100, 33], [100, 260], 12, 4), ([513, 64], [600, 64], 32, 2),
-                                  ([70], [70], 16, 1)])
+                                  ([70], [70], 16, 1), ([4096], [4096], 16, 16), ([3000, 5], [5000, 700], 2, 1),
+                                  ([1500, 2500], [1500, 9000], 8, 8)])
 def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
     qs, ks, heads, kv_heads = case
     pack = heads_per_task(heads, kv_heads)
@@ -377,22 +390,38 @@ def test_plan_covers_every_row_once_with_exact_tile_ranges(case, mask_type):
         ql, kl = qs[b], ks[b]
         far = max(visible_count(mask_type, ql, kl, i) for i in range(r, min(ql, r + rows)))
         assert nt == -(-far // mla.PLAN_KV_COLS), (b, r)
-    # every (item, head) is covered by exactly one task; the heads of a task
-    # share one kv head; the rest is padding
+    # every (item, head) is covered by its tasks' key-tile runs exactly once:
+    # one task over [0, kv_tiles), or consecutive runs of at most the even
+    # share of the work (cut at 512-key multiples under MASK_FREE) when the
+    # item is longer than that; the heads of a task share one kv head; the
+    # rest is padding
     real = tasks[tasks[:, 0] >= 0]
-    covered = sorted((i, h0 + k) for i, h0 in real.tolist() for k in range(pack))
-    assert covered == sorted((i, h) for i in range(len(items)) for h in range(heads))
+    runs = {}
+    for i, h0, k0, k1 in real.tolist():
+        for k in range(pack):
+            runs.setdefault((i, h0 + k), []).append((k0, k1))
+    assert sorted(runs) == sorted((i, h) for i in range(len(items)) for h in range(heads))
+    cap = split_cap(items, heads, kv_heads)
+    gran = 8 if mask_type == mla.MASK_FREE else 1
+    for (i, h), rs in runs.items():
+        rs.sort()
+        nt = int(items[i][2])
+        assert rs[0][0] == 0 and rs[-1][1] == nt and all(a[1] == b[0] for a, b in zip(rs, rs[1:])), (i, h, rs)
+        if nt <= cap:
+            assert rs == [(0, nt)], (i, h, rs, cap)
+        else:
+            assert len(rs) >= 2 and all(0 < k1 - k0 <= cap + gran - 1 and k0 % gran == 0 for k0, k1 in rs), rs
     g = heads // kv_heads
-    assert all(h0 % pack == 0 and h0 // g == (h0 + pack - 1) // g for _, h0 in real.tolist())
+    assert all(h0 % pack == 0 and h0 // g == (h0 + pack - 1) // g for _, h0, _, _ in real.tolist())
     assert len(tasks) % 8 == 0
     # the tasks reading one K/V stream (sequence, kv head) sit on one XCD (task
     # index mod 8), unless the stream holds more than 1/32 of all work
     stream_work, xcds = {}, {}
-    for i, (it, h) in enumerate(tasks.tolist()):
+    for i, (it, h, k0, k1) in enumerate(tasks.tolist()):
         if it < 0:
             continue
         key = (int(items[it][0]), h // (heads // kv_heads))
-        stream_work[key] = stream_work.get(key, 0) + items[it][2] + 1
+        stream_work[key] = stream_work.get(key, 0) + k1 - k0 + 1
         xcds.setdefault(key, set()).add(i % 8)
     total = sum(stream_work.values())
     for key, w in stream_work.items():
@@ -404,10 +433,13 @@ def test_plan_balances_xcds_on_causal_workload():
     """4096-token causal prefill with 128 heads: every XCD gets the same work."""
     seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 128, 128, mla.MASK_CAUSAL)
     work = np.zeros(8)
-    for i, (it, h) in enumerate(tasks.tolist()):
+    for i, (it, h, k0, k1) in enumerate(tasks.tolist()):
         if it >= 0:
-            work[i % 8] += items[it][2] + 1
+            work[i % 8] += k1 - k0 + 1
     assert work.max() == work.min()
+    # plenty of work for the CUs: no item is split
+    real = tasks[tasks[:, 0] >= 0]
+    assert (real[:, 2] == 0).all() and (real[:, 3] == items[real[:, 0], 2]).all()
 
 
 @pytest.mark.parametrize("kv_heads", [128, 16, 1])
@@ -417,10 +449,54 @@ def test_plan_balances_xcds_with_few_kv_heads(kv_heads):
     every XCD's work is within 5% of the mean."""
     seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 128, kv_heads, mla.MASK_CAUSAL)
     work = np.zeros(8)
-    for i, (it, h) in enumerate(tasks.tolist()):
+    for i, (it, h, k0, k1) in enumerate(tasks.tolist()):
         if it >= 0:
-            work[i % 8] += items[it][2] + 1
+            work[i % 8] += k1 - k0 + 1
     assert work.max() <= 1.05 * work.mean(), work
+
+
+def test_plan_splits_the_longest_items_when_work_is_scarce():
+    """4096-token causal prefill at 16 heads: 256 items of 4..64 tiles for 256
+    CUs. Items longer than the even share (36 tiles with 2 per task for the
+    fixed work) are cut in two, so no task is longer than that share."""
+    seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 16, 16, mla.MASK_CAUSAL)
+    real = tasks[tasks[:, 0] >= 0]
+    cap = split_cap(items, 16, 16)
+    assert cap == 36
+    assert (real[:, 3] - real[:, 2]).max() <= cap
+    long_items = int((items[:, 2] > cap).sum())
+    assert long_items == 7  # the items of rows 2304.. see 40, 44, .., 64 tiles
+    assert len(real) == 16 * (16 + long_items)
+
+
+def split_workspace_bytes(items, tasks, head_dim):
+    """mla_prefill's workspace for a plan: launch records, merge records
+    (one per split (item, head pack)), then per partial slot 256 rows of
+    log-sum-exp and of head_dim fp32 values, each array 256-byte aligned."""
+    up = lambda x: -(-x // 256) * 256
+    real = tasks[tasks[:, 0] >= 0]
+    split = real[(real[:, 2] != 0) | (real[:, 3] != items[real[:, 0], 2])]
+    parts = len(split)
+    merges = len({(int(i), int(h)) for i, h in split[:, :2]})
+    if parts == 0:
+        return len(tasks) * 32
+    return up(len(tasks) * 32) + up(merges * 32) + up(parts * 256 * 4) + parts * 256 * head_dim * 4
+
+
+def test_plan_does_not_split_when_the_longest_item_is_near_the_share():
+    """4096-token causal prefill at 24 heads: the even share is 54 tiles and
+    the longest item 64; no item is split (measured slower)."""
+    seqs, items, tasks = mla.mla_prefill_plan_host([4096], [4096], 24, 24, mla.MASK_CAUSAL)
+    real = tasks[tasks[:, 0] >= 0]
+    assert (real[:, 2] == 0).all() and (real[:, 3] == items[real[:, 0], 2]).all()
+
+
+@pytest.mark.parametrize("case", [((3000, 5), (5000, 700), 2, 1, 128), ((900,), (900,), 1, 1, 64),
+                                  ((17, 40), (17, 40), 4, 4, 128)])
+def test_workspace_size_of_split_plans(case):
+    qs, ks, h, hk, d = case
+    seqs, items, tasks = mla.mla_prefill_plan_host(list(qs), list(ks), h, hk, mla.MASK_CAUSAL)
+    assert ws_size(tensors(qs=qs, ks=ks, h=h, hk=hk, d=d)) == split_workspace_bytes(items, tasks, d)
 
 
 def test_plan_padded_offsets():

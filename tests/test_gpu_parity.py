@@ -114,9 +114,15 @@ def test_2d_query_and_output_forms():
 
 
 def test_mask_free_with_causal_tile_equals_causal_bit_exact():
+    # 40 heads: enough work that neither plan splits an item (a split plan
+    # cuts a MASK_FREE item, which runs to the end of its 512-key block, at
+    # other tiles than the causal one, so only the rounding would agree)
     qs, ks = [600, 1100], [1100, 1100]
     _say(f"[gpu] mask-free causal tile q={qs} kv={ks}")
-    t, qs, ks, params = make(qs, ks, 2, 2, seed=7)
+    for mt in (synth.MASK_CAUSAL, synth.MASK_FREE):
+        _, items, tasks = mla.mla_prefill_plan_host(qs, ks, 40, 40, mt)
+        assert ((tasks[:, 2] == 0) & ((tasks[:, 0] < 0) | (tasks[:, 3] == items[tasks[:, 0], 2]))).all()
+    t, qs, ks, params = make(qs, ks, 40, 40, seed=7)
     causal = run_gpu(t, qs, ks, params)
     for dt in (torch.float16, torch.bfloat16):
         tile = synth.causal_mask_tile(dt, DEV)

@@ -142,10 +142,12 @@ def test_mask_free_extreme_tile_entries_match_oracle(dtype, scale):
 
 
 def test_mask_free_causal_tile_still_equals_causal_bit_exact_at_scale_one_and_zero():
+    # 40 heads, so that neither plan splits an item (see the same check at
+    # the default scale)
     qs, ks = [600, 1100], [1100, 1100]
-    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 70, DEV)
+    t = synth.attention_inputs(qs, ks, 40, 40, torch.bfloat16, 1.0, 70, DEV)
     qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
     for scale in (1.0, 0.0, -0.3):
-        causal = run(t, qs, ks, 2, 2, scale, synth.MASK_CAUSAL)
-        free = run(t, qs, ks, 2, 2, scale, synth.MASK_FREE, synth.causal_mask_tile(torch.bfloat16, DEV))
+        causal = run(t, qs, ks, 40, 40, scale, synth.MASK_CAUSAL)
+        free = run(t, qs, ks, 40, 40, scale, synth.MASK_FREE, synth.causal_mask_tile(torch.bfloat16, DEV))
         assert np.array_equal(causal, free), scale

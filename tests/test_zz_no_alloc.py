@@ -1,9 +1,12 @@
 """mla_prefill_no_alloc, the entry point that keeps its work list in the
 library's fixed per-GPU array, against mla_prefill with a workspace from the
-caller. Both run the same kernels on the same plan, so their outputs must
-agree bit for bit. Each pair of no-alloc calls runs back to back on one stream
-with no synchronisation between them, the second on a smaller problem, so a
-work list left behind by the first call, or a copy that overtakes the first
+caller. Both run the same kernels; where mla_prefill runs every item whole the
+plans are the same and the outputs must agree bit for bit, and where it
+splits long items over runs of keys (little work for the compute units) they
+must agree to the attention parity bar (max abs 2e-2, mean abs 2e-3). Each
+pair of no-alloc calls runs back to back on one stream with no
+synchronisation between them, the second on a smaller problem, so a work
+list left behind by the first call, or a copy that overtakes the first
 call's kernel, would show in the second result."""
 import numpy as np
 import pytest
@@ -39,6 +42,14 @@ def with_workspace(a):
     return b["atten_out"]
 
 
+def splits(a):
+    """Does mla_prefill cut any item of this problem into runs of keys?"""
+    _, items, tasks = mla.mla_prefill_plan_host(a["q_seqlen"], a["kv_seqlen"], a["head_num"], a["kv_head_num"],
+                                                a["mask_type"])
+    real = tasks[tasks[:, 0] >= 0]
+    return bool(((real[:, 2] != 0) | (real[:, 3] != items[real[:, 0], 2])).any())
+
+
 def run_pair(big, small):
     stream = torch.cuda.current_stream()
     mla.mla_prefill_no_alloc(**big, stream=stream)
@@ -46,8 +57,13 @@ def run_pair(big, small):
     torch.cuda.synchronize()
     for name, a in (("first (larger)", big), ("second (smaller)", small)):
         want = with_workspace(a)
-        assert torch.isfinite(want).all(), name
-        assert torch.equal(a["atten_out"], want), f"{name} call differs from mla_prefill"
+        got = a["atten_out"]
+        assert torch.isfinite(want).all() and torch.isfinite(got).all(), name
+        if splits(a):
+            err = (got.float() - want.float()).abs()
+            assert err.max().item() <= 2e-2 and err.mean().item() <= 2e-3, f"{name}: {err.max().item()}"
+        else:
+            assert torch.equal(got, want), f"{name} call differs from mla_prefill"
 
 
 def test_no_alloc_varlen_then_tiny():
@@ -62,12 +78,14 @@ def test_no_alloc_varlen_then_tiny():
 
 
 def test_no_alloc_grouped_mask_free_padded_then_head_dim_64():
-    # Grouped heads (16 over 2), a MASK_FREE tile, padded K/V; then a smaller
-    # causal problem with embeddimV 64 whose launch has fewer workgroups.
+    # Grouped heads (16 over 2), a MASK_FREE tile, padded K/V (a problem that
+    # mla_prefill splits); then a smaller causal problem with embeddimV 64
+    # whose launch has fewer workgroups.
     _say("[gpu] no-alloc: grouped MASK_FREE padded, then head-dim 64")
     tile = synth.random_mask_tile(5, torch.bfloat16, DEV)
     big = case([700, 1500], [3000, 2100], 16, 2, torch.bfloat16, 7, synth.MASK_FREE, mask=tile, padded=3072)
     small = case([33, 1], [33, 90], 8, 8, torch.float16, 8, synth.MASK_CAUSAL, d=64)
+    assert splits(big) and not splits(small)
     run_pair(big, small)
 
 
