@@ -61,6 +61,11 @@ CASES = [
     ("head-dim-64", [1000], [2500], 2, 2, torch.bfloat16, synth.MASK_CAUSAL, 64, synth.QK_SCALE),
     ("scale-one", [1300], [1300], 2, 2, torch.bfloat16, synth.MASK_CAUSAL, 128, 1.0),
     ("negative-scale-fp16", [1300], [1300], 2, 2, torch.float16, synth.MASK_CAUSAL, 128, -0.1),
+    ("group-8-over-2", [1200], [2000], 8, 2, torch.bfloat16, synth.MASK_CAUSAL, 128,
+     synth.QK_SCALE),
+    ("group-16-over-4-fp16", [900], [2400], 16, 4, torch.float16, synth.MASK_CAUSAL, 128, synth.QK_SCALE),
+    ("group-2-undefined-d64", [700, 300], [2500, 1300], 6, 3, torch.bfloat16, synth.MASK_UNDEFINED, 64,
+     synth.QK_SCALE),
 ]
 
 
@@ -82,27 +87,35 @@ def test_split_matches_oracle_and_unsplit(case):
         assert (out[:500] == 0).all() and out[500:].abs().sum() > 0  # rows before the first key see nothing
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-def test_split_mask_free_random_tile(dtype):
+MF_CASES = [
+    # name, q_seqlen, kv_seqlen, heads, kv_heads, data dtype, tile dtype, head dim
+    ("bf16-tile", [900, 400], [2600, 1500], 2, 2, torch.bfloat16, torch.bfloat16, 128),
+    ("fp16-tile", [900, 400], [2600, 1500], 2, 2, torch.bfloat16, torch.float16, 128),
+    ("fp16-data-d64-grouped", [1500, 200], [2600, 900], 4, 2, torch.float16, torch.float16, 64),
+]
+
+
+@pytest.mark.parametrize("case", MF_CASES, ids=[c[0] for c in MF_CASES])
+def test_split_mask_free_random_tile(case):
     # runs are cut at multiples of 512 keys, so each run's 512-key blocks are
     # those of the tile
-    qs, ks = [900, 400], [2600, 1500]
-    n = split_tasks(qs, ks, 2, 2, synth.MASK_FREE)
-    _say(f"[gpu] split MASK_FREE random tile {dtype}: {n} split tasks")
+    name, qs, ks, h, hk, dt, tdt, d = case
+    n = split_tasks(qs, ks, h, hk, synth.MASK_FREE)
+    _say(f"[gpu] split MASK_FREE random tile {name}: {n} split tasks")
     assert n > 0
-    _, items, tasks = mla.mla_prefill_plan_host(qs, ks, 2, 2, synth.MASK_FREE)
+    _, items, tasks = mla.mla_prefill_plan_host(qs, ks, h, hk, synth.MASK_FREE)
     assert (tasks[:, 2] % 8 == 0).all()
-    t = synth.attention_inputs(qs, ks, 2, 2, torch.bfloat16, 1.0, 120, DEV)
-    tile = synth.random_mask_tile(121, dtype, DEV)
+    t = synth.attention_inputs(qs, ks, h, hk, dt, 1.0, 120, DEV, d_nope=d)
+    tile = synth.random_mask_tile(121, tdt, DEV)
     qs, ks = np.asarray(qs, np.int32), np.asarray(ks, np.int32)
-    out = mla.prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], qs, ks, 2, 2, synth.QK_SCALE,
+    out = mla.prefill(t["q"], t["q_rope"], t["k"], t["k_rope"], t["v"], qs, ks, h, hk, synth.QK_SCALE,
                       synth.MASK_FREE, tile)
     torch.cuda.synchronize()
     f = {k: x.double().cpu().numpy() for k, x in t.items()}
-    want = oracle.attention(f["q"], f["q_rope"], f["k"], f["k_rope"], f["v"], qs, ks, 2, 2, synth.QK_SCALE,
+    want = oracle.attention(f["q"], f["q_rope"], f["k"], f["k_rope"], f["v"], qs, ks, h, hk, synth.QK_SCALE,
                             synth.MASK_FREE, tile.double().cpu().numpy())
-    check(out, want, "mask-free split")
-    check(unsplit(t, qs, ks, 2, 2, synth.QK_SCALE, synth.MASK_FREE, tile), want, "mask-free unsplit")
+    check(out, want, f"mask-free split {name}")
+    check(unsplit(t, qs, ks, h, hk, synth.QK_SCALE, synth.MASK_FREE, tile), want, f"mask-free unsplit {name}")
 
 
 def test_split_padded_kv_layout():
