@@ -903,10 +903,33 @@ uint64_t prolog_pack_b_bytes(const PrologProblem &pp) {
 uint64_t prolog_pack_b_i8_bytes(const PrologProblem &pp) {
     return align256((uint64_t)mla::prolog_packed_bytes((int32_t)pp.heads, (int32_t)pp.r, true));
 }
+// The first product's split over K. With few rows its output is a handful
+// of 512-column tiles (3 at q_lora_rank 1024 below 129 rows), and so few
+// workgroups cannot pull the 2 * h * (q_lora_rank + 512) bytes of weights at
+// any useful rate. The K stages are then shared out, in runs of a multiple of
+// 4 stages, until the launch has at least 128 workgroups; the runs' fp32 sums
+// go to the workspace and a second kernel adds them and applies the tiles'
+// epilogues.
+constexpr int64_t PROLOG_SPLIT_MIN_WORKGROUPS = 128;
+int32_t prolog_first_splits(const PrologProblem &pp) {
+    const int64_t tiles = ((pp.t + mla::PROLOG_BM - 1) / mla::PROLOG_BM) * (pp.r / mla::PROLOG_BN + 1);
+    const int64_t runs = pp.h / mla::PROLOG_BK / 4;  // K in runs of 4 stages
+    int64_t ks = 1;
+    while (tiles * ks < PROLOG_SPLIT_MIN_WORKGROUPS && ks < runs) {
+        ++ks;
+        while (runs % ks != 0) ++ks;  // the next divisor of runs (runs itself at the latest)
+    }
+    return (int32_t)ks;
+}
+uint64_t prolog_part_bytes(const PrologProblem &pp) {
+    const int32_t ks = prolog_first_splits(pp);
+    if (ks <= 1) return 0;
+    return align256((uint64_t)ks * pp.t * (pp.r + mla::PROLOG_BN) * 4);
+}
 uint64_t prolog_workspace_bytes(const PrologProblem &pp, bool quant = false) {
     if (pp.t == 0) return 0;  // nothing to compute
     return prolog_yq_bytes(pp) + prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp) +
-           (quant ? prolog_pack_b_i8_bytes(pp) : prolog_pack_b_bytes(pp));
+           (quant ? prolog_pack_b_i8_bytes(pp) : prolog_pack_b_bytes(pp)) + prolog_part_bytes(pp);
 }
 
 // The first product, x . [wq_a | wkv], shared by both prolog operators: the
@@ -915,7 +938,7 @@ uint64_t prolog_workspace_bytes(const PrologProblem &pp, bool quant = false) {
 int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, const mla_tensor *wq_a,
                          const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
                          const mla_tensor *gamma_ckv, float eps, const mla_tensor *kv_out, float *y_q,
-                         unsigned char *pack_a, unsigned char *pack_kv, hipStream_t s) {
+                         unsigned char *pack_a, unsigned char *pack_kv, float *part, hipStream_t s) {
     mla::PrologGemmParams g1{};
     g1.a = token_x->data;
     g1.lda = pp.h;
@@ -928,10 +951,17 @@ int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, con
     g1.rope_cos = rope_cos->data;
     g1.rope_sin = rope_sin->data;
     g1.eps = eps;
+    g1.k_splits = prolog_first_splits(pp);
+    g1.part = part;
+    g1.ld_part = pp.r + mla::PROLOG_BN;
     hipError_t e = mla::launch_prolog_pack(g1, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
     e = mla::launch_prolog_gemm(g1, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
+    if (g1.k_splits > 1) {
+        e = mla::launch_prolog_split_reduce(g1, s);
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1 split sums: %s", hipGetErrorString(e));
+    }
     return MLA_OK;
 }
 
@@ -1208,9 +1238,10 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
     unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
     unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
     unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
+    float *part = reinterpret_cast<float *>(pack_b + prolog_pack_b_bytes(pp));
 
     rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
-                              pack_kv, s);
+                              pack_kv, part, s);
     if (rc) return rc;
     hipError_t e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
                                     s);
@@ -1278,9 +1309,10 @@ int mla_prolog_quant(const mla_tensor *token_x, const mla_tensor *wq_a, const ml
     unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
     unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
     unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
+    float *part = reinterpret_cast<float *>(pack_b + prolog_pack_b_i8_bytes(pp));
 
     rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
-                              pack_kv, s);
+                              pack_kv, part, s);
     if (rc) return rc;
     float *scale = static_cast<float *>(qr_scale_out->data);
     hipError_t e = mla::launch_prolog_quant_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, scale,

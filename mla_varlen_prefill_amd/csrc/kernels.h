@@ -212,6 +212,16 @@ struct PrologGemmParams {
     int32_t int8;
     const float *row_scale;  // [M]
     const float *col_scale;  // [N], column n of the segment's weights
+    // Split over K (bf16 only; few output tiles): with k_splits > 1 each
+    // tile runs as k_splits workgroups, workgroup s over stages
+    // [s * nk / k_splits, (s + 1) * nk / k_splits) of the nk = k / PROLOG_BK;
+    // nk / k_splits must be a multiple of 4. Each writes its raw fp32 sums to
+    // part + s * m * ld_part, tile n of the two segments together at column
+    // n * PROLOG_BN, and launch_prolog_split_reduce adds the parts and
+    // applies the segments' epilogues.
+    int32_t k_splits;
+    float *part;
+    int64_t ld_part;
 };
 // An int8 stage is 64 k: the same 64 bytes per row as a bf16 stage of 32 k.
 constexpr int PROLOG_K_MULTIPLE_I8 = 256;
@@ -227,6 +237,8 @@ inline int64_t prolog_packed_bytes(int32_t n_tiles, int32_t k, bool int8 = false
 // stage image the product kernel reads (see prolog.hip).
 hipError_t launch_prolog_pack(const PrologGemmParams &p, hipStream_t stream);
 hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream);
+// The epilogues of a product run with k_splits > 1, on the sum of its parts.
+hipError_t launch_prolog_split_reduce(const PrologGemmParams &p, hipStream_t stream);
 
 // y fp32 [rows, cols] (row stride ld_y) -> out bf16 [rows, cols] (row stride
 // ld_out) = RmsNorm over each row * gamma; cols a multiple of 256.

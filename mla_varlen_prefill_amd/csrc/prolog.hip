@@ -202,7 +202,11 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // tiles of each: its CUs then share one weight tile in L2.
     const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
     const int m_tiles = (p.m + BM - 1) / BM;
-    const int blk = blockIdx.x;
+    // split over K: the k_splits workgroups of a tile are consecutive
+    const bool split_k = !I8 && p.k_splits > 1;
+    const int n_splits = split_k ? p.k_splits : 1;
+    const int split = (int)blockIdx.x % n_splits;
+    const int blk = (int)blockIdx.x / n_splits;
     int tn, tm;
     if (n_tiles % 8 == 0) {
         const int s = blk >> 3;
@@ -221,7 +225,9 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const unsigned char *gamma = static_cast<const unsigned char *>(second ? p.seg[1].gamma : p.seg[0].gamma);
     const int m0 = tm * BM;
     const int rows = min(BM, p.m - m0);
-    const int nk = p.k * ESZ / (BK * 2);  // 64-byte stages
+    const int nk_all = p.k * ESZ / (BK * 2);  // 64-byte stages
+    const int nk = nk_all / n_splits;         // this workgroup's stages: [kbase, kbase + nk)
+    const int kbase = split * nk;
     // int8: the dequantisation scales go out now and are used by the
     // epilogue -- thread tid takes the scale of the tile's column tid, a lane
     // those of its two output rows (rows past the end read 0)
@@ -237,14 +243,15 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // ---- activation stage: 128 rows x 64 bytes; LDS slot tid (row tid / 4,
     // physical chunk tid % 4) receives logical chunk (tid % 4) ^ ((row >> 2)
     // & 3). Rows past the end read as zeros.
-    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * ESZ,
-                               (uint32_t)rows * (uint32_t)p.lda * ESZ);
+    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * ESZ + (int64_t)kbase * 64,
+                               (uint32_t)rows * (uint32_t)p.lda * ESZ - (uint32_t)kbase * 64);
     const int xr = tid >> 2;
     const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * ESZ + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
     // ---- weight stage: block kt of this tile's packed weights, 2048 16-byte
     // slots; load r of a thread takes slot 512 r + tid. Stages past K read
-    // as zeros.
-    const i32x4 rw = make_rsrc(wpk + (int64_t)tj * nk * PROLOG_PACK_BLOCK, (uint32_t)nk * PROLOG_PACK_BLOCK);
+    // as zeros (a split's activation stages past its end read real values,
+    // which meet those zero weights).
+    const i32x4 rw = make_rsrc(wpk + ((int64_t)tj * nk_all + kbase) * PROLOG_PACK_BLOCK, (uint32_t)nk * PROLOG_PACK_BLOCK);
     // DMA of stage kt into ring slot kt % STAGES: lane l's 16 bytes land at
     // base + 16 l, so a wave's base is its first slot.
     auto issue = [&](int kt, int slot) __attribute__((always_inline)) {
@@ -374,12 +381,15 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // store instruction writes whole rows: 16 bytes per lane straight from
     // the accumulators would touch 32 rows 16 bytes at a time, and the
     // partial-line writes cost several times the bytes.
-    if (!I8 && epilogue == PROLOG_STORE_F32) {
+    if (!I8 && (split_k || epilogue == PROLOG_STORE_F32)) {
         // fp32 rows are 2 KB: two passes of 64 rows (tb = 0, 1). Row lr of a
         // pass (= 32 wt + r32) holds chunk c (4 columns) at c ^ ((lr & 7) << 1).
-        float *out = static_cast<float *>(out_base);
-        const i32x4 ro = make_rsrc(out + (int64_t)m0 * ld_out + (int64_t)tj * BN,
-                                   (uint32_t)(((int64_t)rows * ld_out - (int64_t)tj * BN) * 4));
+        // A split's raw sums go to its part, at the tile's column over both
+        // segments.
+        float *out = split_k ? p.part + (int64_t)split * p.m * p.ld_part : static_cast<float *>(out_base);
+        const int64_t ldo = split_k ? p.ld_part : ld_out;
+        const int64_t col0 = (int64_t)(split_k ? tn : tj) * BN;
+        const i32x4 ro = make_rsrc(out + (int64_t)m0 * ldo + col0, (uint32_t)(((int64_t)rows * ldo - col0) * 4));
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             if (tb == 1) block_sync();  // the first pass's rows have been read
@@ -404,7 +414,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
                 const int row = 64 * (q >> 5) + 32 * tb + (q & 31);
                 const i32x4 v =
                     *reinterpret_cast<const i32x4 *>(WS(q >> 4) + (q & 15) * 2048 + ((ch ^ ((q & 7) << 1)) << 4));
-                prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ld_out * 4 + ch * 16, 0, CPOL_NT);
+                prolog_raw_buffer_store_b128(v, ro, (uint32_t)row * (uint32_t)ldo * 4 + ch * 16, 0, CPOL_NT);
             }
         }
         return;
@@ -556,6 +566,77 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     }
 }
 
+// The epilogues of a product run split over K: one wave per (row, tile),
+// 8 columns per lane. The lane adds the parts' raw sums of its columns, then
+// applies the tile's segment epilogue as the product kernel does: the fp32
+// row (PROLOG_STORE_F32), or RmsNorm over the tile's 512 columns times gamma,
+// the rope on columns 448 .. 511 (pairs (2i, 2i + 1) with the row's cos /
+// sin of both columns) and bf16 (PROLOG_NORM_ROPE).
+__global__ __launch_bounds__(256) void prolog_split_reduce_kernel(const PrologGemmParams p) {
+    const int lane = threadIdx.x & 63;
+    const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
+    const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (w >= p.m * n_tiles) return;
+    const int row = w / n_tiles, tn = w % n_tiles;
+    const bool second = tn >= p.seg[0].n_tiles;
+    const PrologSegment &sg = second ? p.seg[1] : p.seg[0];
+    const int tj = second ? tn - p.seg[0].n_tiles : tn;
+    const int c0 = 8 * lane;  // first column of the lane within the tile
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const float *src = p.part + (int64_t)row * p.ld_part + (int64_t)tn * BN + c0;
+    for (int s = 0; s < p.k_splits; ++s) {
+        const float4 a = *reinterpret_cast<const float4 *>(src);
+        const float4 b = *reinterpret_cast<const float4 *>(src + 4);
+        v[0] += a.x;
+        v[1] += a.y;
+        v[2] += a.z;
+        v[3] += a.w;
+        v[4] += b.x;
+        v[5] += b.y;
+        v[6] += b.z;
+        v[7] += b.w;
+        src += (int64_t)p.m * p.ld_part;
+    }
+    if (sg.epilogue == PROLOG_STORE_F32) {
+        float *o = static_cast<float *>(sg.out) + (int64_t)row * sg.ld_out + (int64_t)tj * BN + c0;
+        *reinterpret_cast<float4 *>(o) = float4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<float4 *>(o + 4) = float4{v[4], v[5], v[6], v[7]};
+        return;
+    }
+    float ssq = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ssq = __builtin_fmaf(v[j], v[j], ssq);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ssq += __shfl_xor(ssq, o, 64);
+    const float inv = 1.0f / sqrtf(ssq * (1.0f / BN) + p.eps);
+    const __bf16 *gamma = static_cast<const __bf16 *>(sg.gamma);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float gm = gamma != nullptr ? static_cast<float>(gamma[(int64_t)tj * BN + c0 + j]) : 1.f;
+        v[j] = v[j] * inv * gm;
+    }
+    if (c0 >= BN - PROLOG_ROPE) {
+        const __bf16 *cs = static_cast<const __bf16 *>(p.rope_cos) + (int64_t)row * PROLOG_ROPE + (c0 - (BN - PROLOG_ROPE));
+        const __bf16 *sn = static_cast<const __bf16 *>(p.rope_sin) + (int64_t)row * PROLOG_ROPE + (c0 - (BN - PROLOG_ROPE));
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            const float a0 = v[j] * static_cast<float>(cs[j]) - v[j + 1] * static_cast<float>(sn[j]);
+            const float a1 = v[j + 1] * static_cast<float>(cs[j + 1]) + v[j] * static_cast<float>(sn[j + 1]);
+            v[j] = a0;
+            v[j + 1] = a1;
+        }
+    }
+    bf16x4 lo, hi;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        lo[j] = static_cast<__bf16>(v[j]);
+        hi[j] = static_cast<__bf16>(v[4 + j]);
+    }
+    __bf16 *o = static_cast<__bf16 *>(sg.out) + (int64_t)row * sg.ld_out + (int64_t)tj * BN + c0;
+    *reinterpret_cast<bf16x4 *>(o) = lo;
+    *reinterpret_cast<bf16x4 *>(o + 4) = hi;
+}
+
 // One wave per row: RmsNorm over cols fp32 values, times gamma, to bf16.
 __global__ __launch_bounds__(256) void prolog_rms_rows_kernel(const float *y, int64_t ld_y, const __bf16 *gamma,
                                                               __bf16 *out, int64_t ld_out, int32_t rows,
@@ -666,10 +747,19 @@ hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream) {
     const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
     const int m_tiles = (p.m + PROLOG_BM - 1) / PROLOG_BM;
     if (p.m <= 0 || n_tiles <= 0) return hipSuccess;
+    const unsigned splits = (!p.int8 && p.k_splits > 1) ? (unsigned)p.k_splits : 1u;
     if (p.int8)
         hipLaunchKernelGGL(prolog_gemm_kernel<true>, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
     else
-        hipLaunchKernelGGL(prolog_gemm_kernel<false>, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
+        hipLaunchKernelGGL(prolog_gemm_kernel<false>, dim3((unsigned)(n_tiles * m_tiles) * splits), dim3(NT), 0,
+                           stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prolog_split_reduce(const PrologGemmParams &p, hipStream_t stream) {
+    const int64_t waves = (int64_t)p.m * (p.seg[0].n_tiles + p.seg[1].n_tiles);
+    if (waves <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prolog_split_reduce_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -86,15 +86,23 @@ def test_prolog_other_sizes_match_oracle(cfg):
 
 
 def test_prolog_rows_are_independent():
-    # every output row depends on its own token only: a prefix run gives the
-    # same bits as the full run
+    # every output row depends on its own token only. The first product is
+    # split over K when the call has few 128-row tiles, into a number of runs
+    # that depends on the tile count (h 4096: 16 at 257..384 rows, 32 up to
+    # 128 rows), and the runs' sums are added in run order. A prefix run with
+    # the same tile count gives the same bits as the full run; a shorter one
+    # agrees to the prolog's tolerance.
     _say("[gpu] prolog row independence")
     d = synth.prolog_inputs(300, seed=9, device=DEV)
     full = run_gpu(d)
-    part = {k: (v[:77].contiguous() if k in ("token_x", "rope_cos", "rope_sin") else v) for k, v in d.items()}
-    pre = run_gpu(part)
-    for a, b in zip(full, pre):
-        assert torch.equal(a[:77], b)
+    for n, exact in ((260, True), (77, False)):
+        part = {k: (v[:n].contiguous() if k in ("token_x", "rope_cos", "rope_sin") else v) for k, v in d.items()}
+        pre = run_gpu(part)
+        for name, a, b in zip(("q", "kv", "cq"), full, pre):
+            if exact:
+                assert torch.equal(a[:n], b), (n, name)
+            else:
+                assert_close(b, a[:n].double().cpu().numpy(), f"{n}-row prefix {name}")
 
 
 def test_prolog_workload_sampled():
