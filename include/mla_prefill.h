@@ -317,8 +317,13 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
  *   workspace_size  out: bytes of device workspace mla_prolog needs: the
  *               fp32 product x . wq_a before its norm (t * q_lora_rank * 4,
  *               rounded up to 256 bytes), then copies of wq_a, wkv and wq_b
- *               rearranged for the product kernel (2 bytes per weight); 0
- *               when t = 0.
+ *               rearranged for the product kernel (2 bytes per weight, each
+ *               rounded up to 256 bytes), then, when x . [wq_a | wkv] has
+ *               fewer than 128 tiles of 128 rows x 512 columns and is split
+ *               over K into S runs (S the smallest divisor of h / 128 that
+ *               brings S * tiles to 128, or h / 128), the runs' fp32 sums
+ *               (S * t * (q_lora_rank + 512) * 4 bytes, rounded up to 256);
+ *               0 when t = 0.
  * Supported (the page's constraints fix head_dim 512, h 4096, q_lora_rank
  * 1024, num_heads 64, rope_dim 64, t up to 64k): head_dim = 512,
  * rope_dim = 64, h a multiple of 128, q_lora_rank a multiple of 512, any
@@ -328,7 +333,9 @@ int mla_prefill_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_t
  * enters the second product.
  * mla_prolog enqueues six kernels on stream (the rearrangements of wq_a and
  * of wkv, x . [wq_a | wkv] with the kv epilogue, the c^Q norm, the
- * rearrangement of wq_b, c^Q . wq_b with the q epilogue). The workspace
+ * rearrangement of wq_b, c^Q . wq_b with the q epilogue), and a seventh
+ * that adds the runs of a split first product and applies its epilogues.
+ * The result then differs from an unsplit call only by rounding. The workspace
  * (16-byte aligned, at least the planned size) must stay untouched until they
  * have run. Errors as for mla_prefill.
  */
@@ -370,13 +377,15 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
  *   workspace_size  out: bytes of device workspace mla_prolog_quant needs:
  *               t * q_lora_rank * 4 for x . wq_a, then the rearranged copies
  *               of wq_a and wkv (2 bytes per weight) and of wq_b (1 byte per
- *               weight), each rounded up to 256 bytes; 0 when t = 0.
+ *               weight), then the split first product's sums as for
+ *               mla_prolog, each rounded up to 256 bytes; 0 when t = 0.
  * Supported: as mla_prolog, with q_lora_rank one of 512, 1024, 1536, 2048
  * (the page fixes 1024). mla_prolog_quant enqueues six kernels on stream
  * (the rearrangements of wq_a and wkv, x . [wq_a | wkv] with the kv
  * epilogue, the c^Q norm and quantisation, the rearrangement of wq_b, and
- * qr . wq_b with the dequantisation, per-head norm and rope epilogue); the
- * workspace must stay valid until they have run. Errors as for mla_prefill.
+ * qr . wq_b with the dequantisation, per-head norm and rope epilogue), and
+ * the sum of a split first product as mla_prolog does; the workspace must
+ * stay valid until they have run. Errors as for mla_prefill.
  */
 int mla_prolog_quant_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a,
                                         const mla_tensor *wq_b, const mla_tensor *wkv,

@@ -687,3 +687,20 @@ def test_gather_batch_limit():
                            value=torch.zeros(0, 2, 16, dtype=torch.bfloat16))
     assert c_paged_cache_load(**args(8192)) == "MLA_OK"  # valid; zero tokens, nothing launched
     assert c_paged_cache_load(**args(8193)) == "MLA_ERR_UNSUPPORTED"
+
+
+def test_prolog_workspace_with_split_first_product():
+    # h 4096: 32 runs of 4 stages; at t = 64 the first product has 3 tiles
+    # (q_lora_rank 1024 + the 512-column kv tile), so it is split into all 32
+    # runs, whose fp32 sums follow the packed weights
+    t, h, r, heads, hd = 64, 4096, 1024, 2, 512
+    up = lambda x: -(-x // 256) * 256
+    base = up(t * r * 4) + up(2 * h * r) + up(2 * h * hd) + up(2 * r * heads * hd)
+    got = mla.mla_prolog_get_workspace_size(**prolog_args(t=t, h=h, r=r, heads=heads))
+    assert got == base + up(32 * t * (r + 512) * 4)
+    # 9 tiles at 300 rows: 16 runs (the smallest divisor of 32 giving 128 workgroups)
+    got = mla.mla_prolog_get_workspace_size(**prolog_args(t=300, h=h, r=r, heads=heads))
+    assert got == up(300 * r * 4) + up(2 * h * r) + up(2 * h * hd) + up(2 * r * heads * hd) + up(16 * 300 * (r + 512) * 4)
+    # 129 tiles and more: no split
+    got = mla.mla_prolog_get_workspace_size(**prolog_args(t=128 * 43, h=h, r=r, heads=heads))
+    assert got == up(128 * 43 * r * 4) + up(2 * h * r) + up(2 * h * hd) + up(2 * r * heads * hd)
