@@ -466,8 +466,8 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
         }
     }
     seq_item_first[batch] = (int32_t)plan->items.size();
-    // pieces of each item, in item order (so each sequence's are consecutive)
-    int32_t cap = INT32_MAX;  // longest piece
+    // the longest run of key tiles a task may hold (rule above)
+    int32_t cap = INT32_MAX;
     const int32_t gran = mask_type == MLA_MASK_FREE ? MASK_TILE / FWD_BN : 1;
     if (allow_split) {
         int64_t total = 0, longest = 0;
@@ -482,6 +482,7 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
             cap = (int32_t)std::min<int64_t>(INT32_MAX,
                                              std::max<int64_t>(SPLIT_MIN_TILES, share * SPLIT_SHARE_PERCENT / 100));
     }
+    // pieces of each item, in item order (so each sequence's are consecutive)
     std::vector<Piece> pieces;
     std::vector<int32_t> seq_piece_first(batch + 1, 0);  // pieces of sequence b: [seq_piece_first[b], .. [b + 1])
     std::vector<int32_t> item_part_base(plan->items.size(), -1), item_pieces(plan->items.size(), 1);
