@@ -589,12 +589,20 @@ def bench_prolog(steps):
     ws = torch.empty(max(mla.mla_prolog_get_workspace_size(*args), 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     ms = _time(lambda: mla.mla_prolog(*args, ws, stream), steps, stream)
+    # the same calls with the weights packed once (mla_prolog_pack_weights,
+    # outside the timed region: it depends on the weights only)
+    packed = mla.pack_prolog_weights(d["wq_a"], d["wq_b"], d["wkv"])
+    wsp = torch.empty(max(mla.mla_prolog_prepacked_workspace_size(d["token_x"], d["wq_a"]), 1), dtype=torch.uint8,
+                      device="cuda")
+    ms_pp = _time(lambda: mla.mla_prolog_prepacked(*args, packed, wsp, stream), steps, stream)
     flops = synth.PROLOG_FLOP_PER_TOKEN * t
     tf = flops / (ms * 1e-3) / 1e12
-    del d, q, kv, cq, ws
+    tf_pp = flops / (ms_pp * 1e-3) / 1e12
+    del d, q, kv, cq, ws, packed, wsp
     torch.cuda.empty_cache()
     return {"workload": "prolog", "tokens": t, "sizes": dict(synth.PROLOG_SIZES), "flop_per_step": flops,
-            "ms_per_step": ms, "value": tf, "unit": "TFLOP/s", "peak": PEAK_TFLOPS, "frac": tf / PEAK_TFLOPS}
+            "ms_per_step": ms, "value": tf, "unit": "TFLOP/s", "peak": PEAK_TFLOPS, "frac": tf / PEAK_TFLOPS,
+            "prepacked": {"ms_per_step": ms_pp, "value": tf_pp, "frac": tf_pp / PEAK_TFLOPS}}
 
 
 def bench_prolog_quant(steps):
@@ -618,15 +626,21 @@ def bench_prolog_quant(steps):
     ws = torch.empty(max(mla.mla_prolog_quant_get_workspace_size(*args), 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     ms = _time(lambda: mla.mla_prolog_quant(*args, ws, stream), steps, stream)
+    packed = mla.pack_prolog_weights(d["wq_a"], d["wq_b"], d["wkv"])
+    wsp = torch.empty(max(mla.mla_prolog_prepacked_workspace_size(d["token_x"], d["wq_a"]), 1), dtype=torch.uint8,
+                      device="cuda")
+    ms_pp = _time(lambda: mla.mla_prolog_quant_prepacked(*args, packed, wsp, stream), steps, stream)
     bf16_flops = 2 * t * h * (r + hd)
     int8_ops = 2 * t * r * heads * hd
     least_ms = (bf16_flops / (PEAK_TFLOPS * 1e12) + int8_ops / (PEAK_INT8_TOPS * 1e12)) * 1e3
-    del d, q, kv, qr, qs, ws
+    del d, q, kv, qr, qs, ws, packed, wsp
     torch.cuda.empty_cache()
     return {"workload": "prolog_quant", "tokens": t, "sizes": dict(synth.PROLOG_SIZES), "bf16_flop_per_step":
             bf16_flops, "int8_op_per_step": int8_ops, "ms_per_step": ms,
             "value": (bf16_flops + int8_ops) / (ms * 1e-3) / 1e12, "unit": "TOP/s (bf16 FLOP + int8 OP)",
-            "least_ms_at_peaks": least_ms, "frac": least_ms / ms}
+            "least_ms_at_peaks": least_ms, "frac": least_ms / ms,
+            "prepacked": {"ms_per_step": ms_pp, "value": (bf16_flops + int8_ops) / (ms_pp * 1e-3) / 1e12,
+                          "frac": least_ms / ms_pp}}
 
 
 def _progress(msg):

@@ -400,6 +400,53 @@ int mla_prolog_quant(const mla_tensor *token_x, const mla_tensor *wq_a, const ml
                      float eps, const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
                      const mla_tensor *qr_scale_out, void *workspace, uint64_t workspace_size, void *stream);
 
+/*
+ * Prolog weights packed once -- for callers that run the prolog many times
+ * with the same weights (every inference deployment). mla_prolog and
+ * mla_prolog_quant rearrange wq_a, wkv and wq_b into the product kernel's
+ * stage layout on every call (a third of a call at 64 tokens, 2-3% at
+ * 16384); these entry points do it once.
+ *
+ *   mla_prolog_weights_size  host only: *packed_size = bytes of the packed
+ *       weights: the rearranged copies of wq_a [h, q_lora_rank] and wkv
+ *       [h, 512] (2 bytes per weight) and of wq_b [q_lora_rank, num_heads *
+ *       512] (2 bytes per weight in bf16, 1 in int8), each rounded up to 256
+ *       bytes. Shapes, dtypes and supported sizes as for mla_prolog (wq_b
+ *       int8 selects the quantised layout).
+ *   mla_prolog_pack_weights  enqueues the rearrangement into packed (device,
+ *       16-byte aligned, at least *packed_size bytes, owned by the caller) on
+ *       stream. The packed buffer depends only on the weights: it stays
+ *       valid for any number of calls while the weights are unchanged.
+ *   mla_prolog_prepacked_workspace_size  host only: the workspace of the two
+ *       prepacked operators for token_x [t, h] and wq_a [h, q_lora_rank]:
+ *       t * q_lora_rank * 4 bytes for x . wq_a, then the split first
+ *       product's sums as for mla_prolog, each rounded up to 256; 0 when
+ *       t = 0.
+ *   mla_prolog_prepacked / mla_prolog_quant_prepacked  as mla_prolog /
+ *       mla_prolog_quant with the same arguments, plus the packed buffer of
+ *       these weights (packed_size bytes); the weight descriptors are still
+ *       validated, their data is not read. Outputs equal those of the
+ *       packing operators bit for bit. Errors as for mla_prolog, and
+ *       MLA_ERR_WORKSPACE for a packed buffer smaller than the weights need.
+ */
+int mla_prolog_weights_size(const mla_tensor *wq_a, const mla_tensor *wq_b, const mla_tensor *wkv,
+                            uint64_t *packed_size);
+int mla_prolog_pack_weights(const mla_tensor *wq_a, const mla_tensor *wq_b, const mla_tensor *wkv, void *packed,
+                            uint64_t packed_size, void *stream);
+int mla_prolog_prepacked_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a,
+                                        uint64_t *workspace_size);
+int mla_prolog_prepacked(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                         const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                         const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
+                         const mla_tensor *kv_out, const mla_tensor *qr_out, const void *packed,
+                         uint64_t packed_size, void *workspace, uint64_t workspace_size, void *stream);
+int mla_prolog_quant_prepacked(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                               const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                               const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale,
+                               float eps, const mla_tensor *q_out, const mla_tensor *kv_out,
+                               const mla_tensor *qr_out, const mla_tensor *qr_scale_out, const void *packed,
+                               uint64_t packed_size, void *workspace, uint64_t workspace_size, void *stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char *mla_last_error(void);
 

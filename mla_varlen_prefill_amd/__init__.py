@@ -26,6 +26,8 @@ __all__ = [
     "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "prefill_paged",
     "mla_prolog_get_workspace_size", "mla_prolog", "prolog",
     "mla_prolog_quant_get_workspace_size", "mla_prolog_quant", "prolog_quant",
+    "mla_prolog_weights_size", "mla_prolog_pack_weights", "mla_prolog_prepacked_workspace_size",
+    "mla_prolog_prepacked", "mla_prolog_quant_prepacked", "pack_prolog_weights",
 ]
 
 # MLA_PREFILL_LIBRARY selects another build of the same library (the host
@@ -99,6 +101,14 @@ def _load():
                                                                    ctypes.POINTER(ctypes.c_uint64)]
     lib.mla_prolog_quant.argtypes = [T] * 9 + [ctypes.c_float, T, T, T, T, ctypes.c_void_p, ctypes.c_uint64,
                                                ctypes.c_void_p]
+    lib.mla_prolog_weights_size.argtypes = [T, T, T, ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prolog_pack_weights.argtypes = [T, T, T, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.mla_prolog_prepacked_workspace_size.argtypes = [T, T, ctypes.POINTER(ctypes.c_uint64)]
+    lib.mla_prolog_prepacked.argtypes = [T] * 8 + [ctypes.c_float, T, T, T, ctypes.c_void_p, ctypes.c_uint64,
+                                                   ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    lib.mla_prolog_quant_prepacked.argtypes = [T] * 9 + [ctypes.c_float, T, T, T, T, ctypes.c_void_p,
+                                                         ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                                         ctypes.c_void_p]
     lib.mla_last_error.restype = ctypes.c_char_p
     lib.mla_last_error.argtypes = []
     lib.mla_prefill_plan_host.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -108,7 +118,9 @@ def _load():
     for fn in ("mla_prefill_get_workspace_size", "mla_prefill", "mla_prefill_no_alloc", "paged_cache_load",
                "mla_prefill_plan_host",
                "mla_prefill_paged_get_workspace_size", "mla_prefill_paged", "mla_prolog_get_workspace_size",
-               "mla_prolog", "mla_prolog_quant_get_workspace_size", "mla_prolog_quant"):
+               "mla_prolog", "mla_prolog_quant_get_workspace_size", "mla_prolog_quant", "mla_prolog_weights_size",
+               "mla_prolog_pack_weights", "mla_prolog_prepacked_workspace_size", "mla_prolog_prepacked",
+               "mla_prolog_quant_prepacked"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -390,19 +402,28 @@ def mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv
                       keep), ctypes.c_void_p(ws_ptr), ctypes.c_uint64(ws_size), _stream_ptr(stream)))
 
 
-def prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps=1e-6, stream=None):
+def prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps=1e-6, stream=None, packed=None):
     """Allocate outputs and workspace with torch and run the prolog. Returns
-    (q [t, num_heads, head_dim], kv [t, head_dim], c^Q [t, q_lora_rank])."""
+    (q [t, num_heads, head_dim], kv [t, head_dim], c^Q [t, q_lora_rank]).
+    With ``packed`` (``pack_prolog_weights`` of these weights) the weights are
+    not rearranged again."""
     t, hd, r = token_x.shape[0], wkv.shape[1], wq_a.shape[1]
     heads = wq_b.shape[1] // hd
     dev = token_x.device
     q = torch.empty((t, heads, hd), dtype=torch.bfloat16, device=dev)
     kv = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
     cq = torch.empty((t, r), dtype=torch.bfloat16, device=dev)
-    ws = mla_prolog_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q,
-                                       kv, cq)
-    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
-    mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q, kv, cq, workspace, stream)
+    if packed is not None:
+        ws = mla_prolog_prepacked_workspace_size(token_x, wq_a)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        mla_prolog_prepacked(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q, kv, cq, packed,
+                             workspace, stream)
+    else:
+        ws = mla_prolog_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q,
+                                           kv, cq)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        mla_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q, kv, cq, workspace,
+                   stream)
     if stream is not None and isinstance(stream, torch.cuda.Stream):
         workspace.record_stream(stream)
     return q, kv, cq
@@ -445,10 +466,12 @@ def mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gam
 
 
 def prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps=1e-6,
-                 stream=None):
+                 stream=None, packed=None):
     """Allocate outputs and workspace with torch and run the quantised prolog.
     Returns (q [t, num_heads, head_dim] bf16, kv [t, head_dim] bf16,
-    c^Q codes [t, q_lora_rank] int8, c^Q scales [t, 1] float32)."""
+    c^Q codes [t, q_lora_rank] int8, c^Q scales [t, 1] float32). With
+    ``packed`` (``pack_prolog_weights`` of these weights) the weights are not
+    rearranged again."""
     t, hd, r = token_x.shape[0], wkv.shape[1], wq_a.shape[1]
     heads = wq_b.shape[1] // hd
     dev = token_x.device
@@ -456,12 +479,97 @@ def prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_c
     kv = torch.empty((t, hd), dtype=torch.bfloat16, device=dev)
     qr = torch.empty((t, r), dtype=torch.int8, device=dev)
     qs = torch.empty((t, 1), dtype=torch.float32, device=dev)
-    ws = mla_prolog_quant_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv,
-                                             wq_b_scale, eps, q, kv, qr, qs)
-    workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
-    mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q, kv, qr,
-                     qs, workspace, stream)
+    if packed is not None:
+        ws = mla_prolog_prepacked_workspace_size(token_x, wq_a)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        mla_prolog_quant_prepacked(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps,
+                                   q, kv, qr, qs, packed, workspace, stream)
+    else:
+        ws = mla_prolog_quant_get_workspace_size(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv,
+                                                 wq_b_scale, eps, q, kv, qr, qs)
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        mla_prolog_quant(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q, kv,
+                         qr, qs, workspace, stream)
     if stream is not None and isinstance(stream, torch.cuda.Stream):
         workspace.record_stream(stream)
     return q, kv, qr, qs
 
+
+def _buf(t):
+    """(pointer or None, size in bytes) of an optional device buffer tensor."""
+    if t is None:
+        return None, 0
+    return (t.data_ptr() if t.numel() else None), t.numel() * t.element_size()
+
+
+def mla_prolog_weights_size(wq_a, wq_b, wkv) -> int:
+    """Bytes of the packed prolog weights (bf16 or int8 wq_b)."""
+    lib = _load()
+    keep = []
+    size = ctypes.c_uint64(0)
+    _check("mla_prolog_weights_size", lib.mla_prolog_weights_size(_desc(wq_a, keep), _desc(wq_b, keep),
+                                                                   _desc(wkv, keep), ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prolog_pack_weights(wq_a, wq_b, wkv, packed, stream=None) -> None:
+    """Enqueue the rearrangement of the three prolog weights into ``packed``."""
+    lib = _load()
+    _on_device([("wq_a", wq_a), ("wq_b", wq_b), ("wkv", wkv), ("packed", packed)], stream)
+    keep = []
+    ptr, size = _buf(packed)
+    _check("mla_prolog_pack_weights", lib.mla_prolog_pack_weights(
+        _desc(wq_a, keep), _desc(wq_b, keep), _desc(wkv, keep), ctypes.c_void_p(ptr), ctypes.c_uint64(size),
+        _stream_ptr(stream)))
+
+
+def pack_prolog_weights(wq_a, wq_b, wkv, stream=None):
+    """Allocate (torch) and fill the packed prolog weights; reuse the result
+    for every call with these weights."""
+    packed = torch.empty(max(mla_prolog_weights_size(wq_a, wq_b, wkv), 1), dtype=torch.uint8, device=wq_a.device)
+    mla_prolog_pack_weights(wq_a, wq_b, wkv, packed, stream)
+    return packed
+
+
+def mla_prolog_prepacked_workspace_size(token_x, wq_a) -> int:
+    """Workspace bytes of the prepacked prolog operators for these shapes."""
+    lib = _load()
+    keep = []
+    size = ctypes.c_uint64(0)
+    _check("mla_prolog_prepacked_workspace_size", lib.mla_prolog_prepacked_workspace_size(
+        _desc(token_x, keep), _desc(wq_a, keep), ctypes.byref(size)))
+    return int(size.value)
+
+
+def mla_prolog_prepacked(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                         qr_out, packed, workspace, stream=None) -> None:
+    """``mla_prolog`` reading the weights from ``packed`` (mla_prolog_pack_weights)."""
+    lib = _load()
+    _on_device([("token_x", token_x), ("wq_a", wq_a), ("wq_b", wq_b), ("wkv", wkv), ("rope_cos", rope_cos),
+                ("rope_sin", rope_sin), ("gamma_cq", gamma_cq), ("gamma_ckv", gamma_ckv), ("q_out", q_out),
+                ("kv_out", kv_out), ("qr_out", qr_out), ("packed", packed), ("workspace", workspace)], stream)
+    keep = []
+    pk, pk_size = _buf(packed)
+    ws, ws_size = _buf(workspace)
+    _check("mla_prolog_prepacked", lib.mla_prolog_prepacked(
+        *_prolog_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out, qr_out,
+                      keep), ctypes.c_void_p(pk), ctypes.c_uint64(pk_size), ctypes.c_void_p(ws),
+        ctypes.c_uint64(ws_size), _stream_ptr(stream)))
+
+
+def mla_prolog_quant_prepacked(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps,
+                               q_out, kv_out, qr_out, qr_scale_out, packed, workspace, stream=None) -> None:
+    """``mla_prolog_quant`` reading the weights from ``packed`` (mla_prolog_pack_weights)."""
+    lib = _load()
+    _on_device([("token_x", token_x), ("wq_a", wq_a), ("wq_b", wq_b), ("wkv", wkv), ("rope_cos", rope_cos),
+                ("rope_sin", rope_sin), ("gamma_cq", gamma_cq), ("gamma_ckv", gamma_ckv),
+                ("wq_b_scale", wq_b_scale), ("q_out", q_out), ("kv_out", kv_out), ("qr_out", qr_out),
+                ("qr_scale_out", qr_scale_out), ("packed", packed), ("workspace", workspace)], stream)
+    keep = []
+    pk, pk_size = _buf(packed)
+    ws, ws_size = _buf(workspace)
+    _check("mla_prolog_quant_prepacked", lib.mla_prolog_quant_prepacked(
+        *_prolog_quant_args(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps,
+                            q_out, kv_out, qr_out, qr_scale_out, keep),
+        ctypes.c_void_p(pk), ctypes.c_uint64(pk_size), ctypes.c_void_p(ws), ctypes.c_uint64(ws_size),
+        _stream_ptr(stream)))

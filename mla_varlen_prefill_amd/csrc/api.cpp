@@ -939,7 +939,7 @@ uint64_t prolog_workspace_bytes(const PrologProblem &pp, bool quant = false) {
 int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, const mla_tensor *wq_a,
                          const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
                          const mla_tensor *gamma_ckv, float eps, const mla_tensor *kv_out, float *y_q,
-                         unsigned char *pack_a, unsigned char *pack_kv, float *part, hipStream_t s) {
+                         unsigned char *pack_a, unsigned char *pack_kv, float *part, bool pack, hipStream_t s) {
     mla::PrologGemmParams g1{};
     g1.a = token_x->data;
     g1.lda = pp.h;
@@ -955,8 +955,11 @@ int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, con
     g1.k_splits = prolog_first_splits(pp);
     g1.part = part;
     g1.ld_part = pp.r + mla::PROLOG_BN;
-    hipError_t e = mla::launch_prolog_pack(g1, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
+    hipError_t e = hipSuccess;
+    if (pack) {
+        e = mla::launch_prolog_pack(g1, s);
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
+    }
     e = mla::launch_prolog_gemm(g1, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
     if (g1.k_splits > 1) {
@@ -964,6 +967,146 @@ int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, con
         if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1 split sums: %s", hipGetErrorString(e));
     }
     return MLA_OK;
+}
+
+// The weight operands alone (mla_prolog_weights_size / pack_weights): the
+// same checks as validate_prolog; wq_b bf16 or int8 (then *quant).
+int validate_prolog_weights(const mla_tensor *wq_a, const mla_tensor *wq_b, const mla_tensor *wkv,
+                            PrologProblem *pp, bool *quant) {
+    int rc;
+    if ((rc = check_bf16(wq_a, "wq_a", 2)) || (rc = check_bf16(wkv, "wkv", 2)) ||
+        (rc = check_tensor(wq_b, "wq_b", true)))
+        return rc;
+    if (wq_b->dtype != MLA_BF16 && wq_b->dtype != MLA_INT8) return fail(MLA_ERR_DTYPE, "wq_b must be bf16 or int8");
+    if (wq_b->ndim != 2) return fail(MLA_ERR_SHAPE, "wq_b: expected 2 dimensions, got %d", wq_b->ndim);
+    *quant = wq_b->dtype == MLA_INT8;
+    const int64_t h = wq_a->shape[0], r = wq_a->shape[1], hd = wkv->shape[1];
+    if (wkv->shape[0] != h) return fail(MLA_ERR_SHAPE, "wkv: expected [h = %lld, head_dim]", (long long)h);
+    if (wq_b->shape[0] != r)
+        return fail(MLA_ERR_SHAPE, "wq_b: expected [q_lora_rank = %lld, num_heads * head_dim]", (long long)r);
+    if (hd != mla::PROLOG_BN) return fail(MLA_ERR_UNSUPPORTED, "head_dim %lld: only 512 is supported", (long long)hd);
+    if (wq_b->shape[1] % hd != 0 || wq_b->shape[1] == 0)
+        return fail(MLA_ERR_SHAPE, "wq_b: width %lld is not num_heads * head_dim (%lld)",
+                    (long long)wq_b->shape[1], (long long)hd);
+    const int64_t heads = wq_b->shape[1] / hd;
+    if (h <= 0 || h % mla::PROLOG_K_MULTIPLE != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "h %lld: a positive multiple of %d is required", (long long)h,
+                    mla::PROLOG_K_MULTIPLE);
+    if (r <= 0 || r % mla::PROLOG_BN != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: a positive multiple of %d is required", (long long)r,
+                    mla::PROLOG_BN);
+    if (*quant && r > mla::PROLOG_QUANT_MAX_COLS)
+        return fail(MLA_ERR_UNSUPPORTED, "q_lora_rank %lld: at most %d in the quantised prolog", (long long)r,
+                    mla::PROLOG_QUANT_MAX_COLS);
+    if (r * heads * hd * 2 >= (int64_t)1 << 31 || h * r * 2 >= (int64_t)1 << 31 ||
+        (int64_t)mla::PROLOG_BM * heads * hd * 2 >= (int64_t)1 << 31)
+        return fail(MLA_ERR_UNSUPPORTED, "operand too large for 32-bit tile offsets");
+    pp->t = 0;
+    pp->h = h;
+    pp->r = r;
+    pp->heads = heads;
+    return MLA_OK;
+}
+
+// Packed weights: the copies of wq_a, wkv and wq_b the product kernel reads,
+// in that order, each 256-byte aligned.
+uint64_t prolog_packed_weights_bytes(const PrologProblem &pp, bool quant) {
+    return prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp) +
+           (quant ? prolog_pack_b_i8_bytes(pp) : prolog_pack_b_bytes(pp));
+}
+// Workspace of the prepacked operators: the fp32 rows of x . wq_a and the
+// split first product's sums.
+uint64_t prolog_prepacked_workspace_bytes(const PrologProblem &pp) {
+    if (pp.t == 0) return 0;
+    return prolog_yq_bytes(pp) + prolog_part_bytes(pp);
+}
+
+// The four prolog operators: quant selects int8 wq_b (qr_out int8, the two
+// scale tensors); packed == nullptr packs the weights into the workspace on
+// every call, else they are read from packed (mla_prolog_pack_weights).
+int prolog_call(bool quant, const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale, float eps,
+                const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
+                const mla_tensor *qr_scale_out, const void *packed, uint64_t packed_size, void *workspace,
+                uint64_t workspace_size, void *stream) {
+    PrologProblem pp;
+    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
+                             qr_out, &pp, quant);
+    if (rc) return rc;
+    if (quant && ((rc = check_scale_vector(wq_b_scale, "wq_b_scale", pp.heads * mla::PROLOG_BN)) ||
+                  (rc = check_scale_vector(qr_scale_out, "qr_scale_out", pp.t))))
+        return rc;
+    const bool pack = packed == nullptr;
+    if (!pack) {
+        const uint64_t pneed = prolog_packed_weights_bytes(pp, quant);
+        if (packed_size < pneed)
+            return fail(MLA_ERR_WORKSPACE, "packed weights of %llu bytes needed, %llu given",
+                        (unsigned long long)pneed, (unsigned long long)packed_size);
+        if ((reinterpret_cast<uintptr_t>(packed) & 15) != 0)
+            return fail(MLA_ERR_WORKSPACE, "packed weights must be 16-byte aligned");
+    }
+    if (pp.t == 0) return ok();
+    const uint64_t need = pack ? prolog_workspace_bytes(pp, quant) : prolog_prepacked_workspace_bytes(pp);
+    if (workspace == nullptr || workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given", (unsigned long long)need,
+                    (unsigned long long)workspace_size);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char *wsb = static_cast<unsigned char *>(workspace);
+    float *y_q = reinterpret_cast<float *>(wsb);
+    unsigned char *pack_a, *pack_kv, *pack_b;
+    float *part;
+    if (pack) {
+        pack_a = wsb + prolog_yq_bytes(pp);
+        pack_kv = pack_a + prolog_pack_a_bytes(pp);
+        pack_b = pack_kv + prolog_pack_kv_bytes(pp);
+        part = reinterpret_cast<float *>(pack_b + (quant ? prolog_pack_b_i8_bytes(pp) : prolog_pack_b_bytes(pp)));
+    } else {
+        pack_a = const_cast<unsigned char *>(static_cast<const unsigned char *>(packed));
+        pack_kv = pack_a + prolog_pack_a_bytes(pp);
+        pack_b = pack_kv + prolog_pack_kv_bytes(pp);
+        part = reinterpret_cast<float *>(wsb + prolog_yq_bytes(pp));
+    }
+
+    rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
+                              pack_kv, part, pack, s);
+    if (rc) return rc;
+    hipError_t e;
+    float *scale = quant ? static_cast<float *>(qr_scale_out->data) : nullptr;
+    if (quant)
+        e = mla::launch_prolog_quant_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, scale, (int32_t)pp.t,
+                                          (int32_t)pp.r, eps, s);
+    else
+        e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r,
+                                        eps, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm: %s", hipGetErrorString(e));
+    // c^Q . wq_b (int8 with quant: dequantisation first): one tile per head
+    // (norm per head, weight 1, rope)
+    mla::PrologGemmParams g2{};
+    g2.a = qr_out->data;
+    g2.lda = pp.r;
+    g2.m = (int32_t)pp.t;
+    g2.k = (int32_t)pp.r;
+    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pack_b, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE,
+                 q_out->data, pp.heads * mla::PROLOG_BN, nullptr};
+    g2.seg[1] = {nullptr, 0, nullptr, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
+    g2.rope_cos = rope_cos->data;
+    g2.rope_sin = rope_sin->data;
+    g2.eps = eps;
+    if (quant) {
+        g2.int8 = 1;
+        g2.row_scale = scale;
+        g2.col_scale = static_cast<const float *>(wq_b_scale->data);
+    }
+    if (pack) {
+        e = mla::launch_prolog_pack(g2, s);
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
+    }
+    e = mla::launch_prolog_gemm(g2, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // namespace
@@ -1222,48 +1365,8 @@ int mla_prolog(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tens
                const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
                const mla_tensor *kv_out, const mla_tensor *qr_out, void *workspace, uint64_t workspace_size,
                void *stream) {
-    PrologProblem pp;
-    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
-                             qr_out, &pp);
-    if (rc) return rc;
-    if (pp.t == 0) return ok();
-    const uint64_t need = prolog_workspace_bytes(pp);
-    if (workspace == nullptr || workspace_size < need)
-        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given", (unsigned long long)need,
-                    (unsigned long long)workspace_size);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    unsigned char *wsb = static_cast<unsigned char *>(workspace);
-    float *y_q = reinterpret_cast<float *>(wsb);
-    unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
-    unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
-    unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
-    float *part = reinterpret_cast<float *>(pack_b + prolog_pack_b_bytes(pp));
-
-    rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
-                              pack_kv, part, s);
-    if (rc) return rc;
-    hipError_t e = mla::launch_prolog_rms_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, (int32_t)pp.t, (int32_t)pp.r, eps,
-                                    s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm: %s", hipGetErrorString(e));
-    // c^Q . wq_b: one tile per head (norm per head, weight 1, rope)
-    mla::PrologGemmParams g2{};
-    g2.a = qr_out->data;
-    g2.lda = pp.r;
-    g2.m = (int32_t)pp.t;
-    g2.k = (int32_t)pp.r;
-    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pack_b, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE,
-                 q_out->data, pp.heads * mla::PROLOG_BN, nullptr};
-    g2.seg[1] = {nullptr, 0, nullptr, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
-    g2.rope_cos = rope_cos->data;
-    g2.rope_sin = rope_sin->data;
-    g2.eps = eps;
-    e = mla::launch_prolog_pack(g2, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
-    e = mla::launch_prolog_gemm(g2, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
-    return ok();
+    return prolog_call(false, token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, nullptr, eps, q_out,
+                       kv_out, qr_out, nullptr, nullptr, 0, workspace, workspace_size, stream);
 }
 
 int mla_prolog_quant_get_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a,
@@ -1290,55 +1393,88 @@ int mla_prolog_quant(const mla_tensor *token_x, const mla_tensor *wq_a, const ml
                      const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale,
                      float eps, const mla_tensor *q_out, const mla_tensor *kv_out, const mla_tensor *qr_out,
                      const mla_tensor *qr_scale_out, void *workspace, uint64_t workspace_size, void *stream) {
-    PrologProblem pp;
-    int rc = validate_prolog(token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, eps, q_out, kv_out,
-                             qr_out, &pp, true);
-    if (rc) return rc;
-    if ((rc = check_scale_vector(wq_b_scale, "wq_b_scale", pp.heads * mla::PROLOG_BN)) ||
-        (rc = check_scale_vector(qr_scale_out, "qr_scale_out", pp.t)))
-        return rc;
-    if (pp.t == 0) return ok();
-    const uint64_t need = prolog_workspace_bytes(pp, true);
-    if (workspace == nullptr || workspace_size < need)
-        return fail(MLA_ERR_WORKSPACE, "workspace of %llu bytes needed, %llu given", (unsigned long long)need,
-                    (unsigned long long)workspace_size);
-    if ((reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-        return fail(MLA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    unsigned char *wsb = static_cast<unsigned char *>(workspace);
-    float *y_q = reinterpret_cast<float *>(wsb);
-    unsigned char *pack_a = wsb + prolog_yq_bytes(pp);
-    unsigned char *pack_kv = pack_a + prolog_pack_a_bytes(pp);
-    unsigned char *pack_b = pack_kv + prolog_pack_kv_bytes(pp);
-    float *part = reinterpret_cast<float *>(pack_b + prolog_pack_b_i8_bytes(pp));
+    return prolog_call(true, token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q_out,
+                       kv_out, qr_out, qr_scale_out, nullptr, 0, workspace, workspace_size, stream);
+}
 
-    rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
-                              pack_kv, part, s);
+int mla_prolog_weights_size(const mla_tensor *wq_a, const mla_tensor *wq_b, const mla_tensor *wkv,
+                            uint64_t *packed_size) {
+    if (packed_size == nullptr) return fail(MLA_ERR_NULL, "packed_size is NULL");
+    PrologProblem pp;
+    bool quant = false;
+    int rc = validate_prolog_weights(wq_a, wq_b, wkv, &pp, &quant);
     if (rc) return rc;
-    float *scale = static_cast<float *>(qr_scale_out->data);
-    hipError_t e = mla::launch_prolog_quant_rows(y_q, pp.r, gamma_cq->data, qr_out->data, pp.r, scale,
-                                                 (int32_t)pp.t, (int32_t)pp.r, eps, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm and quantisation: %s", hipGetErrorString(e));
-    // qr . wq_b in int8: one tile per head (dequantisation, norm per head, rope)
+    *packed_size = prolog_packed_weights_bytes(pp, quant);
+    return ok();
+}
+
+int mla_prolog_pack_weights(const mla_tensor *wq_a, const mla_tensor *wq_b, const mla_tensor *wkv, void *packed,
+                            uint64_t packed_size, void *stream) {
+    PrologProblem pp;
+    bool quant = false;
+    int rc = validate_prolog_weights(wq_a, wq_b, wkv, &pp, &quant);
+    if (rc) return rc;
+    const uint64_t need = prolog_packed_weights_bytes(pp, quant);
+    if (packed == nullptr || packed_size < need)
+        return fail(MLA_ERR_WORKSPACE, "packed weights need %llu bytes, %llu given", (unsigned long long)need,
+                    (unsigned long long)packed_size);
+    if ((reinterpret_cast<uintptr_t>(packed) & 15) != 0)
+        return fail(MLA_ERR_WORKSPACE, "packed weights must be 16-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    unsigned char *pb = static_cast<unsigned char *>(packed);
+    mla::PrologGemmParams g1{};
+    g1.k = (int32_t)pp.h;
+    g1.seg[0] = {wq_a->data, pp.r, pb, (int32_t)(pp.r / mla::PROLOG_BN), mla::PROLOG_STORE_F32, nullptr, 0, nullptr};
+    g1.seg[1] = {wkv->data, mla::PROLOG_BN, pb + prolog_pack_a_bytes(pp), 1, mla::PROLOG_NORM_ROPE, nullptr, 0,
+                 nullptr};
+    hipError_t e = mla::launch_prolog_pack(g1, s);
+    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
     mla::PrologGemmParams g2{};
-    g2.a = qr_out->data;
-    g2.lda = pp.r;
-    g2.m = (int32_t)pp.t;
     g2.k = (int32_t)pp.r;
-    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pack_b, (int32_t)pp.heads, mla::PROLOG_NORM_ROPE,
-                 q_out->data, pp.heads * mla::PROLOG_BN, nullptr};
-    g2.seg[1] = {nullptr, 0, nullptr, 0, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
-    g2.rope_cos = rope_cos->data;
-    g2.rope_sin = rope_sin->data;
-    g2.eps = eps;
-    g2.int8 = 1;
-    g2.row_scale = scale;
-    g2.col_scale = static_cast<const float *>(wq_b_scale->data);
+    g2.int8 = quant ? 1 : 0;
+    g2.seg[0] = {wq_b->data, pp.heads * mla::PROLOG_BN, pb + prolog_pack_a_bytes(pp) + prolog_pack_kv_bytes(pp),
+                 (int32_t)pp.heads, mla::PROLOG_NORM_ROPE, nullptr, 0, nullptr};
     e = mla::launch_prolog_pack(g2, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
-    e = mla::launch_prolog_gemm(g2, s);
-    if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));
     return ok();
+}
+
+int mla_prolog_prepacked_workspace_size(const mla_tensor *token_x, const mla_tensor *wq_a, uint64_t *workspace_size) {
+    if (workspace_size == nullptr) return fail(MLA_ERR_NULL, "workspace_size is NULL");
+    int rc;
+    if ((rc = check_tensor(token_x, "token_x", true)) || (rc = check_tensor(wq_a, "wq_a", true))) return rc;
+    if (token_x->ndim != 2 || wq_a->ndim != 2 || wq_a->shape[0] != token_x->shape[1])
+        return fail(MLA_ERR_SHAPE, "token_x [t, h] and wq_a [h, q_lora_rank] expected");
+    PrologProblem pp;
+    pp.t = token_x->shape[0];
+    pp.h = token_x->shape[1];
+    pp.r = wq_a->shape[1];
+    if (pp.h <= 0 || pp.h % mla::PROLOG_K_MULTIPLE != 0 || pp.r <= 0 || pp.r % mla::PROLOG_BN != 0)
+        return fail(MLA_ERR_UNSUPPORTED, "h must be a positive multiple of %d and q_lora_rank of %d",
+                    mla::PROLOG_K_MULTIPLE, mla::PROLOG_BN);
+    *workspace_size = prolog_prepacked_workspace_bytes(pp);
+    return ok();
+}
+
+int mla_prolog_prepacked(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                         const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                         const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, float eps, const mla_tensor *q_out,
+                         const mla_tensor *kv_out, const mla_tensor *qr_out, const void *packed,
+                         uint64_t packed_size, void *workspace, uint64_t workspace_size, void *stream) {
+    if (packed == nullptr) return fail(MLA_ERR_NULL, "packed is NULL");
+    return prolog_call(false, token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, nullptr, eps, q_out,
+                       kv_out, qr_out, nullptr, packed, packed_size, workspace, workspace_size, stream);
+}
+
+int mla_prolog_quant_prepacked(const mla_tensor *token_x, const mla_tensor *wq_a, const mla_tensor *wq_b,
+                               const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
+                               const mla_tensor *gamma_cq, const mla_tensor *gamma_ckv, const mla_tensor *wq_b_scale,
+                               float eps, const mla_tensor *q_out, const mla_tensor *kv_out,
+                               const mla_tensor *qr_out, const mla_tensor *qr_scale_out, const void *packed,
+                               uint64_t packed_size, void *workspace, uint64_t workspace_size, void *stream) {
+    if (packed == nullptr) return fail(MLA_ERR_NULL, "packed is NULL");
+    return prolog_call(true, token_x, wq_a, wq_b, wkv, rope_cos, rope_sin, gamma_cq, gamma_ckv, wq_b_scale, eps, q_out,
+                       kv_out, qr_out, qr_scale_out, packed, packed_size, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

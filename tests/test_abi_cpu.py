@@ -704,3 +704,48 @@ def test_prolog_workspace_with_split_first_product():
     # 129 tiles and more: no split
     got = mla.mla_prolog_get_workspace_size(**prolog_args(t=128 * 43, h=h, r=r, heads=heads))
     assert got == up(128 * 43 * r * 4) + up(2 * h * r) + up(2 * h * hd) + up(2 * r * heads * hd)
+
+
+def test_prolog_packed_weights_and_prepacked_workspace_sizes():
+    up = lambda x: -(-x // 256) * 256
+    h, r, heads, hd = 4096, 1024, 2, 512
+    a = prolog_args(t=64, h=h, r=r, heads=heads)
+    # wq_a, wkv and wq_b rearranged, 2 bytes per weight (1 for int8 wq_b)
+    assert mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"], a["wkv"]) == up(2 * h * r) + up(2 * h * hd) + \
+        up(2 * r * heads * hd)
+    q = prolog_quant_args(t=64, h=h, r=r, heads=heads)
+    assert mla.mla_prolog_weights_size(q["wq_a"], q["wq_b"], q["wkv"]) == up(2 * h * r) + up(2 * h * hd) + \
+        up(r * heads * hd)
+    # prepacked workspace: x . wq_a and the split sums (32 runs at 64 rows), no weights
+    assert mla.mla_prolog_prepacked_workspace_size(a["token_x"], a["wq_a"]) == up(64 * r * 4) + \
+        up(32 * 64 * (r + 512) * 4)
+    assert mla.mla_prolog_prepacked_workspace_size(a["token_x"][:0], a["wq_a"]) == 0
+    # with the packing operator's workspace: weights + the same
+    assert mla.mla_prolog_get_workspace_size(**a) == mla.mla_prolog_prepacked_workspace_size(a["token_x"], a["wq_a"]) \
+        + mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"], a["wkv"])
+
+
+def test_prolog_prepacked_errors_before_any_launch():
+    keep = []
+    a = prolog_args(t=3)
+    need = mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"], a["wkv"])
+    small = torch.zeros(need - 256, dtype=torch.uint8)
+    ws = torch.zeros(mla.mla_prolog_prepacked_workspace_size(a["token_x"], a["wq_a"]), dtype=torch.uint8)
+    lib = mla._load()
+    args = mla._prolog_args(**a, keep=keep)
+    rc = lib.mla_prolog_prepacked(*args, ctypes.c_void_p(small.data_ptr()), ctypes.c_uint64(small.numel()),
+                                  ctypes.c_void_p(ws.data_ptr()), ctypes.c_uint64(ws.numel()), None)
+    assert c_status(rc) == "MLA_ERR_WORKSPACE" and "packed weights" in mla.mla_last_error()
+    rc = lib.mla_prolog_prepacked(*args, None, ctypes.c_uint64(need), ctypes.c_void_p(ws.data_ptr()),
+                                  ctypes.c_uint64(ws.numel()), None)
+    assert c_status(rc) == "MLA_ERR_NULL"
+    # the weights alone: dtype and shape checks
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_prolog_weights_size(a["wq_a"].half(), a["wq_b"], a["wkv"])
+    assert e.value.status == "MLA_ERR_DTYPE"
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"][:, :1000].contiguous(), a["wkv"])
+    assert e.value.status == "MLA_ERR_SHAPE"
+    with pytest.raises(mla.MlaError) as e:
+        mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"], a["wkv"][:, :256].contiguous())
+    assert e.value.status == "MLA_ERR_UNSUPPORTED"

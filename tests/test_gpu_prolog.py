@@ -136,3 +136,34 @@ def test_prolog_rope_tables_with_unequal_pair_entries():
     rq, rkv, rcq = run_oracle(d)
     for got, ref, what in ((q, rq, "q"), (kv, rkv, "kv"), (cq, rcq, "c^Q")):
         assert_close(got, ref, what)
+
+
+@pytest.mark.parametrize("t", [64, 300, 1024])
+def test_prolog_prepacked_equals_packing_call(t):
+    # weights packed once (mla_prolog_pack_weights) give the packing
+    # operator's outputs bit for bit
+    _say(f"[gpu] prolog prepacked, {t} tokens")
+    d = synth.prolog_inputs(t, seed=31, device=DEV)
+    packed = mla.pack_prolog_weights(d["wq_a"], d["wq_b"], d["wkv"])
+    want = run_gpu(d)
+    got = mla.prolog(d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"], d["gamma_cq"],
+                     d["gamma_ckv"], synth.PROLOG_EPS, packed=packed)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("q", "kv", "cq"), want, got):
+        assert torch.equal(a, b), name
+
+
+def test_prolog_prepacked_buffer_serves_many_calls():
+    # one packed buffer, three calls with other tokens (same weights: the
+    # generator seeds the weights independently of t)
+    _say("[gpu] prolog prepacked, one buffer for several calls")
+    d0 = synth.prolog_inputs(16, seed=32, device=DEV)
+    packed = mla.pack_prolog_weights(d0["wq_a"], d0["wq_b"], d0["wkv"])
+    for t in (1, 130, 16):
+        d = synth.prolog_inputs(t, seed=32, device=DEV)
+        assert all(torch.equal(d[k], d0[k]) for k in ("wq_a", "wq_b", "wkv"))
+        got = mla.prolog(d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"], d["gamma_cq"],
+                         d["gamma_ckv"], synth.PROLOG_EPS, packed=packed)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("q", "kv", "cq"), run_gpu(d), got):
+            assert torch.equal(a, b), (t, name)

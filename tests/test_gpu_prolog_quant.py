@@ -143,3 +143,17 @@ def test_prolog_quant_workload_sampled_rows():
     assert_codes(qr[ri], qs[ri], rqr, rs, rcq, "workload codes")
     assert_close(q[ri], rq, "workload q")
     assert_close(kv[ri], rkv, "workload kv")
+
+
+@pytest.mark.parametrize("t", [37, 300])
+def test_prolog_quant_prepacked_equals_packing_call(t):
+    # int8 wq_b packed once gives the packing operator's outputs bit for bit
+    _say(f"[gpu] quantised prolog prepacked, {t} tokens")
+    d = synth.prolog_quant_inputs(t, seed=33, device=DEV)
+    packed = mla.pack_prolog_weights(d["wq_a"], d["wq_b"], d["wkv"])
+    want = run_gpu(d)
+    got = mla.prolog_quant(d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"],
+                           d["gamma_cq"], d["gamma_ckv"], d["wq_b_scale"], synth.PROLOG_EPS, packed=packed)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("q", "kv", "codes", "scales"), want, got):
+        assert torch.equal(a, b), name
