@@ -262,13 +262,15 @@ int paged_cache_load(const mla_tensor *key_cache, const mla_tensor *value_cache,
  *                 (every sequence starts at position 0 of its table row).
  *   kv_seqlen     HOST int32 [batch]: keys (context length) of each sequence.
  * Supported here: block_size a multiple of MLA_PLAN_KV_COLS (64), at most
- * MLA_PAGED_MAX_KEYS keys per sequence, num_blocks * block_size < 2^31;
- * otherwise MLA_ERR_UNSUPPORTED. max_blocks must cover ceil(kv_len /
+ * MLA_PAGED_MAX_KEYS keys per sequence, num_blocks * block_size < 2^31, at
+ * most 2^20 sequences; otherwise MLA_ERR_UNSUPPORTED. max_blocks must cover ceil(kv_len /
  * block_size) for every sequence (else MLA_ERR_SHAPE). Block ids live on the
  * device and are not checked by the host: a 64-key tile whose block id lies
  * outside [0, num_blocks) reads as zeros (those keys contribute exp(0 - max)
- * weight with a zero value row; they are not an error signal). Workspace,
- * stream and error behaviour as for mla_prefill.
+ * weight with a zero value row; they are not an error signal). Workspace
+ * (including the split of long items over runs of keys and its merge),
+ * stream and error behaviour as for mla_prefill; the plan equals
+ * mla_prefill's for the same lengths, so the two paths agree bit for bit.
  */
 #define MLA_PAGED_MAX_KEYS (2048 * 64)
 int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope,

@@ -311,6 +311,9 @@ int validate_paged(const mla_tensor *q, const mla_tensor *q_rope, const mla_tens
     if (pg->num_blocks * pg->block_size > INT32_MAX)
         return fail(MLA_ERR_UNSUPPORTED, "caches of more than 2^31 - 1 token slots");
     if (block_tables->dtype != MLA_INT32) return fail(MLA_ERR_DTYPE, "block_tables must be int32");
+    if (pr->batch > (1 << mla::PAGED_SEQ_BITS))
+        return fail(MLA_ERR_UNSUPPORTED, "batch %d: the fused path takes at most %d sequences", pr->batch,
+                    1 << mla::PAGED_SEQ_BITS);
     if (block_tables->ndim != 2 || block_tables->shape[0] != pr->batch)
         return fail(MLA_ERR_SHAPE, "block_tables: expected [batch = %d, max_blocks]", pr->batch);
     pg->bt_stride = block_tables->shape[1];
@@ -404,7 +407,7 @@ int32_t pack_shift_for(int32_t heads, int32_t kv_heads) {
 // Work list.
 //  * Items: one per FWD_BM >> pack_shift query rows of each sequence, with the
 //    number of key tiles its rows can see.
-//  * Split items (contiguous K/V only, allow_split): when the launch holds
+//  * Split items (allow_split: not in mla_prefill_no_alloc): when the launch holds
 //    little work for the CUs -- few heads, few sequences -- the longest items
 //    would set its duration alone. Let W be the work of all tasks (tiles plus
 //    TASK_FIXED_TILES each) spread evenly over the CUs. If the longest item
@@ -648,7 +651,8 @@ void write_plan_view(const Plan &p, uint8_t *dst) {
 // The launch records the kernel reads: each task with its item and sequence
 // folded in. Paged K/V carry the sequence index (its block-table row) where
 // contiguous K/V carry the row of the task's first key (pieces of a split
-// item start at key kt0 * FWD_BN; paged plans are never split).
+// item start at key kt0 * FWD_BN); paged K/V carry the sequence index with
+// kt0 above it.
 void write_launch(const Plan &p, int32_t group, bool paged, mla::LaunchRec *dst) {
     for (size_t i = 0; i < p.tasks.size(); ++i) {
         const Task &t = p.tasks[i];
@@ -665,7 +669,7 @@ void write_launch(const Plan &p, int32_t group, bool paged, mla::LaunchRec *dst)
             r.kv_tiles = t.kt1 - t.kt0;
             r.head = t.head;
             r.kv_head = t.head / group;
-            r.kv_off = paged ? it.b : sq.kv_off + k0;
+            r.kv_off = paged ? (it.b | (t.kt0 << mla::PAGED_SEQ_BITS)) : sq.kv_off + k0;
             r.kv_len = sq.kv_len - k0;
             r.part = t.part;
         }
@@ -714,10 +718,10 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
                     const mla_tensor *mask, float qk_scale, const mla_tensor *atten_out, void *workspace,
                     uint64_t workspace_size, bool use_scratch, void *stream) {
     // Items are split only where the workspace is the caller's (not the fixed
-    // array of mla_prefill_no_alloc) and the K/V are contiguous.
+    // array of mla_prefill_no_alloc).
     Plan plan;
     build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
-               !use_scratch && pg == nullptr, &plan);
+               !use_scratch, &plan);
     const uint64_t need = plan_bytes(plan, pr.head_dim);
     if (need == 0) return ok();  // no query rows: nothing to write
     if (use_scratch) {
@@ -1201,7 +1205,7 @@ int mla_prefill_paged_get_workspace_size(const mla_tensor *q, const mla_tensor *
                             mask, head_num, qk_scale, kv_head_num, mask_type, atten_out, &pr, &pg);
     if (rc) return rc;
     Plan plan;
-    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, 0, false, &plan);
+    build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, 0, true, &plan);
     *workspace_size = plan_bytes(plan, pr.head_dim);
     return ok();
 }

@@ -70,7 +70,8 @@ struct LaunchRec {
     int32_t head;      // first query head; -1: padding
     int32_t kv_head;   // the KV head of those query heads
     int32_t q_left;    // query rows of the sequence from the item's first row on
-    int32_t kv_off;    // contiguous K/V: row of the task's first key; paged: the sequence index
+    int32_t kv_off;    // contiguous K/V: row of the task's first key; paged: the sequence index, plus the
+                       // task's first tile (FWD_BN keys) of the sequence << PAGED_SEQ_BITS
     int32_t kv_len;    // keys of the sequence from the task's first key on
     int32_t part;      // -1: write attenOut; else the partial slot (normalised fp32 rows and log-sum-exp)
 };
@@ -125,6 +126,10 @@ struct FwdParams {
 // Key tiles of one sequence the paged kernel can address (its per-tile table
 // lives in LDS): PAGED_MAX_TILES * FWD_BN keys.
 constexpr int PAGED_MAX_TILES = 2048;
+// A paged launch record's kv_off: sequence index in the low PAGED_SEQ_BITS
+// bits, the task's first tile above them (below PAGED_MAX_TILES = 2^11).
+constexpr int PAGED_SEQ_BITS = 20;
+static_assert(PAGED_MAX_TILES <= (1 << (31 - PAGED_SEQ_BITS)), "first tile must fit above the sequence index");
 
 // dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). One workgroup per task.
 hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream);

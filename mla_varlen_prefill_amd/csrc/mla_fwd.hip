@@ -330,19 +330,21 @@ void mla_fwd_kernel(const FwdParams p) {
     constexpr int Q_LOADS = QN_INSTR + 4;
     vec8 qreg[NKS], qrreg[4];
 
-    // ---- paged K/V: first cache row of each key tile of the sequence (block
+    // ---- paged K/V: first cache row of each key tile of the task (block
     // size is a multiple of the tile, so a tile never straddles two blocks);
     // -1 for a tile whose block id lies outside the cache, which then reads
-    // as zeros like rows past the sequence end.
+    // as zeros like rows past the sequence end. A run of a split item starts
+    // at tile kt0 of its sequence.
     int32_t *tile_row = reinterpret_cast<int32_t *>(smem + LDS_BYTES);
     const int n_tiles_seq = min((kv_len + BN - 1) / BN, PAGED_MAX_TILES);
     if (PAGED) {
         const int tpb = p.block_size / BN;
-        const int32_t *bt = p.block_tables + (int64_t)task.kv_off * p.bt_stride;
+        const int seq = task.kv_off & ((1 << PAGED_SEQ_BITS) - 1), kt0 = task.kv_off >> PAGED_SEQ_BITS;
+        const int32_t *bt = p.block_tables + (int64_t)seq * p.bt_stride;
         for (int i = tid; i < n_tiles_seq; i += NT) {
-            const int bi = i / tpb;
+            const int gi = i + kt0, bi = gi / tpb;
             const int blk = bt[bi];
-            tile_row[i] = (blk >= 0 && blk < p.num_blocks) ? blk * p.block_size + (i - bi * tpb) * BN : -1;
+            tile_row[i] = (blk >= 0 && blk < p.num_blocks) ? blk * p.block_size + (gi - bi * tpb) * BN : -1;
         }
         block_sync();
     }

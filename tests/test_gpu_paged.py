@@ -249,3 +249,45 @@ def test_paged_full_workload_sampled_rows():
     err = np.concatenate(errs)
     _say(f"[gpu]   {len(err) // 128} rows compared, max {err.max():.3e} mean {err.mean():.3e}")
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+SPLIT_CASES = [
+    # name, q_seqlen, kv_seqlen, heads, kv_heads, block_size, dtype, mask_type, head dim
+    ("causal-bs128", [3000], [3000], 2, 2, 128, torch.bfloat16, synth.MASK_CAUSAL, 128),
+    ("q-longer-bs64", [2000], [1500], 2, 1, 64, torch.float16, synth.MASK_CAUSAL, 128),
+    ("undefined-d64-bs192", [300, 100], [3000, 2000], 4, 2, 192, torch.bfloat16, synth.MASK_UNDEFINED, 64),
+]
+
+
+def _split_tasks(qs, ks, h, hk, mt):
+    _, items, tasks = mla.mla_prefill_plan_host(qs, ks, h, hk, mt)
+    real = tasks[tasks[:, 0] >= 0]
+    return int(((real[:, 2] != 0) | (real[:, 3] != items[real[:, 0], 2])).sum())
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_paged_split_items(case):
+    # few heads over long sequences: long items run as several key-tile runs
+    # (the run's first tile sits above the sequence index in the launch
+    # record); the result matches the oracle and gather + prefill bit for bit
+    name, qs, ks, h, hk, bs, dtype, mt, dim = case
+    n = _split_tasks(qs, ks, h, hk, mt)
+    _say(f"[gpu] paged split {name}: {n} split tasks")
+    assert n > 0
+    t, qs, ks = make_paged(qs, ks, h, hk, bs, dtype, seed=len(name) + 70, dim=dim)
+    td = to_dev(t)
+    out = run_paged(td, qs, ks, h, hk, mt)
+    assert_close(out, oracle_paged(t, qs, ks, h, hk, mt), name)
+    assert torch.equal(out, run_two_step(td, qs, ks, h, hk, mt)), f"{name}: fused differs from gather + prefill"
+
+
+def test_paged_mask_free_split_random_tile():
+    qs, ks = [1500, 200], [2600, 900]
+    assert _split_tasks(qs, ks, 4, 2, synth.MASK_FREE) > 0
+    _say("[gpu] paged split MASK_FREE random tile")
+    t, qs, ks = make_paged(qs, ks, 4, 2, 128, torch.bfloat16, seed=77)
+    tile = synth.random_mask_tile(78, torch.float16)
+    td = to_dev(t)
+    out = run_paged(td, qs, ks, 4, 2, synth.MASK_FREE, tile.to(DEV))
+    assert_close(out, oracle_paged(t, qs, ks, 4, 2, synth.MASK_FREE, tile), "mask-free split")
+    assert torch.equal(out, run_two_step(td, qs, ks, 4, 2, synth.MASK_FREE, tile.to(DEV)))
