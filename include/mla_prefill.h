@@ -165,7 +165,12 @@ int mla_prefill_get_workspace_size(const mla_tensor *q, const mla_tensor *q_rope
  * such a workgroup writes its rows over its own keys in fp32 with their
  * log-sum-exp into the workspace (head_dim * 4 + 4 bytes per row and run),
  * and a second kernel on the same stream combines the runs of each row. The
- * result then differs from an unsplit run only by rounding. Errors:
+ * result then differs from an unsplit run only by rounding. Under
+ * MLA_MASK_FREE the workspace also ends with 4 KiB in which a small kernel,
+ * enqueued first, records for each 64-entry block of a mask row whether it
+ * is all zero, all -inf or neither; the attention kernel uses this to skip
+ * the per-element mask on all-zero blocks and to skip all -inf blocks, with
+ * the same result bit for bit. Errors:
  * validation codes as above, MLA_ERR_WORKSPACE, MLA_ERR_RUNTIME when a HIP
  * call fails.
  */

@@ -361,6 +361,7 @@ struct Plan {
     std::vector<Task> tasks;  // one per workgroup, in launch order
     std::vector<MergeRec> merges;  // one per (split item, head pack)
     int32_t n_parts = 0;           // partial slots of the split tasks
+    bool mask_free = false;        // MASK_FREE: the workspace may end with the tile's classes
 };
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
@@ -388,10 +389,20 @@ uint64_t records_bytes(const Plan &p) {
     if (p.merges.empty()) return p.tasks.size() * sizeof(mla::LaunchRec);
     return merges_offset(p) + p.merges.size() * sizeof(MergeRec);
 }
-uint64_t plan_bytes(const Plan &p, int64_t head_dim) {
+uint64_t plan_bytes_no_cls(const Plan &p, int64_t head_dim) {
     if (p.items.empty()) return 0;
     if (p.n_parts == 0) return records_bytes(p);
     return part_o_offset(p) + (uint64_t)p.n_parts * PART_ROWS * (uint64_t)head_dim * 4;
+}
+// MASK_FREE: the classes of the tile's 64-key row blocks (MASK_CLS_BYTES)
+// follow, 256-byte aligned (not in mla_prefill_no_alloc's array: without
+// them every diagonal-block tile takes the per-element path, with the same
+// result bit for bit).
+uint64_t cls_offset(const Plan &p, int64_t head_dim) { return align256(plan_bytes_no_cls(p, head_dim)); }
+uint64_t plan_bytes(const Plan &p, int64_t head_dim, bool with_cls = true) {
+    const uint64_t base = plan_bytes_no_cls(p, head_dim);
+    if (base == 0 || !with_cls || !p.mask_free) return base;
+    return cls_offset(p, head_dim) + mla::MASK_CLS_BYTES;
 }
 
 // log2 of the query heads one task runs: the largest power of two, at most
@@ -448,6 +459,7 @@ void build_plan(const int32_t *q_seqlen, const int32_t *kv_seqlen, int32_t batch
     plan->tasks.clear();
     plan->merges.clear();
     plan->n_parts = 0;
+    plan->mask_free = mask_type == MLA_MASK_FREE;
     const int32_t group = kv_heads > 0 ? heads / kv_heads : 1;
     const int32_t ps = pack_shift_for(heads, kv_heads);
     const int32_t rows = FWD_BM >> ps;
@@ -722,7 +734,8 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     Plan plan;
     build_plan(pr.q_seqlen, pr.kv_seqlen, pr.batch, pr.heads, pr.kv_heads, pr.mask_type, pr.kv_padded_max_seq,
                !use_scratch, &plan);
-    const uint64_t need = plan_bytes(plan, pr.head_dim);
+    const bool with_cls = !use_scratch && pr.mask_type == MLA_MASK_FREE;
+    const uint64_t need = plan_bytes(plan, pr.head_dim, with_cls);
     if (need == 0) return ok();  // no query rows: nothing to write
     if (use_scratch) {
         if (need > MLA_NO_ALLOC_WORKSPACE_BYTES)
@@ -758,6 +771,12 @@ int plan_and_launch(const Problem &pr, const PagedProblem *pg, const int32_t *bl
     p.k_rope = k_rope;
     p.v = v;
     p.mask = (pr.mask_type == MLA_MASK_FREE) ? mask->data : nullptr;
+    if (with_cls) {
+        uint8_t *cls = ws + cls_offset(plan, pr.head_dim);
+        e = mla::launch_mask_classify(mask->data, mask->dtype == MLA_BF16 ? 1 : 0, cls, s);
+        if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "mask tile classes: %s", hipGetErrorString(e));
+        p.mask_cls = cls;
+    }
     p.out = atten_out->data;
     p.launch = static_cast<const mla::LaunchRec *>(workspace);
     if (plan.n_parts > 0) {

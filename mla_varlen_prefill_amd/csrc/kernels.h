@@ -101,6 +101,10 @@ struct FwdParams {
     const void *k_rope;   // rows of Hkv * 64
     const void *v;        // rows of Hkv * D
     const void *mask;     // [512, 512] or nullptr
+    // MASK_FREE: class of each (tile row, 64-key block) of the mask tile,
+    // uint8 [512][8] (MASK_CLS_*), or nullptr (every diagonal-block tile then
+    // takes the per-element path)
+    const uint8_t *mask_cls;
     void *out;            // [nq, H, D]
     const LaunchRec *launch;  // one record per workgroup
     float *part_o;            // partial rows: [parts, PART_ROWS, head_dim] fp32 (tasks with part >= 0)
@@ -133,6 +137,12 @@ static_assert(PAGED_MAX_TILES <= (1 << (31 - PAGED_SEQ_BITS)), "first tile must 
 
 // dtype: 1 = fp16, 2 = bf16 (enum mla_dtype). One workgroup per task.
 hipError_t launch_mla_fwd(const FwdParams &p, int dtype, bool paged, hipStream_t stream);
+
+// Classes of the MASK_FREE tile's 64-entry row blocks: every entry +-0, every
+// entry -inf, or anything else.
+constexpr uint8_t MASK_CLS_ZERO = 0, MASK_CLS_MIXED = 1, MASK_CLS_DEAD = 2;
+constexpr int MASK_CLS_BYTES = 512 * 8;
+hipError_t launch_mask_classify(const void *mask, int mask_is_bf16, uint8_t *cls, hipStream_t stream);
 
 struct MergeParams {
     const MergeRec *merges;

@@ -297,6 +297,12 @@ void mla_fwd_kernel(const FwdParams p) {
     const int pos = wpos0 + r32;                    // ... and of this lane's row
     const int wpos1 = wpos0 + 31;
 
+    // MASK_FREE: this lane's row of the tile classes (see the tile visibility
+    // below), loaded ahead of the DMA so that its latency overlaps theirs
+    uint64_t mask_cls_row = 0;
+    if (MF && p.mask_cls != nullptr)
+        mask_cls_row = *reinterpret_cast<const uint64_t *>(p.mask_cls + (size_t)(pos & (MASK_TILE - 1)) * 8);
+
     // ---- Q and Q-rope of the wave's 32 rows go HBM -> LDS by DMA, whole rows
     // per instruction (4 rows of Q-nope, or 8 of Q-rope, per 1 KB), into the
     // wave's staging slot; they are read back into VGPRs below as the B
@@ -565,6 +571,27 @@ void mla_fwd_kernel(const FwdParams p) {
     } else if (MF) {
         kt_vis = min(n_kt, wpos1 >= 0 ? ((wpos1 >> 9) + 1) * (MASK_TILE / BN) : 0);
         kt_full = min(kt_full, wpos0 >= 0 ? (wpos0 >> 9) * (MASK_TILE / BN) : 0);
+    }
+    // MASK_FREE with a classified tile, the wave's rows all in one 512-key
+    // block: within that block, a leading run of 64-key tiles whose tile
+    // entries are 0 for every row of the wave is whole (a zero entry gives
+    // the unmasked arguments bit for bit), and tiles past the last one with
+    // any entry other than -inf for some row are invisible (such a tile
+    // changes no row's state). With the causal tile this gives the causal
+    // mode's counts.
+    if (MF && p.mask_cls != nullptr && wpos0 >= 0 && (wpos0 >> 9) == (wpos1 >> 9)) {
+        uint64_t zero_bits = 0, live_bits = 0;  // tile k of the block: zero for every row / live for some row
+#pragma unroll
+        for (int k = 0; k < MASK_TILE / BN; ++k) {
+            const uint32_t c = (uint32_t)(mask_cls_row >> (8 * k)) & 0xffu;
+            if (__builtin_amdgcn_ballot_w64(c == MASK_CLS_ZERO) == ~0ull) zero_bits |= 1ull << k;
+            if (__builtin_amdgcn_ballot_w64(c != MASK_CLS_DEAD) != 0ull) live_bits |= 1ull << k;
+        }
+        const int diag0 = (wpos0 >> 9) * (MASK_TILE / BN);
+        const int run = __builtin_ctzll(~zero_bits);  // leading tiles zero for every row (at most 8)
+        const int live = live_bits != 0 ? 63 - __builtin_clzll(live_bits) : -1;  // last live tile, or -1
+        kt_full = min(kv_len / BN, diag0 + run);
+        kt_vis = min(kt_vis, diag0 + live + 1);
     }
     kt_vis = __builtin_amdgcn_readfirstlane(kt_vis);
     kt_full = __builtin_amdgcn_readfirstlane(kt_full);
@@ -1123,7 +1150,36 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256))) void mla_merge
                                           ((tok * p.heads + h) * DN + 4 * c) * 2) = o4;
 }
 
+// ---- MASK_FREE tile classes: thread (row, block) looks at the 64 entries
+// of its row block (128 bytes) and writes MASK_CLS_ZERO if all are +-0,
+// MASK_CLS_DEAD if all are -inf, else MASK_CLS_MIXED.
+__global__ __launch_bounds__(256) void mask_classify_kernel(const unsigned short *mask, int is_bf16, uint8_t *cls) {
+    const int q = blockIdx.x * 256 + threadIdx.x;  // row * 8 + block
+    if (q >= MASK_TILE * (MASK_TILE / BN)) return;
+    const unsigned short ninf = is_bf16 ? 0xff80u : 0xfc00u;
+    const uint4 *src = reinterpret_cast<const uint4 *>(mask + (size_t)(q >> 3) * MASK_TILE + (q & 7) * BN);
+    bool zero = true, dead = true;
+#pragma unroll
+    for (int i = 0; i < BN / 8; ++i) {
+        const uint4 v = src[i];
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned short lo = (unsigned short)(w[j] & 0xffffu), hi = (unsigned short)(w[j] >> 16);
+            zero = zero && (lo & 0x7fffu) == 0 && (hi & 0x7fffu) == 0;
+            dead = dead && lo == ninf && hi == ninf;
+        }
+    }
+    cls[q] = zero ? MASK_CLS_ZERO : (dead ? MASK_CLS_DEAD : MASK_CLS_MIXED);
+}
+
 }  // namespace
+
+hipError_t launch_mask_classify(const void *mask, int mask_is_bf16, uint8_t *cls, hipStream_t stream) {
+    hipLaunchKernelGGL(mask_classify_kernel, dim3(MASK_TILE * (MASK_TILE / BN) / 256), dim3(256), 0, stream,
+                       static_cast<const unsigned short *>(mask), mask_is_bf16, cls);
+    return hipGetLastError();
+}
 
 hipError_t launch_mla_merge(const MergeParams &p, int dtype, hipStream_t stream) {
     if (p.n_merges <= 0) return hipSuccess;

@@ -749,3 +749,15 @@ def test_prolog_prepacked_errors_before_any_launch():
     with pytest.raises(mla.MlaError) as e:
         mla.mla_prolog_weights_size(a["wq_a"], a["wq_b"], a["wkv"][:, :256].contiguous())
     assert e.value.status == "MLA_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("case", [((17, 40), (17, 40), 4, 4), ((3000, 5), (5000, 700), 2, 1)])
+def test_mask_free_workspace_ends_with_the_tile_classes(case):
+    # MASK_FREE: after the plan's arrays, 256-byte aligned, one class byte per
+    # (tile row, 64-key block): 512 * 8 bytes
+    qs, ks, h, hk = case
+    up = lambda x: -(-x // 256) * 256
+    _, items, tasks = mla.mla_prefill_plan_host(list(qs), list(ks), h, hk, mla.MASK_FREE)
+    t = tensors(qs=qs, ks=ks, h=h, hk=hk)
+    t.update(mask=torch.zeros(512, 512, dtype=torch.float16), mask_type=mla.MASK_FREE)
+    assert ws_size(t) == up(split_workspace_bytes(items, tasks, 128)) + 512 * 8
