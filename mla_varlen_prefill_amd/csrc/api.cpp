@@ -945,6 +945,22 @@ int32_t prolog_first_splits(const PrologProblem &pp) {
     }
     return (int32_t)ks;
 }
+// The kv tile (x . wkv) moves from the first product's launch to the
+// second's, its workgroups first, where that takes a round of workgroups off
+// the first launch: one product workgroup fills a CU (its LDS ring), so the
+// first launch runs ceil(tiles * row tiles / CUs) rounds of workgroups over
+// K = h, and its kv tiles then cost the second launch (many rounds over
+// K = q_lora_rank) their share, row tiles / CUs of such a round. bf16 only
+// (the quantised second product is int8), and never with a split first
+// product. The kv tile's arithmetic is the same either way.
+bool prolog_kv_with_second(const PrologProblem &pp, bool quant) {
+    if (quant || prolog_first_splits(pp) > 1) return false;
+    const int64_t cus = (int64_t)MLA_XCDS * MLA_CUS_PER_XCD;
+    const int64_t m_tiles = (pp.t + mla::PROLOG_BM - 1) / mla::PROLOG_BM;
+    const int64_t a_tiles = pp.r / mla::PROLOG_BN;
+    auto rounds = [&](int64_t tiles) { return (tiles * m_tiles + cus - 1) / cus; };
+    return rounds(a_tiles + 1) > rounds(a_tiles) && m_tiles < cus;
+}
 uint64_t prolog_part_bytes(const PrologProblem &pp) {
     const int32_t ks = prolog_first_splits(pp);
     if (ks <= 1) return 0;
@@ -958,11 +974,13 @@ uint64_t prolog_workspace_bytes(const PrologProblem &pp, bool quant = false) {
 
 // The first product, x . [wq_a | wkv], shared by both prolog operators: the
 // wq_a tiles store fp32 rows for the c^Q norm, the wkv tile is the kv row
-// (norm * gamma_ckv, rope).
+// (norm * gamma_ckv, rope). With kv_later the wkv tile is packed here but
+// not run (the second product's launch runs it).
 int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, const mla_tensor *wq_a,
                          const mla_tensor *wkv, const mla_tensor *rope_cos, const mla_tensor *rope_sin,
                          const mla_tensor *gamma_ckv, float eps, const mla_tensor *kv_out, float *y_q,
-                         unsigned char *pack_a, unsigned char *pack_kv, float *part, bool pack, hipStream_t s) {
+                         unsigned char *pack_a, unsigned char *pack_kv, float *part, bool pack, bool kv_later,
+                         hipStream_t s) {
     mla::PrologGemmParams g1{};
     g1.a = token_x->data;
     g1.lda = pp.h;
@@ -983,6 +1001,7 @@ int prolog_first_product(const PrologProblem &pp, const mla_tensor *token_x, con
         e = mla::launch_prolog_pack(g1, s);
         if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 1: %s", hipGetErrorString(e));
     }
+    if (kv_later) g1.seg[1].n_tiles = 0;
     e = mla::launch_prolog_gemm(g1, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 1: %s", hipGetErrorString(e));
     if (g1.k_splits > 1) {
@@ -1093,8 +1112,9 @@ int prolog_call(bool quant, const mla_tensor *token_x, const mla_tensor *wq_a, c
         part = reinterpret_cast<float *>(wsb + prolog_yq_bytes(pp));
     }
 
+    const bool kv_later = prolog_kv_with_second(pp, quant);
     rc = prolog_first_product(pp, token_x, wq_a, wkv, rope_cos, rope_sin, gamma_ckv, eps, kv_out, y_q, pack_a,
-                              pack_kv, part, pack, s);
+                              pack_kv, part, pack, kv_later, s);
     if (rc) return rc;
     hipError_t e;
     float *scale = quant ? static_cast<float *>(qr_scale_out->data) : nullptr;
@@ -1106,7 +1126,7 @@ int prolog_call(bool quant, const mla_tensor *token_x, const mla_tensor *wq_a, c
                                         eps, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog c^Q norm: %s", hipGetErrorString(e));
     // c^Q . wq_b (int8 with quant: dequantisation first): one tile per head
-    // (norm per head, weight 1, rope)
+    // (norm per head, weight 1, rope); with kv_later also the kv tile, on x
     mla::PrologGemmParams g2{};
     g2.a = qr_out->data;
     g2.lda = pp.r;
@@ -1126,6 +1146,13 @@ int prolog_call(bool quant, const mla_tensor *token_x, const mla_tensor *wq_a, c
     if (pack) {
         e = mla::launch_prolog_pack(g2, s);
         if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog weight packing 2: %s", hipGetErrorString(e));
+    }
+    if (kv_later) {
+        g2.seg[1] = {wkv->data, mla::PROLOG_BN, pack_kv, 1, mla::PROLOG_NORM_ROPE, kv_out->data, mla::PROLOG_BN,
+                     gamma_ckv->data};
+        g2.a1 = token_x->data;
+        g2.lda1 = pp.h;
+        g2.k1 = (int32_t)pp.h;
     }
     e = mla::launch_prolog_gemm(g2, s);
     if (e != hipSuccess) return fail(MLA_ERR_RUNTIME, "prolog product 2: %s", hipGetErrorString(e));

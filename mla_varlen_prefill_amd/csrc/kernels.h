@@ -237,6 +237,14 @@ struct PrologGemmParams {
     int32_t k_splits;
     float *part;
     int64_t ld_part;
+    // bf16 only, k_splits 1: when a1 is set, seg[1] reads its own activation
+    // a1 [M, lda1] over K = k1 (a multiple of PROLOG_K_MULTIPLE, its packed
+    // weights laid out for k1), and its workgroups come first in the launch.
+    // launch_prolog_pack does not take this form (pack such a segment with
+    // its own a, lda and k).
+    const void *a1;
+    int64_t lda1;
+    int32_t k1;
 };
 // An int8 stage is 64 k: the same 64 bytes per row as a bf16 stage of 32 k.
 constexpr int PROLOG_K_MULTIPLE_I8 = 256;

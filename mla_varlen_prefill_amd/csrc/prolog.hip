@@ -199,16 +199,24 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
 
     // ---- which tile. When the column tiles split evenly over the 8 XCDs,
     // XCD x takes column tiles x, x + 8, ... one after another, all row
-    // tiles of each: its CUs then share one weight tile in L2.
-    const int n_tiles = p.seg[0].n_tiles + p.seg[1].n_tiles;
+    // tiles of each: its CUs then share one weight tile in L2. A second
+    // segment with an operand of its own (a1) goes first, tile by tile: its
+    // workgroups are the launch's longest, and a multiple of 8 of them keeps
+    // the first segment's blocks on the same XCDs.
+    const bool lead = !I8 && p.a1 != nullptr;
+    const int n_tiles = lead ? p.seg[0].n_tiles : p.seg[0].n_tiles + p.seg[1].n_tiles;
     const int m_tiles = (p.m + BM - 1) / BM;
+    const int lead_blocks = lead ? p.seg[1].n_tiles * m_tiles : 0;
     // split over K: the k_splits workgroups of a tile are consecutive
     const bool split_k = !I8 && p.k_splits > 1;
     const int n_splits = split_k ? p.k_splits : 1;
     const int split = (int)blockIdx.x % n_splits;
-    const int blk = (int)blockIdx.x / n_splits;
+    int blk = (int)blockIdx.x / n_splits;
     int tn, tm;
-    if (n_tiles % 8 == 0) {
+    if (blk < lead_blocks) {
+        tn = p.seg[0].n_tiles + blk / m_tiles;
+        tm = blk % m_tiles;
+    } else if ((blk -= lead_blocks, n_tiles % 8 == 0)) {
         const int s = blk >> 3;
         tn = (blk & 7) + 8 * (s / m_tiles);
         tm = s % m_tiles;
@@ -217,6 +225,10 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
         tm = blk / n_tiles;
     }
     const bool second = tn >= p.seg[0].n_tiles;
+    const bool own_a = lead && second;
+    const void *a_ptr = own_a ? p.a1 : p.a;
+    const int64_t lda = own_a ? p.lda1 : p.lda;
+    const int32_t k_len = own_a ? p.k1 : p.k;
     const int tj = second ? tn - p.seg[0].n_tiles : tn;
     const unsigned char *wpk = static_cast<const unsigned char *>(second ? p.seg[1].wp : p.seg[0].wp);
     const int epilogue = second ? p.seg[1].epilogue : p.seg[0].epilogue;
@@ -225,7 +237,7 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     const unsigned char *gamma = static_cast<const unsigned char *>(second ? p.seg[1].gamma : p.seg[0].gamma);
     const int m0 = tm * BM;
     const int rows = min(BM, p.m - m0);
-    const int nk_all = p.k * ESZ / (BK * 2);  // 64-byte stages
+    const int nk_all = k_len * ESZ / (BK * 2);  // 64-byte stages
     const int nk = nk_all / n_splits;         // this workgroup's stages: [kbase, kbase + nk)
     const int kbase = split * nk;
     // int8: the dequantisation scales go out now and are used by the
@@ -243,10 +255,10 @@ void prolog_gemm_kernel(const PrologGemmParams p) {
     // ---- activation stage: 128 rows x 64 bytes; LDS slot tid (row tid / 4,
     // physical chunk tid % 4) receives logical chunk (tid % 4) ^ ((row >> 2)
     // & 3). Rows past the end read as zeros.
-    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(p.a) + (int64_t)m0 * p.lda * ESZ + (int64_t)kbase * 64,
-                               (uint32_t)rows * (uint32_t)p.lda * ESZ - (uint32_t)kbase * 64);
+    const i32x4 ra = make_rsrc(static_cast<const unsigned char *>(a_ptr) + (int64_t)m0 * lda * ESZ + (int64_t)kbase * 64,
+                               (uint32_t)rows * (uint32_t)lda * ESZ - (uint32_t)kbase * 64);
     const int xr = tid >> 2;
-    const uint32_t xoff = (uint32_t)xr * (uint32_t)p.lda * ESZ + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
+    const uint32_t xoff = (uint32_t)xr * (uint32_t)lda * ESZ + ((((tid & 3) ^ ((xr >> 2) & 3))) << 4);
     // ---- weight stage: block kt of this tile's packed weights, 2048 16-byte
     // slots; load r of a thread takes slot 512 r + tid. Stages past K read
     // as zeros (a split's activation stages past its end read real values,
@@ -727,6 +739,7 @@ __global__ __launch_bounds__(256) void prolog_quant_rows_kernel(const float *y, 
 }  // namespace
 
 hipError_t launch_prolog_pack(const PrologGemmParams &p, hipStream_t stream) {
+    if (p.a1 != nullptr) return hipErrorInvalidValue;
     const int32_t nk = p.k / (p.int8 ? 2 * PROLOG_BK : PROLOG_BK);
     for (int i = 0; i < 2; ++i) {
         const PrologSegment &sg = p.seg[i];
@@ -748,6 +761,7 @@ hipError_t launch_prolog_gemm(const PrologGemmParams &p, hipStream_t stream) {
     const int m_tiles = (p.m + PROLOG_BM - 1) / PROLOG_BM;
     if (p.m <= 0 || n_tiles <= 0) return hipSuccess;
     const unsigned splits = (!p.int8 && p.k_splits > 1) ? (unsigned)p.k_splits : 1u;
+    if (p.a1 != nullptr && (p.int8 || splits > 1 || p.seg[1].n_tiles <= 0)) return hipErrorInvalidValue;
     if (p.int8)
         hipLaunchKernelGGL(prolog_gemm_kernel<true>, dim3((unsigned)(n_tiles * m_tiles)), dim3(NT), 0, stream, p);
     else

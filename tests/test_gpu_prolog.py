@@ -11,7 +11,9 @@ Covered: the page's sizes at several t (one token, ragged tails of the
 128-row tile, several tiles), other head counts (the column tiles not a
 multiple of 8, which changes the launch's tile order), a smaller
 q_lora_rank and h, row independence (a row's bits do not depend on the other
-rows), and the measured 16384-token workload on sampled rows.
+rows), the measured 16384-token workload on sampled rows, and the kv tile
+run in the second product's launch (bit-exact against a call that runs it in
+the first).
 """
 import numpy as np
 import pytest
@@ -118,6 +120,29 @@ def test_prolog_workload_sampled():
     assert_close(q[idx], rq, "workload q")
     assert_close(kv[idx], rkv, "workload kv")
     assert_close(cq[idx], rcq, "workload c^Q")
+
+
+def test_prolog_kv_tile_in_second_launch_is_bit_exact():
+    # At the page's sizes from 86 to 128 row tiles (about 10.9K to 16K tokens)
+    # the kv tile runs in the second product's launch, ahead of the head
+    # tiles. Same arithmetic: the first 8192 rows of the 16384-token call
+    # equal an 8192-token call (kv tile in the first launch; neither call
+    # splits the first product over K) bit for bit, and so does the
+    # prepacked operator.
+    t, n = synth.PROLOG_TOKENS, 8192
+    _say(f"[gpu] prolog kv tile placement, {t} vs {n} tokens")
+    d = synth.prolog_inputs(t, seed=41, device=DEV)
+    full = run_gpu(d)
+    part = {k: (v[:n].contiguous() if k in ("token_x", "rope_cos", "rope_sin") else v) for k, v in d.items()}
+    sub = run_gpu(part)
+    for name, a, b in zip(("q", "kv", "cq"), full, sub):
+        assert torch.equal(a[:n], b), name
+    packed = mla.pack_prolog_weights(d["wq_a"], d["wq_b"], d["wkv"])
+    got = mla.prolog(d["token_x"], d["wq_a"], d["wq_b"], d["wkv"], d["rope_cos"], d["rope_sin"], d["gamma_cq"],
+                     d["gamma_ckv"], synth.PROLOG_EPS, packed=packed)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("q", "kv", "cq"), full, got):
+        assert torch.equal(a, b), "prepacked " + name
 
 
 def test_prolog_rope_tables_with_unequal_pair_entries():
