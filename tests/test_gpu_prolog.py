@@ -122,16 +122,18 @@ def test_prolog_workload_sampled():
     assert_close(cq[idx], rcq, "workload c^Q")
 
 
-def test_prolog_kv_tile_in_second_launch_is_bit_exact():
-    # At the page's sizes from 86 to 128 row tiles (about 10.9K to 16K tokens)
-    # the kv tile runs in the second product's launch, ahead of the head
-    # tiles. Same arithmetic: the first 8192 rows of the 16384-token call
-    # equal an 8192-token call (kv tile in the first launch; neither call
-    # splits the first product over K) bit for bit, and so does the
-    # prepacked operator.
-    t, n = synth.PROLOG_TOKENS, 8192
-    _say(f"[gpu] prolog kv tile placement, {t} vs {n} tokens")
-    d = synth.prolog_inputs(t, seed=41, device=DEV)
+@pytest.mark.parametrize("t,heads", [(synth.PROLOG_TOKENS, 64), (11008, 3)], ids=["page-16384", "3-heads-11008"])
+def test_prolog_kv_tile_in_second_launch_is_bit_exact(t, heads):
+    # From 86 to 128 row tiles (about 10.9K to 16K tokens at these sizes) the
+    # kv tile runs in the second product's launch, ahead of the head tiles
+    # (3 heads: the head tiles not a multiple of 8, the other tile order).
+    # Same arithmetic: the first 8192 rows equal an 8192-token call (kv tile
+    # in the first launch; neither call splits the first product over K) bit
+    # for bit, and so does the prepacked operator; sampled rows match the
+    # oracle.
+    n = 8192
+    _say(f"[gpu] prolog kv tile placement, {t} vs {n} tokens, {heads} heads")
+    d = synth.prolog_inputs(t, num_heads=heads, seed=41, device=DEV)
     full = run_gpu(d)
     part = {k: (v[:n].contiguous() if k in ("token_x", "rope_cos", "rope_sin") else v) for k, v in d.items()}
     sub = run_gpu(part)
@@ -143,6 +145,12 @@ def test_prolog_kv_tile_in_second_launch_is_bit_exact():
     torch.cuda.synchronize()
     for name, a, b in zip(("q", "kv", "cq"), full, got):
         assert torch.equal(a, b), "prepacked " + name
+    rows = np.array(sorted({0, n - 1, n, t - 1} | set(np.random.default_rng(43).integers(0, t, 12).tolist())),
+                    np.int64)
+    rq, rkv, rcq = run_oracle(d, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    for got_, ref, what in ((full[0][idx], rq, "q"), (full[1][idx], rkv, "kv"), (full[2][idx], rcq, "c^Q")):
+        assert_close(got_, ref, what)
 
 
 def test_prolog_rope_tables_with_unequal_pair_entries():
